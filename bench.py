@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked gated-delta-rule forward pass on one MI355X.
+
+One step = one gdn_chunk_fwd call over the main workload (B=4, H=16, T=8192,
+d_k=d_v=128, C=64, bf16 q/k/v, fp32 gates, zero initial state, fp32 final
+state), inputs resident in HBM before the timed region.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                  [--no-decode] [--pmc-pass]
+  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   (writes the HBM-traffic
+                  summary under profiles/ from two rocprofv3 --pmc runs)
+
+Roofline: the dominant (only) kernel of a step is chunk_fwd_kernel; its
+algorithmic bytes per launch are the minimal HBM traffic: read q, k, v
+(bf16), alpha, beta (fp32) once, write o (bf16) and the final state (fp32)
+once.  Its average launch duration is measured with HIP events recorded on
+the stream the kernel is launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MAIN = dict(B=4, H=16, T=8192, d=128, C=64, seed=3)
+DECODE = dict(N=256, H=16, d=128, steps=64, seed=5)
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chunk_fwd_main.txt")
+KERNEL_SOURCES = ["gdn_common.hpp", "chunk_fwd.hpp", "gdn_api.hip"]
+
+
+def alg_bytes_main(B, H, T, d):
+    tok = B * H * T
+    return tok * d * 2 * 3 + tok * 4 * 2 + tok * d * 2 + B * H * d * d * 4
+
+
+def alg_flops_main(B, H, T, d, C):
+    # full C x C tiles: 10*C*d + 6*d^2 per token-head
+    return B * H * T * (10 * C * d + 6 * d * d)
+
+
+def alg_bytes_decode(N, H, d):
+    heads = N * H
+    return 2 * heads * d * d * 4 + heads * (3 * d * 2 + 2 * 4 + d * 2)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gated_deltanet_sequence_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None
+    when it is missing or was taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE, encoding="utf-8") as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def main_inputs(torch, dev):
+    from gated_deltanet_sequence_amd import inputs
+    x = inputs.make_fwd_inputs(MAIN["B"], MAIN["H"], MAIN["T"], MAIN["d"], "bf16",
+                               seed=MAIN["seed"], init_state=False)
+    xd = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
+    return x, xd
+
+
+def time_chunk(torch, xd, steps, warmup):
+    from gated_deltanet_sequence_amd.binding import gdn_chunk_fwd
+    B, H, T, d = xd["q"].shape
+    o = torch.empty_like(xd["v"])
+    sT = torch.empty((B, H, d, d), dtype=torch.float32, device=xd["q"].device)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        gdn_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None, MAIN["C"],
+                      o=o, final_state=sT, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, kms, o, sT
+
+
+def time_decode(torch, dev, steps_override=None):
+    from gated_deltanet_sequence_amd import inputs
+    from gated_deltanet_sequence_amd.binding import gdn_recurrent_step
+    N, H, d, steps = DECODE["N"], DECODE["H"], DECODE["d"], DECODE["steps"]
+    x = inputs.make_decode_inputs(N, H, d, steps, "bf16", seed=DECODE["seed"])
+    state = x["s0"].to(dev)
+    qs = [t.to(dev) for t in x["q"]]
+    ks = [t.to(dev) for t in x["k"]]
+    vs = [t.to(dev) for t in x["v"]]
+    als = [t.to(dev) for t in x["alpha"]]
+    bes = [t.to(dev) for t in x["beta"]]
+    o = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    # warm-up on a scratch copy so the timed 64 steps start from S0
+    scratch = state.clone()
+    for t in range(4):
+        gdn_recurrent_step(qs[t], ks[t], vs[t], als[t], bes[t], scratch, o=o, stream=stream)
+    del scratch
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for t in range(steps):
+        gdn_recurrent_step(qs[t], ks[t], vs[t], als[t], bes[t], state, o=o, stream=stream)
+        ev[t + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[t].elapsed_time(ev[t + 1]) for t in range(steps)]
+    avg_ms = sum(per) / steps
+    byts = alg_bytes_decode(N, H, d)
+    return {"workload": "decode: 256 sequences x H=16, d_k=d_v=128, fp32 state [256,16,128,128] "
+                        "updated in place, bf16 q/k/v, 64 consecutive steps",
+            "tokens_per_s": N / (avg_ms * 1e-3), "ms_per_step": avg_ms,
+            "alg_bytes_per_step": byts, "achieved_GBs": byts / (avg_ms * 1e-3) / 1e9,
+            "hbm_frac": byts / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def cpu_baseline(x, o_gpu, sT_gpu):
+    """The fp64 oracle on the host cores over the whole main workload, plus
+    the parity of this run's GPU output against it."""
+    import numpy as np
+
+    import oracle
+    from gated_deltanet_sequence_amd import inputs
+    f = inputs.to_f32_numpy
+    q, k, v = f(x["q"]), f(x["k"]), f(x["v"])
+    a, b = x["alpha"].numpy(), x["beta"].numpy()
+    cores = oracle.num_threads()
+    t0 = time.perf_counter()
+    ro, rs = oracle.oracle_fwd(q, k, v, a, b, None)
+    dt = time.perf_counter() - t0
+    go = o_gpu.float().cpu().numpy()
+    gs = sT_gpu.cpu().numpy()
+    eo = float(np.max(np.abs(go - ro)) / np.max(np.abs(ro)))
+    es = float(np.max(np.abs(gs - rs)) / np.max(np.abs(rs)))
+    tokens = MAIN["B"] * MAIN["T"]
+    return ({"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+             "sample": "the whole main workload (B=4,H=16,T=8192,d=128: 64 sequences x 8192 "
+                       "tokens), fp64 token loop, %.2f s" % dt},
+            {"max_rel_err_o": eo, "max_rel_err_final_state": es, "tol": 2e-2,
+             "pass": bool(eo <= 2e-2 and es <= 2e-2)})
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Write the traffic summary from two rocprofv3 --pmc runs of
+    `bench.py --pmc-pass` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch)."""
+    import csv
+
+    def read(d, counter):
+        rows = []
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path, newline="") as fh:
+                for r in csv.DictReader(fh):
+                    if r.get("Counter_Name") == counter:
+                        rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return rows
+
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = read(d, counter)
+        copy = [v for n, v in rows if "chunk_fwd_kernel" not in n and "recurrent_step" not in n
+                and v > 100000]
+        chunk = [v for n, v in rows if "chunk_fwd_kernel" in n]
+        if not copy or not chunk:
+            raise SystemExit("no %s rows for the copy and chunk kernels in %s" % (counter, d))
+        out[counter] = (max(copy), sum(chunk) / len(chunk))
+    copy_kib = (1 << 29) / 1024.0  # the copy kernel moves 512 MiB each way
+    f_fetch = copy_kib / out["FETCH_SIZE"][0]
+    f_write = copy_kib / out["WRITE_SIZE"][0]
+    fetch_b = out["FETCH_SIZE"][1] * 1024 * f_fetch
+    write_b = out["WRITE_SIZE"][1] * 1024 * f_write
+    alg = alg_bytes_main(MAIN["B"], MAIN["H"], MAIN["T"], MAIN["d"])
+    lines = [
+        "# HBM traffic of chunk_fwd_kernel, main workload (B=4,H=16,T=8192,d=128,C=64, bf16)",
+        "# from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch):",
+        "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -- python3 bench.py --pmc-pass",
+        "#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -- python3 bench.py --pmc-pass",
+        "#   python3 bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        "# Each counter is scaled by (512 MiB / what it reads for a plain 512 MiB device copy",
+        "# in the same run).",
+        "copy_fetch_kib = %.1f" % out["FETCH_SIZE"][0],
+        "copy_write_kib = %.1f" % out["WRITE_SIZE"][0],
+        "fetch_scale = %.4f" % f_fetch,
+        "write_scale = %.4f" % f_write,
+        "chunk_fetch_kib = %.1f" % out["FETCH_SIZE"][1],
+        "chunk_write_kib = %.1f" % out["WRITE_SIZE"][1],
+        "hbm_fetch_bytes = %d" % fetch_b,
+        "hbm_write_bytes = %d" % write_b,
+        "hbm_bytes_per_launch = %d" % (fetch_b + write_b),
+        "algorithmic_bytes_per_launch = %d" % alg,
+        "traffic_over_algorithmic = %.3f" % ((fetch_b + write_b) / alg),
+        "kernel_source_hash = %s" % kernel_source_hash(),
+    ]
+    with open(TRAFFIC_FILE, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="one 512 MiB copy plus two launches, for rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(each (batch, head) sequence is independent; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    x, xd = main_inputs(torch, dev)
+
+    if args.pmc_pass:
+        src = torch.empty(1 << 28, dtype=torch.float16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        time_chunk(torch, xd, steps=2, warmup=1)
+        torch.cuda.synchronize()
+        print("pmc pass done", flush=True)
+        return
+
+    wall, kms, o, sT = time_chunk(torch, xd, args.steps, args.warmup)
+    B, H, T, d, C = MAIN["B"], MAIN["H"], MAIN["T"], MAIN["d"], MAIN["C"]
+    tokens = B * T
+    ms_per_step = wall * 1e3 / args.steps
+    avg_k = sum(kms) / len(kms)
+    alg_b = alg_bytes_main(B, H, T, d)
+    alg_f = alg_flops_main(B, H, T, d, C)
+    achieved = alg_b / (avg_k * 1e-3) / 1e9
+    res = {
+        "metric": "tokens/s chunked GDN fwd (H16,d128,T8K) + % MFMA/HBM roofline",
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: q,k ~N(0,1) L2-normalised, v ~N(0,1), "
+                "alpha=exp(-softplus(N(0,1))), beta=sigmoid(N(0,1)))",
+        "config": {"workload": "main: B=4, H=16, T=8192, d_k=d_v=128, C=64, bf16 q/k/v, "
+                               "fp32 alpha/beta, zero initial state, fp32 final state",
+                   "B": B, "H": H, "T": T, "d": d, "chunk_size": C},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": read_traffic(),
+                     "kernel": "chunk_fwd_kernel", "alg_bytes_per_launch": alg_b,
+                     "avg_launch_ms": avg_k,
+                     "mfma_achieved_TFLOPs": alg_f / (avg_k * 1e-3) / 1e12,
+                     "mfma_frac": alg_f / (avg_k * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+        "token_heads_per_s": B * H * T / (ms_per_step * 1e-3),
+    }
+    if not args.no_decode:
+        res["decode"] = time_decode(torch, dev)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"], res["parity"] = cpu_baseline(x, o, sT)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

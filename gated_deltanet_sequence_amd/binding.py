@@ -1,0 +1,151 @@
+"""Thin ctypes binding over libgdn.so (C ABI in include/gdn.h).
+
+Argument marshalling only: every step of the forward pass and of the decode
+step runs in the HIP kernels behind the C ABI.  PyTorch provides the device
+memory and the stream.  There is no fallback: if the library is missing or a
+tensor is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import _build
+
+GDN_OK = 0
+GDN_ERR_INVALID_ARG = 1
+GDN_ERR_UNSUPPORTED = 2
+GDN_ERR_ALIGNMENT = 3
+GDN_ERR_HIP = 4
+
+GDN_F32 = 0
+GDN_BF16 = 1
+
+_DTYPES = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
+_lib = None
+
+
+class GDNError(RuntimeError):
+    """A nonzero return code of the C ABI."""
+
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed: %s (code %d)" % (where, strerror(code), code))
+
+
+def load_library(path: str | None = None):
+    """Load libgdn.so (building it first only if no build exists at all)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    lib_path = path or _build.LIB
+    if not os.path.exists(lib_path):
+        _build.build()
+    lib = ctypes.CDLL(lib_path)
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    i32 = ctypes.c_int
+    lib.gdn_chunk_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32, p]
+    lib.gdn_chunk_fwd.restype = i32
+    lib.gdn_recurrent_step.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, p]
+    lib.gdn_recurrent_step.restype = i32
+    lib.gdn_strerror.argtypes = [i32]
+    lib.gdn_strerror.restype = ctypes.c_char_p
+    lib.gdn_version.argtypes = []
+    lib.gdn_version.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load_library().gdn_strerror(int(code)).decode()
+
+
+def version() -> str:
+    return load_library().gdn_version().decode()
+
+
+def _dev_ptr(t, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def gdn_chunk_fwd(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 64, *,
+                  o=None, final_state=None, output_final_state: bool = True, stream=None):
+    """Chunked forward pass.  q, k [B,H,T,dk], v [B,H,T,dv] (bf16 or fp32);
+    alpha, beta [B,H,T] fp32; initial_state [B,H,dv,dk] fp32 or None.
+
+    Returns (o [B,H,T,dv] in the input dtype, final_state [B,H,dv,dk] fp32 or
+    None).  ``final_state`` may be passed (and may be ``initial_state`` itself
+    for an in-place carry)."""
+    if q.dtype not in _DTYPES:
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
+    B, H, T, dk = q.shape
+    dv = v.shape[3]
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H, T):
+            raise ValueError("%s must be fp32 [B,H,T]" % name)
+    if initial_state is not None and (initial_state.dtype != torch.float32 or
+                                      tuple(initial_state.shape) != (B, H, dv, dk)):
+        raise ValueError("initial_state must be fp32 [B,H,dv,dk]")
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    rc = lib.gdn_chunk_fwd(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                           _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                           _dev_ptr(initial_state, "initial_state"), _dev_ptr(o, "o"),
+                           _dev_ptr(final_state, "final_state"), B, H, T, dk, dv,
+                           int(chunk_size), _DTYPES[q.dtype], _stream_ptr(stream, q.device))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gdn_recurrent_step(q, k, v, alpha, beta, state, *, o=None, stream=None):
+    """One decode step.  q, k [N,H,dk], v [N,H,dv] (bf16 or fp32); alpha, beta
+    [N,H] fp32; state [N,H,dv,dk] fp32, updated IN PLACE.  Returns o [N,H,dv]."""
+    if q.dtype not in _DTYPES:
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k must be [N,H,dk] and v [N,H,dv]")
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (N, H):
+            raise ValueError("%s must be fp32 [N,H]" % name)
+    if state.dtype != torch.float32 or tuple(state.shape) != (N, H, dv, dk):
+        raise ValueError("state must be fp32 [N,H,dv,dk]")
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    lib = load_library()
+    rc = lib.gdn_recurrent_step(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                                _dev_ptr(state, "state"), _dev_ptr(o, "o"), N, H, dk, dv,
+                                _DTYPES[q.dtype], _stream_ptr(stream, q.device))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_recurrent_step")
+    return o

@@ -1,0 +1,117 @@
+/*
+ * gdn.h — C ABI of the MI355X (gfx950) gated-delta-rule library (libgdn.so).
+ *
+ * The operation.  Per (batch b, head h) the library carries an fp32 state
+ * S in R^{dv x dk} (row i = value index, column j = key index) through the
+ * gated delta rule
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,
+ *
+ * i.e. per token: decay the state by alpha_t, read r = S k_t, form the
+ * delta-rule error u = beta_t (v_t - r), add u k_t^T, and read o_t from the
+ * updated state.  Sources (web pages, by title and section):
+ *   [P1] "Gated DeltaNet GPU并行实现：拆解线性注意力循环的两种高效方案"
+ *        §2.1 the delta rule S_t = S_{t-1} - beta_t (S_{t-1} k_t - v_t) k_t^T and
+ *        its affine-map form; §2.2 a scalar forgetting gate multiplying the old
+ *        state; §3.2-§3.3 the chunked evaluation (matmuls inside a chunk, the
+ *        state carried serially from chunk to chunk, one workgroup carrying all
+ *        chunks of a sequence); §4.1 inputs in (batch, head, seq_len, d) with d
+ *        contiguous; §4.4 state kept in fp32 while matmul inputs are bf16 with
+ *        fp32 accumulation; §5.2 (second pitfall) non-contiguous or misaligned
+ *        inputs must not be taken silently.
+ *   [P3] "线性注意力机制与Gated DeltaNet的优化实践" §2.1 the output of token i
+ *        includes token i (o_t is read after the update); §3.1 a single-step
+ *        in-place state update kernel on global fp32 memory (the decode step
+ *        below adds the erase term and the output).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or synchronises.  Work is enqueued on
+ *     `hip_stream` (a hipStream_t; NULL = the null stream) and the call
+ *     returns once it is enqueued.  The library holds no state between calls
+ *     and is safe to call from several host threads on different streams.
+ *   - Layouts are dense row-major exactly as written (no strides).  Every
+ *     tensor pointer must be 16-byte aligned.
+ *   - Arguments are validated before anything is launched; on any error no
+ *     device work is enqueued and the call returns a nonzero code.  Faults
+ *     inside a kernel surface at the caller's next synchronisation.
+ *   - Values are not inspected: NaN/Inf propagate.  There is no 1/sqrt(d)
+ *     query scaling and no normalisation of q or k inside the library.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define GDN_OK 0
+#define GDN_ERR_INVALID_ARG 1 /* NULL pointer, negative size, aliasing, bad dtype */
+#define GDN_ERR_UNSUPPORTED 2 /* shape/chunk size this build does not handle      */
+#define GDN_ERR_ALIGNMENT 3   /* a tensor pointer is not 16-byte aligned           */
+#define GDN_ERR_HIP 4         /* the HIP runtime reported an error on launch       */
+
+/* Element type of q, k, v and o.  alpha, beta and every state are fp32. */
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/*
+ * gdn_chunk_fwd — chunked forward pass over T tokens for B*H independent
+ * sequences ([P1] §3.2-§3.3).
+ *
+ *   q, k           [B,H,T,dk]  dtype   queries and keys, d contiguous
+ *   v              [B,H,T,dv]  dtype   values
+ *   alpha          [B,H,T]     fp32    forgetting gate, expected in (0,1]
+ *   beta           [B,H,T]     fp32    write strength, expected in [0,1]
+ *   initial_state  [B,H,dv,dk] fp32    S_0, or NULL for a zero state
+ *   o              [B,H,T,dv]  dtype   OUT: o_t = S_t q_t
+ *   final_state    [B,H,dv,dk] fp32    OUT: S_T, or NULL to skip it.
+ *                                      May alias initial_state (each workgroup
+ *                                      reads its part of S_0 before writing).
+ *   chunk_size     tokens per chunk; this build supports 64.  T need not be a
+ *                  multiple: the missing tokens of the last chunk act as
+ *                  identity maps (alpha = 1, beta = 0) and produce no output.
+ *   dk, dv         64 or 128, dk == dv.
+ *   T              >= 0.  T == 0 writes final_state = initial_state (or zeros).
+ *
+ * `o` must not overlap any input.  Alpha must be > 0: the chunk form works
+ * with log(alpha) (alpha == 0 gives -inf logs and NaN results).
+ */
+int gdn_chunk_fwd(const void* q, const void* k, const void* v,
+                  const float* alpha, const float* beta,
+                  const float* initial_state, void* o, float* final_state,
+                  int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                  int64_t chunk_size, gdn_dtype dtype, void* hip_stream);
+
+/*
+ * gdn_recurrent_step — one decode step: one new token for each of N*H
+ * sequences, applied to the state IN PLACE ([P3] §3.1 analog, with the
+ * erase term of [P1] §2.1 and the output of [P3] §2.1).
+ *
+ *   q, k    [N,H,dk] dtype     v [N,H,dv] dtype
+ *   alpha, beta [N,H] fp32
+ *   state   [N,H,dv,dk] fp32   IN: S_{t-1}, OUT: S_t (updated in place)
+ *   o       [N,H,dv] dtype     OUT: S_t q_t
+ *   dk, dv  64 or 128, dk == dv.  N, H >= 0 (N*H == 0 is a no-op).
+ *
+ * `o` must not overlap any input or the state.
+ */
+int gdn_recurrent_step(const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta, float* state,
+                       void* o, int64_t N, int64_t H, int64_t dk, int64_t dv,
+                       gdn_dtype dtype, void* hip_stream);
+
+/* Static, human-readable text for a return code (never NULL). */
+const char* gdn_strerror(int code);
+
+/* Version of the library as "major.minor.patch" (static string). */
+const char* gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,98 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects every invalid argument with its documented code
+before touching the device.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_sequence_amd import _build
+from gated_deltanet_sequence_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+A = 0x10000          # 16-byte aligned fake device addresses (never dereferenced)
+MB = 1 << 20
+
+
+def declared_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if _build.is_stale():
+        _build.build()
+    return binding.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"gdn_chunk_fwd", "gdn_recurrent_step", "gdn_strerror", "gdn_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror_and_version(lib):
+    for code in range(0, 5):
+        s = binding.strerror(code)
+        assert s and s != "unknown gdn error code"
+    assert binding.strerror(99) == "unknown gdn error code"
+    assert re.match(r"^\d+\.\d+\.\d+$", binding.version())
+
+
+def fwd(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, alpha=A + 192 * MB, beta=A + 200 * MB,
+        s0=None, o=A + 256 * MB, sT=None, B=1, H=1, T=64, dk=64, dv=64, C=64, dtype=1):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gdn_chunk_fwd(P(q), P(k), P(v), P(alpha), P(beta), P(s0), P(o), P(sT),
+                             B, H, T, dk, dv, C, dtype, None)
+
+
+def step(lib, q=A, k=A + MB, v=A + 2 * MB, alpha=A + 3 * MB, beta=A + 4 * MB,
+         state=A + 8 * MB, o=A + 64 * MB, N=1, H=1, dk=64, dv=64, dtype=1):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gdn_recurrent_step(P(q), P(k), P(v), P(alpha), P(beta), P(state), P(o),
+                                  N, H, dk, dv, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(alpha=None), 1),
+    (dict(beta=None), 1), (dict(o=None), 1),
+    (dict(B=-1), 1), (dict(H=-2), 1), (dict(T=-1), 1), (dict(C=0), 1), (dict(dtype=7), 1),
+    (dict(dk=32, dv=32), 2), (dict(dk=64, dv=128), 2), (dict(dk=256, dv=256), 2),
+    (dict(C=32), 2), (dict(C=128), 2), (dict(dtype=0, dk=128, dv=128), 2),
+    (dict(q=A + 8), 3), (dict(v=A + 128 * MB + 2), 3), (dict(o=A + 256 * MB + 4), 3),
+    (dict(s0=A + 300 * MB + 8), 3), (dict(sT=A + 400 * MB + 12), 3),
+    (dict(o=A + 112), 1),                  # output overlaps q
+    (dict(o=A + 192 * MB), 1),             # output overlaps alpha
+    (dict(sT=A + 256 * MB + 16), 1),       # final state overlaps the output
+])
+def test_chunk_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def test_chunk_fwd_empty_is_noop(lib):
+    # no sequences, or no tokens and no state to write: nothing is launched
+    assert fwd(lib, B=0) == 0
+    assert fwd(lib, H=0) == 0
+    assert fwd(lib, T=0, sT=None) == 0
+    assert fwd(lib, B=0, q=None, k=None, v=None, alpha=None, beta=None, o=None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(state=None), 1), (dict(o=None), 1), (dict(N=-1), 1),
+    (dict(dtype=3), 1), (dict(dk=96, dv=96), 2), (dict(dk=64, dv=128), 2),
+    (dict(state=A + 8 * MB + 4), 3), (dict(k=A + MB + 2), 3),
+    (dict(o=A + 8 * MB), 1),               # output overlaps the state
+])
+def test_recurrent_step_rejects(lib, kw, code):
+    assert step(lib, **kw) == code
+
+
+def test_recurrent_step_empty_is_noop(lib):
+    assert step(lib, N=0) == 0
+    assert step(lib, H=0, q=None, state=None, o=None) == 0
