@@ -10,7 +10,7 @@ state), inputs resident in HBM before the timed region.  Prints ONE JSON line.
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   (writes the HBM-traffic
                   summary under profiles/ from two rocprofv3 --pmc runs)
 
-Roofline: the dominant (only) kernel of a step is chunk_fwd_kernel; its
+Roofline: the dominant (only) kernel of a step is chunk_fwd_pipe_kernel; its
 algorithmic bytes per launch are the minimal HBM traffic: read q, k, v
 (bf16), alpha, beta (fp32) once, write o (bf16) and the final state (fp32)
 once.  Its average launch duration is measured with HIP events recorded on
@@ -35,7 +35,7 @@ DECODE = dict(N=256, H=16, d=128, steps=64, seed=5)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chunk_fwd_main.txt")
-KERNEL_SOURCES = ["gdn_common.hpp", "chunk_fwd.hpp", "gdn_api.hip"]
+KERNEL_SOURCES = ["gdn_common.hpp", "chunk_fwd_pipe.hpp", "gdn_api.hip"]
 
 
 def alg_bytes_main(B, H, T, d):
@@ -193,9 +193,9 @@ def summarize_pmc(fetch_dir, write_dir):
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = read(d, counter)
-        copy = [v for n, v in rows if "chunk_fwd_kernel" not in n and "recurrent_step" not in n
+        copy = [v for n, v in rows if "chunk_fwd" not in n and "recurrent_step" not in n
                 and v > 100000]
-        chunk = [v for n, v in rows if "chunk_fwd_kernel" in n]
+        chunk = [v for n, v in rows if "chunk_fwd" in n]
         if not copy or not chunk:
             raise SystemExit("no %s rows for the copy and chunk kernels in %s" % (counter, d))
         out[counter] = (max(copy), sum(chunk) / len(chunk))
@@ -206,7 +206,7 @@ def summarize_pmc(fetch_dir, write_dir):
     write_b = out["WRITE_SIZE"][1] * 1024 * f_write
     alg = alg_bytes_main(MAIN["B"], MAIN["H"], MAIN["T"], MAIN["d"])
     lines = [
-        "# HBM traffic of chunk_fwd_kernel, main workload (B=4,H=16,T=8192,d=128,C=64, bf16)",
+        "# HBM traffic of chunk_fwd_pipe_kernel, main workload (B=4,H=16,T=8192,d=128,C=64, bf16)",
         "# from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch):",
         "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -- python3 bench.py --pmc-pass",
         "#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -- python3 bench.py --pmc-pass",
@@ -296,7 +296,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": read_traffic(),
-                     "kernel": "chunk_fwd_kernel", "alg_bytes_per_launch": alg_b,
+                     "kernel": "chunk_fwd_pipe_kernel", "alg_bytes_per_launch": alg_b,
                      "avg_launch_ms": avg_k,
                      "mfma_achieved_TFLOPs": alg_f / (avg_k * 1e-3) / 1e12,
                      "mfma_frac": alg_f / (avg_k * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},

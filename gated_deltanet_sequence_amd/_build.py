@@ -11,7 +11,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn.so")
 
 SOURCES = ["gdn_api.hip"]
-HEADERS = ["gdn_common.hpp", "chunk_fwd.hpp", "recurrent_step.hpp"]
+HEADERS = ["gdn_common.hpp", "chunk_fwd.hpp", "chunk_fwd_pipe.hpp", "recurrent_step.hpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -21,6 +21,9 @@ HIPCC_FLAGS = [
     "-shared",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the kernels read every accumulator with VALU
+    # ops, and AGPR<->VGPR copies would cost a 4-cycle VALU issue each
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

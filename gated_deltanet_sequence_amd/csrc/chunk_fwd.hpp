@@ -209,19 +209,19 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(
       const bool ok = t < Tlen;
       const float a = ok ? ac[t] : 1.f;
       const float b = ok ? bc[t] : 0.f;
-      float gs = log2f(a);
+      float gs = fast_log2(a);
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(gs, off, 64);
         if (lane >= off) gs += y;
       }
       const float glast = __shfl(gs, 63, 64);
-      const float e = exp2f(gs);
+      const float e = fast_exp2(gs);
       sm.g[lane] = gs;
       sm.beta[lane] = b;
       sm.eg[lane] = e;
       sm.beg[lane] = b * e;
-      sm.el[lane] = exp2f(glast - gs);
+      sm.el[lane] = fast_exp2(glast - gs);
     }
     if (ch + 1 < nchunks) load_chunk(ch + 1);
     __syncthreads();
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(
       for (int e = 0; e < 4; ++e) {
         const int s = s0 + e;
         const bool in = kind == 0 ? (s < r) : (s <= r);
-        const float d = in ? exp2f(gr - sm.g[s]) : 0.f;
+        const float d = in ? fast_exp2(gr - sm.g[s]) : 0.f;
         val[e] = (kind == 0 ? sm.beta[r] : 1.f) * d * acc[e];
       }
       T* dst = kind == 0 ? sm.Lb : sm.P;

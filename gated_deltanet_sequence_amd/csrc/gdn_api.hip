@@ -6,6 +6,7 @@
 
 #include "gdn.h"
 #include "chunk_fwd.hpp"
+#include "chunk_fwd_pipe.hpp"
 #include "recurrent_step.hpp"
 
 namespace {
@@ -36,6 +37,19 @@ int launch_chunk(const void* q, const void* k, const void* v, const float* alpha
   hipLaunchKernelGGL((gdn::chunk_fwd_kernel<E, DK, DVS, C, NW>), dim3((unsigned)nblocks),
                      dim3(NW * 64), 0, stream, static_cast<const E*>(q), static_cast<const E*>(k),
                      static_cast<const E*>(v), alpha, beta, s0, static_cast<E*>(o), sT,
+                     (int)nchain, T, (int)dv, xcd_map);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int launch_chunk_pipe(const void* q, const void* k, const void* v, const float* alpha,
+                      const float* beta, const float* s0, void* o, float* sT, int64_t nchain,
+                      int64_t T, int64_t dv, hipStream_t stream) {
+  const int64_t nblocks = nchain * (dv / gdn::pipe::DVS);
+  if (nblocks > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+  const int xcd_map = (nchain % 8) == 0;
+  hipLaunchKernelGGL(gdn::pipe::chunk_fwd_pipe_kernel, dim3((unsigned)nblocks), dim3(256), 0,
+                     stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                     static_cast<const bf16_t*>(v), alpha, beta, s0, static_cast<bf16_t*>(o), sT,
                      (int)nchain, T, (int)dv, xcd_map);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -96,8 +110,8 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (dtype == GDN_BF16) {
     if (dk == 128)
-      return launch_chunk<bf16_t, 128, 32, 64, 4>(q, k, v, alpha, beta, initial_state, o,
-                                                  final_state, nchain, T, dv, stream);
+      return launch_chunk_pipe(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv,
+                               stream);
     return launch_chunk<bf16_t, 64, 16, 64, 4>(q, k, v, alpha, beta, initial_state, o,
                                                final_state, nchain, T, dv, stream);
   }

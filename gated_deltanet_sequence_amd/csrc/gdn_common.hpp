@@ -25,13 +25,20 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t x) {
   return __uint_as_float(((uint32_t)x) << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 (NaN stays NaN).
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware:
+// v_cvt_pk_bf16_f32; NaN stays NaN).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two fp32 values -> packed bf16 pair (low half = a), one conversion instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// Native base-2 exponential / logarithm (v_exp_f32 / v_log_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 template <class T> struct Elem;
 template <> struct Elem<bf16_t> {
@@ -48,10 +55,7 @@ template <class T> struct Pack4;
 template <> struct Pack4<bf16_t> {
   typedef uint2 type;
   static __device__ __forceinline__ uint2 make(float a, float b, float c, float d) {
-    uint2 r;
-    r.x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-    r.y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
-    return r;
+    return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
   }
 };
 template <> struct Pack4<float> {
