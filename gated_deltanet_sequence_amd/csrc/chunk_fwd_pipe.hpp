@@ -18,42 +18,35 @@
 //   O = diag(2^g) Q S^T + P U
 //   S' = 2^(g_C) S + U^T diag(2^(g_C - g)) K
 //
-// Workgroup = 4 waves (one per SIMD), one (sequence, 32-row value slice) per
-// workgroup, one barrier per period.  In period p:
-//   wave 0 (state)   runs the S-dependent part of chunk p.  The fp32 state
-//                    slice stays in MFMA accumulators for the whole sequence,
-//                    and so do Z = K S^T, Y, U and O: an accumulator tile holds
-//                    4 consecutive rows per lane, so two vertically adjacent
-//                    tiles are a valid 32-deep MFMA operand once the k index is
-//                    permuted as kappa(g, e) = e < 4 ? 4g + e : 16 + 4g + e - 4.
-//                    The LDS operands it meets (Q, K, P, Ti) are stored with
-//                    their columns in that same kappa order.
-//   wave 1 (stage+P) writes chunk p+1 (K, Q, V^T, gate tables) into LDS from
-//                    registers loaded one period earlier, issues the loads of
-//                    chunk p+2, and builds P for chunk p+1.
-//   wave 2 (inverse) builds Ti = (I + L)^-1 of chunk p+1 from L.
-//   wave 3 (L)       builds L of chunk p+2 from keys it loaded one period
-//                    earlier, then issues the loads of chunk p+3.
-// Every buffer a wave writes in period p is read by another wave only after
-// the barrier that ends period p, and no buffer is rewritten while another wave
-// still reads it (double buffering by chunk parity).
+// Workgroup = 6 waves, one (sequence, 32-row value slice) per workgroup, one
+// workgroup barrier per period.  Waves 0..3 run on four different SIMDs and
+// wave 4 (5) shares the SIMD of wave 0 (1).  In period p:
+//   waves 0, 1 (state)  each own 16 rows of the value slice.  They finish the
+//                       output of chunk p-1 (O += P U) and run the S-dependent
+//                       part of chunk p.  The fp32 state stays in MFMA
+//                       accumulators for the whole sequence.
+//   wave 2 (P)          builds P of chunk p and touches the cache lines of
+//                       chunk p+6 so that later loads hit L2.
+//   wave 3 (L)          builds L and the gate tables of chunk p+2 from keys and
+//                       gates it loaded one period earlier, then loads p+3.
+//   wave 4 (inverse)    builds Ti = (I + L)^-1 of chunk p+1.
+//   wave 5 (loader)     moves K, Q, V of chunk p+1 into LDS with LDS-DMA loads
+//                       and waits for them.
+// Every buffer written in period p is read by another wave only after the
+// barrier that ends period p, and none is rewritten while another wave still
+// reads it (double buffering by chunk parity).
 //
-// Cost model this code is written for (gfx950, measured): a wave64 VALU op
-// occupies its SIMD for 4 cycles and a 16x16x32 bf16 MFMA for 16, so every
-// role keeps its per-chunk VALU count small: LDS addresses are per-lane bases
-// fixed before the chunk loop plus compile-time offsets, and global traffic
-// goes through buffer instructions whose descriptors hold the sequence base in
-// scalar registers.  Reads past the end of a sequence return zero and stores
-// past it are dropped by the buffer range check, so the ragged last chunk
-// needs no per-element predicates.
-//
-// LDS layout.  K and Q tiles are 64 rows x 128 columns (bf16) with the
-// columns of each 32-column block in kappa order; the sixteen 16-byte octets
-// of a row are XOR-swizzled by f(row) = ((row & 3) << 2) | ((row >> 2) & 3),
-// which keeps both the 16-lane b128 fragment reads (16 consecutive rows, one
-// octet) and the transposed 8-byte reads (4 consecutive rows x 4 chunks) free
-// of bank conflicts.  P and Ti are 64 x 64 with kappa-ordered columns and
-// octets swizzled by (row >> 1) & 7.
+// Operand layouts.  An MFMA accumulator tile gives each lane 4 consecutive
+// rows of one column; two vertically adjacent tiles form one 32-deep operand
+// whose k index runs kappa(g, e) = e < 4 ? 4g + e : 16 + 4g + e - 4 over the
+// lane's eight values.  The key index of the state is relabelled so that this
+// kappa order is the natural column order of q and k: internal key
+// 32b + 16h + 4a + e is global key 32b + 8a + 4h + e.  Hence K and Q sit in
+// LDS in their global layout (rows of 256 bytes, 16-byte octets XOR-swizzled
+// per row) and the relabelling only touches the addresses of the initial and
+// final state.  Token-indexed operands (P, Ti) keep kappa order where an
+// accumulator meets them.  Transposed operands (K^T, V^T, Ti) come from the
+// gfx950 transposed LDS read.
 #pragma once
 
 #include "gdn_common.hpp"
@@ -63,33 +56,45 @@ namespace pipe {
 
 constexpr int C = 64;
 constexpr int DK = 128;
-constexpr int DVS = 32;
-constexpr int LDT = 72;  // padded stride (elements) of 64-wide scratch rows
-constexpr int LDD = 20;  // stride (floats) of the fp32 diagonal blocks of L
+constexpr int DVS = 32;   // value columns per workgroup
+constexpr int NWAVES = 6;
+constexpr int TTS = 72;   // row stride (elements) of Ti^T
+constexpr int LDR = 20;   // row stride (floats) of the fp32 diagonal blocks of L
 
 enum { G_BETA = 0, G_BEG = 1, G_EG = 2, G_EL = 3, G_LOG = 4, G_N = 5 };
 
+// Lower bound applied to log2(alpha): a gate of 0 then gives decay factors
+// that are 0 in fp32 without turning differences of prefix sums into NaN.
+constexpr float LOG2_ALPHA_MIN = -200.f;
+
+// Wave 2 touches every 128-byte line of chunk p + PREFETCH_AHEAD in period p,
+// so that the loads of the later periods find their lines in L2.
+constexpr int PREFETCH_AHEAD = 6;
+
+// Targets of LDS-DMA loads are arrays of their own: the compiler then sees
+// that the LDS reads which follow such a load in the same wave touch other
+// objects, and does not wait for the load before them.
+__shared__ __attribute__((aligned(16))) bf16_t lds_K[2][C * DK];  // [token][key], octets swizzled by swz_kq(token)
+__shared__ __attribute__((aligned(16))) bf16_t lds_Q[2][C * DK];
+__shared__ __attribute__((aligned(16))) bf16_t lds_V[2][C * DVS];  // [token][slice column]
+__shared__ __attribute__((aligned(16))) uint32_t lds_touch[64];    // landing area of the L2 prefetch (never read)
+
 struct __attribute__((aligned(16))) Smem {
-  bf16_t K[2][C * DK];      // kappa-ordered, swizzled
-  bf16_t Q[2][C * DK];
-  bf16_t P[2][C * C];       // kappa-ordered columns, swizzled
-  bf16_t Ti[2][C * C];
-  bf16_t Vt[2][DVS * LDT];  // value slice transposed: [value col][token]
-  float gate[2][G_N][C];
-  float egl[2][4];          // 2^(g_C)
-  bf16_t Lb[2][C * LDT];    // L row-major (operands of the blocked inverse)
-  float Ld[2][4][16][LDD];  // fp32 diagonal 16x16 blocks of L
-  bf16_t Trm[C * LDT];      // inverse being built, row-major
-  bf16_t Tt[C * LDT];       // its transpose
-  bf16_t Mt[32 * LDT];      // partial products of the blocked inverse
-  float lg3[2][C];          // L wave: log2-prefix and beta of its chunk
+  bf16_t P[2][C * C];       // [r][s], s kappa-ordered, octets swizzled by swz_p(r)
+  bf16_t Tt[2][C * TTS];    // Ti^T: [s][t]
+  float gate[3][G_N][C];    // written two periods before use: three buffers
+  float egl[3][4];          // 2^(g_C)
+  float Ld[2][4][16][LDR];  // strictly-lower diagonal 16x16 blocks of L, fp32
+  bf16_t Lo[2][6][64 * 4];  // off-diagonal 16x16 blocks of L, MFMA A-operand order
 };
 
 __device__ __forceinline__ int swz_kq(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-__device__ __forceinline__ int swz_pt(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz_p(int row) { return (row >> 1) & 7; }
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // raw buffer (stride 0), word 3 = 0x00020000 (gfx9 family untyped access)
@@ -115,41 +120,63 @@ template <class T>
 __device__ __forceinline__ void lds_put(char* base, int off, T v) {
   *reinterpret_cast<T*>(base + off) = v;
 }
+// gfx950 transposed read: within each 16-lane group, lane m receives element
+// m % 4 of the 8-byte rows whose addresses lanes m/4, m/4 + 4, m/4 + 8 and
+// m/4 + 12 supply.
+__device__ __forceinline__ uint2 lds_tr(const char* base, int off) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off));
+  return __builtin_bit_cast(uint2, v);
+}
 __device__ __forceinline__ bf16x8_t as_op(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ __forceinline__ bf16x8_t as_op(uint2 lo, uint2 hi) {
+  return as_op(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+__device__ __forceinline__ i16x4_t as_op4(uint2 u) { return __builtin_bit_cast(i16x4_t, u); }
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
+// One accumulator tile -> 16-deep operand (4 values per lane).
+__device__ __forceinline__ uint2 pack_tile(const f32x4& t) {
+  return make_uint2(pack2(t[0], t[1]), pack2(t[2], t[3]));
+}
 // Two vertically adjacent accumulator tiles -> one kappa-ordered operand.
 __device__ __forceinline__ bf16x8_t pack_op(const f32x4& lo, const f32x4& hi) {
-  return as_op(make_uint4(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]),
-                          pack2(hi[2], hi[3])));
+  return as_op(pack_tile(lo), pack_tile(hi));
 }
 __device__ __forceinline__ f32x4 mfma(bf16x8_t a, bf16x8_t b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma16(uint2 a, uint2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_op4(a), as_op4(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ float4 as_f4(f32x4 v) { return make_float4(v[0], v[1], v[2], v[3]); }
 // Order this wave's LDS writes before its later LDS reads (single-wave
-// producer/consumer through LDS).
+// producer/consumer through LDS).  The LDS unit executes the instructions of
+// one wave in issue order, and the compiler keeps a read after a write to the
+// same array, so draining the LDS counter is enough.  (A memory-model fence
+// here would also wait for the wave's outstanding LDS-DMA loads.)
 __device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Inclusive prefix sum over the 64 lanes.
-__device__ __forceinline__ float wave_prefix_sum(float x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trips):
+// row_shr 1, 2, 4, 8 scan each row of 16 lanes; row_bcast15 and row_bcast31
+// then add the totals of the preceding rows.  Lanes without a source take 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_src(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x += dpp_src<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_src<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_src<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_src<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_src<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_src<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
   return x;
 }
-
-// Byte offset of the b128 MFMA fragment (rows 0..15, 32-column block blk) of
-// lane (lr, lg) in a kappa-ordered swizzled tile with `noct` octets per row;
-// row block rb adds rb * 16 * noct * 16 bytes.
-__device__ __forceinline__ int frag_base(int lr, int lg, int blk, int noct, int swz) {
-  return lr * noct * 16 + (((4 * blk + lg) ^ swz) << 4);
+__device__ __forceinline__ float lane63(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
 // Per-sequence buffer descriptors.
@@ -158,291 +185,225 @@ struct Seq {
   int64_t T;
 };
 
-// ============================================================ wave 0: state
+// Global key column of the first of the 4 state values a lane holds in
+// accumulator tile jb (the relabelling described at the top of the file).
+__device__ __forceinline__ int state_col(int jb, int lg) {
+  return 32 * (jb >> 1) + 8 * lg + 4 * (jb & 1);
+}
+
+// ============================================================ waves 0, 1: state
 struct StateAddr {
-  int kq[4];   // fragment base per 32-column block
-  int pt[2];   // P / Ti fragment base per 32-token block
-  int tr[4];   // transposed-read supplier base per pair of key blocks
-  int vt;      // V^T read base
-  uint32_t o;  // lane part of the output byte offset
+  int frag[4];  // K/Q fragment (token row lr, octet 4pp + lg) per key block pp
+  int ktr[4];   // K^T supplier address per key block
+  int vtr;      // V^T supplier address
+  int ttr;      // Ti supplier address (rows of Ti^T)
+  int pfr[2];   // P fragment per 32-token block
+  uint32_t o;   // lane part of the output byte offset
 };
 
-__device__ __forceinline__ StateAddr state_addr(int lane, int DV) {
+__device__ __forceinline__ StateAddr state_addr(int lane, int X, int DV) {
   const int lr = lane & 15, lg = lane >> 4;
+  const int a = lr & 3, r = lr >> 2;  // as a supplier of transposed reads
   StateAddr A;
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) A.kq[pp] = frag_base(lr, lg, pp, 16, swz_kq(lr));
+  for (int pp = 0; pp < 4; ++pp) {
+    A.frag[pp] = lr * 256 + (((4 * pp + lg) ^ swz_kq(lr)) << 4);
+    // token 4 lg + r (+ 32-token and 16-token offsets added per read), whose
+    // swizzle is (r << 2) | lg; key octet 4 pp + a
+    A.ktr[pp] = (4 * lg + r) * 256 + (((4 * pp + a) ^ ((r << 2) | lg)) << 4);
+  }
+  A.vtr = (4 * lg + r) * (DVS * 2) + 32 * X + 8 * a;
+  A.ttr = (4 * lg + r) * (TTS * 2) + 8 * a;
 #pragma unroll
-  for (int pp = 0; pp < 2; ++pp) A.pt[pp] = frag_base(lr, lg, pp, 8, swz_pt(lr));
-  const int sr = lr >> 2, sq = lane & 3;  // supplier token row / 4-column chunk
-  const int t = 4 * lg + sr;              // supplier token of the first read
-  const int sw = (sr << 2) | lg;          // = swz_kq(t + 16 m) for every m
-#pragma unroll
-  for (int h = 0; h < 4; ++h) A.tr[h] = t * 256 + (((4 * h + sq) ^ sw) << 4);
-  A.vt = lr * (LDT * 2) + lg * 8;
-  A.o = (uint32_t)((lr * DV + 4 * lg) * 2);
+  for (int pp = 0; pp < 2; ++pp) A.pfr[pp] = lr * 128 + (((4 * pp + lg) ^ swz_p(lr)) << 4);
+  A.o = (uint32_t)((lr * DV + 16 * X + 4 * lg) * 2);
   return A;
 }
 
-__device__ __forceinline__ void state_chunk(Smem& sm, const Seq& sq, const StateAddr& A,
-                                            f32x4 (&Sacc)[2][8], int64_t p, int DV, int lane) {
-  const int buf = (int)(p & 1);
-  const char* Kb = reinterpret_cast<const char*>(sm.K[buf]);
-  const char* Qb = reinterpret_cast<const char*>(sm.Q[buf]);
-  const char* Tb = reinterpret_cast<const char*>(sm.Ti[buf]);
-  const char* Pb = reinterpret_cast<const char*>(sm.P[buf]);
-  const char* Vb = reinterpret_cast<const char*>(sm.Vt[buf]);
-  const float* gt = &sm.gate[buf][0][0];
+struct StateRegs {
+  f32x4 S[8];        // state tiles: value row lr, internal keys 16 jb + 4 lg + e
+  f32x4 Oprev[4];    // Q S^T part of the previous chunk's output (per 16-token block)
+  bf16x8_t Uprev[2]; // U of the previous chunk as kappa operands
+};
+
+// O of chunk c = Oprev + U P^T, stored to global memory.
+__device__ __forceinline__ void state_finish_output(const Smem& sm, const Seq& sq, const StateAddr& A,
+                                                    const StateRegs& R, int64_t c, int DV) {
+  const char* Pb = reinterpret_cast<const char*>(sm.P[c & 1]);
+  const uint32_t obase = (uint32_t)(c * C * DV * 2) + A.o;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    f32x4 acc = R.Oprev[rb];
+#pragma unroll
+    for (int pp = 0; pp <= rb / 2; ++pp)
+      acc = mfma(R.Uprev[pp], as_op(lds_at<uint4>(Pb, A.pfr[pp] + rb * 2048)), acc);
+    buf_st8(sq.o, obase + (uint32_t)(rb * 16 * DV * 2), pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
+  }
+}
+
+__device__ __forceinline__ void state_chunk(const Smem& sm, const StateAddr& A, StateRegs& R,
+                                            int64_t c, int lane) {
+  const int buf = (int)(c & 1);
+  const char* Kb = reinterpret_cast<const char*>(lds_K[buf]);
+  const char* Qb = reinterpret_cast<const char*>(lds_Q[buf]);
+  const char* Vb = reinterpret_cast<const char*>(lds_V[buf]);
+  const char* Tb = reinterpret_cast<const char*>(sm.Tt[buf]);
+  const int gb = (int)(c % 3);
+  const float* gt = &sm.gate[gb][0][0];
   const int lr = lane & 15, lg = lane >> 4;
 
-  // Operands of S for contractions over the key index.
-  bf16x8_t Sop[2][4];
+  // Operands of S for contractions over the key index (natural key order).
+  bf16x8_t Sop[4];
 #pragma unroll
-  for (int ib = 0; ib < 2; ++ib)
+  for (int pp = 0; pp < 4; ++pp) Sop[pp] = pack_op(R.S[2 * pp], R.S[2 * pp + 1]);
+  const float decay = sm.egl[gb][0];
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) Sop[ib][pp] = pack_op(Sacc[ib][2 * pp], Sacc[ib][2 * pp + 1]);
-  // The decay of the carried state does not depend on this chunk's products.
-  const float decay = sm.egl[buf][0];
-#pragma unroll
-  for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-    for (int jb = 0; jb < 8; ++jb) Sacc[ib][jb] *= decay;
+  for (int jb = 0; jb < 8; ++jb) R.S[jb] *= decay;
 
-  // O1 = S Q^T (tiles [ib][rb]) and Z = K S^T (tiles [rb][ib]).
-  f32x4 Oacc[2][4], Z[4][2];
+  // O1 = S Q^T (tile per 16-token block, rows = value) and Z = K S^T (rows = token).
+  f32x4 O1[4], Z[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
-    bf16x8_t qf[4], kf[4];
+    f32x4 ao = zero4(), az = zero4();
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      qf[pp] = as_op(lds_at<uint4>(Qb, A.kq[pp] + rb * 4096));
-      kf[pp] = as_op(lds_at<uint4>(Kb, A.kq[pp] + rb * 4096));
+      const bf16x8_t qf = as_op(lds_at<uint4>(Qb, A.frag[pp] + rb * 4096));
+      const bf16x8_t kf = as_op(lds_at<uint4>(Kb, A.frag[pp] + rb * 4096));
+      ao = mfma(Sop[pp], qf, ao);
+      az = mfma(kf, Sop[pp], az);
     }
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      f32x4 ao = zero4(), az = zero4();
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        ao = mfma(Sop[ib][pp], qf[pp], ao);
-        az = mfma(kf[pp], Sop[ib][pp], az);
-      }
-      Oacc[ib][rb] = ao;
-      Z[rb][ib] = az;
-    }
+    O1[rb] = ao;
+    Z[rb] = az;
   }
-  // Y = beta V - beta 2^g Z, packed as kappa operands [ib][32-token block].
-  bf16x8_t Yop[2][2];
+  // Y = beta V - beta 2^g Z as kappa operands over tokens.
+  f32x4 y[4];
 #pragma unroll
-  for (int ib = 0; ib < 2; ++ib) {
-    f32x4 y[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const float4 b4 = *reinterpret_cast<const float4*>(gt + G_BETA * C + 16 * rb + 4 * lg);
-      const float4 g4 = *reinterpret_cast<const float4*>(gt + G_BEG * C + 16 * rb + 4 * lg);
-      const uint2 vv = lds_at<uint2>(Vb, A.vt + ib * 16 * LDT * 2 + rb * 32);
-      y[rb][0] = b4.x * __uint_as_float(vv.x << 16) - g4.x * Z[rb][ib][0];
-      y[rb][1] = b4.y * __uint_as_float(vv.x & 0xffff0000u) - g4.y * Z[rb][ib][1];
-      y[rb][2] = b4.z * __uint_as_float(vv.y << 16) - g4.z * Z[rb][ib][2];
-      y[rb][3] = b4.w * __uint_as_float(vv.y & 0xffff0000u) - g4.w * Z[rb][ib][3];
-    }
-    Yop[ib][0] = pack_op(y[0], y[1]);
-    Yop[ib][1] = pack_op(y[2], y[3]);
+  for (int rb = 0; rb < 4; ++rb) {
+    const float4 b4 = *reinterpret_cast<const float4*>(gt + G_BETA * C + 16 * rb + 4 * lg);
+    const float4 g4 = *reinterpret_cast<const float4*>(gt + G_BEG * C + 16 * rb + 4 * lg);
+    const uint2 vv = lds_tr(Vb, A.vtr + rb * 16 * DVS * 2);
+    y[rb][0] = b4.x * __uint_as_float(vv.x << 16) - g4.x * Z[rb][0];
+    y[rb][1] = b4.y * __uint_as_float(vv.x & 0xffff0000u) - g4.y * Z[rb][1];
+    y[rb][2] = b4.z * __uint_as_float(vv.y << 16) - g4.z * Z[rb][2];
+    y[rb][3] = b4.w * __uint_as_float(vv.y & 0xffff0000u) - g4.w * Z[rb][3];
   }
+  const bf16x8_t Yop[2] = {pack_op(y[0], y[1]), pack_op(y[2], y[3])};
   // O1 carries the factor 2^g of its token column.
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const float eg = gt[G_EG * C + 16 * rb + lr];
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) Oacc[ib][rb] *= eg;
-  }
-  // U = Ti Y (tiles [rb][ib]); Ti is lower triangular, so row block rb only
-  // needs the 32-token blocks pp <= rb/2 (the upper blocks inside them are zero).
-  f32x4 U[4][2];
+  for (int rb = 0; rb < 4; ++rb) R.Oprev[rb] = O1[rb] * gt[G_EG * C + 16 * rb + lr];
+  // U = Ti Y; Ti is lower triangular, so row block rb only needs the 32-token
+  // blocks pp <= rb/2 (the upper 16x16 blocks inside them are zero).
+  f32x4 U[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
-    bf16x8_t tf[2];
+    f32x4 acc = zero4();
 #pragma unroll
-    for (int pp = 0; pp <= rb / 2; ++pp) tf[pp] = as_op(lds_at<uint4>(Tb, A.pt[pp] + rb * 2048));
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int pp = 0; pp <= rb / 2; ++pp) acc = mfma(tf[pp], Yop[ib][pp], acc);
-      U[rb][ib] = acc;
+    for (int pp = 0; pp <= rb / 2; ++pp) {
+      const int off = A.ttr + pp * 32 * TTS * 2 + rb * 32;
+      const bf16x8_t tf = as_op(lds_tr(Tb, off), lds_tr(Tb, off + 16 * TTS * 2));
+      acc = mfma(tf, Yop[pp], acc);
     }
+    U[rb] = acc;
   }
   // Operands of U: plain (for O) and scaled by 2^(g_C - g_s) (for S).
-  bf16x8_t Uop[2][2], Uh[2][2];
+  bf16x8_t Uh[2];
 #pragma unroll
   for (int pp = 0; pp < 2; ++pp) {
     const float4 e0 = *reinterpret_cast<const float4*>(gt + G_EL * C + 32 * pp + 4 * lg);
     const float4 e1 = *reinterpret_cast<const float4*>(gt + G_EL * C + 32 * pp + 16 + 4 * lg);
     const f32x4 s0 = {e0.x, e0.y, e0.z, e0.w}, s1 = {e1.x, e1.y, e1.z, e1.w};
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      Uop[ib][pp] = pack_op(U[2 * pp][ib], U[2 * pp + 1][ib]);
-      Uh[ib][pp] = pack_op(U[2 * pp][ib] * s0, U[2 * pp + 1][ib] * s1);
-    }
+    R.Uprev[pp] = pack_op(U[2 * pp], U[2 * pp + 1]);
+    Uh[pp] = pack_op(U[2 * pp] * s0, U[2 * pp + 1] * s1);
   }
-  // O^T += U^T P^T, then store this chunk's outputs (the range check of the
-  // output descriptor drops rows past the end of the sequence).
-  const uint32_t obase = (uint32_t)(p * C * DV * 2) + A.o;
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    bf16x8_t pf[2];
-#pragma unroll
-    for (int pp = 0; pp <= rb / 2; ++pp) pf[pp] = as_op(lds_at<uint4>(Pb, A.pt[pp] + rb * 2048));
-    const uint32_t orow = obase + (uint32_t)(rb * 16 * DV * 2);
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      f32x4 acc = Oacc[ib][rb];
-#pragma unroll
-      for (int pp = 0; pp <= rb / 2; ++pp) acc = mfma(Uop[ib][pp], pf[pp], acc);
-      buf_st8(sq.o, orow + ib * 32, pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
-    }
-  }
-  // S^T += K^T Uh, with K^T fragments from transposed LDS reads: within each
-  // 16-lane group, lane (4*r + q) supplies the address of 4 columns (chunk q)
-  // of token row r, and lane m receives column m of the four rows, i.e. 4
-  // consecutive tokens of one key column.
-  typedef __attribute__((address_space(3))) i16x4_t lds_v4;
+  // S^T += K^T Uh with K^T from transposed reads: supplier lane (a, r) of a
+  // 16-lane group addresses 4 key columns of token 4 lg + r.
 #pragma unroll
   for (int jb = 0; jb < 8; ++jb) {
-    bf16x8_t kt[2];
+    f32x4 acc = R.S[jb];
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
-      const int off = A.tr[jb >> 1] + (jb & 1) * 8 + pp * 32 * 256;
-      const i16x4_t a4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(Kb + off));
-      const i16x4_t b4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(Kb + off + 16 * 256));
-      const uint2 ua = __builtin_bit_cast(uint2, a4), ub = __builtin_bit_cast(uint2, b4);
-      kt[pp] = as_op(make_uint4(ua.x, ua.y, ub.x, ub.y));
+      const int off = A.ktr[jb >> 1] + (jb & 1) * 8 + pp * 32 * 256;
+      const bf16x8_t kt = as_op(lds_tr(Kb, off), lds_tr(Kb, off + 16 * 256));
+      acc = mfma(kt, Uh[pp], acc);
     }
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      f32x4 acc = Sacc[ib][jb];
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) acc = mfma(kt[pp], Uh[ib][pp], acc);
-      Sacc[ib][jb] = acc;
-    }
+    R.S[jb] = acc;
   }
 }
 
-// ============================================================ wave 1: stage + P
-// Register image of one chunk: k/q[it] = 8 columns (8*(lane%16) ..) of token
-// 4*it + lane/16; v[it] = 8 slice columns (8*(lane%4) ..) of token 16*it + lane/4.
-struct ChunkRegs {
-  uint4 k[16];
-  uint4 q[16];
-  uint4 v[4];
-  float a, b;  // alpha, beta of token `lane`
+// ============================================================ K, Q, V into LDS
+// LDS-DMA loads of chunk c into buffers c & 1.  Lane i of a 16-byte LDS-DMA
+// load writes bytes 16 i .. 16 i + 15 after the uniform LDS base, so each lane
+// fetches the global octet that the swizzled layout puts there: for K and Q,
+// instruction it covers tokens 4 it .. 4 it + 3 and lane (lr, lg) fills
+// physical octet lr of token 4 it + lg, i.e. key octet lr ^ swz_kq(4 it + lg).
+struct DmaAddr {
+  uint32_t kq[4];  // per it & 3
+  uint32_t v;
 };
-
-struct StageAddr {
-  uint32_t gkq;   // global byte offset (lane part) of k/q[0]
-  uint32_t gv;    // global byte offset (lane part) of v[0]
-  int wkq[4][2];  // LDS write offsets of the two 4-column halves, per (it & 3)
-  int wvt;        // V^T write base
-  int kq[4];      // fragment bases (as the state wave)
-  int pw[2];      // P write base per 32-token block of s
-};
-
-__device__ __forceinline__ StageAddr stage_addr(int lane, int DV) {
+__device__ __forceinline__ DmaAddr dma_addr(int lane, int DV) {
   const int lr = lane & 15, lg = lane >> 4;
-  StageAddr A;
-  A.gkq = (uint32_t)(lg * DK * 2 + lr * 16);
-  A.gv = (uint32_t)((lane >> 2) * DV * 2 + (lane & 3) * 16);
-  // columns 8*lr .. +7 of a row: 32-column block lr/4, 4-column groups
-  // 2*(lr&1) and 2*(lr&1)+1, in the upper kappa half when (lr>>1)&1
-  const int blk = lr >> 2, q0 = 2 * (lr & 1), half = (lr >> 1) & 1;
+  DmaAddr A;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int sw = (lg << 2) | m;  // swz_kq(4*it + lg) when it & 3 == m
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      A.wkq[m][hh] = lg * 256 + (((4 * blk + q0 + hh) ^ sw) << 4) + half * 8;
-  }
-  A.wvt = (lane & 3) * 8 * (LDT * 2) + (lane >> 2) * 2;
-#pragma unroll
-  for (int pp = 0; pp < 4; ++pp) A.kq[pp] = frag_base(lr, lg, pp, 16, swz_kq(lr));
-#pragma unroll
-  for (int h = 0; h < 2; ++h) A.pw[h] = lr * 128 + (((4 * h + lg) ^ swz_pt(lr)) << 4);
+  for (int m = 0; m < 4; ++m) A.kq[m] = (uint32_t)(lg * 256 + ((lr ^ ((lg << 2) | m)) << 4));
+  A.v = (uint32_t)((lane >> 2) * DV * 2 + (lane & 3) * 16);
   return A;
 }
-
-__device__ __forceinline__ void load_chunk(ChunkRegs& R, const Seq& sq, const StageAddr& A,
-                                           int64_t c, int DV, int lane) {
-  const uint32_t kq0 = (uint32_t)(c * C * DK * 2) + A.gkq;
-#pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    R.k[it] = buf_ld16(sq.k, kq0 + it * 4 * DK * 2);
-    R.q[it] = buf_ld16(sq.q, kq0 + it * 4 * DK * 2);
-  }
-  const uint32_t v0 = (uint32_t)(c * C * DV * 2) + A.gv;
-#pragma unroll
-  for (int it = 0; it < 4; ++it) R.v[it] = buf_ld16(sq.v, v0 + it * 16 * DV * 2);
-  const int64_t t = c * C + lane;
-  const float a = buf_ldf(sq.a, (uint32_t)(t * 4));
-  const float b = buf_ldf(sq.b, (uint32_t)(t * 4));
-  R.a = t < sq.T ? a : 1.f;  // tokens past the end: identity maps
-  R.b = t < sq.T ? b : 0.f;
-}
-
-__device__ __forceinline__ void stage_chunk(Smem& sm, const ChunkRegs& R, const StageAddr& A,
-                                            int64_t c, int lane) {
+__device__ __forceinline__ void dma_chunk(const Seq& sq, const DmaAddr& A, int64_t c, int DV) {
   const int buf = (int)(c & 1);
-  char* Kb = reinterpret_cast<char*>(sm.K[buf]);
-  char* Qb = reinterpret_cast<char*>(sm.Q[buf]);
-  char* Vb = reinterpret_cast<char*>(sm.Vt[buf]);
+  const uint32_t kq0 = (uint32_t)(c * C * DK * 2);
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
-    const int o0 = A.wkq[it & 3][0] + it * 4 * 256;
-    const int o1 = A.wkq[it & 3][1] + it * 4 * 256;
-    lds_put<uint2>(Kb, o0, make_uint2(R.k[it].x, R.k[it].y));
-    lds_put<uint2>(Kb, o1, make_uint2(R.k[it].z, R.k[it].w));
-    lds_put<uint2>(Qb, o0, make_uint2(R.q[it].x, R.q[it].y));
-    lds_put<uint2>(Qb, o1, make_uint2(R.q[it].z, R.q[it].w));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.k, (lds_void*)&lds_K[buf][it * 512], 16, A.kq[it & 3],
+                                             (int)(kq0 + it * 1024), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.q, (lds_void*)&lds_Q[buf][it * 512], 16, A.kq[it & 3],
+                                             (int)(kq0 + it * 1024), 0, 0);
   }
+  const uint32_t v0 = (uint32_t)(c * C * DV * 2);
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const uint32_t w[4] = {R.v[it].x, R.v[it].y, R.v[it].z, R.v[it].w};
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      lds_put<bf16_t>(Vb, A.wvt + (2 * x) * LDT * 2 + it * 32, (bf16_t)(w[x] & 0xffffu));
-      lds_put<bf16_t>(Vb, A.wvt + (2 * x + 1) * LDT * 2 + it * 32, (bf16_t)(w[x] >> 16));
-    }
-  }
-  // gate tables, one lane per token
-  const float gs = wave_prefix_sum(fast_log2(R.a), lane);
-  const float glast = __shfl(gs, 63, 64);
-  const float eg = fast_exp2(gs);
-  float* gt = &sm.gate[buf][0][0];
-  gt[G_BETA * C + lane] = R.b;
-  gt[G_BEG * C + lane] = R.b * eg;
-  gt[G_EG * C + lane] = eg;
-  gt[G_EL * C + lane] = fast_exp2(glast - gs);
-  gt[G_LOG * C + lane] = gs;
-  if (lane == 0) sm.egl[buf][0] = fast_exp2(glast);
+  for (int it = 0; it < 4; ++it)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.v, (lds_void*)&lds_V[buf][it * 512], 16, A.v,
+                                             (int)(v0 + it * 16 * DV * 2), 0, 0);
 }
 
-// P of chunk c from the staged buffers c & 1 (after a wave fence).
-__device__ __forceinline__ void build_p(Smem& sm, const StageAddr& A, int64_t c, int lane) {
+// ============================================================ wave 2: P
+// L2 prefetch of chunk c: one 4-byte load per 128-byte line, landing in a
+// scratch word of LDS (an LDS-DMA load has a side effect, so it is kept, and
+// no register waits for it).  The four slice workgroups of a sequence split
+// the key and query lines; each touches its own value lines.  All 64 lanes
+// take part in every load (lanes 32..63 repeat the lines of lanes 0..31), so
+// the descriptors stay uniform.
+__device__ __forceinline__ void prefetch_chunk(const Seq& sq, int64_t c, int slice, int DV, int lane) {
+  lds_void* land = (lds_void*)&lds_touch[0];
+  const uint32_t kq = (uint32_t)(c * C * DK * 2) + (uint32_t)((32 * slice + (lane & 31)) * 128);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.k, land, 4, kq, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.q, land, 4, kq, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.v, land, 4, (uint32_t)((c * C + lane) * DV * 2), 0, 0, 0);
+  const uint32_t g = (uint32_t)(c * C * 4 + (lane & 1) * 128);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.a, land, 4, g, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.b, land, 4, g, 0, 0, 0);
+}
+
+__device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const int buf = (int)(c & 1);
-  const char* Kb = reinterpret_cast<const char*>(sm.K[buf]);
-  const char* Qb = reinterpret_cast<const char*>(sm.Q[buf]);
-  const float* gt = &sm.gate[buf][0][0];
+  const char* Kb = reinterpret_cast<const char*>(lds_K[buf]);
+  const char* Qb = reinterpret_cast<const char*>(lds_Q[buf]);
+  const float* gt = &sm.gate[c % 3][0][0];
   char* Pb = reinterpret_cast<char*>(sm.P[buf]);
+  int pw[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) pw[h] = lr * 128 + (((4 * h + lg) ^ swz_p(lr)) << 4);
   bf16x8_t kf[4][4];
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) kf[b][pp] = as_op(lds_at<uint4>(Kb, A.kq[pp] + b * 4096));
+    for (int pp = 0; pp < 4; ++pp) kf[b][pp] = as_op(lds_at<uint4>(Kb, A.frag[pp] + b * 4096));
   // tiles [s-block sb][r-block rb], sb <= rb: element (s, r) = k_s . q_r
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     bf16x8_t qf[4];
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) qf[pp] = as_op(lds_at<uint4>(Qb, A.kq[pp] + rb * 4096));
+    for (int pp = 0; pp < 4; ++pp) qf[pp] = as_op(lds_at<uint4>(Qb, A.frag[pp] + rb * 4096));
     const float gr = gt[G_LOG * C + 16 * rb + lr];
 #pragma unroll
     for (int sb = 0; sb <= rb; ++sb) {
@@ -456,98 +417,18 @@ __device__ __forceinline__ void build_p(Smem& sm, const StageAddr& A, int64_t c,
 #pragma unroll
         for (int e = 0; e < 4; ++e) val[e] = (4 * lg + e <= lr) ? val[e] : 0.f;
       }
-      lds_put<uint2>(Pb, A.pw[sb >> 1] + (sb & 1) * 8 + rb * 2048,
+      lds_put<uint2>(Pb, pw[sb >> 1] + (sb & 1) * 8 + rb * 2048,
                      make_uint2(pack2(val[0], val[1]), pack2(val[2], val[3])));
     }
   }
 }
 
-// ============================================================ wave 2: inverse
-// Ti = (I + L)^-1 of chunk c from L buffers c & 1 into Ti buffer c & 1.
-__device__ __forceinline__ void build_inverse(Smem& sm, int64_t c, int lane) {
-  const int lr = lane & 15, lg = lane >> 4;
-  const int lb = (int)(c & 1);
-  // level 0: unit-lower 16x16 diagonal blocks by forward substitution, fp32,
-  // lane = (block lg, column lr); column-oriented so the row updates of one
-  // step are independent.
-  {
-    const float* Lblk = &sm.Ld[lb][lg][0][0];
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (r == lr) ? 1.f : 0.f;
-#pragma unroll
-    for (int s = 0; s < 15; ++s) {
-#pragma unroll
-      for (int r = s + 1; r < 16; ++r) x[r] -= Lblk[r * LDD + s] * x[s];
-    }
-    bf16_t* trm = &sm.Trm[(16 * lg) * LDT + 16 * lg + lr];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) trm[r * LDT] = f32_to_bf16(x[r]);
-    uint4* tt = reinterpret_cast<uint4*>(&sm.Tt[(16 * lg + lr) * LDT + 16 * lg]);
-    tt[0] = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
-    tt[1] = make_uint4(pack2(x[8], x[9]), pack2(x[10], x[11]), pack2(x[12], x[13]), pack2(x[14], x[15]));
-  }
-  wave_lds_fence();
-  // level 1: T[a][b] = -T[a][a] L[a][b] T[b][b], (a,b) = (1,0), (3,2)
-#pragma unroll
-  for (int pr = 0; pr < 2; ++pr) {
-    const int a = 2 * pr + 1, b = 2 * pr;
-    f32x4 acc = Mma<bf16_t>::template run<16>(zero4(), &sm.Lb[lb][16 * a * LDT + 16 * b], LDT,
-                                              &sm.Tt[16 * b * LDT + 16 * b], LDT, lane);
-    store4<bf16_t>(&sm.Mt[(16 * pr + lr) * LDT + 4 * lg], acc[0], acc[1], acc[2], acc[3]);
-  }
-  wave_lds_fence();
-#pragma unroll
-  for (int pr = 0; pr < 2; ++pr) {
-    const int a = 2 * pr + 1, b = 2 * pr;
-    f32x4 acc = Mma<bf16_t>::template run<16>(zero4(), &sm.Trm[16 * a * LDT + 16 * a], LDT,
-                                              &sm.Mt[16 * pr * LDT], LDT, lane);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.Trm[(16 * a + 4 * lg + e) * LDT + 16 * b + lr] = f32_to_bf16(-acc[e]);
-    store4<bf16_t>(&sm.Tt[(16 * b + lr) * LDT + 16 * a + 4 * lg], -acc[0], -acc[1], -acc[2], -acc[3]);
-  }
-  wave_lds_fence();
-  // level 2: T[hi][lo] = -T[hi][hi] L[hi][lo] T[lo][lo] on 32x32 halves
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int rb2 = u >> 1, cb2 = u & 1;
-    f32x4 acc = Mma<bf16_t>::template run<32>(zero4(), &sm.Lb[lb][(32 + 16 * rb2) * LDT], LDT,
-                                              &sm.Tt[16 * cb2 * LDT], LDT, lane);
-    store4<bf16_t>(&sm.Mt[(16 * cb2 + lr) * LDT + 16 * rb2 + 4 * lg], acc[0], acc[1], acc[2], acc[3]);
-  }
-  wave_lds_fence();
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int rb2 = u >> 1, cb2 = u & 1;
-    f32x4 acc = Mma<bf16_t>::template run<32>(zero4(), &sm.Trm[(32 + 16 * rb2) * LDT + 32], LDT,
-                                              &sm.Mt[16 * cb2 * LDT], LDT, lane);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      sm.Trm[(32 + 16 * rb2 + 4 * lg + e) * LDT + 16 * cb2 + lr] = f32_to_bf16(-acc[e]);
-  }
-  wave_lds_fence();
-  // copy the ten lower 16x16 blocks into the kappa-ordered, swizzled Ti buffer
-  char* Tb = reinterpret_cast<char*>(sm.Ti[lb]);
-  const char* Rb = reinterpret_cast<const char*>(sm.Trm);
-  const int rd = lr * LDT * 2 + lg * 8;
-  int wr[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) wr[h] = lr * 128 + (((4 * h + lg) ^ swz_pt(lr)) << 4);
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b <= a; ++b) {
-      const uint2 val = lds_at<uint2>(Rb, rd + a * 16 * LDT * 2 + b * 32);
-      lds_put<uint2>(Tb, wr[b >> 1] + (b & 1) * 8 + a * 2048, val);
-    }
-}
-
 // ============================================================ wave 3: L
-// Keys of one chunk in MFMA fragment layout: kf[rb][pp] = columns
-// 32pp + 8*(lane/16) .. +7 of token 16rb + lane%16.
+// Keys of one chunk in MFMA fragment layout: kf[rb][pp] = key octet 4 pp + lg
+// of token 16 rb + lr.
 struct FragRegs {
   uint4 kf[4][4];
-  float a, b;  // alpha, beta of token `lane`
+  float a, b;  // alpha, beta of token `lane` as loaded (0 past the end)
 };
 
 __device__ __forceinline__ void load_frags(FragRegs& R, const Seq& sq, int64_t c, int lane) {
@@ -558,45 +439,138 @@ __device__ __forceinline__ void load_frags(FragRegs& R, const Seq& sq, int64_t c
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) R.kf[rb][pp] = buf_ld16(sq.k, base + rb * 16 * DK * 2 + pp * 64);
   const int64_t t = c * C + lane;
-  const float a = buf_ldf(sq.a, (uint32_t)(t * 4));
-  const float b = buf_ldf(sq.b, (uint32_t)(t * 4));
-  R.a = t < sq.T ? a : 1.f;
-  R.b = t < sq.T ? b : 0.f;
+  R.a = buf_ldf(sq.a, (uint32_t)(t * 4));
+  R.b = buf_ldf(sq.b, (uint32_t)(t * 4));
 }
 
-__device__ __forceinline__ void build_l(Smem& sm, const FragRegs& R, int64_t c, int lane) {
+// Gate tables and L of chunk c.  L: diagonal blocks as fp32 rows,
+// off-diagonal blocks as bf16 in the order in which the inverse consumes them
+// as MFMA A operands.
+__device__ __forceinline__ void build_l(Smem& sm, const FragRegs& R, int64_t c, int64_t T, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const int lb = (int)(c & 1);
-  const float gs = wave_prefix_sum(fast_log2(R.a), lane);
-  sm.lg3[0][lane] = gs;
-  sm.lg3[1][lane] = R.b;
+  float* gt = &sm.gate[c % 3][0][0];
+  {
+    // one lane per token; tokens past the end are identity maps (alpha 1, beta 0)
+    const bool live = c * C + lane < T;
+    const float a = live ? R.a : 1.f, b = live ? R.b : 0.f;
+    const float gs = wave_prefix_sum(fmaxf(fast_log2(a), LOG2_ALPHA_MIN));
+    const float glast = lane63(gs);
+    const float eg = fast_exp2(gs);
+    gt[G_BETA * C + lane] = b;
+    gt[G_BEG * C + lane] = b * eg;
+    gt[G_EG * C + lane] = eg;
+    gt[G_EL * C + lane] = fast_exp2(glast - gs);
+    gt[G_LOG * C + lane] = gs;
+    if (lane == 0) sm.egl[c % 3][0] = fast_exp2(glast);
+  }
   wave_lds_fence();
-  // tiles [s-block sb][r-block rb], sb <= rb: element (s, r) = k_s . k_r
+  // tiles [s-block sb][r-block rb], sb <= rb: lane holds L[16rb + lr][16sb + 4lg + e]
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const int r = 16 * rb + lr;
-    const float gr = sm.lg3[0][r];
-    const float br = sm.lg3[1][r];
+    const float gr = gt[G_LOG * C + r];
+    const float br = gt[G_BETA * C + r];
 #pragma unroll
     for (int sb = 0; sb <= rb; ++sb) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) acc = mfma(as_op(R.kf[sb][pp]), as_op(R.kf[rb][pp]), acc);
-      const float4 g4 = *reinterpret_cast<const float4*>(&sm.lg3[0][16 * sb + 4 * lg]);
+      const float4 g4 = *reinterpret_cast<const float4*>(gt + G_LOG * C + 16 * sb + 4 * lg);
       float val[4] = {br * fast_exp2(gr - g4.x) * acc[0], br * fast_exp2(gr - g4.y) * acc[1],
                       br * fast_exp2(gr - g4.z) * acc[2], br * fast_exp2(gr - g4.w) * acc[3]};
       if (sb == rb) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) val[e] = (4 * lg + e < lr) ? val[e] : 0.f;
         *reinterpret_cast<float4*>(&sm.Ld[lb][rb][lr][4 * lg]) = make_float4(val[0], val[1], val[2], val[3]);
+      } else {
+        const int tix = rb * (rb - 1) / 2 + sb;
+        *reinterpret_cast<uint2*>(&sm.Lo[lb][tix][lane * 4]) =
+            make_uint2(pack2(val[0], val[1]), pack2(val[2], val[3]));
       }
-      store4<bf16_t>(&sm.Lb[lb][r * LDT + 16 * sb + 4 * lg], val[0], val[1], val[2], val[3]);
+    }
+  }
+}
+
+// ============================================================ wave 4: inverse
+// Forward substitution over key columns 4Q .. 4Q+3 of one unit-lower 16x16
+// block: x[r] -= L[r][s] x[s] for s in the band and r > s, with the band's
+// rows of L read as float4 (all 16 lanes of a group read the same row).
+template <int Q>
+__device__ __forceinline__ void subst_band(float (&x)[16], const float* Lr) {
+  float4 lq[16];
+#pragma unroll
+  for (int r = 4 * Q + 1; r < 16; ++r) lq[r] = *reinterpret_cast<const float4*>(Lr + r * LDR + 4 * Q);
+#pragma unroll
+  for (int s = 4 * Q; s < 4 * Q + 4; ++s) {
+#pragma unroll
+    for (int r = s + 1; r < 16; ++r) {
+      const float4 l4 = lq[r];
+      const float lrs = (s & 3) == 0 ? l4.x : (s & 3) == 1 ? l4.y : (s & 3) == 2 ? l4.z : l4.w;
+      x[r] = fmaf(-lrs, x[s], x[r]);
+    }
+  }
+}
+
+// Ti = (I + L)^-1 of chunk c, written as Ti^T into Tt buffer c & 1.
+//   level 0: the four unit-lower 16x16 diagonal blocks by forward
+//            substitution in fp32; lane = (block lg, column lr).
+//   blocks below the diagonal, one block row at a time:
+//            T_ab = -T_aa sum_{b <= c < a} L_ac T_cb
+//            with 16x16x16 MFMAs whose accumulators are reused as B operands.
+__device__ __forceinline__ void build_inverse(Smem& sm, int64_t c, int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+  const int lb = (int)(c & 1);
+  char* Tb = reinterpret_cast<char*>(sm.Tt[lb]);
+  {
+    const float* Lr = &sm.Ld[lb][lg][0][0];
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = (r == lr) ? 1.f : 0.f;
+    subst_band<0>(x, Lr);
+    subst_band<1>(x, Lr);
+    subst_band<2>(x, Lr);
+    subst_band<3>(x, Lr);
+    // column lr of block lg = row (16 lg + lr) of Ti^T, columns 16 lg .. +15
+    char* dst = Tb + (16 * lg + lr) * (TTS * 2) + 32 * lg;
+    lds_put<uint4>(dst, 0, make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])));
+    lds_put<uint4>(dst, 16, make_uint4(pack2(x[8], x[9]), pack2(x[10], x[11]), pack2(x[12], x[13]), pack2(x[14], x[15])));
+  }
+  wave_lds_fence();
+  // B operand of T_cc: lane holds T_cc[4lg + e][lr] = Ti^T[16c + lr][16c + 4lg + e]
+  uint2 Bd[3];
+#pragma unroll
+  for (int cc = 0; cc < 3; ++cc) Bd[cc] = lds_at<uint2>(Tb, (16 * cc + lr) * (TTS * 2) + (16 * cc + 4 * lg) * 2);
+  // A operand of T_aa: lane holds T_aa[lr][4lg + e], from transposed reads of Ti^T
+  uint2 Ad[4];
+  {
+    const int a = lr & 3, r = lr >> 2;
+#pragma unroll
+    for (int aa = 1; aa < 4; ++aa)
+      Ad[aa] = lds_tr(Tb, (16 * aa + 4 * lg + r) * (TTS * 2) + (16 * aa + 4 * a) * 2);
+  }
+  uint2 Lop[6];
+#pragma unroll
+  for (int t = 0; t < 6; ++t) Lop[t] = *reinterpret_cast<const uint2*>(&sm.Lo[lb][t][lane * 4]);
+  // T blocks below the diagonal as B operands: Tb_[a][b]
+  uint2 Tbo[4][3];
+#pragma unroll
+  for (int a = 1; a < 4; ++a) {
+#pragma unroll
+    for (int b = a - 1; b >= 0; --b) {
+      f32x4 m = zero4();
+#pragma unroll
+      for (int cc = b; cc < a; ++cc) m = mfma16(Lop[a * (a - 1) / 2 + cc], cc == b ? Bd[b] : Tbo[cc][b], m);
+      const f32x4 t = mfma16(Ad[a], pack_tile(-m), zero4());
+      Tbo[a][b] = pack_tile(t);
+      // lane holds T_ab[4lg + e][lr] -> Ti^T[16b + lr][16a + 4lg + e]
+      lds_put<uint2>(Tb, (16 * b + lr) * (TTS * 2) + (16 * a + 4 * lg) * 2, Tbo[a][b]);
     }
   }
 }
 
 // ============================================================ kernel
-__global__ __launch_bounds__(256) void chunk_fwd_pipe_kernel(
+__global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* initial_state, bf16_t* __restrict__ o, float* final_state, int nchain,
@@ -614,6 +588,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_pipe_kernel(
   {
     const int w = blockIdx.x;
     if (xcd_map) {
+      // the slices of one sequence land on one XCD and share its L2
       const int x = w & 7, r = w >> 3;
       slice = r % NS;
       chain = (r / NS) * 8 + x;
@@ -639,78 +614,72 @@ __global__ __launch_bounds__(256) void chunk_fwd_pipe_kernel(
     sq.b = make_rsrc(beta + (int64_t)chain * Tlen, (uint32_t)(Tlen * 4));
   }
   const int64_t nch = (Tlen + C - 1) / C;
-  const int64_t st_off = ((int64_t)chain * DV + (int64_t)slice * DVS) * DK;
 
-  // Zero the triangular buffers: their strictly-upper blocks are never
-  // written but are read as zero by 32-deep products.
+  // Zero P and Ti^T: their blocks above the diagonal are never written but
+  // are read as zero by 32-deep products.
   {
     uint32_t* z = reinterpret_cast<uint32_t*>(&sm.P[0][0]);
-    for (int e = tid; e < 2 * 2 * C * C / 2; e += 256) z[e] = 0u;  // P and Ti
-    uint32_t* z2 = reinterpret_cast<uint32_t*>(&sm.Trm[0]);
-    for (int e = tid; e < 2 * C * LDT / 2; e += 256) z2[e] = 0u;  // Trm and Tt
+    for (int e = tid; e < 2 * C * C / 2; e += 64 * NWAVES) z[e] = 0u;
+    uint32_t* z2 = reinterpret_cast<uint32_t*>(&sm.Tt[0][0]);
+    for (int e = tid; e < 2 * C * TTS / 2; e += 64 * NWAVES) z2[e] = 0u;
   }
 
-  // Each role runs its own loop over periods p = -2 .. nch-1 with exactly one
-  // workgroup barrier per period, so all four waves meet at every barrier.
-  if (wave == 0) {
-    const StateAddr A = state_addr(lane, DV);
-    f32x4 Sacc[2][8];
+  // Each role runs its own loop over periods p = -2 .. nch with exactly one
+  // workgroup barrier per period, so all waves meet at every barrier.
+  if (wave < 2) {
+    const int X = wave;
+    const StateAddr A = state_addr(lane, X, DV);
+    const int64_t st_row = (int64_t)chain * DV + (int64_t)slice * DVS + 16 * X + lr;
+    StateRegs R;
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < 8; ++jb) {
-        Sacc[ib][jb] = zero4();
-        if (initial_state) {
-          const int i = 16 * ib + lr, j = 16 * jb + 4 * lg;
-          const float4 s4 = *reinterpret_cast<const float4*>(initial_state + st_off + (int64_t)i * DK + j);
-          Sacc[ib][jb] = f32x4{s4.x, s4.y, s4.z, s4.w};
-        }
+    for (int jb = 0; jb < 8; ++jb) {
+      R.S[jb] = zero4();
+      if (initial_state) {
+        const float4 s4 = *reinterpret_cast<const float4*>(initial_state + st_row * DK + state_col(jb, lg));
+        R.S[jb] = f32x4{s4.x, s4.y, s4.z, s4.w};
       }
+    }
     __syncthreads();
-    for (int64_t p = -2; p < nch; ++p) {
-      if (p >= 0) state_chunk(sm, sq, A, Sacc, p, DV, lane);
+    for (int64_t p = -2; p <= nch; ++p) {
+      if (p >= 1) state_finish_output(sm, sq, A, R, p - 1, DV);
+      if (p >= 0 && p < nch) state_chunk(sm, A, R, p, lane);
       __syncthreads();
     }
     if (final_state) {
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int jb = 0; jb < 8; ++jb) {
-          const int i = 16 * ib + lr, j = 16 * jb + 4 * lg;
-          *reinterpret_cast<float4*>(final_state + st_off + (int64_t)i * DK + j) =
-              make_float4(Sacc[ib][jb][0], Sacc[ib][jb][1], Sacc[ib][jb][2], Sacc[ib][jb][3]);
-        }
-    }
-  } else if (wave == 1) {
-    const StageAddr A = stage_addr(lane, DV);
-    ChunkRegs R;
-    __syncthreads();
-    for (int64_t p = -2; p < nch; ++p) {
-      const int64_t c1 = p + 1, c2 = p + 2;
-      const bool have1 = c1 >= 0 && c1 < nch;
-      if (have1) stage_chunk(sm, R, A, c1, lane);
-      if (c2 < nch) load_chunk(R, sq, A, c2, DV, lane);
-      if (have1) {
-        wave_lds_fence();
-        build_p(sm, A, c1, lane);
-      }
-      __syncthreads();
+      for (int jb = 0; jb < 8; ++jb)
+        *reinterpret_cast<float4*>(final_state + st_row * DK + state_col(jb, lg)) = as_f4(R.S[jb]);
     }
   } else if (wave == 2) {
+    const StateAddr A = state_addr(lane, 0, DV);
     __syncthreads();
-    for (int64_t p = -2; p < nch; ++p) {
-      const int64_t c1 = p + 1;
-      if (c1 >= 0 && c1 < nch) build_inverse(sm, c1, lane);
+    for (int64_t p = -2; p <= nch; ++p) {
+      if (p >= 0 && p < nch) build_p(sm, A, p, lane);
+      if (p + PREFETCH_AHEAD < nch) prefetch_chunk(sq, p + PREFETCH_AHEAD, slice, DV, lane);
       __syncthreads();
     }
-  } else {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no LDS-DMA write outlives the workgroup
+  } else if (wave == 3) {
     FragRegs R;
     if (nch > 0) load_frags(R, sq, 0, lane);
     __syncthreads();
-    for (int64_t p = -2; p < nch; ++p) {
-      const int64_t c2 = p + 2, c3 = p + 3;
-      if (c2 < nch) build_l(sm, R, c2, lane);
-      if (c3 < nch) load_frags(R, sq, c3, lane);
+    for (int64_t p = -2; p <= nch; ++p) {
+      if (p + 2 < nch) build_l(sm, R, p + 2, Tlen, lane);
+      if (p + 3 < nch) load_frags(R, sq, p + 3, lane);
+      __syncthreads();
+    }
+  } else if (wave == 4) {
+    __syncthreads();
+    for (int64_t p = -2; p <= nch; ++p) {
+      if (p + 1 >= 0 && p + 1 < nch) build_inverse(sm, p + 1, lane);
+      __syncthreads();
+    }
+  } else {
+    const DmaAddr D = dma_addr(lane, DV);
+    __syncthreads();
+    for (int64_t p = -2; p <= nch; ++p) {
+      if (p + 1 >= 0 && p + 1 < nch) dma_chunk(sq, D, p + 1, DV);
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): chunk p+1 is in LDS
       __syncthreads();
     }
   }

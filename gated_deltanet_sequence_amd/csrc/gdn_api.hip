@@ -47,7 +47,7 @@ int launch_chunk_pipe(const void* q, const void* k, const void* v, const float* 
   const int64_t nblocks = nchain * (dv / gdn::pipe::DVS);
   if (nblocks > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
   const int xcd_map = (nchain % 8) == 0;
-  hipLaunchKernelGGL(gdn::pipe::chunk_fwd_pipe_kernel, dim3((unsigned)nblocks), dim3(256), 0,
+  hipLaunchKernelGGL(gdn::pipe::chunk_fwd_pipe_kernel, dim3((unsigned)nblocks), dim3(64 * gdn::pipe::NWAVES), 0,
                      stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                      static_cast<const bf16_t*>(v), alpha, beta, s0, static_cast<bf16_t*>(o), sT,
                      (int)nchain, T, (int)dv, xcd_map);
