@@ -18,9 +18,10 @@
 //   O = diag(2^g) Q S^T + P U
 //   S' = 2^(g_C) S + U^T diag(2^(g_C - g)) K
 //
-// Workgroup = 6 waves, one (sequence, 32-row value slice) per workgroup, one
+// Workgroup = 7 waves, one (sequence, 32-row value slice) per workgroup, one
 // workgroup barrier per period.  Waves 0..3 run on four different SIMDs and
-// wave 4 (5) shares the SIMD of wave 0 (1).  In period p:
+// wave w + 4 shares the SIMD of wave w, so the two state waves get SIMDs that
+// no other busy wave uses.  In period p:
 //   waves 0, 1 (state)  each own 16 rows of the value slice.  They finish the
 //                       output of chunk p-1 (O += P U) and run the S-dependent
 //                       part of chunk p.  The fp32 state stays in MFMA
@@ -29,9 +30,11 @@
 //                       chunk p+6 so that later loads hit L2.
 //   wave 3 (L)          builds L and the gate tables of chunk p+2 from keys and
 //                       gates it loaded one period earlier, then loads p+3.
-//   wave 4 (inverse)    builds Ti = (I + L)^-1 of chunk p+1.
-//   wave 5 (loader)     moves K, Q, V of chunk p+1 into LDS with LDS-DMA loads
-//                       and waits for them.
+//   wave 4 (loader)     moves K, Q, V of chunk p+1 into LDS with LDS-DMA loads
+//                       and waits for them (it issues little, so it may share
+//                       the SIMD of a state wave).
+//   wave 5              only takes part in the barriers.
+//   wave 6 (inverse)    builds Ti = (I + L)^-1 of chunk p+1.
 // Every buffer written in period p is read by another wave only after the
 // barrier that ends period p, and none is rewritten while another wave still
 // reads it (double buffering by chunk parity).
@@ -57,7 +60,7 @@ namespace pipe {
 constexpr int C = 64;
 constexpr int DK = 128;
 constexpr int DVS = 32;   // value columns per workgroup
-constexpr int NWAVES = 6;
+constexpr int NWAVES = 7;
 constexpr int TTS = 72;   // row stride (elements) of Ti^T
 constexpr int LDR = 20;   // row stride (floats) of the fp32 diagonal blocks of L
 
@@ -159,6 +162,17 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Workgroup barrier that orders LDS only.  A full __syncthreads() also waits
+// for every outstanding global load and store of the wave (vmcnt(0)), which
+// would drain the loads that are meant to stay in flight across periods.
+// Data that crosses a barrier here lives in LDS; LDS-DMA loads are waited for
+// explicitly by the wave that issues them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trips):
 // row_shr 1, 2, 4, 8 scan each row of 16 lanes; row_bcast15 and row_bcast31
 // then add the totals of the preceding rows.  Lanes without a source take 0.
@@ -226,23 +240,41 @@ struct StateRegs {
   bf16x8_t Uprev[2]; // U of the previous chunk as kappa operands
 };
 
-// O of chunk c = Oprev + U P^T, stored to global memory.
-__device__ __forceinline__ void state_finish_output(const Smem& sm, const Seq& sq, const StateAddr& A,
-                                                    const StateRegs& R, int64_t c, int DV) {
-  const char* Pb = reinterpret_cast<const char*>(sm.P[c & 1]);
+// One period of a state wave: with FINISH, the output of chunk c - 1
+// (Oprev + Uprev P^T) is completed and stored; with CHAIN, the S-dependent
+// part of chunk c runs.  Both sit in one basic block, and the LDS reads are
+// software-pipelined: every operand is read one step before the products
+// that use it (scheduling barriers keep the order), while the register
+// footprint stays within what two waves per SIMD can hold.
+__device__ __forceinline__ void finish_output(const Seq& sq, const StateAddr& A, const StateRegs& R,
+                                              const bf16x8_t (&pf)[4][2], int64_t c, int DV) {
   const uint32_t obase = (uint32_t)(c * C * DV * 2) + A.o;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     f32x4 acc = R.Oprev[rb];
 #pragma unroll
-    for (int pp = 0; pp <= rb / 2; ++pp)
-      acc = mfma(R.Uprev[pp], as_op(lds_at<uint4>(Pb, A.pfr[pp] + rb * 2048)), acc);
+    for (int pp = 0; pp <= rb / 2; ++pp) acc = mfma(R.Uprev[pp], pf[rb][pp], acc);
     buf_st8(sq.o, obase + (uint32_t)(rb * 16 * DV * 2), pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
   }
 }
+__device__ __forceinline__ void read_p(const Smem& sm, const StateAddr& A, int64_t c, bf16x8_t (&pf)[4][2]) {
+  const char* Pb = reinterpret_cast<const char*>(sm.P[c & 1]);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int pp = 0; pp <= rb / 2; ++pp) pf[rb][pp] = as_op(lds_at<uint4>(Pb, A.pfr[pp] + rb * 2048));
+}
 
-__device__ __forceinline__ void state_chunk(const Smem& sm, const StateAddr& A, StateRegs& R,
-                                            int64_t c, int lane) {
+template <bool FINISH, bool CHAIN>
+__device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, const StateAddr& A,
+                                             StateRegs& R, int64_t c, int DV, int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+  bf16x8_t pf[4][2];
+  if constexpr (!CHAIN) {
+    read_p(sm, A, c - 1, pf);
+    finish_output(sq, A, R, pf, c - 1, DV);
+    return;
+  }
   const int buf = (int)(c & 1);
   const char* Kb = reinterpret_cast<const char*>(lds_K[buf]);
   const char* Qb = reinterpret_cast<const char*>(lds_Q[buf]);
@@ -250,83 +282,132 @@ __device__ __forceinline__ void state_chunk(const Smem& sm, const StateAddr& A, 
   const char* Tb = reinterpret_cast<const char*>(sm.Tt[buf]);
   const int gb = (int)(c % 3);
   const float* gt = &sm.gate[gb][0][0];
-  const int lr = lane & 15, lg = lane >> 4;
+  const float decay = sm.egl[gb][0];
 
-  // Operands of S for contractions over the key index (natural key order).
+  // ---- O1 = S Q^T (tile per 16-token block, rows = value) and Z = K S^T
+  // (rows = token); the fragments of block rb + 1 are read while the products
+  // of block rb run, and the decay of the carried state fills the gaps.
   bf16x8_t Sop[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) Sop[pp] = pack_op(R.S[2 * pp], R.S[2 * pp + 1]);
-  const float decay = sm.egl[gb][0];
-#pragma unroll
-  for (int jb = 0; jb < 8; ++jb) R.S[jb] *= decay;
-
-  // O1 = S Q^T (tile per 16-token block, rows = value) and Z = K S^T (rows = token).
   f32x4 O1[4], Z[4];
+  bf16x8_t qf[2][4], kf[2][4];
+  uint2 vv[4];
+  float4 b4[4], g4[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    qf[0][pp] = as_op(lds_at<uint4>(Qb, A.frag[pp]));
+    kf[0][pp] = as_op(lds_at<uint4>(Kb, A.frag[pp]));
+  }
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
+    const int cur = rb & 1;
+    if (rb < 3) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        qf[cur ^ 1][pp] = as_op(lds_at<uint4>(Qb, A.frag[pp] + (rb + 1) * 4096));
+        kf[cur ^ 1][pp] = as_op(lds_at<uint4>(Kb, A.frag[pp] + (rb + 1) * 4096));
+      }
+    }
+    if (rb == 2) {
+#pragma unroll
+      for (int r2 = 0; r2 < 4; ++r2) {
+        vv[r2] = lds_tr(Vb, A.vtr + r2 * 16 * DVS * 2);
+        b4[r2] = *reinterpret_cast<const float4*>(gt + G_BETA * C + 16 * r2 + 4 * lg);
+        g4[r2] = *reinterpret_cast<const float4*>(gt + G_BEG * C + 16 * r2 + 4 * lg);
+      }
+    }
+    if (rb == 3) {
+      if constexpr (FINISH) read_p(sm, A, c - 1, pf);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 ao = zero4(), az = zero4();
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      const bf16x8_t qf = as_op(lds_at<uint4>(Qb, A.frag[pp] + rb * 4096));
-      const bf16x8_t kf = as_op(lds_at<uint4>(Kb, A.frag[pp] + rb * 4096));
-      ao = mfma(Sop[pp], qf, ao);
-      az = mfma(kf, Sop[pp], az);
+      ao = mfma(Sop[pp], qf[cur][pp], ao);
+      az = mfma(kf[cur][pp], Sop[pp], az);
     }
+    R.S[2 * rb] *= decay;
+    R.S[2 * rb + 1] *= decay;
     O1[rb] = ao;
     Z[rb] = az;
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // Y = beta V - beta 2^g Z as kappa operands over tokens.
+
+  // ---- operands of U = Ti Y and of the scaled U, read while the previous
+  // chunk's output is finished
+  bf16x8_t tf[4][2];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int pp = 0; pp <= rb / 2; ++pp) {
+      const int off = A.ttr + pp * 32 * TTS * 2 + rb * 32;
+      tf[rb][pp] = as_op(lds_tr(Tb, off), lds_tr(Tb, off + 16 * TTS * 2));
+    }
+  f32x4 el[4];
+  float eg[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float4 e = *reinterpret_cast<const float4*>(gt + G_EL * C + 16 * h + 4 * lg);
+    el[h] = f32x4{e.x, e.y, e.z, e.w};
+    eg[h] = gt[G_EG * C + 16 * h + lr];
+  }
+  if constexpr (FINISH) finish_output(sq, A, R, pf, c - 1, DV);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- Y = beta V - beta 2^g Z as kappa operands over tokens
   f32x4 y[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
-    const float4 b4 = *reinterpret_cast<const float4*>(gt + G_BETA * C + 16 * rb + 4 * lg);
-    const float4 g4 = *reinterpret_cast<const float4*>(gt + G_BEG * C + 16 * rb + 4 * lg);
-    const uint2 vv = lds_tr(Vb, A.vtr + rb * 16 * DVS * 2);
-    y[rb][0] = b4.x * __uint_as_float(vv.x << 16) - g4.x * Z[rb][0];
-    y[rb][1] = b4.y * __uint_as_float(vv.x & 0xffff0000u) - g4.y * Z[rb][1];
-    y[rb][2] = b4.z * __uint_as_float(vv.y << 16) - g4.z * Z[rb][2];
-    y[rb][3] = b4.w * __uint_as_float(vv.y & 0xffff0000u) - g4.w * Z[rb][3];
+    y[rb][0] = b4[rb].x * __uint_as_float(vv[rb].x << 16) - g4[rb].x * Z[rb][0];
+    y[rb][1] = b4[rb].y * __uint_as_float(vv[rb].x & 0xffff0000u) - g4[rb].y * Z[rb][1];
+    y[rb][2] = b4[rb].z * __uint_as_float(vv[rb].y << 16) - g4[rb].z * Z[rb][2];
+    y[rb][3] = b4[rb].w * __uint_as_float(vv[rb].y & 0xffff0000u) - g4[rb].w * Z[rb][3];
   }
   const bf16x8_t Yop[2] = {pack_op(y[0], y[1]), pack_op(y[2], y[3])};
-  // O1 carries the factor 2^g of its token column.
+  // ---- U = Ti Y; Ti is lower triangular, so row block rb only needs the
+  // 32-token blocks pp <= rb/2 (the upper 16x16 blocks inside them are zero).
+  // The first K^T operands of the state update are read meanwhile.
+  bf16x8_t kt[2][2];
+  auto read_kt = [&](int jb, bf16x8_t (&dst)[2]) {
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) R.Oprev[rb] = O1[rb] * gt[G_EG * C + 16 * rb + lr];
-  // U = Ti Y; Ti is lower triangular, so row block rb only needs the 32-token
-  // blocks pp <= rb/2 (the upper 16x16 blocks inside them are zero).
+    for (int pp = 0; pp < 2; ++pp) {
+      const int off = A.ktr[jb >> 1] + (jb & 1) * 8 + pp * 32 * 256;
+      dst[pp] = as_op(lds_tr(Kb, off), lds_tr(Kb, off + 16 * 256));
+    }
+  };
+  read_kt(0, kt[0]);
   f32x4 U[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     f32x4 acc = zero4();
 #pragma unroll
-    for (int pp = 0; pp <= rb / 2; ++pp) {
-      const int off = A.ttr + pp * 32 * TTS * 2 + rb * 32;
-      const bf16x8_t tf = as_op(lds_tr(Tb, off), lds_tr(Tb, off + 16 * TTS * 2));
-      acc = mfma(tf, Yop[pp], acc);
-    }
+    for (int pp = 0; pp <= rb / 2; ++pp) acc = mfma(tf[rb][pp], Yop[pp], acc);
     U[rb] = acc;
   }
+  // O1 carries the factor 2^g of its token column.
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) R.Oprev[rb] = O1[rb] * eg[rb];
   // Operands of U: plain (for O) and scaled by 2^(g_C - g_s) (for S).
   bf16x8_t Uh[2];
 #pragma unroll
   for (int pp = 0; pp < 2; ++pp) {
-    const float4 e0 = *reinterpret_cast<const float4*>(gt + G_EL * C + 32 * pp + 4 * lg);
-    const float4 e1 = *reinterpret_cast<const float4*>(gt + G_EL * C + 32 * pp + 16 + 4 * lg);
-    const f32x4 s0 = {e0.x, e0.y, e0.z, e0.w}, s1 = {e1.x, e1.y, e1.z, e1.w};
     R.Uprev[pp] = pack_op(U[2 * pp], U[2 * pp + 1]);
-    Uh[pp] = pack_op(U[2 * pp] * s0, U[2 * pp + 1] * s1);
+    Uh[pp] = pack_op(U[2 * pp] * el[2 * pp], U[2 * pp + 1] * el[2 * pp + 1]);
   }
-  // S^T += K^T Uh with K^T from transposed reads: supplier lane (a, r) of a
-  // 16-lane group addresses 4 key columns of token 4 lg + r.
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- S^T += K^T Uh with K^T from transposed reads: supplier lane (a, r) of
+  // a 16-lane group addresses 4 key columns of token 4 lg + r.  The operands
+  // of tile jb + 1 are read while the products of tile jb run.
 #pragma unroll
   for (int jb = 0; jb < 8; ++jb) {
+    if (jb < 7) read_kt(jb + 1, kt[(jb + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 acc = R.S[jb];
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const int off = A.ktr[jb >> 1] + (jb & 1) * 8 + pp * 32 * 256;
-      const bf16x8_t kt = as_op(lds_tr(Kb, off), lds_tr(Kb, off + 16 * 256));
-      acc = mfma(kt, Uh[pp], acc);
-    }
+    for (int pp = 0; pp < 2; ++pp) acc = mfma(kt[jb & 1][pp], Uh[pp], acc);
     R.S[jb] = acc;
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -639,12 +720,21 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
         R.S[jb] = f32x4{s4.x, s4.y, s4.z, s4.w};
       }
     }
-    __syncthreads();
-    for (int64_t p = -2; p <= nch; ++p) {
-      if (p >= 1) state_finish_output(sm, sq, A, R, p - 1, DV);
-      if (p >= 0 && p < nch) state_chunk(sm, A, R, p, lane);
-      __syncthreads();
+    // the set-up barrier, periods -2 and -1 (nothing to do yet), chunk 0, the
+    // steady state (output of chunk p-1 and chain of chunk p), the last output
+    lds_barrier();
+    lds_barrier();
+    lds_barrier();
+    if (nch > 0) {
+      state_period<false, true>(sm, sq, A, R, 0, DV, lane);
+      lds_barrier();
+      for (int64_t p = 1; p < nch; ++p) {
+        state_period<true, true>(sm, sq, A, R, p, DV, lane);
+        lds_barrier();
+      }
+      state_period<true, false>(sm, sq, A, R, nch, DV, lane);
     }
+    lds_barrier();
     if (final_state) {
 #pragma unroll
       for (int jb = 0; jb < 8; ++jb)
@@ -652,36 +742,39 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     }
   } else if (wave == 2) {
     const StateAddr A = state_addr(lane, 0, DV);
-    __syncthreads();
+    lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
       if (p >= 0 && p < nch) build_p(sm, A, p, lane);
       if (p + PREFETCH_AHEAD < nch) prefetch_chunk(sq, p + PREFETCH_AHEAD, slice, DV, lane);
-      __syncthreads();
+      lds_barrier();
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no LDS-DMA write outlives the workgroup
   } else if (wave == 3) {
     FragRegs R;
     if (nch > 0) load_frags(R, sq, 0, lane);
-    __syncthreads();
+    lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
       if (p + 2 < nch) build_l(sm, R, p + 2, Tlen, lane);
       if (p + 3 < nch) load_frags(R, sq, p + 3, lane);
-      __syncthreads();
+      lds_barrier();
     }
   } else if (wave == 4) {
-    __syncthreads();
-    for (int64_t p = -2; p <= nch; ++p) {
-      if (p + 1 >= 0 && p + 1 < nch) build_inverse(sm, p + 1, lane);
-      __syncthreads();
-    }
-  } else {
     const DmaAddr D = dma_addr(lane, DV);
-    __syncthreads();
+    lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
       if (p + 1 >= 0 && p + 1 < nch) dma_chunk(sq, D, p + 1, DV);
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): chunk p+1 is in LDS
-      __syncthreads();
+      lds_barrier();
     }
+  } else if (wave == 6) {
+    lds_barrier();
+    for (int64_t p = -2; p <= nch; ++p) {
+      if (p + 1 >= 0 && p + 1 < nch) build_inverse(sm, p + 1, lane);
+      lds_barrier();
+    }
+  } else {
+    lds_barrier();
+    for (int64_t p = -2; p <= nch; ++p) lds_barrier();
   }
 }
 
