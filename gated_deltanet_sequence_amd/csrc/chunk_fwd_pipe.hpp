@@ -28,10 +28,12 @@
 //                       accumulators for the whole sequence.
 //   wave 2 (P)          builds P of chunk p and touches the cache lines of
 //                       chunk p+6 so that later loads hit L2.
-//   wave 3 (L)          builds L and the gate tables of chunk p+2 from keys and
-//                       gates it loaded one period earlier, then loads p+3.
-//   wave 4 (loader)     moves K, Q, V of chunk p+1 into LDS with LDS-DMA loads
-//                       and waits for them (it issues little, so it may share
+//   wave 3 (L)          builds L of chunk p+2 from keys it loaded one period
+//                       earlier, then loads the keys of chunk p+3.
+//   wave 4 (loader)     moves K, Q, V of chunk p+1 into LDS with LDS-DMA loads,
+//                       builds the gate tables of chunk p+3 from gates it loaded
+//                       one period earlier, loads the gates of chunk p+4 and
+//                       waits for its loads (it issues little, so it may share
 //                       the SIMD of a state wave).
 //   wave 5              only takes part in the barriers.
 //   wave 6 (inverse)    builds Ti = (I + L)^-1 of chunk p+1.
@@ -85,8 +87,8 @@ __shared__ __attribute__((aligned(16))) uint32_t lds_touch[64];    // landing ar
 struct __attribute__((aligned(16))) Smem {
   bf16_t P[2][C * C];       // [r][s], s kappa-ordered, octets swizzled by swz_p(r)
   bf16_t Tt[2][C * TTS];    // Ti^T: [s][t]
-  float gate[3][G_N][C];    // written two periods before use: three buffers
-  float egl[3][4];          // 2^(g_C)
+  float gate[4][G_N][C];    // written three periods before the last use: four buffers
+  float egl[4][4];          // 2^(g_C)
   float Ld[2][4][16 * LDR + 4];  // strictly-lower diagonal 16x16 blocks of L, fp32
                                 // (blocks padded by 16 bytes: the inverse reads
                                 // the four blocks at once without bank conflicts)
@@ -114,6 +116,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// voff: per-lane byte offset; soff: wave-uniform byte offset (scalar register)
+__device__ __forceinline__ uint4 buf_ld16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ float buf_ldf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -180,6 +187,17 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Barrier for the wave that keeps LDS-DMA prefetch loads in flight across
+// periods: an LDS-scope release fence would wait for those loads too (they
+// write LDS), so this drains only the LDS counter (the wave's own LDS writes
+// are complete) and stops the compiler from moving memory operations across.
+__device__ __forceinline__ void lds_barrier_keep_dma() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trips):
@@ -291,62 +309,70 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   const char* Qb = reinterpret_cast<const char*>(lds_Q[buf]);
   const char* Vb = reinterpret_cast<const char*>(lds_V[buf]);
   const char* Tb = reinterpret_cast<const char*>(sm.Tt[buf]);
-  const int gb = (int)(c % 3);
+  const int gb = (int)(c & 3);
   const float* gt = &sm.gate[gb][0][0];
   const float decay = sm.egl[gb][0];
 
-  // ---- O1 = S Q^T (tile per 16-token block, rows = value) and Z = K S^T
-  // (rows = token); the fragments of block rb + 1 are read while the products
-  // of block rb run, and the decay of the carried state fills the gaps.
+  // The chain of this chunk is ordered so that VALU work runs beside
+  // independent MFMAs: Z = K S^T first, then O1 = S Q^T while Y is formed
+  // from Z, U = Ti Y while O1 is scaled, the previous chunk's O2 while the
+  // operands of U are packed, and finally the state update.
   bf16x8_t Sop[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) Sop[pp] = pack_op(R.S[2 * pp], R.S[2 * pp + 1]);
-  f32x4 O1[4], Z[4];
-  bf16x8_t qf[2][4], kf[2][4];
-  uint2 vv[4];
-  float4 b4[4], g4[4];
+
+  // ---- Z = K S^T (tile per 16-token block, rows = token); the key fragments
+  // of block rb + 1 are read while the products of block rb run, and the
+  // decay of the carried state fills the gaps.
+  f32x4 Z[4];
+  bf16x8_t fr[2][4];
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) {
-    qf[0][pp] = as_op(lds_at<uint4>(Qb, A.frag[pp]));
-    kf[0][pp] = as_op(lds_at<uint4>(Kb, A.frag[pp]));
-  }
+  for (int pp = 0; pp < 4; ++pp) fr[0][pp] = as_op(lds_at<uint4>(Kb, A.frag[pp]));
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const int cur = rb & 1;
-    if (rb < 3) {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        qf[cur ^ 1][pp] = as_op(lds_at<uint4>(Qb, A.frag[pp] + (rb + 1) * 4096));
-        kf[cur ^ 1][pp] = as_op(lds_at<uint4>(Kb, A.frag[pp] + (rb + 1) * 4096));
-      }
-    }
-    if (rb == 2) {
-#pragma unroll
-      for (int r2 = 0; r2 < 4; ++r2) {
-        vv[r2] = lds_tr(Vb, A.vtr + r2 * 16 * DVS * 2);
-        b4[r2] = *reinterpret_cast<const float4*>(gt + G_BETA * C + 16 * r2 + 4 * lg);
-        g4[r2] = *reinterpret_cast<const float4*>(gt + G_BEG * C + 16 * r2 + 4 * lg);
-      }
-    }
-    if (rb == 3) {
-      if constexpr (FINISH) read_p(sm, A, c - 1, pf);
-    }
+    for (int pp = 0; pp < 4; ++pp)
+      fr[cur ^ 1][pp] = as_op(lds_at<uint4>(rb < 3 ? Kb : Qb, A.frag[pp] + (rb < 3 ? (rb + 1) * 4096 : 0)));
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 ao = zero4(), az = zero4();
+    f32x4 az = zero4();
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      ao = mfma(Sop[pp], qf[cur][pp], ao);
-      az = mfma(kf[cur][pp], Sop[pp], az);
-    }
+    for (int pp = 0; pp < 4; ++pp) az = mfma(fr[cur][pp], Sop[pp], az);
     R.S[2 * rb] *= decay;
     R.S[2 * rb + 1] *= decay;
-    O1[rb] = ao;
     Z[rb] = az;
     __builtin_amdgcn_sched_barrier(0);
   }
-
-  // ---- operands of U = Ti Y and of the scaled U, read while the previous
-  // chunk's output is finished
+  // ---- O1 = S Q^T (rows = value, columns = token) while Y = beta V -
+  // beta 2^g Z is formed; V, the gates and Ti are read meanwhile.
+  uint2 vv[4];
+  float4 b4[4], g4[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    vv[rb] = lds_tr(Vb, A.vtr + rb * 16 * DVS * 2);
+    b4[rb] = *reinterpret_cast<const float4*>(gt + G_BETA * C + 16 * rb + 4 * lg);
+    g4[rb] = *reinterpret_cast<const float4*>(gt + G_BEG * C + 16 * rb + 4 * lg);
+  }
+  f32x4 O1[4], y[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int cur = rb & 1;  // block rb of Q sits in fr[cur] (block 0 was read last above)
+    if (rb < 3) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) fr[cur ^ 1][pp] = as_op(lds_at<uint4>(Qb, A.frag[pp] + (rb + 1) * 4096));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 ao = zero4();
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) ao = mfma(Sop[pp], fr[cur][pp], ao);
+    O1[rb] = ao;
+    y[rb][0] = b4[rb].x * __uint_as_float(vv[rb].x << 16) - g4[rb].x * Z[rb][0];
+    y[rb][1] = b4[rb].y * __uint_as_float(vv[rb].x & 0xffff0000u) - g4[rb].y * Z[rb][1];
+    y[rb][2] = b4[rb].z * __uint_as_float(vv[rb].y << 16) - g4[rb].z * Z[rb][2];
+    y[rb][3] = b4[rb].w * __uint_as_float(vv[rb].y & 0xffff0000u) - g4[rb].w * Z[rb][3];
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const bf16x8_t Yop[2] = {pack_op(y[0], y[1]), pack_op(y[2], y[3])};
   bf16x8_t tf[4][2];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
@@ -363,22 +389,8 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     el[h] = f32x4{e.x, e.y, e.z, e.w};
     eg[h] = gt[G_EG * C + 16 * h + lr];
   }
-  if constexpr (FINISH) finish_output(sq, A, R, pf, c - 1, DV);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- Y = beta V - beta 2^g Z as kappa operands over tokens
-  f32x4 y[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    y[rb][0] = b4[rb].x * __uint_as_float(vv[rb].x << 16) - g4[rb].x * Z[rb][0];
-    y[rb][1] = b4[rb].y * __uint_as_float(vv[rb].x & 0xffff0000u) - g4[rb].y * Z[rb][1];
-    y[rb][2] = b4[rb].z * __uint_as_float(vv[rb].y << 16) - g4[rb].z * Z[rb][2];
-    y[rb][3] = b4[rb].w * __uint_as_float(vv[rb].y & 0xffff0000u) - g4[rb].w * Z[rb][3];
-  }
-  const bf16x8_t Yop[2] = {pack_op(y[0], y[1]), pack_op(y[2], y[3])};
-  // ---- U = Ti Y; Ti is lower triangular, so row block rb only needs the
-  // 32-token blocks pp <= rb/2 (the upper 16x16 blocks inside them are zero).
-  // The first K^T operands of the state update are read meanwhile.
+  if constexpr (FINISH) read_p(sm, A, c - 1, pf);
+  // the first K^T operands of the state update
   bf16x8_t kt[2][2];
   auto read_kt = [&](int jb, bf16x8_t (&dst)[2]) {
 #pragma unroll
@@ -388,23 +400,46 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     }
   };
   read_kt(0, kt[0]);
-  f32x4 U[4];
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- U = Ti Y (Ti lower triangular: row block rb needs the 32-token blocks
+  // pp <= rb/2, the upper 16x16 blocks inside them are zero) while O1 takes
+  // the factor 2^g of its token column.
+  f32x4 U[4], Onew[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     f32x4 acc = zero4();
 #pragma unroll
     for (int pp = 0; pp <= rb / 2; ++pp) acc = mfma(tf[rb][pp], Yop[pp], acc);
     U[rb] = acc;
+    Onew[rb] = O1[rb] * eg[rb];
   }
-  // O1 carries the factor 2^g of its token column.
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- output of the previous chunk while the operands of U are packed:
+  // plain (for O) and scaled by 2^(g_C - g_s) (for S).
+  f32x4 Ofin[4];
+  if constexpr (FINISH) {
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) R.Oprev[rb] = O1[rb] * eg[rb];
-  // Operands of U: plain (for O) and scaled by 2^(g_C - g_s) (for S).
+    for (int rb = 0; rb < 4; ++rb) {
+      f32x4 acc = R.Oprev[rb];
+#pragma unroll
+      for (int pp = 0; pp <= rb / 2; ++pp) acc = mfma(R.Uprev[pp], pf[rb][pp], acc);
+      Ofin[rb] = acc;
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) R.Oprev[rb] = Onew[rb];
   bf16x8_t Uh[2];
 #pragma unroll
   for (int pp = 0; pp < 2; ++pp) {
     R.Uprev[pp] = pack_op(U[2 * pp], U[2 * pp + 1]);
     Uh[pp] = pack_op(U[2 * pp] * el[2 * pp], U[2 * pp + 1] * el[2 * pp + 1]);
+  }
+  if constexpr (FINISH) {
+    const uint32_t obase = (uint32_t)((c - 1) * C * DV * 2) + A.o;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+      buf_st8(sq.o, obase + (uint32_t)(rb * 16 * DV * 2), pack2(Ofin[rb][0], Ofin[rb][1]),
+              pack2(Ofin[rb][2], Ofin[rb][3]));
   }
   __builtin_amdgcn_sched_barrier(0);
   // ---- S^T += K^T Uh with K^T from transposed reads: supplier lane (a, r) of
@@ -477,43 +512,68 @@ __device__ __forceinline__ void prefetch_chunk(const Seq& sq, int64_t c, int sli
   __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.b, land, 4, g, 0, 0, 0);
 }
 
+// The 10 lower 16x16 tiles of a 64x64 chunk matrix, in the order the P and
+// L waves build them: (row block rb, column block sb), sb <= rb.
+constexpr int TILE_RB[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+constexpr int TILE_SB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+
+// P of chunk c.  Tiles are software-pipelined: the products of tile t + 1 are
+// issued before the decay, mask and store of tile t.
 __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const int buf = (int)(c & 1);
   const char* Kb = reinterpret_cast<const char*>(lds_K[buf]);
   const char* Qb = reinterpret_cast<const char*>(lds_Q[buf]);
-  const float* gt = &sm.gate[c % 3][0][0];
+  const float* gt = &sm.gate[c & 3][0][0];
   char* Pb = reinterpret_cast<char*>(sm.P[buf]);
   int pw[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) pw[h] = lr * 128 + (((4 * h + lg) ^ swz_p(lr)) << 4);
-  bf16x8_t kf[4][4];
+  bf16x8_t kf[4][4], qf[4][4];
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) kf[b][pp] = as_op(lds_at<uint4>(Kb, A.frag[pp] + b * 4096));
-  // tiles [s-block sb][r-block rb], sb <= rb: element (s, r) = k_s . q_r
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    bf16x8_t qf[4];
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) qf[pp] = as_op(lds_at<uint4>(Qb, A.frag[pp] + rb * 4096));
-    const float gr = gt[G_LOG * C + 16 * rb + lr];
+    for (int pp = 0; pp < 4; ++pp) qf[b][pp] = as_op(lds_at<uint4>(Qb, A.frag[pp] + b * 4096));
+  float gr[4];
+  float4 gs4[4];
 #pragma unroll
-    for (int sb = 0; sb <= rb; ++sb) {
-      f32x4 acc = zero4();
+  for (int b = 0; b < 4; ++b) {
+    gr[b] = gt[G_LOG * C + 16 * b + lr];
+    gs4[b] = *reinterpret_cast<const float4*>(gt + G_LOG * C + 16 * b + 4 * lg);
+  }
+  // element (s, r) = k_s . q_r of tile t
+  auto tile = [&](int t) {
+    f32x4 acc = zero4();
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) acc = mfma(kf[sb][pp], qf[pp], acc);
-      const float4 g4 = *reinterpret_cast<const float4*>(gt + G_LOG * C + 16 * sb + 4 * lg);
-      float val[4] = {fast_exp2(gr - g4.x) * acc[0], fast_exp2(gr - g4.y) * acc[1],
-                      fast_exp2(gr - g4.z) * acc[2], fast_exp2(gr - g4.w) * acc[3]};
-      if (sb == rb) {
+    for (int pp = 0; pp < 4; ++pp) acc = mfma(kf[TILE_SB[t]][pp], qf[TILE_RB[t]][pp], acc);
+    return acc;
+  };
+  f32x4 acc[2];
+  acc[0] = tile(0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = (4 * lg + e <= lr) ? val[e] : 0.f;
-      }
-      lds_put<uint2>(Pb, pw[sb >> 1] + (sb & 1) * 8 + rb * 2048,
-                     make_uint2(pack2(val[0], val[1]), pack2(val[2], val[3])));
+  for (int t = 0; t < 10; ++t) {
+    const int rb = TILE_RB[t], sb = TILE_SB[t];
+    if (sb == 0 && rb >= 1 && rb < 3) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) qf[rb + 1][pp] = as_op(lds_at<uint4>(Qb, A.frag[pp] + (rb + 1) * 4096));
     }
+    if (t + 1 < 10) acc[(t + 1) & 1] = tile(t + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x4 a = acc[t & 1];
+    const float4 g4 = gs4[sb];
+    float val[4] = {fast_exp2(gr[rb] - g4.x) * a[0], fast_exp2(gr[rb] - g4.y) * a[1],
+                    fast_exp2(gr[rb] - g4.z) * a[2], fast_exp2(gr[rb] - g4.w) * a[3]};
+    if (sb == rb) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = (4 * lg + e <= lr) ? val[e] : 0.f;
+    }
+    lds_put<uint2>(Pb, pw[sb >> 1] + (sb & 1) * 8 + rb * 2048,
+                   make_uint2(pack2(val[0], val[1]), pack2(val[2], val[3])));
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -522,67 +582,80 @@ __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c,
 // of token 16 rb + lr.
 struct FragRegs {
   uint4 kf[4][4];
-  float a, b;  // alpha, beta of token `lane` as loaded (0 past the end)
 };
 
 __device__ __forceinline__ void load_frags(FragRegs& R, const Seq& sq, int64_t c, int lane) {
-  const uint32_t base =
-      (uint32_t)(c * C * DK * 2) + (uint32_t)((lane & 15) * DK * 2 + (lane >> 4) * 16);
+  const uint32_t lane_off = (uint32_t)((lane & 15) * DK * 2 + (lane >> 4) * 16);
+  const uint32_t base = (uint32_t)(c * C * DK * 2);
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) R.kf[rb][pp] = buf_ld16(sq.k, base + rb * 16 * DK * 2 + pp * 64);
-  const int64_t t = c * C + lane;
-  R.a = buf_ldf(sq.a, (uint32_t)(t * 4));
-  R.b = buf_ldf(sq.b, (uint32_t)(t * 4));
+    for (int pp = 0; pp < 4; ++pp) R.kf[rb][pp] = buf_ld16s(sq.k, lane_off, base + rb * 16 * DK * 2 + pp * 64);
 }
 
-// Gate tables and L of chunk c.  L: diagonal blocks as fp32 rows,
-// off-diagonal blocks as bf16 in the order in which the inverse consumes them
-// as MFMA A operands.
-__device__ __forceinline__ void build_l(Smem& sm, const FragRegs& R, int64_t c, int64_t T, int lane) {
+// Gate tables of chunk c (alpha, beta of token `lane` as loaded, 0 past the
+// end): beta, beta 2^g, 2^g, 2^(g_C - g), g and 2^(g_C), with g the
+// log2-prefix of alpha.
+__device__ __forceinline__ void build_gates(Smem& sm, float ra, float rb, int64_t c, int64_t T, int lane) {
+  float* gt = &sm.gate[c & 3][0][0];
+  // tokens past the end are identity maps (alpha 1, beta 0)
+  const bool live = c * C + lane < T;
+  const float a = live ? ra : 1.f, b = live ? rb : 0.f;
+  const float gs = wave_prefix_sum(fmaxf(fast_log2(a), LOG2_ALPHA_MIN));
+  const float glast = lane63(gs);
+  const float eg = fast_exp2(gs);
+  gt[G_BETA * C + lane] = b;
+  gt[G_BEG * C + lane] = b * eg;
+  gt[G_EG * C + lane] = eg;
+  gt[G_EL * C + lane] = fast_exp2(glast - gs);
+  gt[G_LOG * C + lane] = gs;
+  if (lane == 0) sm.egl[c & 3][0] = fast_exp2(glast);
+}
+
+// L of chunk c: diagonal blocks as fp32 rows, off-diagonal blocks as bf16 in
+// the order in which the inverse consumes them as MFMA A operands.  beta_r
+// enters through the exponent, beta_r 2^(g_r - g_s) = 2^(g_r + log2 beta_r -
+// g_s) (beta_r = 0 gives 0), and the tiles are software-pipelined as in
+// build_p.
+__device__ __forceinline__ void build_l(Smem& sm, const FragRegs& R, int64_t c, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const int lb = (int)(c & 1);
-  float* gt = &sm.gate[c % 3][0][0];
-  {
-    // one lane per token; tokens past the end are identity maps (alpha 1, beta 0)
-    const bool live = c * C + lane < T;
-    const float a = live ? R.a : 1.f, b = live ? R.b : 0.f;
-    const float gs = wave_prefix_sum(fmaxf(fast_log2(a), LOG2_ALPHA_MIN));
-    const float glast = lane63(gs);
-    const float eg = fast_exp2(gs);
-    gt[G_BETA * C + lane] = b;
-    gt[G_BEG * C + lane] = b * eg;
-    gt[G_EG * C + lane] = eg;
-    gt[G_EL * C + lane] = fast_exp2(glast - gs);
-    gt[G_LOG * C + lane] = gs;
-    if (lane == 0) sm.egl[c % 3][0] = fast_exp2(glast);
+  const float* gt = &sm.gate[c & 3][0][0];
+  float grb[4];
+  float4 gs4[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    grb[b] = gt[G_LOG * C + 16 * b + lr] + fast_log2(gt[G_BETA * C + 16 * b + lr]);
+    gs4[b] = *reinterpret_cast<const float4*>(gt + G_LOG * C + 16 * b + 4 * lg);
   }
-  wave_lds_fence();
-  // tiles [s-block sb][r-block rb], sb <= rb: lane holds L[16rb + lr][16sb + 4lg + e]
+  // tile t: lane holds k_r . k_s for r = 16rb + lr, s = 16sb + 4lg + e
+  auto tile = [&](int t) {
+    f32x4 acc = zero4();
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int r = 16 * rb + lr;
-    const float gr = gt[G_LOG * C + r];
-    const float br = gt[G_BETA * C + r];
+    for (int pp = 0; pp < 4; ++pp) acc = mfma(as_op(R.kf[TILE_SB[t]][pp]), as_op(R.kf[TILE_RB[t]][pp]), acc);
+    return acc;
+  };
+  f32x4 acc[2];
+  acc[0] = tile(0);
 #pragma unroll
-    for (int sb = 0; sb <= rb; ++sb) {
-      f32x4 acc = zero4();
+  for (int t = 0; t < 10; ++t) {
+    const int rb = TILE_RB[t], sb = TILE_SB[t];
+    if (t + 1 < 10) acc[(t + 1) & 1] = tile(t + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x4 a = acc[t & 1];
+    const float4 g4 = gs4[sb];
+    float val[4] = {fast_exp2(grb[rb] - g4.x) * a[0], fast_exp2(grb[rb] - g4.y) * a[1],
+                    fast_exp2(grb[rb] - g4.z) * a[2], fast_exp2(grb[rb] - g4.w) * a[3]};
+    if (sb == rb) {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) acc = mfma(as_op(R.kf[sb][pp]), as_op(R.kf[rb][pp]), acc);
-      const float4 g4 = *reinterpret_cast<const float4*>(gt + G_LOG * C + 16 * sb + 4 * lg);
-      float val[4] = {br * fast_exp2(gr - g4.x) * acc[0], br * fast_exp2(gr - g4.y) * acc[1],
-                      br * fast_exp2(gr - g4.z) * acc[2], br * fast_exp2(gr - g4.w) * acc[3]};
-      if (sb == rb) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = (4 * lg + e < lr) ? val[e] : 0.f;
-        *reinterpret_cast<float4*>(&sm.Ld[lb][rb][lr * LDR + 4 * lg]) = make_float4(val[0], val[1], val[2], val[3]);
-      } else {
-        const int tix = rb * (rb - 1) / 2 + sb;
-        *reinterpret_cast<uint2*>(&sm.Lo[lb][tix][lane * 4]) =
-            make_uint2(pack2(val[0], val[1]), pack2(val[2], val[3]));
-      }
+      for (int e = 0; e < 4; ++e) val[e] = (4 * lg + e < lr) ? val[e] : 0.f;
+      *reinterpret_cast<float4*>(&sm.Ld[lb][rb][lr * LDR + 4 * lg]) = make_float4(val[0], val[1], val[2], val[3]);
+    } else {
+      const int tix = rb * (rb - 1) / 2 + sb;
+      *reinterpret_cast<uint2*>(&sm.Lo[lb][tix][lane * 4]) =
+          make_uint2(pack2(val[0], val[1]), pack2(val[2], val[3]));
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -759,7 +832,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     for (int64_t p = -2; p <= nch; ++p) {
       if (p >= 0 && p < nch) build_p(sm, A, p, lane);
       if (p + PREFETCH_AHEAD < nch) prefetch_chunk(sq, p + PREFETCH_AHEAD, slice, DV, lane);
-      lds_barrier();
+      lds_barrier_keep_dma();
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no LDS-DMA write outlives the workgroup
   } else if (wave == 3) {
@@ -767,15 +840,29 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     if (nch > 0) load_frags(R, sq, 0, lane);
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
-      if (p + 2 < nch) build_l(sm, R, p + 2, Tlen, lane);
+      if (p + 2 < nch) build_l(sm, R, p + 2, lane);
       if (p + 3 < nch) load_frags(R, sq, p + 3, lane);
       lds_barrier();
     }
   } else if (wave == 4) {
+    // gates of chunk p+3 (loaded one period earlier) and K, Q, V of chunk p+1;
+    // the gates of chunk 0 are built before the first period
     const DmaAddr D = dma_addr(lane, DV);
+    float ga = 0.f, gb = 0.f;
+    if (nch > 0) {
+      build_gates(sm, buf_ldf(sq.a, (uint32_t)(lane * 4)), buf_ldf(sq.b, (uint32_t)(lane * 4)), 0, Tlen, lane);
+      ga = buf_ldf(sq.a, (uint32_t)((C + lane) * 4));
+      gb = buf_ldf(sq.b, (uint32_t)((C + lane) * 4));
+    }
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
       if (p + 1 >= 0 && p + 1 < nch) dma_chunk(sq, D, p + 1, DV);
+      if (p + 3 < nch) {
+        build_gates(sm, ga, gb, p + 3, Tlen, lane);
+        const uint32_t t4 = (uint32_t)(((p + 4) * C + lane) * 4);
+        ga = buf_ldf(sq.a, t4);
+        gb = buf_ldf(sq.b, t4);
+      }
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): chunk p+1 is in LDS
       lds_barrier();
     }
