@@ -26,16 +26,16 @@
 //                       output of chunk p-1 (O += P U) and run the S-dependent
 //                       part of chunk p.  The fp32 state stays in MFMA
 //                       accumulators for the whole sequence.
-//   wave 2 (P)          builds P of chunk p and touches the cache lines of
-//                       chunk p+6 so that later loads hit L2.
+//   wave 2 (P)          builds P of chunk p.
 //   wave 3 (L)          builds L of chunk p+2 from keys it loaded one period
 //                       earlier, then loads the keys of chunk p+3.
-//   wave 4 (loader)     moves K, Q, V of chunk p+1 into LDS with LDS-DMA loads,
-//                       builds the gate tables of chunk p+3 from gates it loaded
-//                       one period earlier, loads the gates of chunk p+4 and
-//                       waits for its loads (it issues little, so it may share
-//                       the SIMD of a state wave).
-//   wave 5              only takes part in the barriers.
+//   wave 4 (loader)     moves V of chunk p+1 and K, Q of chunk p+2 into LDS
+//                       with LDS-DMA loads, builds the gate tables of chunk p+3
+//                       from gates it loaded one period earlier and loads the
+//                       gates of chunk p+4 (it issues little, so it may share the
+//                       SIMD of a state wave).
+//   wave 5 (prefetch)   touches the cache lines of chunk p+6 so that later
+//                       loads hit L2, and never waits for those loads.
 //   wave 6 (inverse)    builds Ti = (I + L)^-1 of chunk p+1.
 // Every buffer written in period p is read by another wave only after the
 // barrier that ends period p, and none is rewritten while another wave still
@@ -72,15 +72,17 @@ enum { G_BETA = 0, G_BEG = 1, G_EG = 2, G_EL = 3, G_LOG = 4, G_N = 5 };
 // that are 0 in fp32 without turning differences of prefix sums into NaN.
 constexpr float LOG2_ALPHA_MIN = -200.f;
 
-// Wave 2 touches every 128-byte line of chunk p + PREFETCH_AHEAD in period p,
+// Wave 5 touches every 128-byte line of chunk p + PREFETCH_AHEAD in period p,
 // so that the loads of the later periods find their lines in L2.
 constexpr int PREFETCH_AHEAD = 6;
 
 // Targets of LDS-DMA loads are arrays of their own: the compiler then sees
 // that the LDS reads which follow such a load in the same wave touch other
 // objects, and does not wait for the load before them.
-__shared__ __attribute__((aligned(16))) bf16_t lds_K[2][C * DK];  // [token][key], octets swizzled by swz_kq(token)
-__shared__ __attribute__((aligned(16))) bf16_t lds_Q[2][C * DK];
+// K and Q of chunk c sit in buffer c % 3 (loaded two periods ahead), V of
+// chunk c in buffer c % 2 (loaded one period ahead).
+__shared__ __attribute__((aligned(16))) bf16_t lds_K[3][C * DK];  // [token][key], octets swizzled by swz_kq(token)
+__shared__ __attribute__((aligned(16))) bf16_t lds_Q[3][C * DK];
 __shared__ __attribute__((aligned(16))) bf16_t lds_V[2][C * DVS];  // [token][slice column]
 __shared__ __attribute__((aligned(16))) uint32_t lds_touch[64];    // landing area of the L2 prefetch (never read)
 
@@ -304,9 +306,9 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     finish_output(sq, A, R, pf, c - 1, DV);
     return;
   }
-  const int buf = (int)(c & 1);
-  const char* Kb = reinterpret_cast<const char*>(lds_K[buf]);
-  const char* Qb = reinterpret_cast<const char*>(lds_Q[buf]);
+  const int buf = (int)(c & 1), kqb = (int)(c % 3);
+  const char* Kb = reinterpret_cast<const char*>(lds_K[kqb]);
+  const char* Qb = reinterpret_cast<const char*>(lds_Q[kqb]);
   const char* Vb = reinterpret_cast<const char*>(lds_V[buf]);
   const char* Tb = reinterpret_cast<const char*>(sm.Tt[buf]);
   const int gb = (int)(c & 3);
@@ -458,7 +460,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
 }
 
 // ============================================================ K, Q, V into LDS
-// LDS-DMA loads of chunk c into buffers c & 1.  Lane i of a 16-byte LDS-DMA
+// LDS-DMA loads of chunk c.  Lane i of a 16-byte LDS-DMA
 // load writes bytes 16 i .. 16 i + 15 after the uniform LDS base, so each lane
 // fetches the global octet that the swizzled layout puts there: for K and Q,
 // instruction it covers tokens 4 it .. 4 it + 3 and lane (lr, lg) fills
@@ -477,8 +479,9 @@ __device__ __forceinline__ DmaAddr dma_addr(int lane, int DV) {
   A.v = (uint32_t)((lane >> 2) * DV * 2 + (((lane & 3) ^ (2 * ((lane >> 4) & 1))) << 4));
   return A;
 }
-__device__ __forceinline__ void dma_chunk(const Seq& sq, const DmaAddr& A, int64_t c, int DV) {
-  const int buf = (int)(c & 1);
+// K and Q of chunk c (32 loads) into buffers c % 3.
+__device__ __forceinline__ void dma_kq(const Seq& sq, const DmaAddr& A, int64_t c) {
+  const int buf = (int)(c % 3);
   const uint32_t kq0 = (uint32_t)(c * C * DK * 2);
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
@@ -487,6 +490,10 @@ __device__ __forceinline__ void dma_chunk(const Seq& sq, const DmaAddr& A, int64
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.q, (lds_void*)&lds_Q[buf][it * 512], 16, A.kq[it & 3],
                                              (int)(kq0 + it * 1024), 0, 0);
   }
+}
+// V of chunk c (4 loads) into buffer c % 2.
+__device__ __forceinline__ void dma_v(const Seq& sq, const DmaAddr& A, int64_t c, int DV) {
+  const int buf = (int)(c & 1);
   const uint32_t v0 = (uint32_t)(c * C * DV * 2);
 #pragma unroll
   for (int it = 0; it < 4; ++it)
@@ -521,9 +528,9 @@ constexpr int TILE_SB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 // issued before the decay, mask and store of tile t.
 __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
-  const int buf = (int)(c & 1);
-  const char* Kb = reinterpret_cast<const char*>(lds_K[buf]);
-  const char* Qb = reinterpret_cast<const char*>(lds_Q[buf]);
+  const int buf = (int)(c & 1), kqb = (int)(c % 3);
+  const char* Kb = reinterpret_cast<const char*>(lds_K[kqb]);
+  const char* Qb = reinterpret_cast<const char*>(lds_Q[kqb]);
   const float* gt = &sm.gate[c & 3][0][0];
   char* Pb = reinterpret_cast<char*>(sm.P[buf]);
   int pw[2];
@@ -659,7 +666,40 @@ __device__ __forceinline__ void build_l(Smem& sm, const FragRegs& R, int64_t c, 
   }
 }
 
-// ============================================================ wave 4: inverse
+// ============================================================ wave 4: loader
+// In period p the loader builds the gate tables of chunk p+3 (gates loaded one
+// period earlier), then loads the gates of chunk p+4, V of chunk p+1 and K, Q
+// of chunk p+2, in that order.  It ends the period once V of chunk p+1 (and
+// with it K, Q of chunk p+1, issued one period earlier) is in LDS, while K, Q
+// of chunk p+2 stay in flight.  The gate tables of chunk 0 come before the
+// first period.
+__device__ __forceinline__ void loader_prologue(Smem& sm, const Seq& sq, int64_t nch, float& ga, float& gb,
+                                                int lane) {
+  ga = gb = 0.f;
+  if (nch > 0) {
+    build_gates(sm, buf_ldf(sq.a, (uint32_t)(lane * 4)), buf_ldf(sq.b, (uint32_t)(lane * 4)), 0, sq.T, lane);
+    ga = buf_ldf(sq.a, (uint32_t)((C + lane) * 4));
+    gb = buf_ldf(sq.b, (uint32_t)((C + lane) * 4));
+  }
+}
+__device__ __forceinline__ void loader_period(Smem& sm, const Seq& sq, const DmaAddr& D, int64_t p, int64_t nch,
+                                              int DV, float& ga, float& gb, int lane) {
+  if (p + 3 < nch) {
+    build_gates(sm, ga, gb, p + 3, sq.T, lane);
+    const uint32_t t4 = (uint32_t)(((p + 4) * C + lane) * 4);
+    ga = buf_ldf(sq.a, t4);
+    gb = buf_ldf(sq.b, t4);
+  }
+  if (p + 1 >= 0 && p + 1 < nch) dma_v(sq, D, p + 1, DV);
+  if (p + 2 >= 0 && p + 2 < nch) {
+    dma_kq(sq, D, p + 2);
+    __builtin_amdgcn_s_waitcnt(0x8f70);  // vmcnt(32): all but the 32 loads of K, Q of chunk p+2
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  }
+}
+
+// ============================================================ wave 6: inverse
 // Forward substitution over key columns 4Q .. 4Q+3 of one unit-lower 16x16
 // block: x[r] -= L[r][s] x[s] for s in the band and r > s, with the band's
 // rows of L read as float4 (all 16 lanes of a group read the same row).
@@ -831,10 +871,8 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
       if (p >= 0 && p < nch) build_p(sm, A, p, lane);
-      if (p + PREFETCH_AHEAD < nch) prefetch_chunk(sq, p + PREFETCH_AHEAD, slice, DV, lane);
-      lds_barrier_keep_dma();
+      lds_barrier();
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no LDS-DMA write outlives the workgroup
   } else if (wave == 3) {
     FragRegs R;
     if (nch > 0) load_frags(R, sq, 0, lane);
@@ -845,25 +883,12 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
       lds_barrier();
     }
   } else if (wave == 4) {
-    // gates of chunk p+3 (loaded one period earlier) and K, Q, V of chunk p+1;
-    // the gates of chunk 0 are built before the first period
     const DmaAddr D = dma_addr(lane, DV);
-    float ga = 0.f, gb = 0.f;
-    if (nch > 0) {
-      build_gates(sm, buf_ldf(sq.a, (uint32_t)(lane * 4)), buf_ldf(sq.b, (uint32_t)(lane * 4)), 0, Tlen, lane);
-      ga = buf_ldf(sq.a, (uint32_t)((C + lane) * 4));
-      gb = buf_ldf(sq.b, (uint32_t)((C + lane) * 4));
-    }
+    float ga, gb;
+    loader_prologue(sm, sq, nch, ga, gb, lane);
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
-      if (p + 1 >= 0 && p + 1 < nch) dma_chunk(sq, D, p + 1, DV);
-      if (p + 3 < nch) {
-        build_gates(sm, ga, gb, p + 3, Tlen, lane);
-        const uint32_t t4 = (uint32_t)(((p + 4) * C + lane) * 4);
-        ga = buf_ldf(sq.a, t4);
-        gb = buf_ldf(sq.b, t4);
-      }
-      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): chunk p+1 is in LDS
+      loader_period(sm, sq, D, p, nch, DV, ga, gb, lane);
       lds_barrier();
     }
   } else if (wave == 6) {
@@ -873,8 +898,13 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
       lds_barrier();
     }
   } else {
+    // wave 5: the L2 prefetch, issued by a wave that never waits for it
     lds_barrier();
-    for (int64_t p = -2; p <= nch; ++p) lds_barrier();
+    for (int64_t p = -2; p <= nch; ++p) {
+      if (p + PREFETCH_AHEAD < nch) prefetch_chunk(sq, p + PREFETCH_AHEAD, slice, DV, lane);
+      lds_barrier_keep_dma();
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no LDS-DMA write outlives the workgroup
   }
 }
 
