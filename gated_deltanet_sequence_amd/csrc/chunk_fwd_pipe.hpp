@@ -148,6 +148,35 @@ __device__ __forceinline__ uint2 lds_tr(const char* base, int off) {
   const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off));
   return __builtin_bit_cast(uint2, v);
 }
+// LDS pointer of one lane: buffer start plus a per-lane offset, computed once
+// per period.  The empty asm hides the sum from the optimiser, which would
+// otherwise fold the per-read constants into per-read address registers;
+// this way every read adds its constant in the instruction's offset field.
+typedef const __attribute__((address_space(3))) char* lptr;
+__device__ __forceinline__ lptr lane_base(const void* buf, int lane_off) {
+  uint32_t a = (uint32_t)(uintptr_t)(lptr)buf + (uint32_t)lane_off;
+  asm volatile("" : "+v"(a));
+  return (lptr)(uintptr_t)a;
+}
+template <class T> struct Ld3;
+template <> struct Ld3<uint4> {
+  static __device__ __forceinline__ uint4 get(lptr p) {
+    const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+};
+template <> struct Ld3<uint2> {
+  static __device__ __forceinline__ uint2 get(lptr p) {
+    const u32x2_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>(p);
+    return make_uint2(v.x, v.y);
+  }
+};
+template <class T>
+__device__ __forceinline__ T ld3(lptr base, int off) { return Ld3<T>::get(base + off); }
+__device__ __forceinline__ uint2 tr3(lptr base, int off) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off));
+  return __builtin_bit_cast(uint2, v);
+}
 __device__ __forceinline__ bf16x8_t as_op(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 __device__ __forceinline__ bf16x8_t as_op(uint2 lo, uint2 hi) {
   return as_op(make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -289,11 +318,11 @@ __device__ __forceinline__ void finish_output(const Seq& sq, const StateAddr& A,
   }
 }
 __device__ __forceinline__ void read_p(const Smem& sm, const StateAddr& A, int64_t c, bf16x8_t (&pf)[4][2]) {
-  const char* Pb = reinterpret_cast<const char*>(sm.P[c & 1]);
+  const lptr pb[2] = {lane_base(sm.P[c & 1], A.pfr[0]), lane_base(sm.P[c & 1], A.pfr[1])};
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int pp = 0; pp <= rb / 2; ++pp) pf[rb][pp] = as_op(lds_at<uint4>(Pb, A.pfr[pp] + rb * 2048));
+    for (int pp = 0; pp <= rb / 2; ++pp) pf[rb][pp] = as_op(ld3<uint4>(pb[pp], rb * 2048));
 }
 
 template <bool FINISH, bool CHAIN>
@@ -307,10 +336,15 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     return;
   }
   const int buf = (int)(c & 1), kqb = (int)(c % 3);
-  const char* Kb = reinterpret_cast<const char*>(lds_K[kqb]);
-  const char* Qb = reinterpret_cast<const char*>(lds_Q[kqb]);
-  const char* Vb = reinterpret_cast<const char*>(lds_V[buf]);
-  const char* Tb = reinterpret_cast<const char*>(sm.Tt[buf]);
+  lptr kf_b[4], qf_b[4], kt_b[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    kf_b[pp] = lane_base(lds_K[kqb], A.frag[pp]);
+    qf_b[pp] = lane_base(lds_Q[kqb], A.frag[pp]);
+    kt_b[pp] = lane_base(lds_K[kqb], A.ktr[pp]);
+  }
+  const lptr v_b = lane_base(lds_V[buf], A.vtr);
+  const lptr t_b = lane_base(sm.Tt[buf], A.ttr);
   const int gb = (int)(c & 3);
   const float* gt = &sm.gate[gb][0][0];
   const float decay = sm.egl[gb][0];
@@ -329,13 +363,13 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   f32x4 Z[4];
   bf16x8_t fr[2][4];
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) fr[0][pp] = as_op(lds_at<uint4>(Kb, A.frag[pp]));
+  for (int pp = 0; pp < 4; ++pp) fr[0][pp] = as_op(ld3<uint4>(kf_b[pp], 0));
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const int cur = rb & 1;
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp)
-      fr[cur ^ 1][pp] = as_op(lds_at<uint4>(rb < 3 ? Kb : Qb, A.frag[pp] + (rb < 3 ? (rb + 1) * 4096 : 0)));
+      fr[cur ^ 1][pp] = as_op(rb < 3 ? ld3<uint4>(kf_b[pp], (rb + 1) * 4096) : ld3<uint4>(qf_b[pp], 0));
     __builtin_amdgcn_sched_barrier(0);
     f32x4 az = zero4();
 #pragma unroll
@@ -351,7 +385,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   float4 b4[4], g4[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
-    vv[rb] = lds_tr(Vb, A.vtr + rb * 16 * DVS * 2);
+    vv[rb] = tr3(v_b, rb * 16 * DVS * 2);
     b4[rb] = *reinterpret_cast<const float4*>(gt + G_BETA * C + 16 * rb + 4 * lg);
     g4[rb] = *reinterpret_cast<const float4*>(gt + G_BEG * C + 16 * rb + 4 * lg);
   }
@@ -361,7 +395,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     const int cur = rb & 1;  // block rb of Q sits in fr[cur] (block 0 was read last above)
     if (rb < 3) {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) fr[cur ^ 1][pp] = as_op(lds_at<uint4>(Qb, A.frag[pp] + (rb + 1) * 4096));
+      for (int pp = 0; pp < 4; ++pp) fr[cur ^ 1][pp] = as_op(ld3<uint4>(qf_b[pp], (rb + 1) * 4096));
     }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 ao = zero4();
@@ -380,8 +414,8 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int pp = 0; pp <= rb / 2; ++pp) {
-      const int off = A.ttr + pp * 32 * TTS * 2 + rb * 32;
-      tf[rb][pp] = as_op(lds_tr(Tb, off), lds_tr(Tb, off + 16 * TTS * 2));
+      const int off = pp * 32 * TTS * 2 + rb * 32;
+      tf[rb][pp] = as_op(tr3(t_b, off), tr3(t_b, off + 16 * TTS * 2));
     }
   f32x4 el[4];
   float eg[4];
@@ -397,8 +431,8 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   auto read_kt = [&](int jb, bf16x8_t (&dst)[2]) {
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
-      const int off = A.ktr[jb >> 1] + (jb & 1) * 8 + pp * 32 * 256;
-      dst[pp] = as_op(lds_tr(Kb, off), lds_tr(Kb, off + 16 * 256));
+      const int off = (jb & 1) * 8 + pp * 32 * 256;
+      dst[pp] = as_op(tr3(kt_b[jb >> 1], off), tr3(kt_b[jb >> 1], off + 16 * 256));
     }
   };
   read_kt(0, kt[0]);
@@ -529,8 +563,12 @@ constexpr int TILE_SB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const int buf = (int)(c & 1), kqb = (int)(c % 3);
-  const char* Kb = reinterpret_cast<const char*>(lds_K[kqb]);
-  const char* Qb = reinterpret_cast<const char*>(lds_Q[kqb]);
+  lptr kf_b[4], qf_b[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    kf_b[pp] = lane_base(lds_K[kqb], A.frag[pp]);
+    qf_b[pp] = lane_base(lds_Q[kqb], A.frag[pp]);
+  }
   const float* gt = &sm.gate[c & 3][0][0];
   char* Pb = reinterpret_cast<char*>(sm.P[buf]);
   int pw[2];
@@ -540,11 +578,11 @@ __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c,
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) kf[b][pp] = as_op(lds_at<uint4>(Kb, A.frag[pp] + b * 4096));
+    for (int pp = 0; pp < 4; ++pp) kf[b][pp] = as_op(ld3<uint4>(kf_b[pp], b * 4096));
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) qf[b][pp] = as_op(lds_at<uint4>(Qb, A.frag[pp] + b * 4096));
+    for (int pp = 0; pp < 4; ++pp) qf[b][pp] = as_op(ld3<uint4>(qf_b[pp], b * 4096));
   float gr[4];
   float4 gs4[4];
 #pragma unroll
@@ -566,7 +604,7 @@ __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c,
     const int rb = TILE_RB[t], sb = TILE_SB[t];
     if (sb == 0 && rb >= 1 && rb < 3) {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) qf[rb + 1][pp] = as_op(lds_at<uint4>(Qb, A.frag[pp] + (rb + 1) * 4096));
+      for (int pp = 0; pp < 4; ++pp) qf[rb + 1][pp] = as_op(ld3<uint4>(qf_b[pp], (rb + 1) * 4096));
     }
     if (t + 1 < 10) acc[(t + 1) & 1] = tile(t + 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -701,13 +739,15 @@ __device__ __forceinline__ void loader_period(Smem& sm, const Seq& sq, const Dma
 
 // ============================================================ wave 6: inverse
 // Forward substitution over key columns 4Q .. 4Q+3 of one unit-lower 16x16
-// block: x[r] -= L[r][s] x[s] for s in the band and r > s, with the band's
-// rows of L read as float4 (all 16 lanes of a group read the same row).
+// block: x[r] -= L[r][s] x[s] for s in the band and r > s.  The band's rows of
+// L (float4, read by all 16 lanes of a group at once) are read one band ahead.
 template <int Q>
-__device__ __forceinline__ void subst_band(float (&x)[16], const float* Lr) {
-  float4 lq[16];
+__device__ __forceinline__ void subst_read(float4 (&lq)[16], const float* Lr) {
 #pragma unroll
   for (int r = 4 * Q + 1; r < 16; ++r) lq[r] = *reinterpret_cast<const float4*>(Lr + r * LDR + 4 * Q);
+}
+template <int Q>
+__device__ __forceinline__ void subst_band(float (&x)[16], const float4 (&lq)[16]) {
 #pragma unroll
   for (int s = 4 * Q; s < 4 * Q + 4; ++s) {
 #pragma unroll
@@ -719,25 +759,31 @@ __device__ __forceinline__ void subst_band(float (&x)[16], const float* Lr) {
   }
 }
 
-// Ti = (I + L)^-1 of chunk c, written as Ti^T into Tt buffer c & 1.
-//   level 0: the four unit-lower 16x16 diagonal blocks by forward
-//            substitution in fp32; lane = (block lg, column lr).
-//   blocks below the diagonal, one block row at a time:
-//            T_ab = -T_aa sum_{b <= c < a} L_ac T_cb
-//            with 16x16x16 MFMAs whose accumulators are reused as B operands.
 __device__ __forceinline__ void build_inverse(Smem& sm, int64_t c, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const int lb = (int)(c & 1);
   char* Tb = reinterpret_cast<char*>(sm.Tt[lb]);
+  // off-diagonal blocks of L, needed only after the diagonal blocks are done
+  uint2 Lop[6];
+#pragma unroll
+  for (int t = 0; t < 6; ++t) Lop[t] = *reinterpret_cast<const uint2*>(&sm.Lo[lb][t][lane * 4]);
   {
     const float* Lr = &sm.Ld[lb][lg][0];
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = (r == lr) ? 1.f : 0.f;
-    subst_band<0>(x, Lr);
-    subst_band<1>(x, Lr);
-    subst_band<2>(x, Lr);
-    subst_band<3>(x, Lr);
+    float4 la[16], lbb[16];
+    subst_read<0>(la, Lr);
+    subst_read<1>(lbb, Lr);
+    __builtin_amdgcn_sched_barrier(0);
+    subst_band<0>(x, la);
+    subst_read<2>(la, Lr);
+    __builtin_amdgcn_sched_barrier(0);
+    subst_band<1>(x, lbb);
+    subst_read<3>(lbb, Lr);
+    __builtin_amdgcn_sched_barrier(0);
+    subst_band<2>(x, la);
+    subst_band<3>(x, lbb);
     // column lr of block lg = row (16 lg + lr) of Ti^T, columns 16 lg .. +15
     char* dst = Tb + (16 * lg + lr) * (TTS * 2) + 32 * lg;
     lds_put<uint4>(dst, 0, make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])));
@@ -756,9 +802,6 @@ __device__ __forceinline__ void build_inverse(Smem& sm, int64_t c, int lane) {
     for (int aa = 1; aa < 4; ++aa)
       Ad[aa] = lds_tr(Tb, (16 * aa + 4 * lg + r) * (TTS * 2) + (16 * aa + 4 * a) * 2);
   }
-  uint2 Lop[6];
-#pragma unroll
-  for (int t = 0; t < 6; ++t) Lop[t] = *reinterpret_cast<const uint2*>(&sm.Lo[lb][t][lane * 4]);
   // T blocks below the diagonal as B operands: Tb_[a][b]
   uint2 Tbo[4][3];
 #pragma unroll
