@@ -209,7 +209,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_fwd_kernel(
       const bool ok = t < Tlen;
       const float a = ok ? ac[t] : 1.f;
       const float b = ok ? bc[t] : 0.f;
-      float gs = fast_log2(a);
+      float gs = fmaxf(fast_log2(a), LOG2_ALPHA_MIN);
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(gs, off, 64);

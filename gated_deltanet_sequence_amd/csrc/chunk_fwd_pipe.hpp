@@ -18,10 +18,11 @@
 //   O = diag(2^g) Q S^T + P U
 //   S' = 2^(g_C) S + U^T diag(2^(g_C - g)) K
 //
-// Workgroup = 7 waves, one (sequence, 32-row value slice) per workgroup, one
-// workgroup barrier per period.  Waves 0..3 run on four different SIMDs and
-// wave w + 4 shares the SIMD of wave w, so the two state waves get SIMDs that
-// no other busy wave uses.  In period p:
+// Workgroup = 8 wave slots (7 working waves), one (sequence, 32-row value
+// slice) per workgroup, one workgroup barrier per period.  Waves 0..3 run on
+// four different SIMDs and wave w + 4 shares the SIMD of wave w: the state
+// waves share their SIMDs only with the prefetch wave and the empty slot, the
+// P wave shares with the loader, and the L wave with the inverse.  In period p:
 //   waves 0, 1 (state)  each own 16 rows of the value slice.  They finish the
 //                       output of chunk p-1 (O += P U) and run the S-dependent
 //                       part of chunk p.  The fp32 state stays in MFMA
@@ -29,14 +30,13 @@
 //   wave 2 (P)          builds P of chunk p.
 //   wave 3 (L)          builds L of chunk p+2 from keys it loaded one period
 //                       earlier, then loads the keys of chunk p+3.
-//   wave 4 (loader)     moves V of chunk p+1 and K, Q of chunk p+2 into LDS
+//   wave 4 (prefetch)   touches the cache lines of chunk p+6 so that later
+//                       loads hit L2, and never waits for those loads.
+//   wave 6 (loader)     moves V of chunk p+1 and K, Q of chunk p+2 into LDS
 //                       with LDS-DMA loads, builds the gate tables of chunk p+3
 //                       from gates it loaded one period earlier and loads the
-//                       gates of chunk p+4 (it issues little, so it may share the
-//                       SIMD of a state wave).
-//   wave 5 (prefetch)   touches the cache lines of chunk p+6 so that later
-//                       loads hit L2, and never waits for those loads.
-//   wave 6 (inverse)    builds Ti = (I + L)^-1 of chunk p+1.
+//                       gates of chunk p+4.
+//   wave 7 (inverse)    builds Ti = (I + L)^-1 of chunk p+1.
 // Every buffer written in period p is read by another wave only after the
 // barrier that ends period p, and none is rewritten while another wave still
 // reads it (double buffering by chunk parity).
@@ -55,6 +55,7 @@
 #pragma once
 
 #include "gdn_common.hpp"
+#include <type_traits>
 
 namespace gdn {
 namespace pipe {
@@ -62,17 +63,17 @@ namespace pipe {
 constexpr int C = 64;
 constexpr int DK = 128;
 constexpr int DVS = 32;   // value columns per workgroup
-constexpr int NWAVES = 7;
+// Wave slots and roles.  Waves 0..3 run on four different SIMDs and wave
+// w + 4 shares the SIMD of wave w; slot 5 is left empty (that wave exits at
+// once), so the second state wave has a SIMD of its own.
+constexpr int NWAVES = 8;
+constexpr int W_P = 2, W_L = 3, W_PREFETCH = 4, W_IDLE = 5, W_LOADER = 6, W_INV = 7;
 constexpr int TTS = 72;   // row stride (elements) of Ti^T
 constexpr int LDR = 20;   // row stride (floats) of the fp32 diagonal blocks of L
 
-enum { G_BETA = 0, G_BEG = 1, G_EG = 2, G_EL = 3, G_LOG = 4, G_N = 5 };
+enum { G_BETA = 0, G_ER = 1, G_EG = 2, G_EL = 3, G_LOG = 4, G_N = 5 };
 
-// Lower bound applied to log2(alpha): a gate of 0 then gives decay factors
-// that are 0 in fp32 without turning differences of prefix sums into NaN.
-constexpr float LOG2_ALPHA_MIN = -200.f;
-
-// Wave 5 touches every 128-byte line of chunk p + PREFETCH_AHEAD in period p,
+// The prefetch wave touches every 128-byte line of chunk p + PREFETCH_AHEAD in period p,
 // so that the loads of the later periods find their lines in L2.
 constexpr int PREFETCH_AHEAD = 6;
 
@@ -90,12 +91,19 @@ struct __attribute__((aligned(16))) Smem {
   bf16_t P[2][C * C];       // [r][s], s kappa-ordered, octets swizzled by swz_p(r)
   bf16_t Tt[2][C * TTS];    // Ti^T: [s][t]
   float gate[4][G_N][C];    // written three periods before the last use: four buffers
-  float egl[4][4];          // 2^(g_C)
+  float egl[4][4];          // 2^(g_C), and 1 where the decay factors of P and L may be split
   float Ld[2][4][16 * LDR + 4];  // strictly-lower diagonal 16x16 blocks of L, fp32
                                 // (blocks padded by 16 bytes: the inverse reads
                                 // the four blocks at once without bank conflicts)
   bf16_t Lo[2][6][64 * 4];  // off-diagonal 16x16 blocks of L, MFMA A-operand order
 };
+
+// The decay 2^(g_r - g_s) of P and L is split into 2^(g_r - g_C) 2^(g_C - g_s)
+// when g_C >= SPLIT_MIN; whether it is, is uniform over the wave.
+constexpr float SPLIT_MIN = -120.f;
+__device__ __forceinline__ bool split_decay(const Smem& sm, int64_t c) {
+  return __builtin_amdgcn_readfirstlane(__float_as_int(sm.egl[c & 3][1])) != 0;
+}
 
 // XOR applied to the 16-byte octet index of K/Q row `row`.  LDS bank rules on
 // gfx950 (64 banks of 4 bytes): a 16-byte read serves 16 lanes per cycle,
@@ -357,55 +365,54 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) Sop[pp] = pack_op(R.S[2 * pp], R.S[2 * pp + 1]);
 
-  // ---- Z = K S^T (tile per 16-token block, rows = token); the key fragments
-  // of block rb + 1 are read while the products of block rb run, and the
-  // decay of the carried state fills the gaps.
+  // ---- Z = K S^T (tile per 16-token block, rows = token).  The fragments
+  // of the 16-token blocks K0..K3, Q0..Q3 pass through a ring of three
+  // register slots (block n in slot n % 3), read two blocks ahead of their
+  // products; the decay of the carried state fills the gaps.
   f32x4 Z[4];
-  bf16x8_t fr[2][4];
-#pragma unroll
-  for (int pp = 0; pp < 4; ++pp) fr[0][pp] = as_op(ld3<uint4>(kf_b[pp], 0));
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int cur = rb & 1;
+  bf16x8_t fr[3][4];
+  auto read_block = [&](int n) {
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp)
-      fr[cur ^ 1][pp] = as_op(rb < 3 ? ld3<uint4>(kf_b[pp], (rb + 1) * 4096) : ld3<uint4>(qf_b[pp], 0));
+      fr[n % 3][pp] = as_op(n < 4 ? ld3<uint4>(kf_b[pp], n * 4096) : ld3<uint4>(qf_b[pp], (n - 4) * 4096));
+  };
+  read_block(0);
+  read_block(1);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    read_block(rb + 2);
     __builtin_amdgcn_sched_barrier(0);
     f32x4 az = zero4();
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) az = mfma(fr[cur][pp], Sop[pp], az);
+    for (int pp = 0; pp < 4; ++pp) az = mfma(fr[rb % 3][pp], Sop[pp], az);
     R.S[2 * rb] *= decay;
     R.S[2 * rb + 1] *= decay;
     Z[rb] = az;
     __builtin_amdgcn_sched_barrier(0);
   }
-  // ---- O1 = S Q^T (rows = value, columns = token) while Y = beta V -
-  // beta 2^g Z is formed; V, the gates and Ti are read meanwhile.
+  // ---- O1 = S Q^T (rows = value, columns = token) while Y = beta (V -
+  // 2^g Z) is formed; V, the gates and Ti are read meanwhile.
   uint2 vv[4];
   float4 b4[4], g4[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     vv[rb] = tr3(v_b, rb * 16 * DVS * 2);
     b4[rb] = *reinterpret_cast<const float4*>(gt + G_BETA * C + 16 * rb + 4 * lg);
-    g4[rb] = *reinterpret_cast<const float4*>(gt + G_BEG * C + 16 * rb + 4 * lg);
+    g4[rb] = *reinterpret_cast<const float4*>(gt + G_EG * C + 16 * rb + 4 * lg);
   }
   f32x4 O1[4], y[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
-    const int cur = rb & 1;  // block rb of Q sits in fr[cur] (block 0 was read last above)
-    if (rb < 3) {
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) fr[cur ^ 1][pp] = as_op(ld3<uint4>(qf_b[pp], (rb + 1) * 4096));
-    }
+    if (rb < 2) read_block(rb + 6);  // Q block rb sits in slot (4 + rb) % 3
     __builtin_amdgcn_sched_barrier(0);
     f32x4 ao = zero4();
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) ao = mfma(Sop[pp], fr[cur][pp], ao);
+    for (int pp = 0; pp < 4; ++pp) ao = mfma(Sop[pp], fr[(4 + rb) % 3][pp], ao);
     O1[rb] = ao;
-    y[rb][0] = b4[rb].x * __uint_as_float(vv[rb].x << 16) - g4[rb].x * Z[rb][0];
-    y[rb][1] = b4[rb].y * __uint_as_float(vv[rb].x & 0xffff0000u) - g4[rb].y * Z[rb][1];
-    y[rb][2] = b4[rb].z * __uint_as_float(vv[rb].y << 16) - g4[rb].z * Z[rb][2];
-    y[rb][3] = b4[rb].w * __uint_as_float(vv[rb].y & 0xffff0000u) - g4[rb].w * Z[rb][3];
+    y[rb][0] = b4[rb].x * fmaf(-g4[rb].x, Z[rb][0], __uint_as_float(vv[rb].x << 16));
+    y[rb][1] = b4[rb].y * fmaf(-g4[rb].y, Z[rb][1], __uint_as_float(vv[rb].x & 0xffff0000u));
+    y[rb][2] = b4[rb].z * fmaf(-g4[rb].z, Z[rb][2], __uint_as_float(vv[rb].y << 16));
+    y[rb][3] = b4[rb].w * fmaf(-g4[rb].w, Z[rb][3], __uint_as_float(vv[rb].y & 0xffff0000u));
     __builtin_amdgcn_sched_barrier(0);
   }
   const bf16x8_t Yop[2] = {pack_op(y[0], y[1]), pack_op(y[2], y[3])};
@@ -426,8 +433,9 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     eg[h] = gt[G_EG * C + 16 * h + lr];
   }
   if constexpr (FINISH) read_p(sm, A, c - 1, pf);
-  // the first K^T operands of the state update
-  bf16x8_t kt[2][2];
+  // the first K^T operands of the state update (ring of three slots, tile jb
+  // in slot jb % 3)
+  bf16x8_t kt[3][2];
   auto read_kt = [&](int jb, bf16x8_t (&dst)[2]) {
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
@@ -436,6 +444,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     }
   };
   read_kt(0, kt[0]);
+  read_kt(1, kt[1]);
   __builtin_amdgcn_sched_barrier(0);
   // ---- U = Ti Y (Ti lower triangular: row block rb needs the 32-token blocks
   // pp <= rb/2, the upper 16x16 blocks inside them are zero) while O1 takes
@@ -480,14 +489,14 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   __builtin_amdgcn_sched_barrier(0);
   // ---- S^T += K^T Uh with K^T from transposed reads: supplier lane (a, r) of
   // a 16-lane group addresses 4 key columns of token 4 lg + r.  The operands
-  // of tile jb + 1 are read while the products of tile jb run.
+  // of tile jb + 2 are read while the products of tile jb run.
 #pragma unroll
   for (int jb = 0; jb < 8; ++jb) {
-    if (jb < 7) read_kt(jb + 1, kt[(jb + 1) & 1]);
+    if (jb < 6) read_kt(jb + 2, kt[(jb + 2) % 3]);
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc = R.S[jb];
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) acc = mfma(kt[jb & 1][pp], Uh[pp], acc);
+    for (int pp = 0; pp < 2; ++pp) acc = mfma(kt[jb % 3][pp], Uh[pp], acc);
     R.S[jb] = acc;
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -583,12 +592,15 @@ __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c,
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) qf[b][pp] = as_op(ld3<uint4>(qf_b[pp], b * 4096));
+  // decay of element (s, r): 2^(g_r - g_C) 2^(g_C - g_s) when split, else
+  // 2^(g_r - g_s) from the log table
+  const bool split = split_decay(sm, c);
   float gr[4];
   float4 gs4[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    gr[b] = gt[G_LOG * C + 16 * b + lr];
-    gs4[b] = *reinterpret_cast<const float4*>(gt + G_LOG * C + 16 * b + 4 * lg);
+    gr[b] = gt[(split ? G_ER : G_LOG) * C + 16 * b + lr];
+    gs4[b] = *reinterpret_cast<const float4*>(gt + (split ? G_EL : G_LOG) * C + 16 * b + 4 * lg);
   }
   // element (s, r) = k_s . q_r of tile t
   auto tile = [&](int t) {
@@ -597,29 +609,37 @@ __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c,
     for (int pp = 0; pp < 4; ++pp) acc = mfma(kf[TILE_SB[t]][pp], qf[TILE_RB[t]][pp], acc);
     return acc;
   };
-  f32x4 acc[2];
-  acc[0] = tile(0);
+  auto run = [&](auto SPLIT) {
+    f32x4 acc[2];
+    acc[0] = tile(0);
 #pragma unroll
-  for (int t = 0; t < 10; ++t) {
-    const int rb = TILE_RB[t], sb = TILE_SB[t];
-    if (sb == 0 && rb >= 1 && rb < 3) {
+    for (int t = 0; t < 10; ++t) {
+      const int rb = TILE_RB[t], sb = TILE_SB[t];
+      if (sb == 0 && rb >= 1 && rb < 3) {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) qf[rb + 1][pp] = as_op(ld3<uint4>(qf_b[pp], (rb + 1) * 4096));
+        for (int pp = 0; pp < 4; ++pp) qf[rb + 1][pp] = as_op(ld3<uint4>(qf_b[pp], (rb + 1) * 4096));
+      }
+      if (t + 1 < 10) acc[(t + 1) & 1] = tile(t + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x4 a = acc[t & 1];
+      const float g[4] = {gs4[sb].x, gs4[sb].y, gs4[sb].z, gs4[sb].w};
+      float val[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        val[e] = decltype(SPLIT)::value ? a[e] * g[e] * gr[rb] : fast_exp2(gr[rb] - g[e]) * a[e];
+      if (sb == rb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = (4 * lg + e <= lr) ? val[e] : 0.f;
+      }
+      lds_put<uint2>(Pb, pw[sb >> 1] + (sb & 1) * 8 + rb * 2048,
+                     make_uint2(pack2(val[0], val[1]), pack2(val[2], val[3])));
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (t + 1 < 10) acc[(t + 1) & 1] = tile(t + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    const f32x4 a = acc[t & 1];
-    const float4 g4 = gs4[sb];
-    float val[4] = {fast_exp2(gr[rb] - g4.x) * a[0], fast_exp2(gr[rb] - g4.y) * a[1],
-                    fast_exp2(gr[rb] - g4.z) * a[2], fast_exp2(gr[rb] - g4.w) * a[3]};
-    if (sb == rb) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) val[e] = (4 * lg + e <= lr) ? val[e] : 0.f;
-    }
-    lds_put<uint2>(Pb, pw[sb >> 1] + (sb & 1) * 8 + rb * 2048,
-                   make_uint2(pack2(val[0], val[1]), pack2(val[2], val[3])));
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  };
+  if (split)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
 
 // ============================================================ wave 3: L
@@ -639,8 +659,11 @@ __device__ __forceinline__ void load_frags(FragRegs& R, const Seq& sq, int64_t c
 }
 
 // Gate tables of chunk c (alpha, beta of token `lane` as loaded, 0 past the
-// end): beta, beta 2^g, 2^g, 2^(g_C - g), g and 2^(g_C), with g the
-// log2-prefix of alpha.
+// end): beta, 2^(g - g_C), 2^g, 2^(g_C - g), g and 2^(g_C), with g the
+// log2-prefix of alpha.  The decay 2^(g_r - g_s) of P and L is the product
+// 2^(g_r - g_C) 2^(g_C - g_s) of two table entries when g_C >= SPLIT_MIN (both
+// factors then lie in the normal fp32 range); otherwise P and L take one exp2
+// per element.
 __device__ __forceinline__ void build_gates(Smem& sm, float ra, float rb, int64_t c, int64_t T, int lane) {
   float* gt = &sm.gate[c & 3][0][0];
   // tokens past the end are identity maps (alpha 1, beta 0)
@@ -648,30 +671,32 @@ __device__ __forceinline__ void build_gates(Smem& sm, float ra, float rb, int64_
   const float a = live ? ra : 1.f, b = live ? rb : 0.f;
   const float gs = wave_prefix_sum(fmaxf(fast_log2(a), LOG2_ALPHA_MIN));
   const float glast = lane63(gs);
-  const float eg = fast_exp2(gs);
   gt[G_BETA * C + lane] = b;
-  gt[G_BEG * C + lane] = b * eg;
-  gt[G_EG * C + lane] = eg;
+  gt[G_ER * C + lane] = fast_exp2(gs - glast);
+  gt[G_EG * C + lane] = fast_exp2(gs);
   gt[G_EL * C + lane] = fast_exp2(glast - gs);
   gt[G_LOG * C + lane] = gs;
-  if (lane == 0) sm.egl[c & 3][0] = fast_exp2(glast);
+  if (lane == 0) {
+    sm.egl[c & 3][0] = fast_exp2(glast);
+    sm.egl[c & 3][1] = glast >= SPLIT_MIN ? 1.f : 0.f;
+  }
 }
-
 // L of chunk c: diagonal blocks as fp32 rows, off-diagonal blocks as bf16 in
-// the order in which the inverse consumes them as MFMA A operands.  beta_r
-// enters through the exponent, beta_r 2^(g_r - g_s) = 2^(g_r + log2 beta_r -
-// g_s) (beta_r = 0 gives 0), and the tiles are software-pipelined as in
-// build_p.
+// the order in which the inverse consumes them as MFMA A operands.  The row
+// factor beta_r multiplies the decay (split as in build_p), and the tiles are
+// software-pipelined as in build_p.
 __device__ __forceinline__ void build_l(Smem& sm, const FragRegs& R, int64_t c, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const int lb = (int)(c & 1);
   const float* gt = &sm.gate[c & 3][0][0];
-  float grb[4];
+  const bool split = split_decay(sm, c);
+  float grb[4], br[4];
   float4 gs4[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    grb[b] = gt[G_LOG * C + 16 * b + lr] + fast_log2(gt[G_BETA * C + 16 * b + lr]);
-    gs4[b] = *reinterpret_cast<const float4*>(gt + G_LOG * C + 16 * b + 4 * lg);
+    grb[b] = gt[(split ? G_ER : G_LOG) * C + 16 * b + lr];
+    br[b] = gt[G_BETA * C + 16 * b + lr];
+    gs4[b] = *reinterpret_cast<const float4*>(gt + (split ? G_EL : G_LOG) * C + 16 * b + 4 * lg);
   }
   // tile t: lane holds k_r . k_s for r = 16rb + lr, s = 16sb + 4lg + e
   auto tile = [&](int t) {
@@ -680,28 +705,39 @@ __device__ __forceinline__ void build_l(Smem& sm, const FragRegs& R, int64_t c, 
     for (int pp = 0; pp < 4; ++pp) acc = mfma(as_op(R.kf[TILE_SB[t]][pp]), as_op(R.kf[TILE_RB[t]][pp]), acc);
     return acc;
   };
-  f32x4 acc[2];
-  acc[0] = tile(0);
+  auto run = [&](auto SPLIT) {
+    float rf[4];  // row factor: beta_r 2^(g_r - g_C) when split, else g_r
 #pragma unroll
-  for (int t = 0; t < 10; ++t) {
-    const int rb = TILE_RB[t], sb = TILE_SB[t];
-    if (t + 1 < 10) acc[(t + 1) & 1] = tile(t + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    const f32x4 a = acc[t & 1];
-    const float4 g4 = gs4[sb];
-    float val[4] = {fast_exp2(grb[rb] - g4.x) * a[0], fast_exp2(grb[rb] - g4.y) * a[1],
-                    fast_exp2(grb[rb] - g4.z) * a[2], fast_exp2(grb[rb] - g4.w) * a[3]};
-    if (sb == rb) {
+    for (int b = 0; b < 4; ++b) rf[b] = decltype(SPLIT)::value ? br[b] * grb[b] : grb[b];
+    f32x4 acc[2];
+    acc[0] = tile(0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) val[e] = (4 * lg + e < lr) ? val[e] : 0.f;
-      *reinterpret_cast<float4*>(&sm.Ld[lb][rb][lr * LDR + 4 * lg]) = make_float4(val[0], val[1], val[2], val[3]);
-    } else {
-      const int tix = rb * (rb - 1) / 2 + sb;
-      *reinterpret_cast<uint2*>(&sm.Lo[lb][tix][lane * 4]) =
-          make_uint2(pack2(val[0], val[1]), pack2(val[2], val[3]));
+    for (int t = 0; t < 10; ++t) {
+      const int rb = TILE_RB[t], sb = TILE_SB[t];
+      if (t + 1 < 10) acc[(t + 1) & 1] = tile(t + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x4 a = acc[t & 1];
+      const float g[4] = {gs4[sb].x, gs4[sb].y, gs4[sb].z, gs4[sb].w};
+      float val[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        val[e] = decltype(SPLIT)::value ? a[e] * g[e] * rf[rb] : fast_exp2(rf[rb] - g[e]) * (a[e] * br[rb]);
+      if (sb == rb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = (4 * lg + e < lr) ? val[e] : 0.f;
+        *reinterpret_cast<float4*>(&sm.Ld[lb][rb][lr * LDR + 4 * lg]) = make_float4(val[0], val[1], val[2], val[3]);
+      } else {
+        const int tix = rb * (rb - 1) / 2 + sb;
+        *reinterpret_cast<uint2*>(&sm.Lo[lb][tix][lane * 4]) =
+            make_uint2(pack2(val[0], val[1]), pack2(val[2], val[3]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  };
+  if (split)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
 
 // ============================================================ wave 4: loader
@@ -759,7 +795,7 @@ __device__ __forceinline__ void subst_band(float (&x)[16], const float4 (&lq)[16
   }
 }
 
-__device__ __forceinline__ void build_inverse(Smem& sm, int64_t c, int lane) {
+__device__ __forceinline__ void build_inverse(Smem& sm, int64_t c, const float (&xinit)[16], int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const int lb = (int)(c & 1);
   char* Tb = reinterpret_cast<char*>(sm.Tt[lb]);
@@ -771,7 +807,7 @@ __device__ __forceinline__ void build_inverse(Smem& sm, int64_t c, int lane) {
     const float* Lr = &sm.Ld[lb][lg][0];
     float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (r == lr) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) x[r] = xinit[r];
     float4 la[16], lbb[16];
     subst_read<0>(la, Lr);
     subst_read<1>(lbb, Lr);
@@ -874,6 +910,13 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     for (int e = tid; e < 2 * C * TTS / 2; e += 64 * NWAVES) z2[e] = 0u;
   }
 
+  // The empty slot only helps to zero P and Ti^T.  Its stores are complete
+  // before it ends, and a barrier waits only for waves that have not ended.
+  if (wave == W_IDLE) {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    return;
+  }
+
   // Each role runs its own loop over periods p = -2 .. nch with exactly one
   // workgroup barrier per period, so all waves meet at every barrier.
   if (wave < 2) {
@@ -909,14 +952,14 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
       for (int jb = 0; jb < 8; ++jb)
         *reinterpret_cast<float4*>(final_state + st_row * DK + state_col(jb, lg)) = as_f4(R.S[jb]);
     }
-  } else if (wave == 2) {
+  } else if (wave == W_P) {
     const StateAddr A = state_addr(lane, 0, DV);
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
       if (p >= 0 && p < nch) build_p(sm, A, p, lane);
       lds_barrier();
     }
-  } else if (wave == 3) {
+  } else if (wave == W_L) {
     FragRegs R;
     if (nch > 0) load_frags(R, sq, 0, lane);
     lds_barrier();
@@ -925,7 +968,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
       if (p + 3 < nch) load_frags(R, sq, p + 3, lane);
       lds_barrier();
     }
-  } else if (wave == 4) {
+  } else if (wave == W_LOADER) {
     const DmaAddr D = dma_addr(lane, DV);
     float ga, gb;
     loader_prologue(sm, sq, nch, ga, gb, lane);
@@ -934,14 +977,18 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
       loader_period(sm, sq, D, p, nch, DV, ga, gb, lane);
       lds_barrier();
     }
-  } else if (wave == 6) {
+  } else if (wave == W_INV) {
+    // column lr of the identity: the start of the forward substitution
+    float xinit[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xinit[r] = (r == lr) ? 1.f : 0.f;
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
-      if (p + 1 >= 0 && p + 1 < nch) build_inverse(sm, p + 1, lane);
+      if (p + 1 >= 0 && p + 1 < nch) build_inverse(sm, p + 1, xinit, lane);
       lds_barrier();
     }
-  } else {
-    // wave 5: the L2 prefetch, issued by a wave that never waits for it
+  } else if (wave == W_PREFETCH) {
+    // the L2 prefetch, issued by a wave that never waits for it
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
       if (p + PREFETCH_AHEAD < nch) prefetch_chunk(sq, p + PREFETCH_AHEAD, slice, DV, lane);

@@ -16,6 +16,10 @@
 
 namespace gdn {
 
+// Lower bound applied to log2(alpha): a gate of 0 then gives decay factors
+// that are 0 in fp32 without turning differences of prefix sums into NaN.
+constexpr float LOG2_ALPHA_MIN = -200.f;
+
 typedef uint16_t bf16_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));

@@ -15,6 +15,11 @@ all as float32 standard normals):
     both evaluated in fp64 and rounded once to fp32;
   * "slow" gates use alpha = exp(-0.01 * softplus(z_alpha)) (alpha close to 1,
     i.e. a state that forgets slowly);
+  * "fast" gates use alpha = exp(-4 * softplus(z_alpha)) (a chunk of 64 tokens
+    decays by far more than 2^-120);
+  * "resets" gates are the default ones with alpha = 0 exactly where
+    z_alpha > 2.3 (about 1% of tokens: the state is wiped there);
+  * "beta2" gates are the default alpha with beta = 2 sigmoid(z_beta) in (0,2);
   * S0, when requested, is N(0, 0.1) (standard deviation 0.1), fp32.
 
 Every returned tensor is a contiguous CPU tensor; the caller moves it to the
@@ -56,13 +61,17 @@ def _cast(x: np.ndarray, dtype: str) -> torch.Tensor:
 def _gates(rng, shape, gate: str):
     z_a = rng.standard_normal(shape, dtype=np.float32)
     z_b = rng.standard_normal(shape, dtype=np.float32)
-    if gate == "default":
+    if gate in ("default", "beta2"):
         alpha = np.exp(-_softplus64(z_a))
     elif gate == "slow":
         alpha = np.exp(-0.01 * _softplus64(z_a))
+    elif gate == "fast":
+        alpha = np.exp(-4.0 * _softplus64(z_a))
+    elif gate == "resets":
+        alpha = np.where(z_a > 2.3, 0.0, np.exp(-_softplus64(z_a)))
     else:
-        raise ValueError("gate must be 'default' or 'slow'")
-    beta = _sigmoid64(z_b)
+        raise ValueError("gate must be one of 'default', 'slow', 'fast', 'resets', 'beta2'")
+    beta = _sigmoid64(z_b) * (2.0 if gate == "beta2" else 1.0)
     return (torch.from_numpy(alpha.astype(np.float32)).contiguous(),
             torch.from_numpy(beta.astype(np.float32)).contiguous())
 

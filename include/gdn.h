@@ -64,8 +64,9 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *
  *   q, k           [B,H,T,dk]  dtype   queries and keys, d contiguous
  *   v              [B,H,T,dv]  dtype   values
- *   alpha          [B,H,T]     fp32    forgetting gate, expected in (0,1]
- *   beta           [B,H,T]     fp32    write strength, expected in [0,1]
+ *   alpha          [B,H,T]     fp32    forgetting gate in [0,1]
+ *   beta           [B,H,T]     fp32    write strength (the pages draw it from
+ *                                      (0,1); any finite value is accepted)
  *   initial_state  [B,H,dv,dk] fp32    S_0, or NULL for a zero state
  *   o              [B,H,T,dv]  dtype   OUT: o_t = S_t q_t
  *   final_state    [B,H,dv,dk] fp32    OUT: S_T, or NULL to skip it.
@@ -77,8 +78,9 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *   dk, dv         64 or 128, dk == dv.
  *   T              >= 0.  T == 0 writes final_state = initial_state (or zeros).
  *
- * `o` must not overlap any input.  Alpha must be > 0: the chunk form works
- * with log(alpha) (alpha == 0 gives -inf logs and NaN results).
+ * `o` must not overlap any input.  The chunk form works with log2(alpha),
+ * clamped below at -200: a gate under 2^-200 (alpha == 0 included) acts as
+ * 2^-200, which wipes the state up to that factor.
  */
 int gdn_chunk_fwd(const void* q, const void* k, const void* v,
                   const float* alpha, const float* beta,

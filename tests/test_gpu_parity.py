@@ -64,6 +64,15 @@ SMALL_CASES = [
     (4, 4, 130, 64, "bf16", False, "default"),
     (1, 2, 2048, 128, "bf16", True, "slow"),      # alpha close to 1: long memory
     (1, 2, 1024, 64, "f32", True, "slow"),
+    # chunk decay far below 2^-120: P and L take one exp2 per element
+    (2, 2, 700, 128, "bf16", True, "fast"),
+    (1, 2, 300, 64, "f32", True, "fast"),
+    # alpha == 0 at ~1% of tokens: chunks with a reset take the exp2 path, the
+    # others the split decay, in the same call
+    (2, 2, 1500, 128, "bf16", True, "resets"),
+    (1, 2, 500, 64, "f32", True, "resets"),
+    (2, 2, 600, 128, "bf16", True, "beta2"),
+    (1, 1, 400, 64, "f32", True, "beta2"),
 ]
 
 
