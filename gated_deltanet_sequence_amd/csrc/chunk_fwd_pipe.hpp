@@ -376,11 +376,20 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     for (int pp = 0; pp < 4; ++pp)
       fr[n % 3][pp] = as_op(n < 4 ? ld3<uint4>(kf_b[pp], n * 4096) : ld3<uint4>(qf_b[pp], (n - 4) * 4096));
   };
+  // V and the gates of Y, read during the products of blocks 1..3
+  uint2 vv[4];
+  float4 b4[4], g4[4];
   read_block(0);
   read_block(1);
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     read_block(rb + 2);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      if (rb == 1) vv[h] = tr3(v_b, h * 16 * DVS * 2);
+      if (rb == 2) b4[h] = *reinterpret_cast<const float4*>(gt + G_BETA * C + 16 * h + 4 * lg);
+      if (rb == 3) g4[h] = *reinterpret_cast<const float4*>(gt + G_EG * C + 16 * h + 4 * lg);
+    }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 az = zero4();
 #pragma unroll
@@ -391,19 +400,32 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     __builtin_amdgcn_sched_barrier(0);
   }
   // ---- O1 = S Q^T (rows = value, columns = token) while Y = beta (V -
-  // 2^g Z) is formed; V, the gates and Ti are read meanwhile.
-  uint2 vv[4];
-  float4 b4[4], g4[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    vv[rb] = tr3(v_b, rb * 16 * DVS * 2);
-    b4[rb] = *reinterpret_cast<const float4*>(gt + G_BETA * C + 16 * rb + 4 * lg);
-    g4[rb] = *reinterpret_cast<const float4*>(gt + G_EG * C + 16 * rb + 4 * lg);
-  }
+  // 2^g Z) is formed; Ti, the output gates and P are read meanwhile.
   f32x4 O1[4], y[4];
+  bf16x8_t tf[4][2];
+  f32x4 el[4];
+  float eg[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     if (rb < 2) read_block(rb + 6);  // Q block rb sits in slot (4 + rb) % 3
+    if (rb == 2) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int pp = 0; pp <= tb / 2; ++pp) {
+          const int off = pp * 32 * TTS * 2 + tb * 32;
+          tf[tb][pp] = as_op(tr3(t_b, off), tr3(t_b, off + 16 * TTS * 2));
+        }
+    }
+    if (rb == 3) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float4 e = *reinterpret_cast<const float4*>(gt + G_EL * C + 16 * h + 4 * lg);
+        el[h] = f32x4{e.x, e.y, e.z, e.w};
+        eg[h] = gt[G_EG * C + 16 * h + lr];
+      }
+      if constexpr (FINISH) read_p(sm, A, c - 1, pf);
+    }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 ao = zero4();
 #pragma unroll
@@ -416,23 +438,6 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     __builtin_amdgcn_sched_barrier(0);
   }
   const bf16x8_t Yop[2] = {pack_op(y[0], y[1]), pack_op(y[2], y[3])};
-  bf16x8_t tf[4][2];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int pp = 0; pp <= rb / 2; ++pp) {
-      const int off = pp * 32 * TTS * 2 + rb * 32;
-      tf[rb][pp] = as_op(tr3(t_b, off), tr3(t_b, off + 16 * TTS * 2));
-    }
-  f32x4 el[4];
-  float eg[4];
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const float4 e = *reinterpret_cast<const float4*>(gt + G_EL * C + 16 * h + 4 * lg);
-    el[h] = f32x4{e.x, e.y, e.z, e.w};
-    eg[h] = gt[G_EG * C + 16 * h + lr];
-  }
-  if constexpr (FINISH) read_p(sm, A, c - 1, pf);
   // the first K^T operands of the state update (ring of three slots, tile jb
   // in slot jb % 3)
   bf16x8_t kt[3][2];
