@@ -32,7 +32,7 @@
 //                       earlier, then loads the keys of chunk p+3.
 //   wave 4 (prefetch)   touches the cache lines of chunk p+3 so that later
 //                       loads hit L2, and never waits for those loads.
-//   wave 6 (loader)     moves V of chunk p+1 and K, Q of chunk p+2 into LDS
+//   wave 6 (loader)     moves V, K and Q of chunk p+1 into LDS
 //                       with LDS-DMA loads, builds the gate tables of chunk p+3
 //                       from gates it loaded one period earlier and loads the
 //                       gates of chunk p+4.
@@ -83,10 +83,9 @@ constexpr int PREFETCH_AHEAD = 3;
 // Targets of LDS-DMA loads are arrays of their own: the compiler then sees
 // that the LDS reads which follow such a load in the same wave touch other
 // objects, and does not wait for the load before them.
-// K and Q of chunk c sit in buffer c % 3 (loaded two periods ahead), V of
-// chunk c in buffer c % 2 (loaded one period ahead).
-__shared__ __attribute__((aligned(16))) bf16_t lds_K[3][C * DK];  // [token][key], octets swizzled by swz_kq(token)
-__shared__ __attribute__((aligned(16))) bf16_t lds_Q[3][C * DK];
+// K, Q and V of chunk c sit in buffer c % 2 (loaded one period ahead).
+__shared__ __attribute__((aligned(16))) bf16_t lds_K[2][C * DK];  // [token][key], octets swizzled by swz_kq(token)
+__shared__ __attribute__((aligned(16))) bf16_t lds_Q[2][C * DK];
 __shared__ __attribute__((aligned(16))) bf16_t lds_V[2][C * DVS];  // [token][slice column]
 __shared__ __attribute__((aligned(16))) uint32_t lds_touch[64];    // landing area of the L2 prefetch (never read)
 
@@ -346,7 +345,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     finish_output(sq, A, R, pf, c - 1, DV);
     return;
   }
-  const int buf = (int)(c & 1), kqb = (int)(c % 3);
+  const int buf = (int)(c & 1), kqb = buf;
   lptr kf_b[4], qf_b[4], kt_b[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
@@ -530,9 +529,9 @@ __device__ __forceinline__ DmaAddr dma_addr(int lane, int DV) {
   A.v = (uint32_t)((lane >> 2) * DV * 2 + (((lane & 3) ^ (2 * ((lane >> 4) & 1))) << 4));
   return A;
 }
-// K and Q of chunk c (32 loads) into buffers c % 3.
+// K and Q of chunk c (32 loads) into buffers c % 2.
 __device__ __forceinline__ void dma_kq(const Seq& sq, const DmaAddr& A, int64_t c) {
-  const int buf = (int)(c % 3);
+  const int buf = (int)(c & 1);
   const uint32_t kq0 = (uint32_t)(c * C * DK * 2);
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
@@ -579,7 +578,7 @@ constexpr int TILE_SB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 // issued before the decay, mask and store of tile t.
 __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
-  const int buf = (int)(c & 1), kqb = (int)(c % 3);
+  const int buf = (int)(c & 1), kqb = buf;
   lptr kf_b[4], qf_b[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
@@ -750,11 +749,10 @@ __device__ __forceinline__ void build_l(Smem& sm, const FragRegs& R, int64_t c, 
 
 // ============================================================ wave 4: loader
 // In period p the loader builds the gate tables of chunk p+3 (gates loaded one
-// period earlier), then loads the gates of chunk p+4, V of chunk p+1 and K, Q
-// of chunk p+2, in that order.  It ends the period once V of chunk p+1 (and
-// with it K, Q of chunk p+1, issued one period earlier) is in LDS, while K, Q
-// of chunk p+2 stay in flight.  The gate tables of chunk 0 come before the
-// first period.
+// period earlier), then loads the gates of chunk p+4 and V, K, Q of chunk p+1,
+// in that order, and ends the period once V, K, Q of chunk p+1 are in LDS
+// (the prefetch wave has pulled their lines into L2 two periods earlier).
+// The gate tables of chunk 0 come before the first period.
 __device__ __forceinline__ void loader_prologue(Smem& sm, const Seq& sq, int64_t nch, float& ga, float& gb,
                                                 int lane) {
   ga = gb = 0.f;
@@ -773,12 +771,8 @@ __device__ __forceinline__ void loader_period(Smem& sm, const Seq& sq, const Dma
     gb = buf_ldf(sq.b, t4);
   }
   if (p + 1 >= 0 && p + 1 < nch) dma_v(sq, D, p + 1, DV);
-  if (p + 2 >= 0 && p + 2 < nch) {
-    dma_kq(sq, D, p + 2);
-    __builtin_amdgcn_s_waitcnt(0x8f70);  // vmcnt(32): all but the 32 loads of K, Q of chunk p+2
-  } else {
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  }
+  if (p + 1 >= 0 && p + 1 < nch) dma_kq(sq, D, p + 1);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 }
 
 // ============================================================ wave 6: inverse
