@@ -1,5 +1,8 @@
 // Pipelined chunked forward pass of the gated delta rule for bf16 inputs,
-// d_k = d_v = 128, 64-token chunks, on gfx950.
+// d_k = d_v = 128 or 64, 64-token chunks, on gfx950.  The kernel always works
+// on 128 keys; with d = 64 the keys 64..127 are zero in LDS (their loads read
+// past the buffer range, which returns zero) and in the state, so they add
+// nothing.
 //
 // Sources (web pages, by title and section):
 //   [P1] "Gated DeltaNet GPU并行实现：拆解线性注意力循环的两种高效方案"
@@ -265,6 +268,8 @@ __device__ __forceinline__ float lane63(float x) {
 struct Seq {
   __amdgpu_buffer_rsrc_t q, k, v, a, b, o;
   int64_t T;
+  int dk;  // key width of q, k and the state in global memory: 128, or 64
+           // (then keys 64..127 are zero in LDS and in the state)
 };
 
 // Global key column of the first of the 4 state values a lane holds in
@@ -520,11 +525,17 @@ struct DmaAddr {
   uint32_t kq[4];  // per it & 3
   uint32_t v;
 };
-__device__ __forceinline__ DmaAddr dma_addr(int lane, int DV) {
+// With dk = 64 a lane whose key octet is 8 or more reads past the end of the
+// buffer range, which returns zero, so those LDS octets are written as zero.
+constexpr uint32_t OOB_OFFSET = 0x80000000u;
+__device__ __forceinline__ DmaAddr dma_addr(int lane, int DV, int dk) {
   const int lr = lane & 15, lg = lane >> 4;
   DmaAddr A;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) A.kq[m] = (uint32_t)(lg * 256 + ((lr ^ swz_kq(4 * m + lg)) << 4));
+  for (int m = 0; m < 4; ++m) {
+    const int ko = lr ^ swz_kq(4 * m + lg);
+    A.kq[m] = 8 * ko < dk ? (uint32_t)(lg * dk * 2 + (ko << 4)) : OOB_OFFSET;
+  }
   // lane -> token 16 it + lane / 4, physical slot lane % 4 (see vtr)
   A.v = (uint32_t)((lane >> 2) * DV * 2 + (((lane & 3) ^ (2 * ((lane >> 4) & 1))) << 4));
   return A;
@@ -532,13 +543,13 @@ __device__ __forceinline__ DmaAddr dma_addr(int lane, int DV) {
 // K and Q of chunk c (32 loads) into buffers c % 2.
 __device__ __forceinline__ void dma_kq(const Seq& sq, const DmaAddr& A, int64_t c) {
   const int buf = (int)(c & 1);
-  const uint32_t kq0 = (uint32_t)(c * C * DK * 2);
+  const uint32_t row = (uint32_t)(sq.dk * 2), kq0 = (uint32_t)(c * C) * row;
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.k, (lds_void*)&lds_K[buf][it * 512], 16, A.kq[it & 3],
-                                             (int)(kq0 + it * 1024), 0, 0);
+                                             (int)(kq0 + it * 4 * row), 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.q, (lds_void*)&lds_Q[buf][it * 512], 16, A.kq[it & 3],
-                                             (int)(kq0 + it * 1024), 0, 0);
+                                             (int)(kq0 + it * 4 * row), 0, 0);
   }
 }
 // V of chunk c (4 loads) into buffer c % 2.
@@ -560,7 +571,7 @@ __device__ __forceinline__ void dma_v(const Seq& sq, const DmaAddr& A, int64_t c
 // the descriptors stay uniform.
 __device__ __forceinline__ void prefetch_chunk(const Seq& sq, int64_t c, int slice, int DV, int lane) {
   lds_void* land = (lds_void*)&lds_touch[0];
-  const uint32_t kq = (uint32_t)(c * C * DK * 2) + (uint32_t)((32 * slice + (lane & 31)) * 128);
+  const uint32_t kq = (uint32_t)(c * C * sq.dk * 2) + (uint32_t)((32 * slice + (lane & 31)) * 128);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.k, land, 4, kq, 0, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.q, land, 4, kq, 0, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.v, land, 4, (uint32_t)((c * C + lane) * DV * 2), 0, 0, 0);
@@ -657,12 +668,15 @@ struct FragRegs {
 };
 
 __device__ __forceinline__ void load_frags(FragRegs& R, const Seq& sq, int64_t c, int lane) {
-  const uint32_t lane_off = (uint32_t)((lane & 15) * DK * 2 + (lane >> 4) * 16);
-  const uint32_t base = (uint32_t)(c * C * DK * 2);
+  const uint32_t row = (uint32_t)(sq.dk * 2);
+  const uint32_t lane_off = (uint32_t)(lane & 15) * row + (uint32_t)((lane >> 4) * 16);
+  const uint32_t base = (uint32_t)(c * C) * row;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) R.kf[rb][pp] = buf_ld16s(sq.k, lane_off, base + rb * 16 * DK * 2 + pp * 64);
+    for (int pp = 0; pp < 4; ++pp)
+      R.kf[rb][pp] = 32 * pp < sq.dk ? buf_ld16s(sq.k, lane_off, base + rb * 16 * row + pp * 64)
+                                     : make_uint4(0u, 0u, 0u, 0u);
 }
 
 // Gate tables of chunk c (alpha, beta of token `lane` as loaded, 0 past the
@@ -862,7 +876,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* initial_state, bf16_t* __restrict__ o, float* final_state, int nchain,
-    int64_t Tlen, int DV, int xcd_map) {
+    int64_t Tlen, int DV, int dk, int xcd_map) {
   __shared__ Smem sm;
 
   const int tid = threadIdx.x;
@@ -890,9 +904,10 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
   Seq sq;
   sq.T = Tlen;
   {
-    const uint32_t kq_bytes = (uint32_t)(Tlen * DK * 2);
-    sq.q = make_rsrc(q + (int64_t)chain * Tlen * DK, kq_bytes);
-    sq.k = make_rsrc(k + (int64_t)chain * Tlen * DK, kq_bytes);
+    sq.dk = dk;
+    const uint32_t kq_bytes = (uint32_t)(Tlen * dk * 2);
+    sq.q = make_rsrc(q + (int64_t)chain * Tlen * dk, kq_bytes);
+    sq.k = make_rsrc(k + (int64_t)chain * Tlen * dk, kq_bytes);
     // value / output slice: the descriptor range ends with the sequence
     const int64_t vs = (int64_t)chain * Tlen * DV + slice * DVS;
     const uint32_t v_bytes = (uint32_t)((Tlen * DV - slice * DVS) * 2);
@@ -929,8 +944,8 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) {
       R.S[jb] = zero4();
-      if (initial_state) {
-        const float4 s4 = *reinterpret_cast<const float4*>(initial_state + st_row * DK + state_col(jb, lg));
+      if (initial_state && state_col(jb, lg) < dk) {
+        const float4 s4 = *reinterpret_cast<const float4*>(initial_state + st_row * dk + state_col(jb, lg));
         R.S[jb] = f32x4{s4.x, s4.y, s4.z, s4.w};
       }
     }
@@ -952,7 +967,8 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     if (final_state) {
 #pragma unroll
       for (int jb = 0; jb < 8; ++jb)
-        *reinterpret_cast<float4*>(final_state + st_row * DK + state_col(jb, lg)) = as_f4(R.S[jb]);
+        if (state_col(jb, lg) < dk)
+          *reinterpret_cast<float4*>(final_state + st_row * dk + state_col(jb, lg)) = as_f4(R.S[jb]);
     }
   } else if (wave == W_P) {
     const StateAddr A = state_addr(lane, 0, DV);
@@ -971,7 +987,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
       lds_barrier();
     }
   } else if (wave == W_LOADER) {
-    const DmaAddr D = dma_addr(lane, DV);
+    const DmaAddr D = dma_addr(lane, DV, dk);
     float ga, gb;
     loader_prologue(sm, sq, nch, ga, gb, lane);
     lds_barrier();

@@ -43,14 +43,16 @@ int launch_chunk(const void* q, const void* k, const void* v, const float* alpha
 
 int launch_chunk_pipe(const void* q, const void* k, const void* v, const float* alpha,
                       const float* beta, const float* s0, void* o, float* sT, int64_t nchain,
-                      int64_t T, int64_t dv, hipStream_t stream) {
+                      int64_t T, int64_t dk, int64_t dv, hipStream_t stream) {
   const int64_t nblocks = nchain * (dv / gdn::pipe::DVS);
   if (nblocks > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+  // one sequence's q, k or v must fit a 32-bit buffer range
+  if (T * dk * 2 > 0x7fffffff || T * dv * 2 > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
   const int xcd_map = (nchain % 8) == 0;
   hipLaunchKernelGGL(gdn::pipe::chunk_fwd_pipe_kernel, dim3((unsigned)nblocks), dim3(64 * gdn::pipe::NWAVES), 0,
                      stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                      static_cast<const bf16_t*>(v), alpha, beta, s0, static_cast<bf16_t*>(o), sT,
-                     (int)nchain, T, (int)dv, xcd_map);
+                     (int)nchain, T, (int)dv, (int)dk, xcd_map);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
@@ -108,13 +110,9 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
   if (nchain == 0) return GDN_OK;
   if (T == 0 && !final_state) return GDN_OK;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  if (dtype == GDN_BF16) {
-    if (dk == 128)
-      return launch_chunk_pipe(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv,
-                               stream);
-    return launch_chunk<bf16_t, 64, 16, 64, 4>(q, k, v, alpha, beta, initial_state, o,
-                                               final_state, nchain, T, dv, stream);
-  }
+  if (dtype == GDN_BF16)
+    return launch_chunk_pipe(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dk, dv,
+                             stream);
   return launch_chunk<float, 64, 16, 64, 4>(q, k, v, alpha, beta, initial_state, o, final_state,
                                             nchain, T, dv, stream);
 }

@@ -77,6 +77,8 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *                  identity maps (alpha = 1, beta = 0) and produce no output.
  *   dk, dv         64 or 128, dk == dv.
  *   T              >= 0.  T == 0 writes final_state = initial_state (or zeros).
+ *                  For bf16, one sequence's q, k or v (T * d * 2 bytes) must be
+ *                  under 2^31 bytes, else GDN_ERR_UNSUPPORTED.
  *
  * `o` must not overlap any input.  The chunk form works with log2(alpha),
  * clamped below at -200: a gate under 2^-200 (alpha == 0 included) acts as
