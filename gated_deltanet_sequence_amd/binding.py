@@ -49,6 +49,11 @@ def load_library(path: str | None = None):
     i32 = ctypes.c_int
     lib.gdn_chunk_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32, p]
     lib.gdn_chunk_fwd.restype = i32
+    lib.gdn_chunk_fwd_split.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
+                                        p, ctypes.c_size_t, p]
+    lib.gdn_chunk_fwd_split.restype = i32
+    lib.gdn_chunk_fwd_split_workspace.argtypes = [i64, i64, i64, i64, i64, i64, i32]
+    lib.gdn_chunk_fwd_split_workspace.restype = ctypes.c_size_t
     lib.gdn_recurrent_step.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, p]
     lib.gdn_recurrent_step.restype = i32
     lib.gdn_strerror.argtypes = [i32]
@@ -86,14 +91,7 @@ def _stream_ptr(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def gdn_chunk_fwd(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 64, *,
-                  o=None, final_state=None, output_final_state: bool = True, stream=None):
-    """Chunked forward pass.  q, k [B,H,T,dk], v [B,H,T,dv] (bf16 or fp32);
-    alpha, beta [B,H,T] fp32; initial_state [B,H,dv,dk] fp32 or None.
-
-    Returns (o [B,H,T,dv] in the input dtype, final_state [B,H,dv,dk] fp32 or
-    None).  ``final_state`` may be passed (and may be ``initial_state`` itself
-    for an in-place carry)."""
+def _check_fwd_args(q, k, v, alpha, beta, initial_state):
     if q.dtype not in _DTYPES:
         raise TypeError("q/k/v must be bfloat16 or float32")
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -108,6 +106,18 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 64
     if initial_state is not None and (initial_state.dtype != torch.float32 or
                                       tuple(initial_state.shape) != (B, H, dv, dk)):
         raise ValueError("initial_state must be fp32 [B,H,dv,dk]")
+    return B, H, T, dk, dv
+
+
+def gdn_chunk_fwd(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 64, *,
+                  o=None, final_state=None, output_final_state: bool = True, stream=None):
+    """Chunked forward pass.  q, k [B,H,T,dk], v [B,H,T,dv] (bf16 or fp32);
+    alpha, beta [B,H,T] fp32; initial_state [B,H,dv,dk] fp32 or None.
+
+    Returns (o [B,H,T,dv] in the input dtype, final_state [B,H,dv,dk] fp32 or
+    None).  ``final_state`` may be passed (and may be ``initial_state`` itself
+    for an in-place carry)."""
+    B, H, T, dk, dv = _check_fwd_args(q, k, v, alpha, beta, initial_state)
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     if final_state is None and output_final_state:
@@ -120,6 +130,40 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 64
                            int(chunk_size), _DTYPES[q.dtype], _stream_ptr(stream, q.device))
     if rc != GDN_OK:
         raise GDNError(rc, "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gdn_chunk_fwd_split_workspace(B, H, T, dk, dv, chunk_size: int = 64, dtype=torch.bfloat16) -> int:
+    """Bytes of workspace gdn_chunk_fwd_split needs on the current device (0: no split)."""
+    return int(load_library().gdn_chunk_fwd_split_workspace(B, H, T, dk, dv, int(chunk_size),
+                                                            _DTYPES[dtype]))
+
+
+def gdn_chunk_fwd_split(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 64, *,
+                        o=None, final_state=None, output_final_state: bool = True,
+                        workspace=None, stream=None):
+    """gdn_chunk_fwd with every sequence split into segments that run in
+    parallel (for few, long sequences).  Same arguments and result; the
+    workspace (a uint8 GPU tensor) is allocated here when not given."""
+    B, H, T, dk, dv = _check_fwd_args(q, k, v, alpha, beta, initial_state)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    need = gdn_chunk_fwd_split_workspace(B, H, T, dk, dv, chunk_size, q.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    rc = lib.gdn_chunk_fwd_split(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                 _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                                 _dev_ptr(initial_state, "initial_state"), _dev_ptr(o, "o"),
+                                 _dev_ptr(final_state, "final_state"), B, H, T, dk, dv,
+                                 int(chunk_size), _DTYPES[q.dtype],
+                                 _dev_ptr(workspace, "workspace"), ws_bytes,
+                                 _stream_ptr(stream, q.device))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_chunk_fwd_split")
     return o, final_state
 
 

@@ -872,11 +872,35 @@ __device__ __forceinline__ void build_inverse(Smem& sm, int64_t c, const float (
 }
 
 // ============================================================ kernel
+// How the workgroups of one launch map onto (sequence, token range) pairs.
+//   SEQ:     chain i is sequence i, all T tokens; state from initial_state[i]
+//            (zero if NULL) to final_state[i] (skipped if NULL).
+//   SPLIT_A: the first G-1 segments of L tokens of every sequence, twice:
+//            kind 0 from a zero state with V (chain state -> ws slot
+//            "tilde"), kind 1 from the identity with V read as zero (-> slot
+//            "trans"); no output.  Kind 1 gives the segment's transition M:
+//            a state S entering the segment leaves it as S M + tilde.
+//   SPLIT_C: all G segments of every sequence, segment g starting from ws
+//            slot "start", with output; the last segment's state goes to
+//            final_state.
+// ws holds tilde and trans, nseq * (G-1) states of d x d floats each
+// (index seq * (G-1) + g), then start, nseq * G states (index seq * G + g;
+// start of segment 0 is a copy of initial_state).
+enum { MAP_SEQ = 0, MAP_SPLIT_A = 1, MAP_SPLIT_C = 2 };
+struct ChainMap {
+  int mode, nseq, G;
+  int64_t T, L;  // tokens per sequence, tokens per segment (a multiple of C)
+  float* ws;
+};
+__host__ __device__ inline int map_chains(const ChainMap& m) {
+  return m.mode == MAP_SEQ ? m.nseq : m.mode == MAP_SPLIT_A ? 2 * m.nseq * (m.G - 1) : m.nseq * m.G;
+}
+
 __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
-    const float* initial_state, bf16_t* __restrict__ o, float* final_state, int nchain,
-    int64_t Tlen, int DV, int dk, int xcd_map) {
+    const float* initial_state, bf16_t* __restrict__ o, float* final_state, ChainMap cm,
+    int DV, int dk, int xcd_map) {
   __shared__ Smem sm;
 
   const int tid = threadIdx.x;
@@ -886,6 +910,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
   const int lg = lane >> 4;
 
   const int NS = DV / DVS;
+  const int nchain = map_chains(cm);
   int chain, slice;
   {
     const int w = blockIdx.x;
@@ -901,20 +926,50 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
   }
   if (chain >= nchain) return;
 
+  // this chain's sequence, token range, start and end state, and whether it
+  // reads V and writes output
+  const int64_t dd = (int64_t)dk * DV;  // floats per state
+  int seq = chain;
+  int64_t t0 = 0, Tlen = cm.T;
+  bool v_on = true, o_on = true, s0_ident = false;
+  const float* s0 = initial_state ? initial_state + (int64_t)chain * dd : nullptr;
+  float* sT = final_state ? final_state + (int64_t)chain * dd : nullptr;
+  if (cm.mode == MAP_SPLIT_A) {
+    const int per = cm.nseq * (cm.G - 1);
+    const int kind = chain / per, r = chain % per;
+    seq = r / (cm.G - 1);
+    t0 = (int64_t)(r % (cm.G - 1)) * cm.L;
+    Tlen = cm.L;
+    o_on = false;
+    v_on = kind == 0;
+    s0_ident = kind == 1;
+    s0 = nullptr;
+    sT = cm.ws + ((int64_t)kind * per + r) * dd;
+  } else if (cm.mode == MAP_SPLIT_C) {
+    seq = chain / cm.G;
+    const int g = chain % cm.G;
+    t0 = (int64_t)g * cm.L;
+    Tlen = g == cm.G - 1 ? cm.T - t0 : cm.L;
+    s0 = cm.ws + (2 * (int64_t)cm.nseq * (cm.G - 1) + (int64_t)seq * cm.G + g) * dd;
+    sT = g == cm.G - 1 && final_state ? final_state + (int64_t)seq * dd : nullptr;
+  }
+
   Seq sq;
   sq.T = Tlen;
   {
     sq.dk = dk;
+    const int64_t tok = (int64_t)seq * cm.T + t0;  // first token in memory
     const uint32_t kq_bytes = (uint32_t)(Tlen * dk * 2);
-    sq.q = make_rsrc(q + (int64_t)chain * Tlen * dk, kq_bytes);
-    sq.k = make_rsrc(k + (int64_t)chain * Tlen * dk, kq_bytes);
-    // value / output slice: the descriptor range ends with the sequence
-    const int64_t vs = (int64_t)chain * Tlen * DV + slice * DVS;
+    sq.q = make_rsrc(q + tok * dk, kq_bytes);
+    sq.k = make_rsrc(k + tok * dk, kq_bytes);
+    // value / output slice: the descriptor range ends with the token range;
+    // an empty range reads zeros and drops stores
+    const int64_t vs = tok * DV + slice * DVS;
     const uint32_t v_bytes = (uint32_t)((Tlen * DV - slice * DVS) * 2);
-    sq.v = make_rsrc(v + vs, v_bytes);
-    sq.o = make_rsrc(o + vs, v_bytes);
-    sq.a = make_rsrc(alpha + (int64_t)chain * Tlen, (uint32_t)(Tlen * 4));
-    sq.b = make_rsrc(beta + (int64_t)chain * Tlen, (uint32_t)(Tlen * 4));
+    sq.v = make_rsrc(v + vs, v_on ? v_bytes : 0u);
+    sq.o = make_rsrc(o + vs, o_on ? v_bytes : 0u);
+    sq.a = make_rsrc(alpha + tok, (uint32_t)(Tlen * 4));
+    sq.b = make_rsrc(beta + tok, (uint32_t)(Tlen * 4));
   }
   const int64_t nch = (Tlen + C - 1) / C;
 
@@ -939,13 +994,16 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
   if (wave < 2) {
     const int X = wave;
     const StateAddr A = state_addr(lane, X, DV);
-    const int64_t st_row = (int64_t)chain * DV + (int64_t)slice * DVS + 16 * X + lr;
+    const int st_row = slice * DVS + 16 * X + lr;  // value row of the state
     StateRegs R;
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) {
       R.S[jb] = zero4();
-      if (initial_state && state_col(jb, lg) < dk) {
-        const float4 s4 = *reinterpret_cast<const float4*>(initial_state + st_row * dk + state_col(jb, lg));
+      if (s0_ident) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) R.S[jb][e] = st_row == state_col(jb, lg) + e ? 1.f : 0.f;
+      } else if (s0 && state_col(jb, lg) < dk) {
+        const float4 s4 = *reinterpret_cast<const float4*>(s0 + (int64_t)st_row * dk + state_col(jb, lg));
         R.S[jb] = f32x4{s4.x, s4.y, s4.z, s4.w};
       }
     }
@@ -964,11 +1022,11 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
       state_period<true, false>(sm, sq, A, R, nch, DV, lane);
     }
     lds_barrier();
-    if (final_state) {
+    if (sT) {
 #pragma unroll
       for (int jb = 0; jb < 8; ++jb)
         if (state_col(jb, lg) < dk)
-          *reinterpret_cast<float4*>(final_state + st_row * dk + state_col(jb, lg)) = as_f4(R.S[jb]);
+          *reinterpret_cast<float4*>(sT + (int64_t)st_row * dk + state_col(jb, lg)) = as_f4(R.S[jb]);
     }
   } else if (wave == W_P) {
     const StateAddr A = state_addr(lane, 0, DV);

@@ -8,6 +8,7 @@
 #include "chunk_fwd.hpp"
 #include "chunk_fwd_pipe.hpp"
 #include "recurrent_step.hpp"
+#include "split_combine.hpp"
 
 namespace {
 
@@ -42,18 +43,62 @@ int launch_chunk(const void* q, const void* k, const void* v, const float* alpha
 }
 
 int launch_chunk_pipe(const void* q, const void* k, const void* v, const float* alpha,
-                      const float* beta, const float* s0, void* o, float* sT, int64_t nchain,
-                      int64_t T, int64_t dk, int64_t dv, hipStream_t stream) {
+                      const float* beta, const float* s0, void* o, float* sT,
+                      const gdn::pipe::ChainMap& cm, int64_t dk, int64_t dv, hipStream_t stream) {
+  const int64_t nchain = gdn::pipe::map_chains(cm);
   const int64_t nblocks = nchain * (dv / gdn::pipe::DVS);
   if (nblocks > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
   // one sequence's q, k or v must fit a 32-bit buffer range
-  if (T * dk * 2 > 0x7fffffff || T * dv * 2 > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+  if (cm.T * dk * 2 > 0x7fffffff || cm.T * dv * 2 > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
   const int xcd_map = (nchain % 8) == 0;
   hipLaunchKernelGGL(gdn::pipe::chunk_fwd_pipe_kernel, dim3((unsigned)nblocks), dim3(64 * gdn::pipe::NWAVES), 0,
                      stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                     static_cast<const bf16_t*>(v), alpha, beta, s0, static_cast<bf16_t*>(o), sT,
-                     (int)nchain, T, (int)dv, (int)dk, xcd_map);
+                     static_cast<const bf16_t*>(v), alpha, beta, s0, static_cast<bf16_t*>(o), sT, cm,
+                     (int)dv, (int)dk, xcd_map);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+gdn::pipe::ChainMap seq_map(int64_t nchain, int64_t T) {
+  gdn::pipe::ChainMap cm{};
+  cm.mode = gdn::pipe::MAP_SEQ;
+  cm.nseq = (int)nchain;
+  cm.G = 1;
+  cm.T = T;
+  cm.L = T;
+  cm.ws = nullptr;
+  return cm;
+}
+
+// Segments for the sequence-split pass: G segments of L tokens (a multiple of
+// the chunk size; the last one shorter), chosen so that its first launch
+// (2 (G-1) chains per sequence) still fits the device's CUs in one wave of
+// workgroups and every segment has at least MIN_SEG tokens.  G = 1 means no
+// split.
+constexpr int64_t MIN_SEG = 512;
+void split_plan(int64_t nseq, int64_t T, int64_t dv, int& G, int64_t& L) {
+  G = 1;
+  L = T;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) {
+    (void)hipGetLastError();
+    return;
+  }
+  const int64_t ns = dv / gdn::pipe::DVS;
+  int64_t g = 1 + ncu / (2 * nseq * ns);
+  g = g < T / MIN_SEG ? g : T / MIN_SEG;
+  if (g < 2) return;
+  const int64_t C = gdn::pipe::C;
+  L = ((T + g - 1) / g + C - 1) / C * C;
+  G = (int)((T + L - 1) / L);
+  if (G < 2) {
+    G = 1;
+    L = T;
+  }
+}
+
+size_t split_ws_bytes(int64_t nseq, int G, int64_t d) {
+  return G < 2 ? 0 : (size_t)(2 * nseq * (G - 1) + nseq * G) * (size_t)(d * d) * sizeof(float);
 }
 
 template <class E, int DK, int DV>
@@ -83,10 +128,13 @@ const char* gdn_strerror(int code) {
 
 const char* gdn_version(void) { return "0.1.0"; }
 
-int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
-                  const float* beta, const float* initial_state, void* o, float* final_state,
-                  int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk_size,
-                  gdn_dtype dtype, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+// Argument checks shared by the forward entry points: GDN_OK, or the error.
+int check_fwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+              const float* initial_state, void* o, float* final_state, int64_t B, int64_t H,
+              int64_t T, int64_t dk, int64_t dv, int64_t chunk_size, gdn_dtype dtype) {
   if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0 || chunk_size <= 0) return GDN_ERR_INVALID_ARG;
   if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
   const int64_t nchain = B * H;
@@ -107,14 +155,86 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
     for (const Range& r : ins)
       if (overlaps(ro, r)) return GDN_ERR_INVALID_ARG;
   }
+  return GDN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                  const float* beta, const float* initial_state, void* o, float* final_state,
+                  int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk_size,
+                  gdn_dtype dtype, void* hip_stream) {
+  const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
+                           chunk_size, dtype);
+  if (rc != GDN_OK) return rc;
+  const int64_t nchain = B * H;
   if (nchain == 0) return GDN_OK;
   if (T == 0 && !final_state) return GDN_OK;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (dtype == GDN_BF16)
-    return launch_chunk_pipe(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dk, dv,
-                             stream);
+    return launch_chunk_pipe(q, k, v, alpha, beta, initial_state, o, final_state, seq_map(nchain, T),
+                             dk, dv, stream);
   return launch_chunk<float, 64, 16, 64, 4>(q, k, v, alpha, beta, initial_state, o, final_state,
                                             nchain, T, dv, stream);
+}
+
+size_t gdn_chunk_fwd_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                                     int64_t chunk_size, gdn_dtype dtype) {
+  if (B <= 0 || H <= 0 || T <= 0 || dk != dv || (dk != 64 && dk != 128) || chunk_size != 64 ||
+      dtype != GDN_BF16)
+    return 0;
+  int G;
+  int64_t L;
+  split_plan(B * H, T, dv, G, L);
+  return split_ws_bytes(B * H, G, dk);
+}
+
+int gdn_chunk_fwd_split(const void* q, const void* k, const void* v, const float* alpha,
+                        const float* beta, const float* initial_state, void* o, float* final_state,
+                        int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk_size,
+                        gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
+                           chunk_size, dtype);
+  if (rc != GDN_OK) return rc;
+  const int64_t nchain = B * H;
+  int G = 1;
+  int64_t L = T;
+  if (dtype == GDN_BF16 && nchain > 0 && T > 0) split_plan(nchain, T, dv, G, L);
+  if (G < 2)
+    return gdn_chunk_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
+                         chunk_size, dtype, hip_stream);
+  const size_t need = split_ws_bytes(nchain, G, dk);
+  if (!workspace || workspace_bytes < need) return GDN_ERR_INVALID_ARG;
+  if (misaligned(workspace)) return GDN_ERR_ALIGNMENT;
+  {
+    const Range rw{workspace, (int64_t)need};
+    const int64_t esz = 2;
+    const Range others[] = {{q, nchain * T * dk * esz}, {k, nchain * T * dk * esz},
+                            {v, nchain * T * dv * esz}, {o, nchain * T * dv * esz},
+                            {alpha, nchain * T * 4},    {beta, nchain * T * 4},
+                            {initial_state, nchain * dv * dk * 4}, {final_state, nchain * dv * dk * 4}};
+    for (const Range& r : others)
+      if (overlaps(rw, r)) return GDN_ERR_INVALID_ARG;
+  }
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  gdn::pipe::ChainMap cm{};
+  cm.nseq = (int)nchain;
+  cm.G = G;
+  cm.T = T;
+  cm.L = L;
+  cm.ws = static_cast<float*>(workspace);
+  // 1: per segment, the state from zero and the transition (first G-1 segments)
+  cm.mode = gdn::pipe::MAP_SPLIT_A;
+  int r = launch_chunk_pipe(q, k, v, alpha, beta, nullptr, o, nullptr, cm, dk, dv, stream);
+  if (r != GDN_OK) return r;
+  // 2: the start state of every segment
+  hipLaunchKernelGGL(gdn::split::split_combine_kernel, dim3((unsigned)(nchain * (dk / gdn::split::ROWS))),
+                     dim3(gdn::split::THREADS), 0, stream, initial_state, cm.ws, (int)nchain, G, (int)dk);
+  if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
+  // 3: every segment from its start state, with output
+  cm.mode = gdn::pipe::MAP_SPLIT_C;
+  return launch_chunk_pipe(q, k, v, alpha, beta, nullptr, o, final_state, cm, dk, dv, stream);
 }
 
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,

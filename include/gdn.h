@@ -42,6 +42,7 @@
 #ifndef GDN_H
 #define GDN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -89,6 +90,43 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v,
                   const float* initial_state, void* o, float* final_state,
                   int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
                   int64_t chunk_size, gdn_dtype dtype, void* hip_stream);
+
+/*
+ * gdn_chunk_fwd_split — the same result as gdn_chunk_fwd, for workloads with
+ * few sequences (B*H small against the number of CUs), by splitting every
+ * sequence into G segments that run in parallel ([P1] §3.3 splitting a long
+ * sequence into parts, joined by composing their affine maps, §2.3):
+ *   1. for each of the first G-1 segments, its state from a zero start and
+ *      its transition matrix M (the state map S -> S M + tilde), in one launch;
+ *   2. the start state of every segment, start_{g+1} = start_g M_g + tilde_g
+ *      (fp32);
+ *   3. every segment from its start state, writing o and (last segment)
+ *      final_state.
+ * The work is about (3G-2)/G times that of gdn_chunk_fwd, spread over G
+ * times as many workgroups.  G is chosen from B*H, T and the device's CU
+ * count; when it comes out as 1 (enough sequences, or T under 1024 tokens),
+ * this is gdn_chunk_fwd itself and the workspace is not touched.  bf16 only
+ * (fp32 inputs always take gdn_chunk_fwd).
+ *
+ *   workspace        device memory owned by the caller, at least
+ *                    gdn_chunk_fwd_split_workspace(...) bytes, 16-byte
+ *                    aligned, overlapping no other argument; its contents
+ *                    on entry do not matter.  Calls that share a workspace
+ *                    must not overlap in time.
+ * Other arguments, errors and aliasing as for gdn_chunk_fwd; a missing or too
+ * small workspace (when G > 1) returns GDN_ERR_INVALID_ARG.
+ */
+int gdn_chunk_fwd_split(const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta,
+                        const float* initial_state, void* o, float* final_state,
+                        int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                        int64_t chunk_size, gdn_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes gdn_chunk_fwd_split needs for these sizes on the current
+ * device (0: it would not split).  A host-side query; launches nothing. */
+size_t gdn_chunk_fwd_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk,
+                                     int64_t dv, int64_t chunk_size, gdn_dtype dtype);
 
 /*
  * gdn_recurrent_step — one decode step: one new token for each of N*H

@@ -96,3 +96,30 @@ def test_recurrent_step_rejects(lib, kw, code):
 def test_recurrent_step_empty_is_noop(lib):
     assert step(lib, N=0) == 0
     assert step(lib, H=0, q=None, state=None, o=None) == 0
+
+
+def fwd_split(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, alpha=A + 192 * MB, beta=A + 200 * MB,
+              s0=None, o=A + 256 * MB, sT=None, B=1, H=1, T=64, dk=64, dv=64, C=64, dtype=1,
+              ws=None, ws_bytes=0):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gdn_chunk_fwd_split(P(q), P(k), P(v), P(alpha), P(beta), P(s0), P(o), P(sT),
+                                   B, H, T, dk, dv, C, dtype, P(ws), ws_bytes, None)
+
+
+def test_split_rejects_invalid_arguments(lib):
+    assert fwd_split(lib, B=-1) == binding.GDN_ERR_INVALID_ARG
+    assert fwd_split(lib, dtype=7) == binding.GDN_ERR_INVALID_ARG
+    assert fwd_split(lib, q=None) == binding.GDN_ERR_INVALID_ARG
+    assert fwd_split(lib, dk=96, dv=96) == binding.GDN_ERR_UNSUPPORTED
+    assert fwd_split(lib, C=32) == binding.GDN_ERR_UNSUPPORTED
+    assert fwd_split(lib, k=A + 8) == binding.GDN_ERR_ALIGNMENT
+    assert fwd_split(lib, o=A) == binding.GDN_ERR_INVALID_ARG  # output overlaps q
+
+
+def test_split_workspace_query_is_host_only(lib):
+    f = lib.gdn_chunk_fwd_split_workspace
+    assert f(1, 16, 131072, 128, 128, 64, 0) == 0      # fp32: never split
+    assert f(1, 16, 131072, 96, 96, 64, 1) == 0        # unsupported width
+    assert f(1, 16, 131072, 128, 128, 32, 1) == 0      # unsupported chunk size
+    assert f(0, 16, 131072, 128, 128, 64, 1) == 0      # nothing to do
+    assert f(1, 16, 131072, 128, 128, 64, 1) >= 0      # no GPU here: 0; on a GPU: > 0
