@@ -6,7 +6,7 @@ d_k=d_v=128, C=64, bf16 q/k/v, fp32 gates, zero initial state, fp32 final
 state), inputs resident in HBM before the timed region.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--no-decode] [--pmc-pass]
+                  [--no-decode] [--no-long] [--pmc-pass]
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   (writes the HBM-traffic
                   summary under profiles/ from two rocprofv3 --pmc runs)
 
@@ -139,6 +139,49 @@ def time_chunk(torch, xd, steps, warmup, settle_ms=SETTLE_MS):
     return wall, kms, o, sT
 
 
+LONG = dict(B=1, H=16, T=131072, d=128, seed=4)
+
+
+def time_long(torch, dev, launches=10):
+    """The long-context workload (16 sequences of 131072 tokens, S0 ~ N(0,0.1))
+    through the sequence-split entry point and, for comparison, the plain
+    one; mean of `launches` back-to-back launches between two events."""
+    from gated_deltanet_sequence_amd import inputs
+    from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd, gdn_chunk_fwd_split,
+                                                     gdn_chunk_fwd_split_workspace)
+    B, H, T, d = LONG["B"], LONG["H"], LONG["T"], LONG["d"]
+    x = inputs.make_fwd_inputs(B, H, T, d, "bf16", seed=LONG["seed"], init_state=True)
+    xd = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
+    o = torch.empty_like(xd["v"])
+    sT = torch.empty_like(xd["s0"])
+    need = gdn_chunk_fwd_split_workspace(B, H, T, d, d, 64, torch.bfloat16)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    args = (xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"], 64)
+    runs = {
+        "split": lambda: gdn_chunk_fwd_split(*args, o=o, final_state=sT, workspace=ws, stream=stream),
+        "plain": lambda: gdn_chunk_fwd(*args, o=o, final_state=sT, stream=stream),
+    }
+    alg = B * H * T * (3 * d * 2 + 8 + d * 2) + 2 * B * H * d * d * 4
+    res = {"workload": "long context: B=1, H=16, T=131072, d_k=d_v=128, C=64, bf16 q/k/v, "
+                       "fp32 gates, S0 ~ N(0,0.1)", "alg_bytes": alg, "split_workspace_bytes": need}
+    for name, f in runs.items():
+        f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        res[name + "_ms"] = ms
+        res[name + "_tokens_per_s"] = B * T / (ms * 1e-3)
+        res[name + "_hbm_frac"] = alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    return res
+
+
 def time_decode(torch, dev, steps_override=None):
     from gated_deltanet_sequence_amd import inputs
     from gated_deltanet_sequence_amd.binding import gdn_recurrent_step
@@ -266,6 +309,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context (sequence-split) report")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="one 512 MiB copy plus two launches, for rocprofv3 --pmc runs")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -338,6 +383,8 @@ def main():
     }
     if not args.no_decode:
         res["decode"] = time_decode(torch, dev)
+    if not args.no_long:
+        res["long_context"] = time_long(torch, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"], res["parity"] = cpu_baseline(x, o, sT)
     print(json.dumps(res), flush=True)
