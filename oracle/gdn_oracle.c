@@ -143,3 +143,59 @@ int gdn_oracle_step(const float* q, const float* k, const float* v,
     }
     return failed ? 2 : 0;
 }
+
+/*
+ * Gated linear attention without the delta rule ([P3] §2.3: the state decays
+ * by a gate and gains the outer product of the token's key and value, with no
+ * erase term).  In the orientation used above (S is d_v x d_k, row i = value
+ * index):  S_t = alpha_t S_{t-1} + beta_t v_t k_t^T,  o_t = S_t q_t,  token by
+ * token in fp64:
+ *     S <- alpha_t * S
+ *     S <- S + beta_t v_t k_t^T
+ *     o_t <- S q_t
+ * Same layouts and return codes as gdn_oracle_fwd.
+ */
+int gla_oracle_fwd(const float* q, const float* k, const float* v,
+                   const float* alpha, const float* beta, const float* s0,
+                   double* o, double* sT, int64_t B, int64_t H, int64_t T,
+                   int64_t dk, int64_t dv) {
+    if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return 1;
+    if (!o && T > 0) return 1;
+    const int64_t chains = B * H;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < chains; ++c) {
+        double* S = (double*)malloc(sizeof(double) * (size_t)(dv * dk));
+        if (!S) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        if (s0) {
+            const float* s = s0 + c * dv * dk;
+            for (int64_t e = 0; e < dv * dk; ++e) S[e] = (double)s[e];
+        } else {
+            memset(S, 0, sizeof(double) * (size_t)(dv * dk));
+        }
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t tok = c * T + t;
+            const float* qt = q + tok * dk;
+            const float* kt = k + tok * dk;
+            const double a = (double)alpha[tok], b = (double)beta[tok];
+            for (int64_t i = 0; i < dv; ++i) {
+                double* row = S + i * dk;
+                const double w = b * (double)v[tok * dv + i];
+                double acc = 0.0;
+                for (int64_t j = 0; j < dk; ++j) {
+                    row[j] = a * row[j] + w * (double)kt[j];
+                    acc += row[j] * (double)qt[j];
+                }
+                o[tok * dv + i] = acc;
+            }
+        }
+        if (sT) memcpy(sT + c * dv * dk, S, sizeof(double) * (size_t)(dv * dk));
+        free(S);
+    }
+    return failed ? 2 : 0;
+}
+
