@@ -6,7 +6,7 @@ d_k=d_v=128, C=64, bf16 q/k/v, fp32 gates, zero initial state, fp32 final
 state), inputs resident in HBM before the timed region.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--no-decode] [--no-long] [--pmc-pass]
+                  [--no-decode] [--no-long] [--no-gla] [--pmc-pass]
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   (writes the HBM-traffic
                   summary under profiles/ from two rocprofv3 --pmc runs)
 
@@ -182,6 +182,35 @@ def time_long(torch, dev, launches=10):
     return res
 
 
+def time_gla(torch, xd, launches=50):
+    """Gated linear attention without the delta rule (gla_chunk_fwd) on the
+    main workload's inputs: mean launch time over `launches` back-to-back
+    launches between two events, and its HBM-roofline fraction (same
+    algorithmic bytes as the main path)."""
+    from gated_deltanet_sequence_amd.binding import gla_chunk_fwd
+    B, H, T, d = xd["q"].shape
+    o = torch.empty_like(xd["v"])
+    sT = torch.empty((B, H, d, d), dtype=torch.float32, device=xd["q"].device)
+    stream = torch.cuda.current_stream()
+    f = lambda: gla_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None, 64,
+                              o=o, final_state=sT, stream=stream)
+    for _ in range(5):
+        f()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(launches):
+        f()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    alg = alg_bytes_main(B, H, T, d)
+    return {"workload": "gated linear attention (no delta rule) on the main workload's inputs",
+            "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def time_decode(torch, dev, steps_override=None):
     from gated_deltanet_sequence_amd import inputs
     from gated_deltanet_sequence_amd.binding import gdn_recurrent_step
@@ -311,6 +340,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the long-context (sequence-split) report")
+    ap.add_argument("--no-gla", action="store_true",
+                    help="skip the gated-linear-attention report")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="one 512 MiB copy plus two launches, for rocprofv3 --pmc runs")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -385,6 +416,8 @@ def main():
         res["decode"] = time_decode(torch, dev)
     if not args.no_long:
         res["long_context"] = time_long(torch, dev)
+    if not args.no_gla:
+        res["gla"] = time_gla(torch, xd)
     if not args.no_cpu_baseline:
         res["cpu_baseline"], res["parity"] = cpu_baseline(x, o, sT)
     print(json.dumps(res), flush=True)

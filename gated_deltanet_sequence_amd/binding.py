@@ -49,6 +49,8 @@ def load_library(path: str | None = None):
     i32 = ctypes.c_int
     lib.gdn_chunk_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32, p]
     lib.gdn_chunk_fwd.restype = i32
+    lib.gla_chunk_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32, p]
+    lib.gla_chunk_fwd.restype = i32
     lib.gdn_chunk_fwd_split.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
                                         p, ctypes.c_size_t, p]
     lib.gdn_chunk_fwd_split.restype = i32
@@ -130,6 +132,26 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 64
                            int(chunk_size), _DTYPES[q.dtype], _stream_ptr(stream, q.device))
     if rc != GDN_OK:
         raise GDNError(rc, "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gla_chunk_fwd(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 64, *,
+                  o=None, final_state=None, output_final_state: bool = True, stream=None):
+    """Gated linear attention without the delta rule,
+    S_t = alpha_t S_{t-1} + beta_t v_t k_t^T, o_t = S_t q_t (bf16 q/k/v).
+    Same arguments and result as gdn_chunk_fwd."""
+    B, H, T, dk, dv = _check_fwd_args(q, k, v, alpha, beta, initial_state)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    rc = load_library().gla_chunk_fwd(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                      _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                                      _dev_ptr(initial_state, "initial_state"), _dev_ptr(o, "o"),
+                                      _dev_ptr(final_state, "final_state"), B, H, T, dk, dv,
+                                      int(chunk_size), _DTYPES[q.dtype], _stream_ptr(stream, q.device))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gla_chunk_fwd")
     return o, final_state
 
 

@@ -340,7 +340,7 @@ __device__ __forceinline__ void read_p(const Smem& sm, const StateAddr& A, int64
     for (int pp = 0; pp <= rb / 2; ++pp) pf[rb][pp] = as_op(ld3<uint4>(pb[pp], rb * 2048));
 }
 
-template <bool FINISH, bool CHAIN>
+template <bool FINISH, bool CHAIN, bool GLA>
 __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, const StateAddr& A,
                                              StateRegs& R, int64_t c, int DV, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
@@ -395,7 +395,8 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     for (int h = 0; h < 4; ++h) {
       if (rb == 1) vv[h] = tr3(v_b, h * 16 * DVS * 2);
       if (rb == 2) b4[h] = *reinterpret_cast<const float4*>(gt + G_BETA * C + 16 * h + 4 * lg);
-      if (rb == 3) g4[h] = *reinterpret_cast<const float4*>(gt + G_EG * C + 16 * h + 4 * lg);
+      if (rb == 3) g4[h] = GLA ? make_float4(0.f, 0.f, 0.f, 0.f)
+                               : *reinterpret_cast<const float4*>(gt + G_EG * C + 16 * h + 4 * lg);
     }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 az = zero4();
@@ -896,6 +897,11 @@ __host__ __device__ inline int map_chains(const ChainMap& m) {
   return m.mode == MAP_SEQ ? m.nseq : m.mode == MAP_SPLIT_A ? 2 * m.nseq * (m.G - 1) : m.nseq * m.G;
 }
 
+// GLA: gated linear attention without the delta rule ([P3] §2.3),
+// S_t = alpha_t S_{t-1} + beta_t v_t k_t^T.  Its chunk form is the one above
+// with L = 0 (so Ti = I) and Y = diag(beta) V: the L wave stays idle, L is
+// zero from the start, and the state waves drop the K S^T term of Y.
+template <bool GLA>
 __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -980,6 +986,12 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     for (int e = tid; e < 2 * C * C / 2; e += 64 * NWAVES) z[e] = 0u;
     uint32_t* z2 = reinterpret_cast<uint32_t*>(&sm.Tt[0][0]);
     for (int e = tid; e < 2 * C * TTS / 2; e += 64 * NWAVES) z2[e] = 0u;
+    if (GLA) {
+      uint32_t* z3 = reinterpret_cast<uint32_t*>(&sm.Ld[0][0][0]);
+      for (int e = tid; e < (int)(sizeof(sm.Ld) / 4); e += 64 * NWAVES) z3[e] = 0u;
+      uint32_t* z4 = reinterpret_cast<uint32_t*>(&sm.Lo[0][0][0]);
+      for (int e = tid; e < (int)(sizeof(sm.Lo) / 4); e += 64 * NWAVES) z4[e] = 0u;
+    }
   }
 
   // The empty slot only helps to zero P and Ti^T.  Its stores are complete
@@ -1013,13 +1025,13 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     lds_barrier();
     lds_barrier();
     if (nch > 0) {
-      state_period<false, true>(sm, sq, A, R, 0, DV, lane);
+      state_period<false, true, GLA>(sm, sq, A, R, 0, DV, lane);
       lds_barrier();
       for (int64_t p = 1; p < nch; ++p) {
-        state_period<true, true>(sm, sq, A, R, p, DV, lane);
+        state_period<true, true, GLA>(sm, sq, A, R, p, DV, lane);
         lds_barrier();
       }
-      state_period<true, false>(sm, sq, A, R, nch, DV, lane);
+      state_period<true, false, GLA>(sm, sq, A, R, nch, DV, lane);
     }
     lds_barrier();
     if (sT) {
@@ -1037,11 +1049,11 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     }
   } else if (wave == W_L) {
     FragRegs R;
-    if (nch > 0) load_frags(R, sq, 0, lane);
+    if (!GLA && nch > 0) load_frags(R, sq, 0, lane);
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
-      if (p + 2 < nch) build_l(sm, R, p + 2, lane);
-      if (p + 3 < nch) load_frags(R, sq, p + 3, lane);
+      if (!GLA && p + 2 < nch) build_l(sm, R, p + 2, lane);
+      if (!GLA && p + 3 < nch) load_frags(R, sq, p + 3, lane);
       lds_barrier();
     }
   } else if (wave == W_LOADER) {

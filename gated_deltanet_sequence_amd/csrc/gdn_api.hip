@@ -42,6 +42,7 @@ int launch_chunk(const void* q, const void* k, const void* v, const float* alpha
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+template <bool GLA = false>
 int launch_chunk_pipe(const void* q, const void* k, const void* v, const float* alpha,
                       const float* beta, const float* s0, void* o, float* sT,
                       const gdn::pipe::ChainMap& cm, int64_t dk, int64_t dv, hipStream_t stream) {
@@ -51,7 +52,7 @@ int launch_chunk_pipe(const void* q, const void* k, const void* v, const float* 
   // one sequence's q, k or v must fit a 32-bit buffer range
   if (cm.T * dk * 2 > 0x7fffffff || cm.T * dv * 2 > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
   const int xcd_map = (nchain % 8) == 0;
-  hipLaunchKernelGGL(gdn::pipe::chunk_fwd_pipe_kernel, dim3((unsigned)nblocks), dim3(64 * gdn::pipe::NWAVES), 0,
+  hipLaunchKernelGGL(gdn::pipe::chunk_fwd_pipe_kernel<GLA>, dim3((unsigned)nblocks), dim3(64 * gdn::pipe::NWAVES), 0,
                      stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
                      static_cast<const bf16_t*>(v), alpha, beta, s0, static_cast<bf16_t*>(o), sT, cm,
                      (int)dv, (int)dk, xcd_map);
@@ -177,6 +178,21 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
                              dk, dv, stream);
   return launch_chunk<float, 64, 16, 64, 4>(q, k, v, alpha, beta, initial_state, o, final_state,
                                             nchain, T, dv, stream);
+}
+
+int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                  const float* beta, const float* initial_state, void* o, float* final_state,
+                  int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk_size,
+                  gdn_dtype dtype, void* hip_stream) {
+  const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
+                           chunk_size, dtype);
+  if (rc != GDN_OK) return rc;
+  if (dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  const int64_t nchain = B * H;
+  if (nchain == 0) return GDN_OK;
+  if (T == 0 && !final_state) return GDN_OK;
+  return launch_chunk_pipe<true>(q, k, v, alpha, beta, initial_state, o, final_state,
+                                 seq_map(nchain, T), dk, dv, static_cast<hipStream_t>(hip_stream));
 }
 
 size_t gdn_chunk_fwd_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,

@@ -92,6 +92,23 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v,
                   int64_t chunk_size, gdn_dtype dtype, void* hip_stream);
 
 /*
+ * gla_chunk_fwd — chunked forward pass of gated linear attention without the
+ * delta rule ([P3] §2.3: the state decays by a gate and gains the key-value
+ * outer product, with no erase term; [P3] §2.1 inclusive output):
+ *
+ *     S_t = alpha_t S_{t-1} + beta_t v_t k_t^T,      o_t = S_t q_t,
+ *
+ * with the same state orientation (S is d_v x d_k) as gdn_chunk_fwd.  Same
+ * arguments, layouts, chunk size, aliasing and error codes as gdn_chunk_fwd;
+ * bf16 only (GDN_ERR_UNSUPPORTED for fp32).
+ */
+int gla_chunk_fwd(const void* q, const void* k, const void* v,
+                  const float* alpha, const float* beta,
+                  const float* initial_state, void* o, float* final_state,
+                  int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                  int64_t chunk_size, gdn_dtype dtype, void* hip_stream);
+
+/*
  * gdn_chunk_fwd_split — the same result as gdn_chunk_fwd, for workloads with
  * few sequences (B*H small against the number of CUs), by splitting every
  * sequence into G segments that run in parallel ([P1] §3.3 splitting a long
