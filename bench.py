@@ -6,7 +6,7 @@ d_k=d_v=128, C=64, bf16 q/k/v, fp32 gates, zero initial state, fp32 final
 state), inputs resident in HBM before the timed region.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--no-decode] [--no-long] [--no-gla] [--pmc-pass]
+                  [--no-decode] [--no-long] [--no-gla] [--no-routes] [--pmc-pass]
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   (writes the HBM-traffic
                   summary under profiles/ from two rocprofv3 --pmc runs)
 
@@ -211,6 +211,54 @@ def time_gla(torch, xd, launches=50):
             "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+ROUTES = dict(B=1, H=8, T=16384, d=64, seed=6)
+
+
+def time_routes(torch, dev, launches=5):
+    """The pages' route comparison shape (d=64, 8 heads, 16384 tokens, batch
+    1, bf16): the chunked pass, the blocked parallel-scan route, and the
+    per-token route (one decode-step launch per token).  Mean times."""
+    from gated_deltanet_sequence_amd import inputs
+    from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd, gdn_recurrent_step, gdn_scan_fwd,
+                                                     gdn_scan_fwd_workspace)
+    B, H, T, d = ROUTES["B"], ROUTES["H"], ROUTES["T"], ROUTES["d"]
+    x = inputs.make_fwd_inputs(B, H, T, d, "bf16", seed=ROUTES["seed"])
+    xd = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
+    ws = torch.empty(gdn_scan_fwd_workspace(B, H, T, d, d, torch.bfloat16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    a = (xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None)
+    res = {"workload": "route comparison: B=1, H=8, T=16384, d_k=d_v=64, bf16 q/k/v, fp32 gates, zero S0"}
+    for name, f in (("chunked", lambda: gdn_chunk_fwd(*a, 64, stream=stream)),
+                    ("scan", lambda: gdn_scan_fwd(*a, workspace=ws, stream=stream))):
+        f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name + "_ms"] = e0.elapsed_time(e1) / launches
+    # per-token route: T launches of the decode step over the B*H heads
+    n = B * H
+    cols = {nm: [xd[nm][:, :, t].reshape(n, 1, -1).contiguous() for t in range(T)] for nm in ("q", "k", "v")}
+    gates = {nm: [xd[nm][:, :, t].reshape(n, 1).contiguous() for t in range(T)] for nm in ("alpha", "beta")}
+    state = torch.zeros(n, 1, d, d, dtype=torch.float32, device=dev)
+    outs = torch.empty(T, n, 1, d, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in range(T):
+        gdn_recurrent_step(cols["q"][t], cols["k"][t], cols["v"][t], gates["alpha"][t], gates["beta"][t],
+                           state, o=outs[t], stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    res["token_loop_ms"] = e0.elapsed_time(e1)
+    return res
+
+
 def time_decode(torch, dev, steps_override=None):
     from gated_deltanet_sequence_amd import inputs
     from gated_deltanet_sequence_amd.binding import gdn_recurrent_step
@@ -342,6 +390,8 @@ def main():
                     help="skip the long-context (sequence-split) report")
     ap.add_argument("--no-gla", action="store_true",
                     help="skip the gated-linear-attention report")
+    ap.add_argument("--no-routes", action="store_true",
+                    help="skip the chunked / scan / per-token route comparison")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="one 512 MiB copy plus two launches, for rocprofv3 --pmc runs")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -418,6 +468,8 @@ def main():
         res["long_context"] = time_long(torch, dev)
     if not args.no_gla:
         res["gla"] = time_gla(torch, xd)
+    if not args.no_routes:
+        res["routes"] = time_routes(torch, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"], res["parity"] = cpu_baseline(x, o, sT)
     print(json.dumps(res), flush=True)

@@ -51,6 +51,11 @@ def load_library(path: str | None = None):
     lib.gdn_chunk_fwd.restype = i32
     lib.gla_chunk_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32, p]
     lib.gla_chunk_fwd.restype = i32
+    lib.gdn_scan_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i32,
+                                 p, ctypes.c_size_t, p]
+    lib.gdn_scan_fwd.restype = i32
+    lib.gdn_scan_fwd_workspace.argtypes = [i64, i64, i64, i64, i64, i32]
+    lib.gdn_scan_fwd_workspace.restype = ctypes.c_size_t
     lib.gdn_chunk_fwd_split.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
                                         p, ctypes.c_size_t, p]
     lib.gdn_chunk_fwd_split.restype = i32
@@ -152,6 +157,37 @@ def gla_chunk_fwd(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 64
                                       int(chunk_size), _DTYPES[q.dtype], _stream_ptr(stream, q.device))
     if rc != GDN_OK:
         raise GDNError(rc, "gla_chunk_fwd")
+    return o, final_state
+
+
+def gdn_scan_fwd_workspace(B, H, T, dk, dv, dtype=torch.bfloat16) -> int:
+    """Bytes of workspace gdn_scan_fwd needs."""
+    return int(load_library().gdn_scan_fwd_workspace(B, H, T, dk, dv, _DTYPES[dtype]))
+
+
+def gdn_scan_fwd(q, k, v, alpha, beta, initial_state=None, *, o=None, final_state=None,
+                 output_final_state: bool = True, workspace=None, stream=None):
+    """The same recurrence by the blocked parallel-scan route (fp32 state;
+    bf16 or fp32 q/k/v; d 64 or 128).  Same arguments and result as
+    gdn_chunk_fwd without the chunk size; the workspace (uint8 GPU tensor) is
+    allocated here when not given."""
+    B, H, T, dk, dv = _check_fwd_args(q, k, v, alpha, beta, initial_state)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    need = gdn_scan_fwd_workspace(B, H, T, dk, dv, q.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().gdn_scan_fwd(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                     _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                                     _dev_ptr(initial_state, "initial_state"), _dev_ptr(o, "o"),
+                                     _dev_ptr(final_state, "final_state"), B, H, T, dk, dv,
+                                     _DTYPES[q.dtype], _dev_ptr(workspace, "workspace"), ws_bytes,
+                                     _stream_ptr(stream, q.device))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_scan_fwd")
     return o, final_state
 
 

@@ -9,6 +9,7 @@
 #include "chunk_fwd_pipe.hpp"
 #include "recurrent_step.hpp"
 #include "split_combine.hpp"
+#include "scan_route.hpp"
 
 namespace {
 
@@ -98,6 +99,48 @@ void split_plan(int64_t nseq, int64_t T, int64_t dv, int& G, int64_t& L) {
   }
 }
 
+// Blocks of the scan route: L tokens (a multiple of the staging tile), about
+// sqrt(32 T), which balances the per-block token loops (length L) against
+// the sequential chain of block maps (length T / L).
+void scan_plan(int64_t T, int& G, int64_t& L) {
+  const int64_t tile = gdn::scan::TILE;
+  int64_t l = 1;
+  while (l * l < 32 * T) l *= 2;
+  L = (l + tile - 1) / tile * tile;
+  G = T > 0 ? (int)((T + L - 1) / L) : 1;
+}
+size_t scan_ws_bytes(int64_t nseq, int G, int64_t d) {
+  return (size_t)(2 * nseq * (G - 1) + nseq * G) * (size_t)(d * d) * sizeof(float);
+}
+
+template <class E, int D>
+int launch_scan(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                const float* s0, void* o, float* sT, int64_t nseq, int64_t T, float* ws, hipStream_t stream) {
+  int G;
+  int64_t L;
+  scan_plan(T, G, L);
+  using namespace gdn::scan;
+  const E* qq = static_cast<const E*>(q);
+  const E* kk = static_cast<const E*>(k);
+  const E* vv = static_cast<const E*>(v);
+  E* oo = static_cast<E*>(o);
+  if (G > 1) {
+    const int64_t nb = scan_blocks(SCAN_AGG, (int)nseq, G, D);
+    if (nb > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((scan_tokens_kernel<E, D>), dim3((unsigned)nb), dim3(THREADS), 0, stream, qq, kk,
+                       vv, alpha, beta, oo, sT, (int)SCAN_AGG, (int)nseq, G, T, L, ws);
+    if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
+  }
+  hipLaunchKernelGGL(gdn::split::split_combine_kernel, dim3((unsigned)(nseq * (D / gdn::split::ROWS))),
+                     dim3(gdn::split::THREADS), 0, stream, s0, ws, (int)nseq, G, D);
+  if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
+  const int64_t nb = scan_blocks(SCAN_OUT, (int)nseq, G, D);
+  if (nb > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((scan_tokens_kernel<E, D>), dim3((unsigned)nb), dim3(THREADS), 0, stream, qq, kk, vv,
+                     alpha, beta, oo, sT, (int)SCAN_OUT, (int)nseq, G, T, L, ws);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 size_t split_ws_bytes(int64_t nseq, int G, int64_t d) {
   return G < 2 ? 0 : (size_t)(2 * nseq * (G - 1) + nseq * G) * (size_t)(d * d) * sizeof(float);
 }
@@ -133,16 +176,18 @@ const char* gdn_version(void) { return "0.1.0"; }
 
 namespace {
 // Argument checks shared by the forward entry points: GDN_OK, or the error.
+// f32_any_width: fp32 inputs may have d = 128 too (the scan route).
 int check_fwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
               const float* initial_state, void* o, float* final_state, int64_t B, int64_t H,
-              int64_t T, int64_t dk, int64_t dv, int64_t chunk_size, gdn_dtype dtype) {
+              int64_t T, int64_t dk, int64_t dv, int64_t chunk_size, gdn_dtype dtype,
+              bool f32_any_width = false) {
   if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0 || chunk_size <= 0) return GDN_ERR_INVALID_ARG;
   if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
   const int64_t nchain = B * H;
   const bool has_tokens = nchain > 0 && T > 0;
   if (has_tokens && (!q || !k || !v || !alpha || !beta || !o)) return GDN_ERR_INVALID_ARG;
   if (dk != dv || (dk != 64 && dk != 128) || chunk_size != 64) return GDN_ERR_UNSUPPORTED;
-  if (dtype == GDN_F32 && dk != 64) return GDN_ERR_UNSUPPORTED;
+  if (dtype == GDN_F32 && dk != 64 && !f32_any_width) return GDN_ERR_UNSUPPORTED;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(alpha) || misaligned(beta) ||
       misaligned(initial_state) || misaligned(o) || misaligned(final_state))
     return GDN_ERR_ALIGNMENT;
@@ -193,6 +238,52 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
   if (T == 0 && !final_state) return GDN_OK;
   return launch_chunk_pipe<true>(q, k, v, alpha, beta, initial_state, o, final_state,
                                  seq_map(nchain, T), dk, dv, static_cast<hipStream_t>(hip_stream));
+}
+
+size_t gdn_scan_fwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                              gdn_dtype dtype) {
+  if (B <= 0 || H <= 0 || T < 0 || dk != dv || (dk != 64 && dk != 128) ||
+      (dtype != GDN_F32 && dtype != GDN_BF16))
+    return 0;
+  int G;
+  int64_t L;
+  scan_plan(T, G, L);
+  return scan_ws_bytes(B * H, G, dk);
+}
+
+int gdn_scan_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                 const float* beta, const float* initial_state, void* o, float* final_state,
+                 int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, gdn_dtype dtype,
+                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
+                           64, dtype, true);
+  if (rc != GDN_OK) return rc;
+  const int64_t nseq = B * H;
+  if (nseq == 0) return GDN_OK;
+  if (T == 0 && !final_state) return GDN_OK;
+  int G;
+  int64_t L;
+  scan_plan(T, G, L);
+  const size_t need = scan_ws_bytes(nseq, G, dk);
+  if (!workspace || workspace_bytes < need) return GDN_ERR_INVALID_ARG;
+  if (misaligned(workspace)) return GDN_ERR_ALIGNMENT;
+  {
+    const int64_t esz = dtype == GDN_BF16 ? 2 : 4;
+    const Range rw{workspace, (int64_t)need};
+    const Range others[] = {{q, nseq * T * dk * esz}, {k, nseq * T * dk * esz},
+                            {v, nseq * T * dv * esz}, {o, nseq * T * dv * esz},
+                            {alpha, nseq * T * 4},    {beta, nseq * T * 4},
+                            {initial_state, nseq * dv * dk * 4}, {final_state, nseq * dv * dk * 4}};
+    for (const Range& r : others)
+      if (overlaps(rw, r)) return GDN_ERR_INVALID_ARG;
+  }
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  float* ws = static_cast<float*>(workspace);
+  if (dtype == GDN_BF16)
+    return dk == 128 ? launch_scan<bf16_t, 128>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, ws, stream)
+                     : launch_scan<bf16_t, 64>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, ws, stream);
+  return dk == 128 ? launch_scan<float, 128>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, ws, stream)
+                   : launch_scan<float, 64>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, ws, stream);
 }
 
 size_t gdn_chunk_fwd_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,

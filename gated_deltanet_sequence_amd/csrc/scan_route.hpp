@@ -1,0 +1,162 @@
+// Parallel-scan route of the gated delta rule on gfx950 (the pages' other
+// route besides the chunked one, kept for the route comparison).
+//
+// Sources (web pages, by title and section):
+//   [P1] "Gated DeltaNet GPU并行实现：拆解线性注意力循环的两种高效方案"
+//        §2.3 each token is an affine map of the state and maps compose
+//        associatively; §3.1 evaluate the recurrence as a parallel scan over
+//        those maps; §3.4 / §5.1 the scan and chunked routes compared.
+//
+// The token map is S -> S A_t + B_t with A_t = alpha_t (I - beta_t k_t k_t^T)
+// and B_t = beta_t v_t k_t^T.  The scan is blocked: every block of L tokens
+// of a sequence is reduced to its map (A_blk, B_blk), the blocks' start
+// states follow from the exclusive scan over those maps
+// (start_{g+1} = start_g A_g + B_g, split_combine_kernel), and every block
+// then replays its tokens from its start state to write the outputs.
+//   AGG: blocks 0 .. G-2, kind 0: B_blk (zero start, with V), kind 1: A_blk
+//        (identity start, V read as zero); written to ws slots tilde, trans.
+//   OUT: blocks 0 .. G-1 from ws slot start, output o; the last block's
+//        state is the final state.
+// Reducing a block to its map is the token loop itself on the stacked state
+// [B; A] (a rank-1 update per token, O(d^2) instead of a d^3 product).
+//
+// Layout: a workgroup owns 16 rows of one state; 16 consecutive lanes hold a
+// row (D / 16 columns each), and row dot products are summed across those
+// lanes with DPP rotations.  Tokens are staged 32 at a time in LDS.
+#pragma once
+
+#include "gdn_common.hpp"
+
+namespace gdn {
+namespace scan {
+
+enum { SCAN_AGG = 0, SCAN_OUT = 1 };
+constexpr int TPR = 16;              // threads per state row
+constexpr int THREADS = 256;
+constexpr int RPW = THREADS / TPR;   // rows per workgroup
+constexpr int TILE = 32;             // tokens per LDS tile
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));  // row_ror:8
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xf, 0xf, false));  // row_ror:4
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4e, 0xf, 0xf, false));   // quad [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, false));   // quad [1,0,3,2]
+  return v;
+}
+
+// Workgroups per launch.
+__host__ __device__ inline int64_t scan_blocks(int mode, int nseq, int G, int D) {
+  const int64_t per = mode == SCAN_AGG ? 2 * (int64_t)(G - 1) : (int64_t)G;
+  return (int64_t)nseq * per * (D / RPW);
+}
+
+template <class E, int D>
+__global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, E* __restrict__ o,
+    float* __restrict__ final_state, int mode, int nseq, int G, int64_t T, int64_t L,
+    float* __restrict__ ws) {
+  constexpr int CPT = D / TPR;  // columns per thread
+  __shared__ float ks[TILE][D], qs[TILE][D];
+  __shared__ float vs[TILE][RPW], os[TILE][RPW];
+  __shared__ float as_[TILE], bs_[TILE];
+
+  int64_t b = blockIdx.x;
+  const int rg = (int)(b % (D / RPW));
+  b /= D / RPW;
+  int seq, g, kind;
+  if (mode == SCAN_AGG) {
+    kind = (int)(b % 2);
+    b /= 2;
+    g = (int)(b % (G - 1));
+    seq = (int)(b / (G - 1));
+  } else {
+    kind = 2;
+    g = (int)(b % G);
+    seq = (int)(b / G);
+  }
+  if (seq >= nseq) return;
+  const int tid = threadIdx.x, rl = tid / TPR, x = tid % TPR;
+  const int row = rg * RPW + rl;
+  const int c0 = x * CPT;
+  const int64_t t0 = (int64_t)g * L;
+  const int64_t len = (mode == SCAN_OUT && g == G - 1) ? T - t0 : L;
+  const int64_t dd = (int64_t)D * D, per = (int64_t)nseq * (G - 1);
+  const int64_t base = (int64_t)seq * T + t0;  // first token in memory
+
+  float s[CPT];
+  if (kind == 0) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) s[j] = 0.f;
+  } else if (kind == 1) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) s[j] = row == c0 + j ? 1.f : 0.f;
+  } else {
+    const float* st = ws + (2 * per + (int64_t)seq * G + g) * dd + (int64_t)row * D + c0;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) s[j] = st[j];
+  }
+
+  for (int64_t tt = 0; tt < len; tt += TILE) {
+    const int n = (int)(len - tt < TILE ? len - tt : TILE);
+    // stage the tile: keys, queries, this workgroup's value rows, gates
+    for (int e = tid; e < TILE * D; e += THREADS) {
+      const int t = e / D, c = e % D;
+      const bool in = t < n;
+      ks[t][c] = in ? Elem<E>::to_f32(k[(base + tt + t) * D + c]) : 0.f;
+      qs[t][c] = in ? Elem<E>::to_f32(q[(base + tt + t) * D + c]) : 0.f;
+    }
+    for (int e = tid; e < TILE * RPW; e += THREADS) {
+      const int t = e / RPW, r = e % RPW;
+      vs[t][r] = (t < n && kind != 1) ? Elem<E>::to_f32(v[(base + tt + t) * D + rg * RPW + r]) : 0.f;
+    }
+    if (tid < TILE) {
+      as_[tid] = tid < n ? alpha[base + tt + tid] : 1.f;
+      bs_[tid] = tid < n ? beta[base + tt + tid] : 0.f;
+    }
+    __syncthreads();
+    for (int t = 0; t < n; ++t) {
+      const float a = as_[t], bt = bs_[t];
+      float kr[CPT];
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) kr[j] = ks[t][c0 + j];
+      // S <- alpha S;  r = S k;  u = beta (v - r);  S <- S + u k^T
+      float r = 0.f;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        s[j] *= a;
+        r = fmaf(s[j], kr[j], r);
+      }
+      r = row16_sum(r);
+      const float u = bt * (vs[t][rl] - r);
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) s[j] = fmaf(u, kr[j], s[j]);
+      if (mode == SCAN_OUT) {
+        float oq = 0.f;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) oq = fmaf(s[j], qs[t][c0 + j], oq);
+        oq = row16_sum(oq);
+        if (x == 0) os[t][rl] = oq;
+      }
+    }
+    __syncthreads();
+    if (mode == SCAN_OUT) {
+      for (int e = tid; e < n * RPW; e += THREADS) {
+        const int t = e / RPW, r = e % RPW;
+        o[(base + tt + t) * D + rg * RPW + r] = Elem<E>::from_f32(os[t][r]);
+      }
+    }
+  }
+
+  float* dst = nullptr;
+  if (mode == SCAN_AGG) dst = ws + ((int64_t)kind * per + (int64_t)seq * (G - 1) + g) * dd;
+  else if (g == G - 1 && final_state) dst = final_state + (int64_t)seq * dd;
+  if (dst) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) dst[(int64_t)row * D + c0 + j] = s[j];
+  }
+}
+
+}  // namespace scan
+}  // namespace gdn

@@ -109,6 +109,34 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v,
                   int64_t chunk_size, gdn_dtype dtype, void* hip_stream);
 
 /*
+ * gdn_scan_fwd — the same recurrence as gdn_chunk_fwd by the other route of
+ * [P1]: a (blocked) parallel scan over the per-token affine maps
+ * S -> S A_t + B_t, A_t = alpha_t (I - beta_t k_t k_t^T), B_t = beta_t v_t k_t^T
+ * ([P1] §2.3 maps compose associatively, §3.1 scan route, §3.4/§5.1 the
+ * routes compared).  Each block of L tokens is reduced to its map by a
+ * per-token loop, the block start states follow from the maps in order, and
+ * every block replays its tokens from its start state.  fp32 state and
+ * arithmetic; bf16 or fp32 q/k/v; d 64 or 128 for both dtypes.
+ *
+ *   workspace   caller-owned device memory of at least
+ *               gdn_scan_fwd_workspace(...) bytes (never 0 for B*H > 0),
+ *               16-byte aligned, overlapping no other argument.  Calls that
+ *               share a workspace must not overlap in time.
+ * Other arguments, layouts, aliasing and errors as for gdn_chunk_fwd (no
+ * chunk size); a missing or too small workspace returns GDN_ERR_INVALID_ARG.
+ */
+int gdn_scan_fwd(const void* q, const void* k, const void* v,
+                 const float* alpha, const float* beta,
+                 const float* initial_state, void* o, float* final_state,
+                 int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                 gdn_dtype dtype, void* workspace, size_t workspace_bytes,
+                 void* hip_stream);
+
+/* Workspace bytes gdn_scan_fwd needs for these sizes.  Host-only. */
+size_t gdn_scan_fwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                              gdn_dtype dtype);
+
+/*
  * gdn_chunk_fwd_split — the same result as gdn_chunk_fwd, for workloads with
  * few sequences (B*H small against the number of CUs), by splitting every
  * sequence into G segments that run in parallel ([P1] §3.3 splitting a long

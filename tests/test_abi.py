@@ -123,3 +123,21 @@ def test_split_workspace_query_is_host_only(lib):
     assert f(1, 16, 131072, 128, 128, 32, 1) == 0      # unsupported chunk size
     assert f(0, 16, 131072, 128, 128, 64, 1) == 0      # nothing to do
     assert f(1, 16, 131072, 128, 128, 64, 1) >= 0      # no GPU here: 0; on a GPU: > 0
+
+
+def test_scan_rejects_invalid_arguments_and_sizes_workspace(lib):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def scan(B=1, H=1, T=64, dk=64, dv=64, dtype=1, q=A, o=A + 256 * MB, ws=A + 512 * MB, wsb=0):
+        return lib.gdn_scan_fwd(P(q), P(A + 64 * MB), P(A + 128 * MB), P(A + 192 * MB),
+                                P(A + 200 * MB), None, P(o), None, B, H, T, dk, dv, dtype,
+                                P(ws), wsb, None)
+    assert scan(B=-1) == binding.GDN_ERR_INVALID_ARG
+    assert scan(dtype=9) == binding.GDN_ERR_INVALID_ARG
+    assert scan(dk=96, dv=96) == binding.GDN_ERR_UNSUPPORTED
+    assert scan(q=A + 4) == binding.GDN_ERR_ALIGNMENT
+    assert scan(o=A) == binding.GDN_ERR_INVALID_ARG
+    need = lib.gdn_scan_fwd_workspace(1, 1, 64, 64, 64, 1)
+    assert need == 64 * 64 * 4                        # one block: the start-state slot only
+    assert scan(wsb=need - 4) == binding.GDN_ERR_INVALID_ARG
+    assert lib.gdn_scan_fwd_workspace(1, 1, 64, 128, 128, 0) == 128 * 128 * 4   # fp32 d = 128
