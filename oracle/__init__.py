@@ -13,7 +13,8 @@ Sources (web pages, by title and section):
        §2.1 (delta-rule update), §2.2 (scalar gate), §1.3 / §5.3 (naive token
        loop as the correctness baseline).
   [P3] "线性注意力机制与Gated DeltaNet的优化实践", §2.1 (inclusive output),
-       §2.3 (gated linear attention without the delta rule: ``oracle_gla_fwd``).
+       §2.3 (gated linear attention without the delta rule: ``oracle_gla_fwd``);
+  [P1] §2.2 also allows a per-dimension gate: ``oracle_fwd_vecgate``.
 
 Pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle_pins.py``:
 composed affine maps vs. the loop (with a negative control), beta=0 pure decay,
@@ -58,6 +59,8 @@ def _bind(path):
     lib.gdn_oracle_step.restype = ctypes.c_int
     lib.gla_oracle_fwd.argtypes = [f, f, f, f, f, f, f, f, i64, i64, i64, i64, i64]
     lib.gla_oracle_fwd.restype = ctypes.c_int
+    lib.gdn_oracle_fwd_vecgate.argtypes = [f, f, f, f, f, f, f, f, i64, i64, i64, i64, i64]
+    lib.gdn_oracle_fwd_vecgate.restype = ctypes.c_int
     lib.gdn_oracle_num_threads.argtypes = []
     lib.gdn_oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -139,6 +142,29 @@ def oracle_gla_fwd(q, k, v, alpha, beta, s0=None, _lib_override=None):
                             _ptr(s0), _ptr(o), _ptr(sT), B, H, T, dk, dv)
     if rc != 0:
         raise RuntimeError("gla_oracle_fwd failed with code %d" % rc)
+    return o, sT
+
+
+def oracle_fwd_vecgate(q, k, v, alpha, beta, s0=None, _lib_override=None):
+    """The delta rule with a per-dimension gate alpha [B,H,T,dk] that decays
+    the key columns of the state ([P1] §2.2): S_t = S_{t-1} Diag(alpha_t)
+    (I - beta_t k_t k_t^T) + beta_t v_t k_t^T, o_t = S_t q_t, in fp64.
+    Returns (o, sT) like ``oracle_fwd``."""
+    lib = _lib_override if _lib_override is not None else _load()
+    q, k, v, alpha, beta = (_f32(x) for x in (q, k, v, alpha, beta))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == (B, H, T, dk) and v.shape == (B, H, T, dv)
+    assert alpha.shape == (B, H, T, dk) and beta.shape == (B, H, T)
+    if s0 is not None:
+        s0 = _f32(s0)
+        assert s0.shape == (B, H, dv, dk)
+    o = np.zeros((B, H, T, dv), dtype=np.float64)
+    sT = np.zeros((B, H, dv, dk), dtype=np.float64)
+    rc = lib.gdn_oracle_fwd_vecgate(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                    _ptr(s0), _ptr(o), _ptr(sT), B, H, T, dk, dv)
+    if rc != 0:
+        raise RuntimeError("gdn_oracle_fwd_vecgate failed with code %d" % rc)
     return o, sT
 
 

@@ -199,3 +199,64 @@ int gla_oracle_fwd(const float* q, const float* k, const float* v,
     return failed ? 2 : 0;
 }
 
+/*
+ * The delta rule with a per-dimension gate ([P1] §2.2: the gate may be a
+ * vector instead of a scalar).  Reading: alpha_t in (0,1]^{d_k} decays the
+ * key columns of the state (S is d_v x d_k), i.e.
+ *     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,
+ * token by token in fp64:
+ *     S[i][j] <- alpha_t[j] * S[i][j]
+ *     r <- S k_t;  u <- beta_t (v_t - r);  S <- S + u k_t^T;  o_t <- S q_t
+ * alpha is [B,H,T,dk]; everything else as in gdn_oracle_fwd.
+ */
+int gdn_oracle_fwd_vecgate(const float* q, const float* k, const float* v,
+                           const float* alpha, const float* beta, const float* s0,
+                           double* o, double* sT, int64_t B, int64_t H, int64_t T,
+                           int64_t dk, int64_t dv) {
+    if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return 1;
+    if (!o && T > 0) return 1;
+    const int64_t chains = B * H;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < chains; ++c) {
+        double* S = (double*)malloc(sizeof(double) * (size_t)(dv * dk));
+        if (!S) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        if (s0) {
+            const float* s = s0 + c * dv * dk;
+            for (int64_t e = 0; e < dv * dk; ++e) S[e] = (double)s[e];
+        } else {
+            memset(S, 0, sizeof(double) * (size_t)(dv * dk));
+        }
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t tok = c * T + t;
+            const float* qt = q + tok * dk;
+            const float* kt = k + tok * dk;
+            const float* at = alpha + tok * dk;
+            const double bt = (double)beta[tok];
+            for (int64_t i = 0; i < dv; ++i) {
+                double* row = S + i * dk;
+                double r = 0.0;
+                for (int64_t j = 0; j < dk; ++j) {
+                    row[j] *= (double)at[j];
+                    r += row[j] * (double)kt[j];
+                }
+                const double u = bt * ((double)v[tok * dv + i] - r);
+                double acc = 0.0;
+                for (int64_t j = 0; j < dk; ++j) {
+                    row[j] += u * (double)kt[j];
+                    acc += row[j] * (double)qt[j];
+                }
+                o[tok * dv + i] = acc;
+            }
+        }
+        if (sT) memcpy(sT + c * dv * dk, S, sizeof(double) * (size_t)(dv * dk));
+        free(S);
+    }
+    return failed ? 2 : 0;
+}
+
