@@ -104,9 +104,10 @@ def test_gla_and_delta_rule_differ_on_generic_keys():
 MUTATIONS = {
     "no_decay": ("row[j] = a * row[j] + w * (double)kt[j];", "row[j] = row[j] + w * (double)kt[j];"),
     "no_beta": ("const double w = b * (double)v[tok * dv + i];", "const double w = (double)v[tok * dv + i];"),
-    "key_for_query": ("acc += row[j] * (double)qt[j];", "acc += row[j] * (double)kt[j];"),
-    "output_before_update": ("acc += row[j] * (double)qt[j];",
-                             "acc += (row[j] - w * (double)kt[j]) * (double)qt[j];"),
+    "key_for_query": ("row[j] = a * row[j] + w * (double)kt[j];\n                    acc += row[j] * (double)qt[j];",
+                      "row[j] = a * row[j] + w * (double)kt[j];\n                    acc += row[j] * (double)kt[j];"),
+    "output_before_update": ("row[j] = a * row[j] + w * (double)kt[j];\n                    acc += row[j] * (double)qt[j];",
+                             "row[j] = a * row[j] + w * (double)kt[j];\n                    acc += (row[j] - w * (double)kt[j]) * (double)qt[j];"),
 }
 
 
