@@ -220,16 +220,20 @@ def time_routes(torch, dev, launches=5):
     per-token route (one decode-step launch per token).  Mean times."""
     from gated_deltanet_sequence_amd import inputs
     from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd, gdn_recurrent_step, gdn_scan_fwd,
-                                                     gdn_scan_fwd_workspace)
+                                                     gdn_scan_fwd_vecgate, gdn_scan_fwd_workspace)
     B, H, T, d = ROUTES["B"], ROUTES["H"], ROUTES["T"], ROUTES["d"]
     x = inputs.make_fwd_inputs(B, H, T, d, "bf16", seed=ROUTES["seed"])
     xd = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
     ws = torch.empty(gdn_scan_fwd_workspace(B, H, T, d, d, torch.bfloat16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     a = (xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None)
+    # the same gates repeated over the key dimension, for the per-dimension-gate route
+    av = xd["alpha"][..., None].expand(-1, -1, -1, d).contiguous()
     res = {"workload": "route comparison: B=1, H=8, T=16384, d_k=d_v=64, bf16 q/k/v, fp32 gates, zero S0"}
     for name, f in (("chunked", lambda: gdn_chunk_fwd(*a, 64, stream=stream)),
-                    ("scan", lambda: gdn_scan_fwd(*a, workspace=ws, stream=stream))):
+                    ("scan", lambda: gdn_scan_fwd(*a, workspace=ws, stream=stream)),
+                    ("scan_vecgate", lambda: gdn_scan_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"],
+                                                                  None, workspace=ws, stream=stream))):
         f()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)

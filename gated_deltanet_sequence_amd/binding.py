@@ -54,6 +54,8 @@ def load_library(path: str | None = None):
     lib.gdn_scan_fwd.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i32,
                                  p, ctypes.c_size_t, p]
     lib.gdn_scan_fwd.restype = i32
+    lib.gdn_scan_fwd_vecgate.argtypes = lib.gdn_scan_fwd.argtypes
+    lib.gdn_scan_fwd_vecgate.restype = i32
     lib.gdn_scan_fwd_workspace.argtypes = [i64, i64, i64, i64, i64, i32]
     lib.gdn_scan_fwd_workspace.restype = ctypes.c_size_t
     lib.gdn_chunk_fwd_split.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
@@ -98,7 +100,7 @@ def _stream_ptr(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _check_fwd_args(q, k, v, alpha, beta, initial_state):
+def _check_fwd_args(q, k, v, alpha, beta, initial_state, alpha_per_dim=False):
     if q.dtype not in _DTYPES:
         raise TypeError("q/k/v must be bfloat16 or float32")
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -107,9 +109,11 @@ def _check_fwd_args(q, k, v, alpha, beta, initial_state):
         raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
     B, H, T, dk = q.shape
     dv = v.shape[3]
-    for name, t in (("alpha", alpha), ("beta", beta)):
-        if t.dtype != torch.float32 or tuple(t.shape) != (B, H, T):
-            raise ValueError("%s must be fp32 [B,H,T]" % name)
+    ashape = (B, H, T, dk) if alpha_per_dim else (B, H, T)
+    if alpha.dtype != torch.float32 or tuple(alpha.shape) != ashape:
+        raise ValueError("alpha must be fp32 %s" % ("[B,H,T,dk]" if alpha_per_dim else "[B,H,T]"))
+    if beta.dtype != torch.float32 or tuple(beta.shape) != (B, H, T):
+        raise ValueError("beta must be fp32 [B,H,T]")
     if initial_state is not None and (initial_state.dtype != torch.float32 or
                                       tuple(initial_state.shape) != (B, H, dv, dk)):
         raise ValueError("initial_state must be fp32 [B,H,dv,dk]")
@@ -166,12 +170,12 @@ def gdn_scan_fwd_workspace(B, H, T, dk, dv, dtype=torch.bfloat16) -> int:
 
 
 def gdn_scan_fwd(q, k, v, alpha, beta, initial_state=None, *, o=None, final_state=None,
-                 output_final_state: bool = True, workspace=None, stream=None):
+                 output_final_state: bool = True, workspace=None, stream=None, _vecgate=False):
     """The same recurrence by the blocked parallel-scan route (fp32 state;
     bf16 or fp32 q/k/v; d 64 or 128).  Same arguments and result as
     gdn_chunk_fwd without the chunk size; the workspace (uint8 GPU tensor) is
     allocated here when not given."""
-    B, H, T, dk, dv = _check_fwd_args(q, k, v, alpha, beta, initial_state)
+    B, H, T, dk, dv = _check_fwd_args(q, k, v, alpha, beta, initial_state, alpha_per_dim=_vecgate)
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     if final_state is None and output_final_state:
@@ -180,15 +184,22 @@ def gdn_scan_fwd(q, k, v, alpha, beta, initial_state=None, *, o=None, final_stat
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = load_library().gdn_scan_fwd(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+    fn = load_library().gdn_scan_fwd_vecgate if _vecgate else load_library().gdn_scan_fwd
+    rc = fn(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
                                      _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
                                      _dev_ptr(initial_state, "initial_state"), _dev_ptr(o, "o"),
                                      _dev_ptr(final_state, "final_state"), B, H, T, dk, dv,
                                      _DTYPES[q.dtype], _dev_ptr(workspace, "workspace"), ws_bytes,
                                      _stream_ptr(stream, q.device))
     if rc != GDN_OK:
-        raise GDNError(rc, "gdn_scan_fwd")
+        raise GDNError(rc, "gdn_scan_fwd_vecgate" if _vecgate else "gdn_scan_fwd")
     return o, final_state
+
+
+def gdn_scan_fwd_vecgate(q, k, v, alpha, beta, initial_state=None, **kw):
+    """gdn_scan_fwd with a per-dimension gate alpha [B,H,T,dk] (fp32) that
+    decays the key columns of the state."""
+    return gdn_scan_fwd(q, k, v, alpha, beta, initial_state, _vecgate=True, **kw)
 
 
 def gdn_chunk_fwd_split_workspace(B, H, T, dk, dv, chunk_size: int = 64, dtype=torch.bfloat16) -> int:

@@ -113,7 +113,7 @@ size_t scan_ws_bytes(int64_t nseq, int G, int64_t d) {
   return (size_t)(2 * nseq * (G - 1) + nseq * G) * (size_t)(d * d) * sizeof(float);
 }
 
-template <class E, int D>
+template <class E, int D, bool VEC>
 int launch_scan(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                 const float* s0, void* o, float* sT, int64_t nseq, int64_t T, float* ws, hipStream_t stream) {
   int G;
@@ -127,7 +127,7 @@ int launch_scan(const void* q, const void* k, const void* v, const float* alpha,
   if (G > 1) {
     const int64_t nb = scan_blocks(SCAN_AGG, (int)nseq, G, D);
     if (nb > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((scan_tokens_kernel<E, D>), dim3((unsigned)nb), dim3(THREADS), 0, stream, qq, kk,
+    hipLaunchKernelGGL((scan_tokens_kernel<E, D, VEC>), dim3((unsigned)nb), dim3(THREADS), 0, stream, qq, kk,
                        vv, alpha, beta, oo, sT, (int)SCAN_AGG, (int)nseq, G, T, L, ws);
     if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
   }
@@ -136,7 +136,7 @@ int launch_scan(const void* q, const void* k, const void* v, const float* alpha,
   if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
   const int64_t nb = scan_blocks(SCAN_OUT, (int)nseq, G, D);
   if (nb > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((scan_tokens_kernel<E, D>), dim3((unsigned)nb), dim3(THREADS), 0, stream, qq, kk, vv,
+  hipLaunchKernelGGL((scan_tokens_kernel<E, D, VEC>), dim3((unsigned)nb), dim3(THREADS), 0, stream, qq, kk, vv,
                      alpha, beta, oo, sT, (int)SCAN_OUT, (int)nseq, G, T, L, ws);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -180,7 +180,7 @@ namespace {
 int check_fwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
               const float* initial_state, void* o, float* final_state, int64_t B, int64_t H,
               int64_t T, int64_t dk, int64_t dv, int64_t chunk_size, gdn_dtype dtype,
-              bool f32_any_width = false) {
+              bool f32_any_width = false, bool alpha_per_dim = false) {
   if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0 || chunk_size <= 0) return GDN_ERR_INVALID_ARG;
   if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
   const int64_t nchain = B * H;
@@ -195,7 +195,7 @@ int check_fwd(const void* q, const void* k, const void* v, const float* alpha, c
   if (has_tokens) {
     const Range ro{o, nchain * T * dv * esz};
     const Range ins[] = {{q, nchain * T * dk * esz}, {k, nchain * T * dk * esz},
-                         {v, nchain * T * dv * esz}, {alpha, nchain * T * 4},
+                         {v, nchain * T * dv * esz}, {alpha, nchain * T * (alpha_per_dim ? dk : 1) * 4},
                          {beta, nchain * T * 4},     {initial_state, nchain * dv * dk * 4},
                          {final_state, nchain * dv * dk * 4}};
     for (const Range& r : ins)
@@ -251,12 +251,16 @@ size_t gdn_scan_fwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64
   return scan_ws_bytes(B * H, G, dk);
 }
 
-int gdn_scan_fwd(const void* q, const void* k, const void* v, const float* alpha,
-                 const float* beta, const float* initial_state, void* o, float* final_state,
-                 int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, gdn_dtype dtype,
-                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+template <bool VEC>
+int scan_fwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+             const float* initial_state, void* o, float* final_state, int64_t B, int64_t H, int64_t T,
+             int64_t dk, int64_t dv, gdn_dtype dtype, void* workspace, size_t workspace_bytes,
+             void* hip_stream) {
   const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
-                           64, dtype, true);
+                           64, dtype, true, VEC);
   if (rc != GDN_OK) return rc;
   const int64_t nseq = B * H;
   if (nseq == 0) return GDN_OK;
@@ -272,7 +276,7 @@ int gdn_scan_fwd(const void* q, const void* k, const void* v, const float* alpha
     const Range rw{workspace, (int64_t)need};
     const Range others[] = {{q, nseq * T * dk * esz}, {k, nseq * T * dk * esz},
                             {v, nseq * T * dv * esz}, {o, nseq * T * dv * esz},
-                            {alpha, nseq * T * 4},    {beta, nseq * T * 4},
+                            {alpha, nseq * T * (VEC ? dk : 1) * 4}, {beta, nseq * T * 4},
                             {initial_state, nseq * dv * dk * 4}, {final_state, nseq * dv * dk * 4}};
     for (const Range& r : others)
       if (overlaps(rw, r)) return GDN_ERR_INVALID_ARG;
@@ -280,10 +284,29 @@ int gdn_scan_fwd(const void* q, const void* k, const void* v, const float* alpha
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   float* ws = static_cast<float*>(workspace);
   if (dtype == GDN_BF16)
-    return dk == 128 ? launch_scan<bf16_t, 128>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, ws, stream)
-                     : launch_scan<bf16_t, 64>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, ws, stream);
-  return dk == 128 ? launch_scan<float, 128>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, ws, stream)
-                   : launch_scan<float, 64>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, ws, stream);
+    return dk == 128 ? launch_scan<bf16_t, 128, VEC>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, ws, stream)
+                     : launch_scan<bf16_t, 64, VEC>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, ws, stream);
+  return dk == 128 ? launch_scan<float, 128, VEC>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, ws, stream)
+                   : launch_scan<float, 64, VEC>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, ws, stream);
+}
+}  // namespace
+
+extern "C" {
+
+int gdn_scan_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                 const float* beta, const float* initial_state, void* o, float* final_state,
+                 int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, gdn_dtype dtype,
+                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return scan_fwd<false>(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv, dtype,
+                         workspace, workspace_bytes, hip_stream);
+}
+
+int gdn_scan_fwd_vecgate(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, const float* initial_state, void* o, float* final_state,
+                         int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, gdn_dtype dtype,
+                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return scan_fwd<true>(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv, dtype,
+                        workspace, workspace_bytes, hip_stream);
 }
 
 size_t gdn_chunk_fwd_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,

@@ -20,6 +20,11 @@
 // Reducing a block to its map is the token loop itself on the stacked state
 // [B; A] (a rank-1 update per token, O(d^2) instead of a d^3 product).
 //
+// VEC: a per-dimension gate alpha_t in (0,1]^{d_k} ([P1] §2.2 allows a vector
+// gate) that decays the key columns of the state, A_t = Diag(alpha_t)(I -
+// beta_t k_t k_t^T); alpha is then [B,H,T,d_k].  The maps stay affine, so the
+// same blocked scan applies.
+//
 // Layout: a workgroup owns 16 rows of one state; 16 consecutive lanes hold a
 // row (D / 16 columns each), and row dot products are summed across those
 // lanes with DPP rotations.  Tokens are staged 32 at a time in LDS.
@@ -51,7 +56,7 @@ __host__ __device__ inline int64_t scan_blocks(int mode, int nseq, int G, int D)
   return (int64_t)nseq * per * (D / RPW);
 }
 
-template <class E, int D>
+template <class E, int D, bool VEC = false>
 __global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, E* __restrict__ o,
@@ -61,6 +66,7 @@ __global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
   __shared__ float ks[TILE][D], qs[TILE][D];
   __shared__ float vs[TILE][RPW], os[TILE][RPW];
   __shared__ float as_[TILE], bs_[TILE];
+  __shared__ float av[VEC ? TILE : 1][VEC ? D : 1];  // per-dimension gates
 
   int64_t b = blockIdx.x;
   const int rg = (int)(b % (D / RPW));
@@ -112,8 +118,14 @@ __global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
       vs[t][r] = (t < n && kind != 1) ? Elem<E>::to_f32(v[(base + tt + t) * D + rg * RPW + r]) : 0.f;
     }
     if (tid < TILE) {
-      as_[tid] = tid < n ? alpha[base + tt + tid] : 1.f;
+      as_[tid] = (!VEC && tid < n) ? alpha[base + tt + tid] : 1.f;
       bs_[tid] = tid < n ? beta[base + tt + tid] : 0.f;
+    }
+    if constexpr (VEC) {
+      for (int e = tid; e < TILE * D; e += THREADS) {
+        const int t = e / D, c = e % D;
+        av[t][c] = t < n ? alpha[(base + tt + t) * D + c] : 1.f;
+      }
     }
     __syncthreads();
     for (int t = 0; t < n; ++t) {
@@ -125,7 +137,7 @@ __global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
       float r = 0.f;
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
-        s[j] *= a;
+        s[j] *= VEC ? av[t][c0 + j] : a;
         r = fmaf(s[j], kr[j], r);
       }
       r = row16_sum(r);

@@ -132,6 +132,20 @@ int gdn_scan_fwd(const void* q, const void* k, const void* v,
                  gdn_dtype dtype, void* workspace, size_t workspace_bytes,
                  void* hip_stream);
 
+/*
+ * gdn_scan_fwd_vecgate — gdn_scan_fwd with a per-dimension gate ([P1] §2.2
+ * allows a vector gate): alpha is [B,H,T,dk] fp32, each entry in [0,1], and
+ * decays the key columns of the state,
+ *     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
+ * Everything else, the workspace size included, as for gdn_scan_fwd.
+ */
+int gdn_scan_fwd_vecgate(const void* q, const void* k, const void* v,
+                         const float* alpha, const float* beta,
+                         const float* initial_state, void* o, float* final_state,
+                         int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                         gdn_dtype dtype, void* workspace, size_t workspace_bytes,
+                         void* hip_stream);
+
 /* Workspace bytes gdn_scan_fwd needs for these sizes.  Host-only. */
 size_t gdn_scan_fwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
                               gdn_dtype dtype);
