@@ -28,6 +28,9 @@
 // recomputed by each slice's workgroup.  The fp32 state slice lives in MFMA
 // accumulators for the whole sequence; a bf16 copy in LDS feeds the products.
 //
+// The library uses this kernel for fp32 inputs (d = 64); bf16 inputs take the
+// pipelined kernel of chunk_fwd_pipe.hpp.
+//
 // All tensors are dense row-major; pointers are 16-byte aligned (checked on
 // the host).
 #pragma once

@@ -78,9 +78,11 @@ enum { G_BETA = 0, G_ER = 1, G_EG = 2, G_EL = 3, G_LOG = 4, G_N = 5 };
 
 // The prefetch wave touches every 128-byte line of chunk p + PREFETCH_AHEAD in period p,
 // so that the loads of the later periods find their lines in L2.  Three
-// chunks ahead is the measured optimum: at five or more, lines are evicted
-// before use and HBM traffic rises above the algorithmic bytes (1.34x at
-// six); at two, the K/Q loads of the loader (two periods ahead) gain nothing.
+// chunks ahead (two periods before the loader's DMA of that chunk) is the
+// measured optimum: at five or more, lines are evicted before use and HBM
+// traffic rises above the algorithmic bytes (1.34x at six); at two the lines
+// arrive too late for the DMA and the kernel is 40 % slower; four is as fast
+// as three.
 constexpr int PREFETCH_AHEAD = 3;
 
 // Targets of LDS-DMA loads are arrays of their own: the compiler then sees
@@ -563,7 +565,7 @@ __device__ __forceinline__ void dma_v(const Seq& sq, const DmaAddr& A, int64_t c
                                              (int)(v0 + it * 16 * DV * 2), 0, 0);
 }
 
-// ============================================================ wave 2: P
+// ============================================================ prefetch wave
 // L2 prefetch of chunk c: one 4-byte load per 128-byte line, landing in a
 // scratch word of LDS (an LDS-DMA load has a side effect, so it is kept, and
 // no register waits for it).  The four slice workgroups of a sequence split
@@ -581,6 +583,7 @@ __device__ __forceinline__ void prefetch_chunk(const Seq& sq, int64_t c, int sli
   __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.b, land, 4, g, 0, 0, 0);
 }
 
+// ============================================================ P wave
 // The 10 lower 16x16 tiles of a 64x64 chunk matrix, in the order the P and
 // L waves build them: (row block rb, column block sb), sb <= rb.
 constexpr int TILE_RB[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
@@ -661,7 +664,7 @@ __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c,
     run(std::false_type{});
 }
 
-// ============================================================ wave 3: L
+// ============================================================ L wave
 // Keys of one chunk in MFMA fragment layout: kf[rb][pp] = key octet 4 pp + lg
 // of token 16 rb + lr.
 struct FragRegs {
@@ -762,7 +765,7 @@ __device__ __forceinline__ void build_l(Smem& sm, const FragRegs& R, int64_t c, 
     run(std::false_type{});
 }
 
-// ============================================================ wave 4: loader
+// ============================================================ loader wave
 // In period p the loader builds the gate tables of chunk p+3 (gates loaded one
 // period earlier), then loads the gates of chunk p+4 and V, K, Q of chunk p+1,
 // in that order, and ends the period once V, K, Q of chunk p+1 are in LDS
@@ -790,7 +793,7 @@ __device__ __forceinline__ void loader_period(Smem& sm, const Seq& sq, const Dma
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 }
 
-// ============================================================ wave 6: inverse
+// ============================================================ inverse wave
 // Forward substitution over key columns 4Q .. 4Q+3 of one unit-lower 16x16
 // block: x[r] -= L[r][s] x[s] for s in the band and r > s.  The band's rows of
 // L (float4, read by all 16 lanes of a group at once) are read one band ahead.
