@@ -1,0 +1,78 @@
+"""Edge cases of the sequence-split, scan, vector-gate and GLA entry points
+on the GPU: zero tokens (the final state is the initial one, or zero), no
+sequences, fewer tokens than one chunk or block, and a final state that
+aliases the initial state.  Results are compared with the fp64 oracles or
+with exact expectations."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_deltanet_sequence_amd import inputs
+from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd_split, gdn_scan_fwd, gdn_scan_fwd_vecgate,
+                                                 gla_chunk_fwd)
+
+from _helpers import TOL, maxrel, oracle_inputs, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _vec(alpha, d):
+    return alpha[..., None].expand(*alpha.shape, d).contiguous()
+
+
+ENTRIES = {
+    "split": lambda xd: gdn_chunk_fwd_split(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"], 64),
+    "scan": lambda xd: gdn_scan_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"]),
+    "scan_vecgate": lambda xd: gdn_scan_fwd_vecgate(xd["q"], xd["k"], xd["v"], _vec(xd["alpha"], xd["q"].shape[3]),
+                                                    xd["beta"], xd["s0"]),
+    "gla": lambda xd: gla_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"], 64),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ENTRIES))
+def test_zero_tokens_keeps_state(name):
+    x = inputs.make_fwd_inputs(2, 3, 0, 128, "bf16", seed=61, init_state=True)
+    o, sT = ENTRIES[name](to_dev(x))
+    torch.cuda.synchronize()
+    assert o.shape == (2, 3, 0, 128)
+    assert torch.equal(sT.cpu(), x["s0"])
+    x["s0"] = None
+    o, sT = ENTRIES[name](to_dev(x))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(sT).item() == 0
+
+
+@pytest.mark.parametrize("name", sorted(ENTRIES))
+def test_no_sequences(name):
+    x = inputs.make_fwd_inputs(0, 4, 100, 64, "bf16", seed=62, init_state=True)
+    o, sT = ENTRIES[name](to_dev(x))
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and sT.numel() == 0
+
+
+@pytest.mark.parametrize("name", ["split", "scan", "scan_vecgate"])
+@pytest.mark.parametrize("T", [1, 17, 63])
+def test_short_sequences_match_oracle(name, T):
+    x = inputs.make_fwd_inputs(1, 2, T, 64, "bf16", seed=63 + T, init_state=True)
+    o, sT = ENTRIES[name](to_dev(x))
+    torch.cuda.synchronize()
+    (q, k, v, a, b), s0 = oracle_inputs(x)
+    ro, rs = oracle.oracle_fwd(q, k, v, a, b, s0)
+    assert maxrel(to_np(o), ro) <= TOL["bf16"] and maxrel(to_np(sT), rs) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("name", ["scan", "gla"])
+def test_final_state_aliases_initial_state(name):
+    x = inputs.make_fwd_inputs(1, 2, 700, 128, "bf16", seed=64, init_state=True)
+    xd = to_dev(x)
+    ref_o, ref_s = ENTRIES[name](xd)
+    torch.cuda.synchronize()
+    s = xd["s0"].clone()
+    if name == "scan":
+        o, s2 = gdn_scan_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], s, final_state=s)
+    else:
+        o, s2 = gla_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], s, 64, final_state=s)
+    torch.cuda.synchronize()
+    assert s2.data_ptr() == s.data_ptr()
+    assert torch.equal(o, ref_o) and torch.equal(s, ref_s)
