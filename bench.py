@@ -276,10 +276,17 @@ def time_decode(torch, dev, steps_override=None):
     bes = [t.to(dev) for t in x["beta"]]
     o = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
-    # warm-up on a scratch copy so the timed 64 steps start from S0
+    # warm-up on a scratch copy, long enough for the clocks to settle, so the
+    # timed 64 steps start from S0 on a GPU under sustained load
     scratch = state.clone()
-    for t in range(4):
+    it = [0]
+
+    def warm():
+        t = it[0] % steps
+        it[0] += 1
         gdn_recurrent_step(qs[t], ks[t], vs[t], als[t], bes[t], scratch, o=o, stream=stream)
+
+    settle_clocks(torch, warm)
     del scratch
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
@@ -289,11 +296,12 @@ def time_decode(torch, dev, steps_override=None):
         ev[t + 1].record(stream)
     torch.cuda.synchronize()
     per = [ev[t].elapsed_time(ev[t + 1]) for t in range(steps)]
-    avg_ms = sum(per) / steps
+    avg_ms = ev[0].elapsed_time(ev[steps]) / steps
     byts = alg_bytes_decode(N, H, d)
     return {"workload": "decode: 256 sequences x H=16, d_k=d_v=128, fp32 state [256,16,128,128] "
                         "updated in place, bf16 q/k/v, 64 consecutive steps",
             "tokens_per_s": N / (avg_ms * 1e-3), "ms_per_step": avg_ms,
+            "step_ms_median": sorted(per)[steps // 2],
             "alg_bytes_per_step": byts, "achieved_GBs": byts / (avg_ms * 1e-3) / 1e9,
             "hbm_frac": byts / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 

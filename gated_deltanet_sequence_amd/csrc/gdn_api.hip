@@ -149,7 +149,8 @@ template <class E, int DK, int DV>
 int launch_step(const void* q, const void* k, const void* v, const float* alpha,
                 const float* beta, float* state, void* o, int64_t nheads, hipStream_t stream) {
   if (nheads > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((gdn::recurrent_step_kernel<E, DK, DV>), dim3((unsigned)nheads), dim3(256), 0,
+  constexpr int NT = DK == 128 ? 512 : 256;
+  hipLaunchKernelGGL((gdn::recurrent_step_kernel<E, DK, DV, NT>), dim3((unsigned)nheads), dim3(NT), 0,
                      stream, static_cast<const E*>(q), static_cast<const E*>(k),
                      static_cast<const E*>(v), alpha, beta, state, static_cast<E*>(o), nheads);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;

@@ -16,12 +16,17 @@
 //     S_i <- alpha S_i + u_i k^T                     (written in place)
 // Every row is independent, so the state is read once and written once.
 //
-// Layout of one workgroup (256 threads) = one head: LPR = dk/4 consecutive
+// Layout of one workgroup (NT threads) = one head: LPR = dk/4 consecutive
 // lanes hold one row as float4s (a 16-byte coalesced load per lane), and
-// 256/LPR row groups stride over the dv rows.  The per-row dot products are
-// reduced across the LPR lanes with a halving exchange: each step sends half
-// of the still-partial rows to the partner lane, so every step halves the
-// values a lane carries instead of reducing every row separately.
+// NT/LPR row groups stride over the dv rows.  NT = 512 for d = 128 keeps a
+// lane's share of the state at 8 rows (about 70 VGPRs, 7 waves per SIMD), so
+// enough heads are resident per CU for their loads and stores to overlap;
+// with 256 threads (16 rows per lane) only 4 waves fit and the step runs
+// measurably slower than an in-place read-modify-write of the same bytes.
+// The per-row dot products are reduced across the LPR lanes with a halving
+// exchange: each step sends half of the still-partial rows to the partner
+// lane, so every step halves the values a lane carries instead of reducing
+// every row separately.
 #pragma once
 
 #include "gdn_common.hpp"
@@ -67,13 +72,13 @@ __device__ __forceinline__ int halving_row_index(int x) {
   return idx;
 }
 
-template <class T, int DK, int DV>
-__global__ __launch_bounds__(256) void recurrent_step_kernel(
+template <class T, int DK, int DV, int NT>
+__global__ __launch_bounds__(NT) void recurrent_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     float* __restrict__ state, T* __restrict__ o, int64_t nheads) {
   constexpr int LPR = DK / 4;        // lanes per row
-  constexpr int RG = 256 / LPR;      // row groups
+  constexpr int RG = NT / LPR;       // row groups
   constexpr int R = DV / RG;         // rows per lane
   static_assert(LPR <= 64 && (LPR & (LPR - 1)) == 0, "row must fit a wave");
   static_assert(R >= 1 && (R & (R - 1)) == 0 && R <= LPR, "rows per lane");
