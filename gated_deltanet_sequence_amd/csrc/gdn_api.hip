@@ -22,6 +22,16 @@ struct Range {
   int64_t bytes;
 };
 
+// Size limits shared by every entry point: at most 2^31 - 1 sequences and
+// tokens, and 2^48 token-sequences, so that byte counts (times d * 4 <= 2^9)
+// stay far inside int64.
+constexpr int64_t MAX_SEQS = 0x7fffffff, MAX_TOKENS = 0x7fffffff, MAX_SEQ_TOKENS = int64_t(1) << 48;
+bool too_large(int64_t B, int64_t H, int64_t T) {
+  if (B > MAX_SEQS || H > MAX_SEQS || T > MAX_TOKENS) return true;
+  const int64_t n = B * H;  // < 2^62
+  return n > MAX_SEQS || (T > 0 && n > MAX_SEQ_TOKENS / T);
+}
+
 bool overlaps(Range a, Range b) {
   if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
@@ -184,6 +194,7 @@ int check_fwd(const void* q, const void* k, const void* v, const float* alpha, c
               bool f32_any_width = false, bool alpha_per_dim = false) {
   if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0 || chunk_size <= 0) return GDN_ERR_INVALID_ARG;
   if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (too_large(B, H, T)) return GDN_ERR_UNSUPPORTED;
   const int64_t nchain = B * H;
   const bool has_tokens = nchain > 0 && T > 0;
   if (has_tokens && (!q || !k || !v || !alpha || !beta || !o)) return GDN_ERR_INVALID_ARG;
@@ -244,7 +255,7 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
 size_t gdn_scan_fwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
                               gdn_dtype dtype) {
   if (B <= 0 || H <= 0 || T < 0 || dk != dv || (dk != 64 && dk != 128) ||
-      (dtype != GDN_F32 && dtype != GDN_BF16))
+      (dtype != GDN_F32 && dtype != GDN_BF16) || too_large(B, H, T))
     return 0;
   int G;
   int64_t L;
@@ -313,7 +324,7 @@ int gdn_scan_fwd_vecgate(const void* q, const void* k, const void* v, const floa
 size_t gdn_chunk_fwd_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
                                      int64_t chunk_size, gdn_dtype dtype) {
   if (B <= 0 || H <= 0 || T <= 0 || dk != dv || (dk != 64 && dk != 128) || chunk_size != 64 ||
-      dtype != GDN_BF16)
+      dtype != GDN_BF16 || too_large(B, H, T))
     return 0;
   int G;
   int64_t L;
@@ -373,6 +384,7 @@ int gdn_recurrent_step(const void* q, const void* k, const void* v, const float*
                        int64_t dk, int64_t dv, gdn_dtype dtype, void* hip_stream) {
   if (N < 0 || H < 0 || dk <= 0 || dv <= 0) return GDN_ERR_INVALID_ARG;
   if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
+  if (too_large(N, H, 0)) return GDN_ERR_UNSUPPORTED;
   const int64_t nheads = N * H;
   if (nheads > 0 && (!q || !k || !v || !alpha || !beta || !state || !o)) return GDN_ERR_INVALID_ARG;
   if (dk != dv || (dk != 64 && dk != 128)) return GDN_ERR_UNSUPPORTED;

@@ -38,6 +38,9 @@
  *     inside a kernel surface at the caller's next synchronisation.
  *   - Values are not inspected: NaN/Inf propagate.  There is no 1/sqrt(d)
  *     query scaling and no normalisation of q or k inside the library.
+ *   - Size limits: the number of sequences (B*H, or N*H for the decode step)
+ *     and T are each at most 2^31 - 1, and B*H*T at most 2^48; larger sizes
+ *     return GDN_ERR_UNSUPPORTED (the workspace queries return 0).
  */
 #ifndef GDN_H
 #define GDN_H

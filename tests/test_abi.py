@@ -141,3 +141,19 @@ def test_scan_rejects_invalid_arguments_and_sizes_workspace(lib):
     assert need == 64 * 64 * 4                        # one block: the start-state slot only
     assert scan(wsb=need - 4) == binding.GDN_ERR_INVALID_ARG
     assert lib.gdn_scan_fwd_workspace(1, 1, 64, 128, 128, 0) == 128 * 128 * 4   # fp32 d = 128
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=2 ** 31), dict(H=2 ** 31), dict(T=2 ** 31), dict(B=2 ** 16, H=2 ** 16),
+    dict(B=2 ** 20, H=2 ** 10, T=2 ** 20), dict(B=2 ** 62, H=2 ** 62),
+])
+def test_oversized_shapes_are_rejected_before_any_arithmetic_overflows(lib, kw):
+    """Sizes whose byte counts would not fit int64 (or exceed the limits the
+    header states) are refused with UNSUPPORTED, before anything is launched."""
+    assert fwd(lib, **kw) == binding.GDN_ERR_UNSUPPORTED
+    assert fwd_split(lib, **kw) == binding.GDN_ERR_UNSUPPORTED
+    args = (kw.get("B", 1), kw.get("H", 1), kw.get("T", 64), 128, 128)
+    assert lib.gdn_scan_fwd_workspace(*args, 1) == 0
+    assert lib.gdn_chunk_fwd_split_workspace(*args, 64, 1) == 0
+    if "T" not in kw:
+        assert step(lib, N=kw.get("B", 1), H=kw.get("H", 1)) == binding.GDN_ERR_UNSUPPORTED
