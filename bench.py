@@ -145,7 +145,8 @@ LONG = dict(B=1, H=16, T=131072, d=128, seed=4)
 def time_long(torch, dev, launches=10):
     """The long-context workload (16 sequences of 131072 tokens, S0 ~ N(0,0.1))
     through the sequence-split entry point and, for comparison, the plain
-    one; mean of `launches` back-to-back launches between two events."""
+    one; mean of `launches` back-to-back launches between two events, each
+    after settling the clocks on that entry point."""
     from gated_deltanet_sequence_amd import inputs
     from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd, gdn_chunk_fwd_split,
                                                      gdn_chunk_fwd_split_workspace)
@@ -166,8 +167,7 @@ def time_long(torch, dev, launches=10):
     res = {"workload": "long context: B=1, H=16, T=131072, d_k=d_v=128, C=64, bf16 q/k/v, "
                        "fp32 gates, S0 ~ N(0,0.1)", "alg_bytes": alg, "split_workspace_bytes": need}
     for name, f in runs.items():
-        f()
-        torch.cuda.synchronize()
+        settle_clocks(torch, f)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -194,9 +194,7 @@ def time_gla(torch, xd, launches=50):
     stream = torch.cuda.current_stream()
     f = lambda: gla_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None, 64,
                               o=o, final_state=sT, stream=stream)
-    for _ in range(5):
-        f()
-    torch.cuda.synchronize()
+    settle_clocks(torch, f)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -234,8 +232,7 @@ def time_routes(torch, dev, launches=5):
                     ("scan", lambda: gdn_scan_fwd(*a, workspace=ws, stream=stream)),
                     ("scan_vecgate", lambda: gdn_scan_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"],
                                                                   None, workspace=ws, stream=stream))):
-        f()
-        torch.cuda.synchronize()
+        settle_clocks(torch, f)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)

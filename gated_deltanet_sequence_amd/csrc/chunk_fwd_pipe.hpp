@@ -381,6 +381,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   f32x4 Z[4];
   bf16x8_t fr[3][4];
   auto read_block = [&](int n) {
+    if (GLA && n < 4) return;  // without the delta rule K S^T is not needed
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp)
       fr[n % 3][pp] = as_op(n < 4 ? ld3<uint4>(kf_b[pp], n * 4096) : ld3<uint4>(qf_b[pp], (n - 4) * 4096));
@@ -397,13 +398,14 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     for (int h = 0; h < 4; ++h) {
       if (rb == 1) vv[h] = tr3(v_b, h * 16 * DVS * 2);
       if (rb == 2) b4[h] = *reinterpret_cast<const float4*>(gt + G_BETA * C + 16 * h + 4 * lg);
-      if (rb == 3) g4[h] = GLA ? make_float4(0.f, 0.f, 0.f, 0.f)
-                               : *reinterpret_cast<const float4*>(gt + G_EG * C + 16 * h + 4 * lg);
+      if (!GLA && rb == 3) g4[h] = *reinterpret_cast<const float4*>(gt + G_EG * C + 16 * h + 4 * lg);
     }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 az = zero4();
+    if constexpr (!GLA) {
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) az = mfma(fr[rb % 3][pp], Sop[pp], az);
+      for (int pp = 0; pp < 4; ++pp) az = mfma(fr[rb % 3][pp], Sop[pp], az);
+    }
     R.S[2 * rb] *= decay;
     R.S[2 * rb + 1] *= decay;
     Z[rb] = az;
@@ -418,7 +420,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     if (rb < 2) read_block(rb + 6);  // Q block rb sits in slot (4 + rb) % 3
-    if (rb == 2) {
+    if (!GLA && rb == 2) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
@@ -441,10 +443,17 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) ao = mfma(Sop[pp], fr[(4 + rb) % 3][pp], ao);
     O1[rb] = ao;
-    y[rb][0] = b4[rb].x * fmaf(-g4[rb].x, Z[rb][0], __uint_as_float(vv[rb].x << 16));
-    y[rb][1] = b4[rb].y * fmaf(-g4[rb].y, Z[rb][1], __uint_as_float(vv[rb].x & 0xffff0000u));
-    y[rb][2] = b4[rb].z * fmaf(-g4[rb].z, Z[rb][2], __uint_as_float(vv[rb].y << 16));
-    y[rb][3] = b4[rb].w * fmaf(-g4[rb].w, Z[rb][3], __uint_as_float(vv[rb].y & 0xffff0000u));
+    if constexpr (GLA) {
+      y[rb][0] = b4[rb].x * __uint_as_float(vv[rb].x << 16);
+      y[rb][1] = b4[rb].y * __uint_as_float(vv[rb].x & 0xffff0000u);
+      y[rb][2] = b4[rb].z * __uint_as_float(vv[rb].y << 16);
+      y[rb][3] = b4[rb].w * __uint_as_float(vv[rb].y & 0xffff0000u);
+    } else {
+      y[rb][0] = b4[rb].x * fmaf(-g4[rb].x, Z[rb][0], __uint_as_float(vv[rb].x << 16));
+      y[rb][1] = b4[rb].y * fmaf(-g4[rb].y, Z[rb][1], __uint_as_float(vv[rb].x & 0xffff0000u));
+      y[rb][2] = b4[rb].z * fmaf(-g4[rb].z, Z[rb][2], __uint_as_float(vv[rb].y << 16));
+      y[rb][3] = b4[rb].w * fmaf(-g4[rb].w, Z[rb][3], __uint_as_float(vv[rb].y & 0xffff0000u));
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   const bf16x8_t Yop[2] = {pack_op(y[0], y[1]), pack_op(y[2], y[3])};
@@ -467,10 +476,14 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   f32x4 U[4], Onew[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
-    f32x4 acc = zero4();
+    if constexpr (GLA) {
+      U[rb] = y[rb];  // Ti = I
+    } else {
+      f32x4 acc = zero4();
 #pragma unroll
-    for (int pp = 0; pp <= rb / 2; ++pp) acc = mfma(tf[rb][pp], Yop[pp], acc);
-    U[rb] = acc;
+      for (int pp = 0; pp <= rb / 2; ++pp) acc = mfma(tf[rb][pp], Yop[pp], acc);
+      U[rb] = acc;
+    }
     Onew[rb] = O1[rb] * eg[rb];
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -902,8 +915,9 @@ __host__ __device__ inline int map_chains(const ChainMap& m) {
 
 // GLA: gated linear attention without the delta rule ([P3] §2.3),
 // S_t = alpha_t S_{t-1} + beta_t v_t k_t^T.  Its chunk form is the one above
-// with L = 0 (so Ti = I) and Y = diag(beta) V: the L wave stays idle, L is
-// zero from the start, and the state waves drop the K S^T term of Y.
+// with L = 0 (so Ti = I) and U = Y = diag(beta) V: the L and inverse waves
+// stay idle, and the state waves compute neither K S^T nor the product by Ti.
+// The state chain is then only the decayed accumulation of U^T K.
 template <bool GLA>
 __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -989,12 +1003,6 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     for (int e = tid; e < 2 * C * C / 2; e += 64 * NWAVES) z[e] = 0u;
     uint32_t* z2 = reinterpret_cast<uint32_t*>(&sm.Tt[0][0]);
     for (int e = tid; e < 2 * C * TTS / 2; e += 64 * NWAVES) z2[e] = 0u;
-    if (GLA) {
-      uint32_t* z3 = reinterpret_cast<uint32_t*>(&sm.Ld[0][0][0]);
-      for (int e = tid; e < (int)(sizeof(sm.Ld) / 4); e += 64 * NWAVES) z3[e] = 0u;
-      uint32_t* z4 = reinterpret_cast<uint32_t*>(&sm.Lo[0][0][0]);
-      for (int e = tid; e < (int)(sizeof(sm.Lo) / 4); e += 64 * NWAVES) z4[e] = 0u;
-    }
   }
 
   // The empty slot only helps to zero P and Ti^T.  Its stores are complete
@@ -1075,7 +1083,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     for (int r = 0; r < 16; ++r) xinit[r] = (r == lr) ? 1.f : 0.f;
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
-      if (p + 1 >= 0 && p + 1 < nch) build_inverse(sm, p + 1, xinit, lane);
+      if (!GLA && p + 1 >= 0 && p + 1 < nch) build_inverse(sm, p + 1, xinit, lane);
       lds_barrier();
     }
   } else if (wave == W_PREFETCH) {
