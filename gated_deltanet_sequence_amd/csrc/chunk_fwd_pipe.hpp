@@ -792,18 +792,26 @@ __device__ __forceinline__ void loader_prologue(Smem& sm, const Seq& sq, int64_t
     ga = buf_ldf(sq.a, (uint32_t)((C + lane) * 4));
     gb = buf_ldf(sq.b, (uint32_t)((C + lane) * 4));
   }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no load is pending when the loop starts
 }
 __device__ __forceinline__ void loader_period(Smem& sm, const Seq& sq, const DmaAddr& D, int64_t p, int64_t nch,
                                               int DV, float& ga, float& gb, int lane) {
+  // Every global load of the period is issued first, so that the one wait at
+  // its end covers a single round trip: the gates of chunk p+4 (into new
+  // registers), then V, K and Q of chunk p+1.  The gate tables of chunk p+3
+  // are built meanwhile from the registers loaded one period earlier.
+  float na = 0.f, nb = 0.f;
   if (p + 3 < nch) {
-    build_gates(sm, ga, gb, p + 3, sq.T, lane);
     const uint32_t t4 = (uint32_t)(((p + 4) * C + lane) * 4);
-    ga = buf_ldf(sq.a, t4);
-    gb = buf_ldf(sq.b, t4);
+    na = buf_ldf(sq.a, t4);
+    nb = buf_ldf(sq.b, t4);
   }
   if (p + 1 >= 0 && p + 1 < nch) dma_v(sq, D, p + 1, DV);
   if (p + 1 >= 0 && p + 1 < nch) dma_kq(sq, D, p + 1);
+  if (p + 3 < nch) build_gates(sm, ga, gb, p + 3, sq.T, lane);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  ga = na;
+  gb = nb;
 }
 
 // ============================================================ inverse wave
