@@ -76,23 +76,36 @@ constexpr int LDR = 20;   // row stride (floats) of the fp32 diagonal blocks of 
 
 enum { G_BETA = 0, G_ER = 1, G_EG = 2, G_EL = 3, G_LOG = 4, G_N = 5 };
 
-// The prefetch wave touches every 128-byte line of chunk p + PREFETCH_AHEAD in period p,
-// so that the loads of the later periods find their lines in L2.  Three
-// chunks ahead (two periods before the loader's DMA of that chunk) is the
-// measured optimum: at five or more, lines are evicted before use and HBM
-// traffic rises above the algorithmic bytes (1.34x at six); at two the lines
-// arrive too late for the DMA and the kernel is 40 % slower; four is as fast
-// as three.
+// How far ahead the loader fetches K and Q.  With the delta rule the period
+// is set by the state chain, the L build and the inverse, and K, Q are loaded
+// one chunk ahead (into two of the three buffers).  Without it (GLA) the
+// period is short enough that the loader's DMA round trip becomes the
+// critical path, so K, Q are loaded two chunks ahead and each load has two
+// periods to land: measured 9 % faster for GLA, and 1 % slower for the delta
+// rule, whose loader is not critical.
+template <bool GLA> constexpr int KQ_AHEAD = GLA ? 2 : 1;
+template <bool GLA>
+__device__ __forceinline__ int kq_slot(int64_t c) { return GLA ? (int)(c % 3) : (int)(c & 1); }
+
+// The prefetch wave touches every 128-byte line of chunk
+// p + PREFETCH_AHEAD + KQ_AHEAD - 1 in period p, so that the loads of the
+// later periods find their lines in L2.  Two periods before the loader's DMA
+// of that chunk is the measured optimum: at four or more periods, lines are
+// evicted before use and HBM traffic rises above the algorithmic bytes
+// (1.34x at five); at one the lines arrive too late for the DMA and the
+// kernel is 40 % slower; three is as fast as two.
 constexpr int PREFETCH_AHEAD = 3;
 
 // Targets of LDS-DMA loads are arrays of their own: the compiler then sees
 // that the LDS reads which follow such a load in the same wave touch other
 // objects, and does not wait for the load before them.
-// K, Q and V of chunk c sit in buffer c % 2 (loaded one period ahead).
-__shared__ __attribute__((aligned(16))) bf16_t lds_K[2][C * DK];  // [token][key], octets swizzled by swz_kq(token)
-__shared__ __attribute__((aligned(16))) bf16_t lds_Q[2][C * DK];
+// K and Q of chunk c sit in buffer kq_slot(c), V of chunk c in buffer c % 2
+// (loaded one period ahead).
+__shared__ __attribute__((aligned(16))) bf16_t lds_K[3][C * DK];  // [token][key], octets swizzled by swz_kq(token)
+__shared__ __attribute__((aligned(16))) bf16_t lds_Q[3][C * DK];
 __shared__ __attribute__((aligned(16))) bf16_t lds_V[2][C * DVS];  // [token][slice column]
 __shared__ __attribute__((aligned(16))) uint32_t lds_touch[64];    // landing area of the L2 prefetch (never read)
+__shared__ __attribute__((aligned(16))) float lds_gst[2][C];        // alpha, beta of the next chunk, landed by LDS-DMA
 
 struct __attribute__((aligned(16))) Smem {
   bf16_t P[2][C * C];       // [r][s], s kappa-ordered, octets swizzled by swz_p(r)
@@ -352,7 +365,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     finish_output(sq, A, R, pf, c - 1, DV);
     return;
   }
-  const int buf = (int)(c & 1), kqb = buf;
+  const int buf = (int)(c & 1), kqb = kq_slot<GLA>(c);
   lptr kf_b[4], qf_b[4], kt_b[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
@@ -556,9 +569,11 @@ __device__ __forceinline__ DmaAddr dma_addr(int lane, int DV, int dk) {
   A.v = (uint32_t)((lane >> 2) * DV * 2 + (((lane & 3) ^ (2 * ((lane >> 4) & 1))) << 4));
   return A;
 }
-// K and Q of chunk c (32 loads) into buffers c % 2.
+// K and Q of chunk c (KQ_LOADS loads) into buffers kq_slot(c).
+constexpr int KQ_LOADS = 32;
+template <bool GLA>
 __device__ __forceinline__ void dma_kq(const Seq& sq, const DmaAddr& A, int64_t c) {
-  const int buf = (int)(c & 1);
+  const int buf = kq_slot<GLA>(c);
   const uint32_t row = (uint32_t)(sq.dk * 2), kq0 = (uint32_t)(c * C) * row;
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
@@ -604,9 +619,10 @@ constexpr int TILE_SB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
 // P of chunk c.  Tiles are software-pipelined: the products of tile t + 1 are
 // issued before the decay, mask and store of tile t.
+template <bool GLA>
 __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
-  const int buf = (int)(c & 1), kqb = buf;
+  const int buf = (int)(c & 1), kqb = kq_slot<GLA>(c);
   lptr kf_b[4], qf_b[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
@@ -784,34 +800,78 @@ __device__ __forceinline__ void build_l(Smem& sm, const FragRegs& R, int64_t c, 
 // in that order, and ends the period once V, K, Q of chunk p+1 are in LDS
 // (the prefetch wave has pulled their lines into L2 two periods earlier).
 // The gate tables of chunk 0 come before the first period.
+// Gate tables of chunk 0, and the gates of chunk 1: in registers for the
+// delta rule, landed in lds_gst by LDS-DMA for GLA.
+template <bool GLA>
 __device__ __forceinline__ void loader_prologue(Smem& sm, const Seq& sq, int64_t nch, float& ga, float& gb,
                                                 int lane) {
   ga = gb = 0.f;
   if (nch > 0) {
     build_gates(sm, buf_ldf(sq.a, (uint32_t)(lane * 4)), buf_ldf(sq.b, (uint32_t)(lane * 4)), 0, sq.T, lane);
-    ga = buf_ldf(sq.a, (uint32_t)((C + lane) * 4));
-    gb = buf_ldf(sq.b, (uint32_t)((C + lane) * 4));
+    if constexpr (GLA) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.a, (lds_void*)&lds_gst[0][0], 4, lane * 4, C * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.b, (lds_void*)&lds_gst[1][0], 4, lane * 4, C * 4, 0, 0);
+    } else {
+      ga = buf_ldf(sq.a, (uint32_t)((C + lane) * 4));
+      gb = buf_ldf(sq.b, (uint32_t)((C + lane) * 4));
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no load is pending when the loop starts
 }
+
+// One period of the loader.  Every global load of the period is issued first
+// (the gates of chunk p+4, V of chunk p+1, K and Q of chunk p + KQ_AHEAD),
+// and the gate tables of chunk p+3 are built while they fly, from the gates
+// loaded one period earlier.  The wait at the end makes K, Q, V of chunk p+1
+// and the gates of chunk p+4 complete.
+//   delta rule: the gates go to registers and the wait is vmcnt(0).
+//   GLA: K, Q are two chunks ahead and the wait leaves this period's K, Q
+//   loads in flight (vmcnt(32)).  The gates then go through LDS (lds_gst) by
+//   LDS-DMA: in registers, the compiler would wait for every load before
+//   their use, since its count ignores LDS-DMA loads.
+template <bool GLA>
 __device__ __forceinline__ void loader_period(Smem& sm, const Seq& sq, const DmaAddr& D, int64_t p, int64_t nch,
                                               int DV, float& ga, float& gb, int lane) {
-  // Every global load of the period is issued first, so that the one wait at
-  // its end covers a single round trip: the gates of chunk p+4 (into new
-  // registers), then V, K and Q of chunk p+1.  The gate tables of chunk p+3
-  // are built meanwhile from the registers loaded one period earlier.
-  float na = 0.f, nb = 0.f;
-  if (p + 3 < nch) {
-    const uint32_t t4 = (uint32_t)(((p + 4) * C + lane) * 4);
-    na = buf_ldf(sq.a, t4);
-    nb = buf_ldf(sq.b, t4);
+  constexpr int KA = KQ_AHEAD<GLA>;
+  if constexpr (!GLA) {
+    float na = 0.f, nb = 0.f;
+    if (p + 3 < nch) {
+      const uint32_t t4 = (uint32_t)(((p + 4) * C + lane) * 4);
+      na = buf_ldf(sq.a, t4);
+      nb = buf_ldf(sq.b, t4);
+    }
+    if (p + 1 >= 0 && p + 1 < nch) dma_v(sq, D, p + 1, DV);
+    if (p + KA >= 0 && p + KA < nch) dma_kq<GLA>(sq, D, p + KA);
+    if (p + 3 < nch) build_gates(sm, ga, gb, p + 3, sq.T, lane);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    ga = na;
+    gb = nb;
+  } else {
+    if (p + 3 < nch) {
+      // The gates that landed one period earlier are complete: that period
+      // ended with a wait for every load but its last KQ_LOADS.  The read is
+      // asm because the compiler's own wait before a read of an LDS-DMA
+      // target would be vmcnt(0), i.e. also for the K, Q loads in flight.  It
+      // completes (lgkmcnt(0)) before the DMA below rewrites the gates.
+      const uint32_t ga_addr = (uint32_t)(uintptr_t)(lds_void*)&lds_gst[0][lane];
+      asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %2 offset:%3\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(ga), "=&v"(gb)
+                   : "v"(ga_addr), "i"(C * 4)
+                   : "memory");
+      const uint32_t t4 = (uint32_t)(((p + 4) * C) * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.a, (lds_void*)&lds_gst[0][0], 4, lane * 4, (int)t4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.b, (lds_void*)&lds_gst[1][0], 4, lane * 4, (int)t4, 0, 0);
+    }
+    if (p + 1 >= 0 && p + 1 < nch) dma_v(sq, D, p + 1, DV);
+    const bool kq_next = p + KA >= 0 && p + KA < nch;
+    if (kq_next) dma_kq<GLA>(sq, D, p + KA);
+    if (p + 3 < nch) build_gates(sm, ga, gb, p + 3, sq.T, lane);
+    static_assert(KA == 2 && KQ_LOADS == 32, "the wait below encodes vmcnt(32)");
+    if (kq_next)
+      __builtin_amdgcn_s_waitcnt(0x8f70);  // vmcnt(32): vmcnt bits [15:14] = 2, [3:0] = 0
+    else
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   }
-  if (p + 1 >= 0 && p + 1 < nch) dma_v(sq, D, p + 1, DV);
-  if (p + 1 >= 0 && p + 1 < nch) dma_kq(sq, D, p + 1);
-  if (p + 3 < nch) build_gates(sm, ga, gb, p + 3, sq.T, lane);
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  ga = na;
-  gb = nb;
 }
 
 // ============================================================ inverse wave
@@ -1063,7 +1123,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     const StateAddr A = state_addr(lane, 0, DV);
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
-      if (p >= 0 && p < nch) build_p(sm, A, p, lane);
+      if (p >= 0 && p < nch) build_p<GLA>(sm, A, p, lane);
       lds_barrier();
     }
   } else if (wave == W_L) {
@@ -1078,11 +1138,14 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
   } else if (wave == W_LOADER) {
     const DmaAddr D = dma_addr(lane, DV, dk);
     float ga, gb;
-    loader_prologue(sm, sq, nch, ga, gb, lane);
+    loader_prologue<GLA>(sm, sq, nch, ga, gb, lane);
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
-      loader_period(sm, sq, D, p, nch, DV, ga, gb, lane);
-      lds_barrier();
+      loader_period<GLA>(sm, sq, D, p, nch, DV, ga, gb, lane);
+      if constexpr (GLA)
+        lds_barrier_keep_dma();  // this period's K, Q loads stay in flight
+      else
+        lds_barrier();
     }
   } else if (wave == W_INV) {
     // column lr of the identity: the start of the forward substitution
@@ -1098,7 +1161,8 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     // the L2 prefetch, issued by a wave that never waits for it
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
-      if (p + PREFETCH_AHEAD < nch) prefetch_chunk(sq, p + PREFETCH_AHEAD, slice, DV, lane);
+      constexpr int PA = PREFETCH_AHEAD + KQ_AHEAD<GLA> - 1;
+      if (p + PA < nch) prefetch_chunk(sq, p + PA, slice, DV, lane);
       lds_barrier_keep_dma();
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no LDS-DMA write outlives the workgroup
