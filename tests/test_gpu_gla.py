@@ -19,6 +19,11 @@ pytestmark = pytest.mark.gpu
 CASES = [
     # B, H, T, d, initial state, gate
     (1, 1, 64, 128, False, "default"),
+    # 1 to 3 chunks: the loader's two-chunk lookahead at its boundaries
+    (1, 2, 1, 128, True, "default"),
+    (1, 2, 128, 64, True, "default"),
+    (2, 1, 150, 128, True, "default"),
+    (1, 1, 192, 128, False, "default"),
     (2, 2, 65, 128, True, "default"),
     (2, 4, 1000, 128, True, "default"),
     (1, 3, 300, 64, True, "default"),
