@@ -32,6 +32,12 @@ bool too_large(int64_t B, int64_t H, int64_t T) {
   return n > MAX_SEQS || (T > 0 && n > MAX_SEQ_TOKENS / T);
 }
 
+// The pipelined bf16 kernel addresses one sequence's q, k, v and o through
+// 32-bit buffer offsets: T * d * 2 bytes must stay under 2^31.
+bool pipe_len_ok(int64_t T, int64_t dk, int64_t dv) {
+  return T * dk * 2 <= 0x7fffffff && T * dv * 2 <= 0x7fffffff;
+}
+
 bool overlaps(Range a, Range b) {
   if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
@@ -226,6 +232,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
   const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
                            chunk_size, dtype);
   if (rc != GDN_OK) return rc;
+  if (dtype == GDN_BF16 && !pipe_len_ok(T, dk, dv)) return GDN_ERR_UNSUPPORTED;
   const int64_t nchain = B * H;
   if (nchain == 0) return GDN_OK;
   if (T == 0 && !final_state) return GDN_OK;
@@ -244,7 +251,7 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
   const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
                            chunk_size, dtype);
   if (rc != GDN_OK) return rc;
-  if (dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (dtype != GDN_BF16 || !pipe_len_ok(T, dk, dv)) return GDN_ERR_UNSUPPORTED;
   const int64_t nchain = B * H;
   if (nchain == 0) return GDN_OK;
   if (T == 0 && !final_state) return GDN_OK;
@@ -324,7 +331,7 @@ int gdn_scan_fwd_vecgate(const void* q, const void* k, const void* v, const floa
 size_t gdn_chunk_fwd_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
                                      int64_t chunk_size, gdn_dtype dtype) {
   if (B <= 0 || H <= 0 || T <= 0 || dk != dv || (dk != 64 && dk != 128) || chunk_size != 64 ||
-      dtype != GDN_BF16 || too_large(B, H, T))
+      dtype != GDN_BF16 || too_large(B, H, T) || !pipe_len_ok(T, dk, dv))
     return 0;
   int G;
   int64_t L;
@@ -339,6 +346,7 @@ int gdn_chunk_fwd_split(const void* q, const void* k, const void* v, const float
   const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
                            chunk_size, dtype);
   if (rc != GDN_OK) return rc;
+  if (dtype == GDN_BF16 && !pipe_len_ok(T, dk, dv)) return GDN_ERR_UNSUPPORTED;
   const int64_t nchain = B * H;
   int G = 1;
   int64_t L = T;

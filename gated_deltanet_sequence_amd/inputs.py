@@ -24,13 +24,17 @@ all as float32 standard normals):
 
 Every returned tensor is a contiguous CPU tensor; the caller moves it to the
 device.  The same tensors (widened exactly to fp32) are what the oracle sees.
+
+``make_fwd_inputs_on_device`` draws the same distributions (default gates)
+with torch's generator on the device, for inputs too large to draw on the
+host; its values differ from ``make_fwd_inputs`` for the same seed.
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-__all__ = ["make_fwd_inputs", "make_decode_inputs", "CONFIGS", "to_f32_numpy"]
+__all__ = ["make_fwd_inputs", "make_fwd_inputs_on_device", "make_decode_inputs", "CONFIGS", "to_f32_numpy"]
 
 
 def _softplus64(z: np.ndarray) -> np.ndarray:
@@ -97,6 +101,29 @@ def make_fwd_inputs(B: int, H: int, T: int, d: int, dtype: str = "bf16",
         ).contiguous()
     return {"q": _cast(q, dtype), "k": _cast(k, dtype), "v": _cast(v, dtype),
             "alpha": alpha, "beta": beta, "s0": s0}
+
+
+def make_fwd_inputs_on_device(B: int, H: int, T: int, d: int, seed: int, device) -> dict:
+    """bf16 inputs of one chunked-forward call drawn on ``device`` with
+    ``torch.Generator(device).manual_seed(seed)``, in the order q, k, v,
+    z_alpha, z_beta (fp32 standard normals; default gates, evaluated in fp32;
+    no initial state).  Each tensor is made in place of its draw, so the peak
+    footprint is about one fp32 copy of q."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = {}
+    for name in ("q", "k", "v"):
+        x = torch.randn((B, H, T, d), generator=g, device=device, dtype=torch.float32)
+        if name != "v":
+            x /= torch.linalg.vector_norm(x, dim=-1, keepdim=True).clamp_min_(1e-12)
+        out[name] = x.to(torch.bfloat16)
+        del x
+    z_a = torch.randn((B, H, T), generator=g, device=device, dtype=torch.float32)
+    z_b = torch.randn((B, H, T), generator=g, device=device, dtype=torch.float32)
+    out["alpha"] = torch.exp(-torch.nn.functional.softplus(z_a)).contiguous()
+    out["beta"] = torch.sigmoid(z_b).contiguous()
+    out["s0"] = None
+    return out
 
 
 def make_decode_inputs(N: int, H: int, d: int, steps: int, dtype: str = "bf16",

@@ -157,3 +157,18 @@ def test_oversized_shapes_are_rejected_before_any_arithmetic_overflows(lib, kw):
     assert lib.gdn_chunk_fwd_split_workspace(*args, 64, 1) == 0
     if "T" not in kw:
         assert step(lib, N=kw.get("B", 1), H=kw.get("H", 1)) == binding.GDN_ERR_UNSUPPORTED
+
+
+def test_sequence_over_the_bf16_length_limit_is_rejected(lib):
+    """One sequence's q, k or v must stay under 2^31 bytes on the bf16
+    pipelined path: T = 2^31 / (2 d) is refused before anything else is done
+    with it (also by the split entry point, whatever its workspace)."""
+    G = 1 << 32
+    ptrs = dict(q=A, k=A + 4 * G, v=A + 8 * G, alpha=A + 12 * G, beta=A + 13 * G, o=A + 16 * G)
+    T = 2 ** 31 // 256
+    assert fwd(lib, T=T, dk=128, dv=128, **ptrs) == binding.GDN_ERR_UNSUPPORTED
+    assert fwd_split(lib, T=T, dk=128, dv=128, **ptrs) == binding.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_chunk_fwd_split_workspace(1, 1, T, 128, 128, 64, 1) == 0
+    P = lambda x: ctypes.c_void_p(x)
+    assert lib.gla_chunk_fwd(P(ptrs["q"]), P(ptrs["k"]), P(ptrs["v"]), P(ptrs["alpha"]), P(ptrs["beta"]),
+                             None, P(ptrs["o"]), None, 1, 1, T, 128, 128, 64, 1, None) == binding.GDN_ERR_UNSUPPORTED

@@ -76,3 +76,33 @@ def test_final_state_aliases_initial_state(name):
     torch.cuda.synchronize()
     assert s2.data_ptr() == s.data_ptr()
     assert torch.equal(o, ref_o) and torch.equal(s, ref_s)
+
+
+T_MAX = (2 ** 31 - 1) // (128 * 2)  # longest bf16 sequence at d = 128: q, k, v under 2^31 bytes
+
+
+def test_maximum_sequence_length_tail_matches_oracle():
+    """The longest sequence the bf16 path takes at d = 128 (8,388,607 tokens;
+    buffer offsets up to 2^31 - 1 bytes), on the plain and the sequence-split
+    entry points.  alpha = 0 at token t0 wipes the state (up to the 2^-200
+    clamp of log2 alpha), so the outputs from t0 on and the final state equal
+    the oracle's run over the tokens from t0 on, from a zero state."""
+    from gated_deltanet_sequence_amd.binding import gdn_chunk_fwd, gdn_chunk_fwd_split
+    T, d = T_MAX, 128
+    print("case max length T", T, "d", d, flush=True)
+    x = inputs.make_fwd_inputs_on_device(1, 1, T, d, seed=71, device="cuda")
+    t0 = T - 777
+    x["alpha"][0, 0, t0] = 0.0
+    tail = {n: x[n][:, :, t0:].contiguous().cpu() for n in ("q", "k", "v", "alpha", "beta")}
+    (q, k, v, a, b), _ = oracle_inputs(dict(tail, s0=None))
+    ro, rs = oracle.oracle_fwd(q, k, v, a, b, None)
+    for name, run in (("plain", lambda: gdn_chunk_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], None, 64)),
+                      ("split", lambda: gdn_chunk_fwd_split(x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                                                            None, 64))):
+        print("  entry", name, flush=True)
+        o, sT = run()
+        torch.cuda.synchronize()
+        eo, es = maxrel(to_np(o[:, :, t0:]), ro), maxrel(to_np(sT), rs)
+        print("  err o %.3e  err S_T %.3e" % (eo, es), flush=True)
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+        del o, sT
