@@ -363,8 +363,8 @@ def summarize_pmc(fetch_dir, write_dir):
     lines = [
         "# HBM traffic of chunk_fwd_pipe_kernel, main workload (B=4,H=16,T=8192,d=128,C=64, bf16)",
         "# from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch):",
-        "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -- python3 bench.py --pmc-pass",
-        "#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -- python3 bench.py --pmc-pass",
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -- python3 bench.py --pmc-pass",
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -- python3 bench.py --pmc-pass",
         "# (each pass runs the kernel for %.0f ms to settle the clocks, then %d more launches;" % (SETTLE_MS, PMC_LAUNCHES),
         "#  the figures below average those last %d launches)" % PMC_LAUNCHES,
         "#   python3 bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write",
