@@ -31,14 +31,15 @@
 //                       part of chunk p.  The fp32 state stays in MFMA
 //                       accumulators for the whole sequence.
 //   wave 2 (P)          builds P of chunk p.
-//   wave 3 (L)          builds L of chunk p+2 from keys it loaded one period
-//                       earlier, then loads the keys of chunk p+3.
-//   wave 4 (prefetch)   touches the cache lines of chunk p+3 so that later
-//                       loads hit L2, and never waits for those loads.
-//   wave 6 (loader)     moves V, K and Q of chunk p+1 into LDS
-//                       with LDS-DMA loads, builds the gate tables of chunk p+3
-//                       from gates it loaded one period earlier and loads the
-//                       gates of chunk p+4.
+//   wave 3 (L)          builds L of chunk p+2 from its keys in LDS; it issues
+//                       no global loads.
+//   wave 4 (prefetch)   touches the cache lines of chunk p+3 (the key lines
+//                       of chunk p+5) so that later loads hit L2, and never
+//                       waits for those loads.
+//   wave 6 (loader)     moves V and Q of chunk p+1 and K of chunk p+3 into
+//                       LDS with LDS-DMA loads, builds the gate tables of
+//                       chunk p+3 from gates it loaded one period earlier and
+//                       loads the gates of chunk p+4.
 //   wave 7 (inverse)    builds Ti = (I + L)^-1 of chunk p+1.
 // Every buffer written in period p is read by another wave only after the
 // barrier that ends period p, and none is rewritten while another wave still
@@ -76,16 +77,12 @@ constexpr int LDR = 20;   // row stride (floats) of the fp32 diagonal blocks of 
 
 enum { G_BETA = 0, G_ER = 1, G_EG = 2, G_EL = 3, G_LOG = 4, G_N = 5 };
 
-// How far ahead the loader fetches K and Q.  With the delta rule the period
-// is set by the state chain, the L build and the inverse, and K, Q are loaded
-// one chunk ahead (into two of the three buffers).  Without it (GLA) the
-// period is short enough that the loader's DMA round trip becomes the
+// How far ahead the loader fetches K and Q without the delta rule (GLA): the
+// period is then short enough that the loader's DMA round trip becomes the
 // critical path, so K, Q are loaded two chunks ahead and each load has two
-// periods to land: measured 9 % faster for GLA, and 1 % slower for the delta
-// rule, whose loader is not critical.
+// periods to land (measured 9 % faster than one chunk ahead).  With the delta
+// rule, Q is loaded one chunk ahead and K three (see k_buf below).
 template <bool GLA> constexpr int KQ_AHEAD = GLA ? 2 : 1;
-template <bool GLA>
-__device__ __forceinline__ int kq_slot(int64_t c) { return GLA ? (int)(c % 3) : (int)(c & 1); }
 
 // The prefetch wave touches every 128-byte line of chunk
 // p + PREFETCH_AHEAD + KQ_AHEAD - 1 in period p, so that the loads of the
@@ -93,16 +90,35 @@ __device__ __forceinline__ int kq_slot(int64_t c) { return GLA ? (int)(c % 3) : 
 // of that chunk is the measured optimum: at four or more periods, lines are
 // evicted before use and HBM traffic rises above the algorithmic bytes
 // (1.34x at five); at one the lines arrive too late for the DMA and the
-// kernel is 40 % slower; three is as fast as two.
+// kernel is 40 % slower; three is as fast as two.  With the delta rule the
+// key lines of chunk p+5 are touched instead, two periods before their DMA.
 constexpr int PREFETCH_AHEAD = 3;
 
 // Targets of LDS-DMA loads are arrays of their own: the compiler then sees
 // that the LDS reads which follow such a load in the same wave touch other
 // objects, and does not wait for the load before them.
-// K and Q of chunk c sit in buffer kq_slot(c), V of chunk c in buffer c % 2
-// (loaded one period ahead).
-__shared__ __attribute__((aligned(16))) bf16_t lds_K[3][C * DK];  // [token][key], octets swizzled by swz_kq(token)
+// GLA: K and Q of chunk c in lds_K[c % 3], lds_Q[c % 3] (two chunks ahead).
+// Delta rule: K of chunk c in lds_K4[c % 4], loaded three chunks ahead, so
+// that the L wave reads its keys of chunk c from LDS two periods before the
+// chunk instead of loading them from global memory (loads of one wave that
+// miss L2 hold up the later loads of the whole CU: the L wave's own key loads
+// cost about 5 % of the period); Q of chunk c in lds_Q2[c % 2], one chunk
+// ahead.  V of chunk c in lds_V[c % 2], one chunk ahead.  Rows [token][key]
+// with octets swizzled by swz_kq(token).
+__shared__ __attribute__((aligned(16))) bf16_t lds_K[3][C * DK];
 __shared__ __attribute__((aligned(16))) bf16_t lds_Q[3][C * DK];
+__shared__ __attribute__((aligned(16))) bf16_t lds_K4[4][C * DK];
+__shared__ __attribute__((aligned(16))) bf16_t lds_Q2[2][C * DK];
+template <bool GLA>
+__device__ __forceinline__ bf16_t* k_buf(int64_t c) {
+  if constexpr (GLA) return lds_K[c % 3];
+  else return lds_K4[c & 3];
+}
+template <bool GLA>
+__device__ __forceinline__ bf16_t* q_buf(int64_t c) {
+  if constexpr (GLA) return lds_Q[c % 3];
+  else return lds_Q2[c & 1];
+}
 __shared__ __attribute__((aligned(16))) bf16_t lds_V[2][C * DVS];  // [token][slice column]
 __shared__ __attribute__((aligned(16))) uint32_t lds_touch[64];    // landing area of the L2 prefetch (never read)
 __shared__ __attribute__((aligned(16))) float lds_gst[2][C];        // alpha, beta of the next chunk, landed by LDS-DMA
@@ -365,13 +381,13 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     finish_output(sq, A, R, pf, c - 1, DV);
     return;
   }
-  const int buf = (int)(c & 1), kqb = kq_slot<GLA>(c);
+  const int buf = (int)(c & 1);
   lptr kf_b[4], qf_b[4], kt_b[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
-    kf_b[pp] = lane_base(lds_K[kqb], A.frag[pp]);
-    qf_b[pp] = lane_base(lds_Q[kqb], A.frag[pp]);
-    kt_b[pp] = lane_base(lds_K[kqb], A.ktr[pp]);
+    kf_b[pp] = lane_base(k_buf<GLA>(c), A.frag[pp]);
+    qf_b[pp] = lane_base(q_buf<GLA>(c), A.frag[pp]);
+    kt_b[pp] = lane_base(k_buf<GLA>(c), A.ktr[pp]);
   }
   const lptr v_b = lane_base(lds_V[buf], A.vtr);
   const lptr t_b = lane_base(sm.Tt[buf], A.ttr);
@@ -569,17 +585,27 @@ __device__ __forceinline__ DmaAddr dma_addr(int lane, int DV, int dk) {
   A.v = (uint32_t)((lane >> 2) * DV * 2 + (((lane & 3) ^ (2 * ((lane >> 4) & 1))) << 4));
   return A;
 }
-// K and Q of chunk c (KQ_LOADS loads) into buffers kq_slot(c).
+// dma_rows: 16 rows-of-K (or Q) loads of chunk c into dst; dma_kq: K and Q
+// of chunk c (KQ_LOADS loads) into k_buf(c), q_buf(c).
 constexpr int KQ_LOADS = 32;
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t src, bf16_t* dst, const Seq& sq, const DmaAddr& A,
+                                         int64_t c) {
+  const uint32_t row = (uint32_t)(sq.dk * 2), kq0 = (uint32_t)(c * C) * row;
+#pragma unroll
+  for (int it = 0; it < 16; ++it)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)&dst[it * 512], 16, A.kq[it & 3],
+                                             (int)(kq0 + it * 4 * row), 0, 0);
+}
 template <bool GLA>
 __device__ __forceinline__ void dma_kq(const Seq& sq, const DmaAddr& A, int64_t c) {
-  const int buf = kq_slot<GLA>(c);
+  bf16_t* kb = k_buf<GLA>(c);
+  bf16_t* qb = q_buf<GLA>(c);
   const uint32_t row = (uint32_t)(sq.dk * 2), kq0 = (uint32_t)(c * C) * row;
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.k, (lds_void*)&lds_K[buf][it * 512], 16, A.kq[it & 3],
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.k, (lds_void*)&kb[it * 512], 16, A.kq[it & 3],
                                              (int)(kq0 + it * 4 * row), 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.q, (lds_void*)&lds_Q[buf][it * 512], 16, A.kq[it & 3],
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.q, (lds_void*)&qb[it * 512], 16, A.kq[it & 3],
                                              (int)(kq0 + it * 4 * row), 0, 0);
   }
 }
@@ -600,10 +626,13 @@ __device__ __forceinline__ void dma_v(const Seq& sq, const DmaAddr& A, int64_t c
 // the key and query lines; each touches its own value lines.  All 64 lanes
 // take part in every load (lanes 32..63 repeat the lines of lanes 0..31), so
 // the descriptors stay uniform.
-__device__ __forceinline__ void prefetch_chunk(const Seq& sq, int64_t c, int slice, int DV, int lane) {
+__device__ __forceinline__ void prefetch_keys(const Seq& sq, int64_t c, int slice, int lane) {
+  const uint32_t kq = (uint32_t)(c * C * sq.dk * 2) + (uint32_t)((32 * slice + (lane & 31)) * 128);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.k, (lds_void*)&lds_touch[0], 4, kq, 0, 0, 0);
+}
+__device__ __forceinline__ void prefetch_rest(const Seq& sq, int64_t c, int slice, int DV, int lane) {
   lds_void* land = (lds_void*)&lds_touch[0];
   const uint32_t kq = (uint32_t)(c * C * sq.dk * 2) + (uint32_t)((32 * slice + (lane & 31)) * 128);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.k, land, 4, kq, 0, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.q, land, 4, kq, 0, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.v, land, 4, (uint32_t)((c * C + lane) * DV * 2), 0, 0, 0);
   const uint32_t g = (uint32_t)(c * C * 4 + (lane & 1) * 128);
@@ -622,12 +651,12 @@ constexpr int TILE_SB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 template <bool GLA>
 __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
-  const int buf = (int)(c & 1), kqb = kq_slot<GLA>(c);
+  const int buf = (int)(c & 1);
   lptr kf_b[4], qf_b[4];
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
-    kf_b[pp] = lane_base(lds_K[kqb], A.frag[pp]);
-    qf_b[pp] = lane_base(lds_Q[kqb], A.frag[pp]);
+    kf_b[pp] = lane_base(k_buf<GLA>(c), A.frag[pp]);
+    qf_b[pp] = lane_base(q_buf<GLA>(c), A.frag[pp]);
   }
   const float* gt = &sm.gate[c & 3][0][0];
   char* Pb = reinterpret_cast<char*>(sm.P[buf]);
@@ -695,21 +724,20 @@ __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c,
 
 // ============================================================ L wave
 // Keys of one chunk in MFMA fragment layout: kf[rb][pp] = key octet 4 pp + lg
-// of token 16 rb + lr.
+// of token 16 rb + lr, read from K in LDS with the fragment addresses of the
+// state waves.
 struct FragRegs {
   uint4 kf[4][4];
 };
 
-__device__ __forceinline__ void load_frags(FragRegs& R, const Seq& sq, int64_t c, int lane) {
-  const uint32_t row = (uint32_t)(sq.dk * 2);
-  const uint32_t lane_off = (uint32_t)(lane & 15) * row + (uint32_t)((lane >> 4) * 16);
-  const uint32_t base = (uint32_t)(c * C) * row;
+template <bool GLA>
+__device__ __forceinline__ void read_frags(FragRegs& R, const StateAddr& A, int64_t c) {
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int pp = 0; pp < 4; ++pp) {
+    const lptr b = lane_base(k_buf<GLA>(c), A.frag[pp]);
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp)
-      R.kf[rb][pp] = 32 * pp < sq.dk ? buf_ld16s(sq.k, lane_off, base + rb * 16 * row + pp * 64)
-                                     : make_uint4(0u, 0u, 0u, 0u);
+    for (int rb = 0; rb < 4; ++rb) R.kf[rb][pp] = ld3<uint4>(b, rb * 4096);
+  }
 }
 
 // Gate tables of chunk c (alpha, beta of token `lane` as loaded, 0 past the
@@ -796,17 +824,19 @@ __device__ __forceinline__ void build_l(Smem& sm, const FragRegs& R, int64_t c, 
 
 // ============================================================ loader wave
 // In period p the loader builds the gate tables of chunk p+3 (gates loaded one
-// period earlier), then loads the gates of chunk p+4 and V, K, Q of chunk p+1,
-// in that order, and ends the period once V, K, Q of chunk p+1 are in LDS
-// (the prefetch wave has pulled their lines into L2 two periods earlier).
-// The gate tables of chunk 0 come before the first period.
-// Gate tables of chunk 0, and the gates of chunk 1: in registers for the
-// delta rule, landed in lds_gst by LDS-DMA for GLA.
+// period earlier) and loads the gates of chunk p+4, V and Q of chunk p+1 and
+// K of chunk p+3 (GLA: V of p+1, K and Q of p+2), and ends the period once
+// they are in LDS (the prefetch wave has pulled their lines into L2 two
+// periods earlier).
+// Before the first period: the gate tables of chunk 0, and the gates of
+// chunk 1 (in registers for the delta rule, landed in lds_gst by LDS-DMA for
+// GLA); for the delta rule also K of chunk 0.
 template <bool GLA>
-__device__ __forceinline__ void loader_prologue(Smem& sm, const Seq& sq, int64_t nch, float& ga, float& gb,
-                                                int lane) {
+__device__ __forceinline__ void loader_prologue(Smem& sm, const Seq& sq, const DmaAddr& D, int64_t nch, float& ga,
+                                                float& gb, int lane) {
   ga = gb = 0.f;
   if (nch > 0) {
+    if constexpr (!GLA) dma_rows(sq.k, k_buf<GLA>(0), sq, D, 0);
     build_gates(sm, buf_ldf(sq.a, (uint32_t)(lane * 4)), buf_ldf(sq.b, (uint32_t)(lane * 4)), 0, sq.T, lane);
     if constexpr (GLA) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.a, (lds_void*)&lds_gst[0][0], 4, lane * 4, C * 4, 0, 0);
@@ -819,11 +849,9 @@ __device__ __forceinline__ void loader_prologue(Smem& sm, const Seq& sq, int64_t
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no load is pending when the loop starts
 }
 
-// One period of the loader.  Every global load of the period is issued first
-// (the gates of chunk p+4, V of chunk p+1, K and Q of chunk p + KQ_AHEAD),
+// One period of the loader.  Every global load of the period is issued first,
 // and the gate tables of chunk p+3 are built while they fly, from the gates
-// loaded one period earlier.  The wait at the end makes K, Q, V of chunk p+1
-// and the gates of chunk p+4 complete.
+// loaded one period earlier.
 //   delta rule: the gates go to registers and the wait is vmcnt(0).
 //   GLA: K, Q are two chunks ahead and the wait leaves this period's K, Q
 //   loads in flight (vmcnt(32)).  The gates then go through LDS (lds_gst) by
@@ -840,8 +868,11 @@ __device__ __forceinline__ void loader_period(Smem& sm, const Seq& sq, const Dma
       na = buf_ldf(sq.a, t4);
       nb = buf_ldf(sq.b, t4);
     }
-    if (p + 1 >= 0 && p + 1 < nch) dma_v(sq, D, p + 1, DV);
-    if (p + KA >= 0 && p + KA < nch) dma_kq<GLA>(sq, D, p + KA);
+    if (p + 1 >= 0 && p + 1 < nch) {
+      dma_v(sq, D, p + 1, DV);
+      dma_rows(sq.q, q_buf<GLA>(p + 1), sq, D, p + 1);
+    }
+    if (p + 3 >= 0 && p + 3 < nch) dma_rows(sq.k, k_buf<GLA>(p + 3), sq, D, p + 3);
     if (p + 3 < nch) build_gates(sm, ga, gb, p + 3, sq.T, lane);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     ga = na;
@@ -1127,18 +1158,20 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
       lds_barrier();
     }
   } else if (wave == W_L) {
+    const StateAddr A = state_addr(lane, 0, DV);
     FragRegs R;
-    if (!GLA && nch > 0) load_frags(R, sq, 0, lane);
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
-      if (!GLA && p + 2 < nch) build_l(sm, R, p + 2, lane);
-      if (!GLA && p + 3 < nch) load_frags(R, sq, p + 3, lane);
+      if (!GLA && p + 2 < nch) {
+        read_frags<GLA>(R, A, p + 2);
+        build_l(sm, R, p + 2, lane);
+      }
       lds_barrier();
     }
   } else if (wave == W_LOADER) {
     const DmaAddr D = dma_addr(lane, DV, dk);
     float ga, gb;
-    loader_prologue<GLA>(sm, sq, nch, ga, gb, lane);
+    loader_prologue<GLA>(sm, sq, D, nch, ga, gb, lane);
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
       loader_period<GLA>(sm, sq, D, p, nch, DV, ga, gb, lane);
@@ -1161,8 +1194,16 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     // the L2 prefetch, issued by a wave that never waits for it
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
-      constexpr int PA = PREFETCH_AHEAD + KQ_AHEAD<GLA> - 1;
-      if (p + PA < nch) prefetch_chunk(sq, p + PA, slice, DV, lane);
+      if constexpr (GLA) {
+        constexpr int PA = PREFETCH_AHEAD + KQ_AHEAD<GLA> - 1;
+        if (p + PA < nch) {
+          prefetch_keys(sq, p + PA, slice, lane);
+          prefetch_rest(sq, p + PA, slice, DV, lane);
+        }
+      } else {
+        if (p + 5 < nch) prefetch_keys(sq, p + 5, slice, lane);
+        if (p + 3 < nch) prefetch_rest(sq, p + 3, slice, DV, lane);
+      }
       lds_barrier_keep_dma();
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no LDS-DMA write outlives the workgroup
