@@ -84,6 +84,17 @@ def test_chunk_fwd_small(case):
     check_against_oracle(x, dtype, label="small")
 
 
+# The bf16 kernel keeps K of four consecutive chunks in LDS (loaded three
+# chunks ahead), Q and V of two; every chunk count from 1 to 9, with a ragged
+# last chunk, runs each buffer through its first uses and its wrap-around.
+@pytest.mark.parametrize("nch", list(range(1, 10)))
+@pytest.mark.parametrize("d", [64, 128])
+def test_chunk_counts_around_buffer_depth(nch, d):
+    T = 64 * nch - 7
+    x = inputs.make_fwd_inputs(1, 2, T, d, "bf16", seed=900 + 10 * nch + d, init_state=True)
+    check_against_oracle(x, "bf16", label="chunks=%d" % nch)
+
+
 def _cfg_inputs(name):
     c = dict(inputs.CONFIGS[name])
     C = c.pop("C")
