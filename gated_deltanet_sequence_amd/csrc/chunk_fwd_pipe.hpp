@@ -32,7 +32,8 @@
 //                       accumulators for the whole sequence.
 //   wave 2 (P)          builds P of chunk p.
 //   wave 3 (L)          builds L of chunk p+2 from its keys in LDS; it issues
-//                       no global loads.
+//                       no global loads.  (Without the delta rule it moves Q
+//                       instead, see the kernel.)
 //   wave 4 (prefetch)   touches the cache lines of chunk p+3 (the key lines
 //                       of chunk p+5) so that later loads hit L2, and never
 //                       waits for those loads.
@@ -77,10 +78,12 @@ constexpr int LDR = 20;   // row stride (floats) of the fp32 diagonal blocks of 
 
 enum { G_BETA = 0, G_ER = 1, G_EG = 2, G_EL = 3, G_LOG = 4, G_N = 5 };
 
-// How far ahead the loader fetches K and Q without the delta rule (GLA): the
-// period is then short enough that the loader's DMA round trip becomes the
-// critical path, so K, Q are loaded two chunks ahead and each load has two
-// periods to land (measured 9 % faster than one chunk ahead).  With the delta
+// How far ahead K and Q are fetched without the delta rule (GLA): the period
+// is then short enough that the loader's DMA round trip becomes the critical
+// path, so K, Q are loaded two chunks ahead and each load has two periods to
+// land (measured 9 % faster than one chunk ahead).  The otherwise idle L wave
+// moves Q there, so that the loader's own loads per period shrink (one wave
+// moves only so many bytes per clock; 2.4 % faster).  With the delta
 // rule, Q is loaded one chunk ahead and K three (see k_buf below).
 template <bool GLA> constexpr int KQ_AHEAD = GLA ? 2 : 1;
 
@@ -585,9 +588,7 @@ __device__ __forceinline__ DmaAddr dma_addr(int lane, int DV, int dk) {
   A.v = (uint32_t)((lane >> 2) * DV * 2 + (((lane & 3) ^ (2 * ((lane >> 4) & 1))) << 4));
   return A;
 }
-// dma_rows: 16 rows-of-K (or Q) loads of chunk c into dst; dma_kq: K and Q
-// of chunk c (KQ_LOADS loads) into k_buf(c), q_buf(c).
-constexpr int KQ_LOADS = 32;
+// K (or Q) of chunk c into dst: 16 LDS-DMA loads.
 __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t src, bf16_t* dst, const Seq& sq, const DmaAddr& A,
                                          int64_t c) {
   const uint32_t row = (uint32_t)(sq.dk * 2), kq0 = (uint32_t)(c * C) * row;
@@ -595,19 +596,6 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t src, bf16_t* dst
   for (int it = 0; it < 16; ++it)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)&dst[it * 512], 16, A.kq[it & 3],
                                              (int)(kq0 + it * 4 * row), 0, 0);
-}
-template <bool GLA>
-__device__ __forceinline__ void dma_kq(const Seq& sq, const DmaAddr& A, int64_t c) {
-  bf16_t* kb = k_buf<GLA>(c);
-  bf16_t* qb = q_buf<GLA>(c);
-  const uint32_t row = (uint32_t)(sq.dk * 2), kq0 = (uint32_t)(c * C) * row;
-#pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.k, (lds_void*)&kb[it * 512], 16, A.kq[it & 3],
-                                             (int)(kq0 + it * 4 * row), 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.q, (lds_void*)&qb[it * 512], 16, A.kq[it & 3],
-                                             (int)(kq0 + it * 4 * row), 0, 0);
-  }
 }
 // V of chunk c (4 loads) into buffer c % 2.
 __device__ __forceinline__ void dma_v(const Seq& sq, const DmaAddr& A, int64_t c, int DV) {
@@ -853,10 +841,11 @@ __device__ __forceinline__ void loader_prologue(Smem& sm, const Seq& sq, const D
 // and the gate tables of chunk p+3 are built while they fly, from the gates
 // loaded one period earlier.
 //   delta rule: the gates go to registers and the wait is vmcnt(0).
-//   GLA: K, Q are two chunks ahead and the wait leaves this period's K, Q
-//   loads in flight (vmcnt(32)).  The gates then go through LDS (lds_gst) by
-//   LDS-DMA: in registers, the compiler would wait for every load before
-//   their use, since its count ignores LDS-DMA loads.
+//   GLA: K is two chunks ahead (Q too, moved by the L wave) and the wait
+//   leaves this period's 16 K loads in flight (vmcnt(16)).  The gates then
+//   go through LDS (lds_gst) by LDS-DMA: in registers, the compiler would
+//   wait for every load before their use, since its count ignores LDS-DMA
+//   loads.
 template <bool GLA>
 __device__ __forceinline__ void loader_period(Smem& sm, const Seq& sq, const DmaAddr& D, int64_t p, int64_t nch,
                                               int DV, float& ga, float& gb, int lane) {
@@ -880,9 +869,9 @@ __device__ __forceinline__ void loader_period(Smem& sm, const Seq& sq, const Dma
   } else {
     if (p + 3 < nch) {
       // The gates that landed one period earlier are complete: that period
-      // ended with a wait for every load but its last KQ_LOADS.  The read is
+      // ended with a wait for every load but its last 16 (the K loads).  The read is
       // asm because the compiler's own wait before a read of an LDS-DMA
-      // target would be vmcnt(0), i.e. also for the K, Q loads in flight.  It
+      // target would be vmcnt(0), i.e. also for the K loads in flight.  It
       // completes (lgkmcnt(0)) before the DMA below rewrites the gates.
       const uint32_t ga_addr = (uint32_t)(uintptr_t)(lds_void*)&lds_gst[0][lane];
       asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %2 offset:%3\n\ts_waitcnt lgkmcnt(0)"
@@ -895,11 +884,11 @@ __device__ __forceinline__ void loader_period(Smem& sm, const Seq& sq, const Dma
     }
     if (p + 1 >= 0 && p + 1 < nch) dma_v(sq, D, p + 1, DV);
     const bool kq_next = p + KA >= 0 && p + KA < nch;
-    if (kq_next) dma_kq<GLA>(sq, D, p + KA);
+    if (kq_next) dma_rows(sq.k, k_buf<GLA>(p + KA), sq, D, p + KA);  // Q: the L wave
     if (p + 3 < nch) build_gates(sm, ga, gb, p + 3, sq.T, lane);
-    static_assert(KA == 2 && KQ_LOADS == 32, "the wait below encodes vmcnt(32)");
+    static_assert(KA == 2, "the wait below leaves this period's 16 K loads in flight");
     if (kq_next)
-      __builtin_amdgcn_s_waitcnt(0x8f70);  // vmcnt(32): vmcnt bits [15:14] = 2, [3:0] = 0
+      __builtin_amdgcn_s_waitcnt(0x4f70);  // vmcnt(16): vmcnt bits [15:14] = 1, [3:0] = 0
     else
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   }
@@ -1157,6 +1146,22 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
       if (p >= 0 && p < nch) build_p<GLA>(sm, A, p, lane);
       lds_barrier();
     }
+  } else if (GLA && wave == W_L) {
+    // without the delta rule the L wave moves Q, two chunks ahead, and keeps
+    // each period's 16 loads in flight across the barrier
+    const DmaAddr D = dma_addr(lane, DV, dk);
+    lds_barrier();
+    for (int64_t p = -2; p <= nch; ++p) {
+      const bool q_next = p + 2 >= 0 && p + 2 < nch;
+      if (q_next) {
+        dma_rows(sq.q, q_buf<GLA>(p + 2), sq, D, p + 2);
+        __builtin_amdgcn_s_waitcnt(0x4f70);  // vmcnt(16)
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+      }
+      lds_barrier_keep_dma();
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);
   } else if (wave == W_L) {
     const StateAddr A = state_addr(lane, 0, DV);
     FragRegs R;
@@ -1176,7 +1181,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     for (int64_t p = -2; p <= nch; ++p) {
       loader_period<GLA>(sm, sq, D, p, nch, DV, ga, gb, lane);
       if constexpr (GLA)
-        lds_barrier_keep_dma();  // this period's K, Q loads stay in flight
+        lds_barrier_keep_dma();  // this period's K loads stay in flight
       else
         lds_barrier();
     }
