@@ -1186,6 +1186,10 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
         lds_barrier();
     }
   } else if (wave == W_INV) {
+    // The inverse is the longest role of a period and shares its SIMD with the
+    // L wave, which has slack: it takes the higher issue priority (about 1 %
+    // faster, alternating on one GPU).
+    __builtin_amdgcn_s_setprio(3);
     // column lr of the identity: the start of the forward substitution
     float xinit[16];
 #pragma unroll
