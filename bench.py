@@ -6,7 +6,8 @@ d_k=d_v=128, C=64, bf16 q/k/v, fp32 gates, zero initial state, fp32 final
 state), inputs resident in HBM before the timed region.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--no-decode] [--no-long] [--no-gla] [--no-routes] [--pmc-pass]
+                  [--no-decode] [--no-long] [--no-loop] [--no-gla] [--no-routes]
+                  [--pmc-pass]
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   (writes the HBM-traffic
                   summary under profiles/ from two rocprofv3 --pmc runs)
 
@@ -139,33 +140,36 @@ def time_chunk(torch, xd, steps, warmup, settle_ms=SETTLE_MS):
     return wall, kms, o, sT
 
 
-LONG = dict(B=1, H=16, T=131072, d=128, seed=4)
+LONG = dict(B=1, H=16, T=131072, d=128, seed=4, init_state=True,
+            workload="long context: B=1, H=16, T=131072, d_k=d_v=128, C=64, bf16 q/k/v, "
+                     "fp32 gates, S0 ~ N(0,0.1)")
+LOOP = dict(B=1, H=4, T=8192, d=64, seed=2, init_state=False,
+            workload="the pages' loop case: B=1, H=4, T=8192, d_k=d_v=64, C=64, bf16 q/k/v, "
+                     "fp32 gates, zero S0")
 
 
-def time_long(torch, dev, launches=10):
-    """The long-context workload (16 sequences of 131072 tokens, S0 ~ N(0,0.1))
-    through the sequence-split entry point and, for comparison, the plain
-    one; mean of `launches` back-to-back launches between two events, each
-    after settling the clocks on that entry point."""
+def time_split(torch, dev, cfg, launches=10):
+    """A few-sequence workload through the sequence-split entry point and, for
+    comparison, the plain one; mean of `launches` back-to-back launches
+    between two events, each after settling the clocks on that entry point."""
     from gated_deltanet_sequence_amd import inputs
     from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd, gdn_chunk_fwd_split,
                                                      gdn_chunk_fwd_split_workspace)
-    B, H, T, d = LONG["B"], LONG["H"], LONG["T"], LONG["d"]
-    x = inputs.make_fwd_inputs(B, H, T, d, "bf16", seed=LONG["seed"], init_state=True)
+    B, H, T, d = cfg["B"], cfg["H"], cfg["T"], cfg["d"]
+    x = inputs.make_fwd_inputs(B, H, T, d, "bf16", seed=cfg["seed"], init_state=cfg["init_state"])
     xd = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
     o = torch.empty_like(xd["v"])
-    sT = torch.empty_like(xd["s0"])
+    sT = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
     need = gdn_chunk_fwd_split_workspace(B, H, T, d, d, 64, torch.bfloat16)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    args = (xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"], 64)
+    args = (xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd.get("s0"), 64)
     runs = {
         "split": lambda: gdn_chunk_fwd_split(*args, o=o, final_state=sT, workspace=ws, stream=stream),
         "plain": lambda: gdn_chunk_fwd(*args, o=o, final_state=sT, stream=stream),
     }
-    alg = B * H * T * (3 * d * 2 + 8 + d * 2) + 2 * B * H * d * d * 4
-    res = {"workload": "long context: B=1, H=16, T=131072, d_k=d_v=128, C=64, bf16 q/k/v, "
-                       "fp32 gates, S0 ~ N(0,0.1)", "alg_bytes": alg, "split_workspace_bytes": need}
+    alg = B * H * T * (3 * d * 2 + 8 + d * 2) + (2 if cfg["init_state"] else 1) * B * H * d * d * 4
+    res = {"workload": cfg["workload"], "alg_bytes": alg, "split_workspace_bytes": need}
     for name, f in runs.items():
         settle_clocks(torch, f)
         e0 = torch.cuda.Event(enable_timing=True)
@@ -397,6 +401,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the long-context (sequence-split) report")
+    ap.add_argument("--no-loop", action="store_true",
+                    help="skip the loop-case (sequence-split) report")
     ap.add_argument("--no-gla", action="store_true",
                     help="skip the gated-linear-attention report")
     ap.add_argument("--no-routes", action="store_true",
@@ -474,7 +480,9 @@ def main():
     if not args.no_decode:
         res["decode"] = time_decode(torch, dev)
     if not args.no_long:
-        res["long_context"] = time_long(torch, dev)
+        res["long_context"] = time_split(torch, dev, LONG)
+    if not args.no_loop:
+        res["loop_case"] = time_split(torch, dev, LOOP, launches=100)
     if not args.no_gla:
         res["gla"] = time_gla(torch, xd)
     if not args.no_routes:

@@ -147,8 +147,8 @@ int launch_scan(const void* q, const void* k, const void* v, const float* alpha,
                        vv, alpha, beta, oo, sT, (int)SCAN_AGG, (int)nseq, G, T, L, ws);
     if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
   }
-  hipLaunchKernelGGL(gdn::split::split_combine_kernel, dim3((unsigned)(nseq * (D / gdn::split::ROWS))),
-                     dim3(gdn::split::THREADS), 0, stream, s0, ws, (int)nseq, G, D);
+  hipLaunchKernelGGL(gdn::split::split_combine_kernel<D>, dim3((unsigned)(nseq * (D / gdn::split::ROWS))),
+                     dim3(gdn::split::threads_for<D>()), 0, stream, s0, ws, (int)nseq, G);
   if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
   const int64_t nb = scan_blocks(SCAN_OUT, (int)nseq, G, D);
   if (nb > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
@@ -379,8 +379,12 @@ int gdn_chunk_fwd_split(const void* q, const void* k, const void* v, const float
   int r = launch_chunk_pipe(q, k, v, alpha, beta, nullptr, o, nullptr, cm, dk, dv, stream);
   if (r != GDN_OK) return r;
   // 2: the start state of every segment
-  hipLaunchKernelGGL(gdn::split::split_combine_kernel, dim3((unsigned)(nchain * (dk / gdn::split::ROWS))),
-                     dim3(gdn::split::THREADS), 0, stream, initial_state, cm.ws, (int)nchain, G, (int)dk);
+  if (dk == 128)
+    hipLaunchKernelGGL(gdn::split::split_combine_kernel<128>, dim3((unsigned)(nchain * (128 / gdn::split::ROWS))),
+                       dim3(gdn::split::threads_for<128>()), 0, stream, initial_state, cm.ws, (int)nchain, G);
+  else
+    hipLaunchKernelGGL(gdn::split::split_combine_kernel<64>, dim3((unsigned)(nchain * (64 / gdn::split::ROWS))),
+                       dim3(gdn::split::threads_for<64>()), 0, stream, initial_state, cm.ws, (int)nchain, G);
   if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
   // 3: every segment from its start state, with output
   cm.mode = gdn::pipe::MAP_SPLIT_C;

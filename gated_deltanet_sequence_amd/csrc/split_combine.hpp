@@ -9,6 +9,16 @@
 // Each row of a state evolves alone (the transition multiplies from the
 // right), so a workgroup owns ROWS rows of one sequence and walks all its
 // segments without synchronising with other workgroups.  fp32 throughout.
+//
+// The walk is a chain of G-1 dependent steps, so the time of one step is
+// what counts.  A step is a small dense product, [ROWS x D] = [ROWS x D]
+// [D x D] + [ROWS x D], done with the fp32 MFMA v_mfma_f32_16x16x4f32: one
+// wave per 16-column tile of the result, D / 4 MFMAs per step.  M_g is
+// staged in LDS with coalesced 16-byte loads (row stride padded by 16 floats,
+// so that the four k rows a B fragment spans fall in different banks), and
+// the next segments' M and tilde are loaded into registers several steps
+// ahead.  The rows' current state stays in LDS transposed (prevT[k][i]), so
+// that the A fragment of every MFMA is one contiguous 256-byte read.
 #pragma once
 
 #include "gdn_common.hpp"
@@ -16,52 +26,132 @@
 namespace gdn {
 namespace split {
 
-constexpr int ROWS = 8;
-constexpr int THREADS = 256;
+constexpr int ROWS = 16;  // rows of a state per workgroup: one MFMA tile
 
-// ws layout (floats, d x d per state): tilde[nseq * (G-1)], trans[nseq * (G-1)],
+// Threads of a workgroup: one wave per 16-column tile.
+template <int D>
+constexpr int threads_for() {
+  return 64 * (D / 16);
+}
+
+// Loads into registers the transition of segment `seg` (all of it, as 16-byte
+// vectors in a coalesced order) and this thread's four entries of its
+// zero-start state (rows r0 + ib .. r0 + ib + 3, column jj).
+template <int D>
+__device__ __forceinline__ void fetch_step(f32x4 (&mr)[D * D / 4 / threads_for<D>()], f32x4& tr,
+                                           const float* trans, const float* tilde, int64_t seg, int r0, int t,
+                                           int ib, int jj) {
+  constexpr int64_t DD = (int64_t)D * D;
+  constexpr int NT = threads_for<D>();
+  const f32x4* M = reinterpret_cast<const f32x4*>(trans + seg * DD);
+#pragma unroll
+  for (int v = 0; v < D * D / 4 / NT; ++v) mr[v] = M[t + NT * v];
+  const float* Tl = tilde + seg * DD + (int64_t)(r0 + ib) * D + jj;
+  tr = f32x4{Tl[0], Tl[D], Tl[2 * D], Tl[3 * D]};
+}
+
+// One step of the walk: start_{g+1} = start_g M_g + tilde_g for this
+// workgroup's rows, with M_g and tilde_g taken from the registers (mr, tr),
+// which are then refilled with segment `next` so that its loads overlap the
+// steps in between.  The refill is unconditional (past the last segment the
+// caller passes the last one again): a conditional one leaves the compiler
+// merging register sets, which makes it wait for every load in flight.
+template <int D>
+__device__ __forceinline__ void combine_step(f32x4 (&mr)[D * D / 4 / threads_for<D>()], f32x4& tr, float* Ms,
+                                             float* prevT, float* out, const float* trans, const float* tilde,
+                                             int64_t next, int r0, int t, int ib, int jj) {
+  constexpr int NT = threads_for<D>();
+  constexpr int NV = D * D / 4 / NT;
+  constexpr int LD = D + 16;
+  const int lane = t % 64, ct = t / 64;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int e = 4 * (t + NT * v);
+    *reinterpret_cast<f32x4*>(&Ms[(e / D) * LD + e % D]) = mr[v];
+  }
+  f32x4 acc = tr;
+  __syncthreads();  // M_g and prevT (start_g) in LDS
+  // A[i][kk] = start_g[i][4 kb + kk] (i = lane % 16, kk = lane / 16),
+  // B[kk][j] = M_g[4 kb + kk][16 ct + j] (j = lane % 16)
+  const float* pa = prevT + lane;
+  const float* pb = Ms + (lane / 16) * LD + 16 * ct + lane % 16;
+#pragma unroll
+  for (int kb = 0; kb < D / 4; ++kb)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[64 * kb], pb[4 * kb * LD], acc, 0, 0, 0);
+  // refill once mr and tr are dead, so that the loads land in place
+  fetch_step<D>(mr, tr, trans, tilde, next, r0, t, ib, jj);
+  __syncthreads();  // every read of M_g and prevT done
+  // acc[r] = start_{g+1}[ib + r][jj]
+  *reinterpret_cast<f32x4*>(&prevT[jj * 16 + ib]) = acc;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) out[(ib + r) * D + jj] = acc[r];
+}
+
+// ws layout (floats, D x D per state): tilde[nseq * (G-1)], trans[nseq * (G-1)],
 // start[nseq * G] (start[seq * G + g]); index seq * (G-1) + g for the first two.
-__global__ __launch_bounds__(THREADS) void split_combine_kernel(const float* __restrict__ s0,
-                                                               float* __restrict__ ws, int nseq,
-                                                               int G, int d) {
-  __shared__ float prev[ROWS][128];
-  const int blocks_per_seq = d / ROWS;
+// Grid: nseq * (D / ROWS) workgroups of threads_for<D>() threads.  DEPTH
+// register sets keep the loads of the next DEPTH segments in flight.
+template <int D>
+__global__ __launch_bounds__(threads_for<D>()) void split_combine_kernel(const float* __restrict__ s0,
+                                                                        float* __restrict__ ws, int nseq, int G) {
+  static_assert(D == 64 || D == 128, "state width");
+  constexpr int NT = threads_for<D>();
+  constexpr int NV = D * D / 4 / NT;  // 16-byte vectors of M per thread: 4 (D = 64) or 8 (D = 128)
+  constexpr int DEPTH = D == 128 ? 3 : 4;
+  constexpr int64_t DD = (int64_t)D * D;
+  __shared__ __attribute__((aligned(16))) float Ms[D * (D + 16)];
+  __shared__ __attribute__((aligned(16))) float prevT[D * ROWS];
+
+  constexpr int blocks_per_seq = D / ROWS;
   const int seq = blockIdx.x / blocks_per_seq;
   const int r0 = (blockIdx.x % blocks_per_seq) * ROWS;
   if (seq >= nseq) return;
-  const int64_t dd = (int64_t)d * d, per = (int64_t)nseq * (G - 1);
+  const int t = threadIdx.x;
+  // this thread's entries of a result tile: rows ib .. ib + 3 (of the
+  // workgroup's 16), column jj (the MFMA accumulator layout)
+  const int lane = t % 64;
+  const int ib = 4 * (lane / 16), jj = 16 * (t / 64) + lane % 16;
+  const int64_t per = (int64_t)nseq * (G - 1);
   const float* tilde = ws;
-  const float* trans = ws + per * dd;
-  float* start = ws + 2 * per * dd;
-  const int nout = ROWS * d / THREADS;  // outputs per thread: 4 (d = 128) or 2 (d = 64)
+  const float* trans = ws + per * DD;
+  float* start = ws + 2 * per * DD;
+  const int64_t seg0 = (int64_t)seq * (G - 1);
+
+  f32x4 mr[DEPTH][NV];
+  f32x4 tr[DEPTH];
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s)
+    if (G > 1) fetch_step<D>(mr[s], tr[s], trans, tilde, seg0 + (s + 1 < G ? s : G - 2), r0, t, ib, jj);
 
   // start_0 = S_0 (a copy, so that the caller's final state may alias S_0)
-  for (int e = threadIdx.x; e < ROWS * d; e += THREADS) {
-    const int i = e / d, j = e % d;
-    const float x = s0 ? s0[(int64_t)seq * dd + (int64_t)(r0 + i) * d + j] : 0.f;
-    prev[i][j] = x;
-    start[((int64_t)seq * G) * dd + (int64_t)(r0 + i) * d + j] = x;
+  {
+    float* out = start + ((int64_t)seq * G) * DD + (int64_t)r0 * D;
+    const float* in = s0 ? s0 + (int64_t)seq * DD + (int64_t)r0 * D : nullptr;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (in) x = f32x4{in[ib * D + jj], in[(ib + 1) * D + jj], in[(ib + 2) * D + jj], in[(ib + 3) * D + jj]};
+    *reinterpret_cast<f32x4*>(&prevT[jj * 16 + ib]) = x;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[(ib + r) * D + jj] = x[r];
   }
-  __syncthreads();
-  for (int g = 0; g + 1 < G; ++g) {
-    const int64_t idx = (int64_t)seq * (G - 1) + g;
-    const float* M = trans + idx * dd;
-    const float* Tl = tilde + idx * dd;
-    float* out = start + ((int64_t)seq * G + g + 1) * dd;
-    float acc[4];
-    for (int u = 0; u < nout; ++u) {
-      const int e = threadIdx.x + THREADS * u, i = e / d, j = e % d;
-      float a = Tl[(int64_t)(r0 + i) * d + j];
-      for (int kk = 0; kk < d; ++kk) a = fmaf(prev[i][kk], M[(int64_t)kk * d + j], a);
-      acc[u] = a;
+  // Full groups of DEPTH steps with no branch between them (a branch would
+  // make the compiler wait for loads of later steps too), then the rest.
+  int g0 = 0;
+  for (; g0 + DEPTH < G; g0 += DEPTH) {
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) {
+      const int g = g0 + s;
+      float* out = start + ((int64_t)seq * G + g + 1) * DD + (int64_t)r0 * D;
+      const int64_t next = seg0 + (g + DEPTH + 1 < G ? g + DEPTH : G - 2);
+      combine_step<D>(mr[s], tr[s], Ms, prevT, out, trans, tilde, next, r0, t, ib, jj);
     }
-    __syncthreads();
-    for (int u = 0; u < nout; ++u) {
-      const int e = threadIdx.x + THREADS * u, i = e / d, j = e % d;
-      prev[i][j] = acc[u];
-      out[(int64_t)(r0 + i) * d + j] = acc[u];
+  }
+#pragma unroll
+  for (int s = 0; s + 1 < DEPTH; ++s) {
+    const int g = g0 + s;
+    if (g + 1 < G) {
+      float* out = start + ((int64_t)seq * G + g + 1) * DD + (int64_t)r0 * D;
+      combine_step<D>(mr[s], tr[s], Ms, prevT, out, trans, tilde, seg0 + G - 2, r0, t, ib, jj);
     }
-    __syncthreads();
   }
 }
 
