@@ -367,11 +367,11 @@ def summarize_pmc(fetch_dir, write_dir):
     lines = [
         "# HBM traffic of chunk_fwd_pipe_kernel, main workload (B=4,H=16,T=8192,d=128,C=64, bf16)",
         "# from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch):",
-        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -- python3 bench.py --pmc-pass",
-        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -- python3 bench.py --pmc-pass",
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -- python3 bench.py --pmc-pass" % fetch_dir,
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -- python3 bench.py --pmc-pass" % write_dir,
         "# (each pass runs the kernel for %.0f ms to settle the clocks, then %d more launches;" % (SETTLE_MS, PMC_LAUNCHES),
         "#  the figures below average those last %d launches)" % PMC_LAUNCHES,
-        "#   python3 bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        "#   python3 bench.py --summarize-pmc %s %s" % (fetch_dir, write_dir),
         "# Each counter is scaled by (512 MiB / what it reads for a plain 512 MiB device copy",
         "# in the same run).",
         "copy_fetch_kib = %.1f" % out["FETCH_SIZE"][0],
@@ -416,8 +416,8 @@ def main():
         summarize_pmc(*args.summarize_pmc)
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(each (batch, head) sequence is independent; see DESIGN.md for how it would shard)",
+        print("bench.py runs on one GPU only: there is no multi-GPU path here "
+              "(each (batch, head) sequence is independent, so the work would shard by sequence)",
               file=sys.stderr)
         sys.exit(2)
 
