@@ -55,7 +55,7 @@ extern "C" {
 /* Return codes. */
 #define GDN_OK 0
 #define GDN_ERR_INVALID_ARG 1 /* NULL pointer, negative size, aliasing, bad dtype */
-#define GDN_ERR_UNSUPPORTED 2 /* shape/chunk size this build does not handle      */
+#define GDN_ERR_UNSUPPORTED 2 /* shape/chunk size the library does not handle     */
 #define GDN_ERR_ALIGNMENT 3   /* a tensor pointer is not 16-byte aligned           */
 #define GDN_ERR_HIP 4         /* the HIP runtime reported an error on launch       */
 
@@ -76,7 +76,7 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *   final_state    [B,H,dv,dk] fp32    OUT: S_T, or NULL to skip it.
  *                                      May alias initial_state (each workgroup
  *                                      reads its part of S_0 before writing).
- *   chunk_size     tokens per chunk; this build supports 64.  T need not be a
+ *   chunk_size     tokens per chunk; the library supports 64.  T need not be a
  *                  multiple: the missing tokens of the last chunk act as
  *                  identity maps (alpha = 1, beta = 0) and produce no output.
  *   dk, dv         64 or 128, dk == dv.
