@@ -91,7 +91,9 @@ gdn::pipe::ChainMap seq_map(int64_t nchain, int64_t T) {
 // the chunk size; the last one shorter), chosen so that its first launch
 // (2 (G-1) chains per sequence) still fits the device's CUs in one wave of
 // workgroups and every segment has at least MIN_SEG tokens.  G = 1 means no
-// split.
+// split.  So does a plan of two segments: its first and last launches then
+// run T/2 tokens each, one after the other, which is the plain pass's T
+// tokens plus the extra launches.  Three segments take 2T/3.
 constexpr int64_t MIN_SEG = 512;
 void split_plan(int64_t nseq, int64_t T, int64_t dv, int& G, int64_t& L) {
   G = 1;
@@ -105,11 +107,11 @@ void split_plan(int64_t nseq, int64_t T, int64_t dv, int& G, int64_t& L) {
   const int64_t ns = dv / gdn::pipe::DVS;
   int64_t g = 1 + ncu / (2 * nseq * ns);
   g = g < T / MIN_SEG ? g : T / MIN_SEG;
-  if (g < 2) return;
+  if (g < 3) return;
   const int64_t C = gdn::pipe::C;
   L = ((T + g - 1) / g + C - 1) / C * C;
   G = (int)((T + L - 1) / L);
-  if (G < 2) {
+  if (G < 3) {
     G = 1;
     L = T;
   }

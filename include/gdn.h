@@ -166,8 +166,9 @@ size_t gdn_scan_fwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64
  *      final_state.
  * The work is about (3G-2)/G times that of gdn_chunk_fwd, spread over G
  * times as many workgroups.  G is chosen from B*H, T and the device's CU
- * count; when it comes out as 1 (enough sequences, or T under 1024 tokens),
- * this is gdn_chunk_fwd itself and the workspace is not touched.  bf16 only
+ * count; when fewer than 3 segments would do (enough sequences, or T under
+ * 1536 tokens: two segments take as long as the plain pass), G is 1, this
+ * is gdn_chunk_fwd itself and the workspace is not touched.  bf16 only
  * (fp32 inputs always take gdn_chunk_fwd).
  *
  *   workspace        device memory owned by the caller, at least

@@ -65,7 +65,7 @@ def check_split_against_oracle(x, chains=None, label=""):
 SPLIT_CASES = [
     # B, H, T, d, initial state, gate
     (1, 2, 3000, 128, True, "default"),
-    (1, 1, 1100, 128, False, "default"),   # T/512 = 2 segments: the smallest split
+    (1, 1, 1600, 128, False, "default"),   # T/512 = 3 segments: the smallest split
     (1, 3, 2000, 64, False, "default"),
     (2, 1, 2500, 64, True, "slow"),        # long memory: the start states matter
     (1, 2, 4096, 128, True, "resets"),
