@@ -69,6 +69,11 @@ SPLIT_CASES = [
     (1, 3, 2000, 64, False, "default"),
     (2, 1, 2500, 64, True, "slow"),        # long memory: the start states matter
     (1, 2, 4096, 128, True, "resets"),
+    # the start-state walk runs whole groups of 4 (d = 64) or 3 (d = 128)
+    # segments, then the rest: one group and a rest of 3, groups and no rest
+    (1, 1, 4096, 64, True, "slow"),        # G = 8
+    (1, 1, 4608, 64, False, "default"),    # G = 9
+    (1, 1, 3584, 128, True, "slow"),       # G = 7
 ]
 
 
