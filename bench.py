@@ -218,21 +218,26 @@ ROUTES = dict(B=1, H=8, T=16384, d=64, seed=6)
 
 def time_routes(torch, dev, launches=5):
     """The pages' route comparison shape (d=64, 8 heads, 16384 tokens, batch
-    1, bf16): the chunked pass, the blocked parallel-scan route, and the
-    per-token route (one decode-step launch per token).  Mean times."""
+    1, bf16): the chunked pass (plain and sequence-split), the blocked
+    parallel-scan route, and the per-token route (one decode-step launch per
+    token).  Mean times."""
     from gated_deltanet_sequence_amd import inputs
-    from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd, gdn_recurrent_step, gdn_scan_fwd,
-                                                     gdn_scan_fwd_vecgate, gdn_scan_fwd_workspace)
+    from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd, gdn_chunk_fwd_split,
+                                                     gdn_chunk_fwd_split_workspace, gdn_recurrent_step,
+                                                     gdn_scan_fwd, gdn_scan_fwd_vecgate, gdn_scan_fwd_workspace)
     B, H, T, d = ROUTES["B"], ROUTES["H"], ROUTES["T"], ROUTES["d"]
     x = inputs.make_fwd_inputs(B, H, T, d, "bf16", seed=ROUTES["seed"])
     xd = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
     ws = torch.empty(gdn_scan_fwd_workspace(B, H, T, d, d, torch.bfloat16), dtype=torch.uint8, device=dev)
+    wsp = torch.empty(max(gdn_chunk_fwd_split_workspace(B, H, T, d, d, 64, torch.bfloat16), 16),
+                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     a = (xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None)
     # the same gates repeated over the key dimension, for the per-dimension-gate route
     av = xd["alpha"][..., None].expand(-1, -1, -1, d).contiguous()
     res = {"workload": "route comparison: B=1, H=8, T=16384, d_k=d_v=64, bf16 q/k/v, fp32 gates, zero S0"}
     for name, f in (("chunked", lambda: gdn_chunk_fwd(*a, 64, stream=stream)),
+                    ("chunked_split", lambda: gdn_chunk_fwd_split(*a, 64, workspace=wsp, stream=stream)),
                     ("scan", lambda: gdn_scan_fwd(*a, workspace=ws, stream=stream)),
                     ("scan_vecgate", lambda: gdn_scan_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"],
                                                                   None, workspace=ws, stream=stream))):
