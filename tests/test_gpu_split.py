@@ -131,3 +131,13 @@ def test_config_long_split_sampled():
                                init_state=c["init_state"])
     assert workspace(x) > 0
     check_split_against_oracle(x, chains=[0, 7, 15], label="long")
+
+
+def test_config_loop_split():
+    """The pages' loop case (B=1, H=4, T=8192, d=64) in full through the split
+    entry point, as timed by the benchmark (16 segments of 512 tokens)."""
+    c = dict(inputs.CONFIGS["loop"])
+    x = inputs.make_fwd_inputs(c["B"], c["H"], c["T"], c["d"], c["dtype"], seed=c["seed"],
+                               init_state=c["init_state"])
+    assert workspace(x) > 0
+    check_split_against_oracle(x, label="loop")
