@@ -141,3 +141,29 @@ def test_config_loop_split():
                                init_state=c["init_state"])
     assert workspace(x) > 0
     check_split_against_oracle(x, label="loop")
+
+
+def _plan(nseq, T, dv, ncu):
+    """The segment plan as documented for gdn_chunk_fwd_split: the most
+    segments whose first launch (2 (G-1) chains of dv/32 workgroups per
+    sequence) fits the CUs in one wave, each at least 512 tokens, in
+    multiples of 64 tokens; fewer than 3 segments means no split."""
+    g = min(1 + ncu // (2 * nseq * (dv // 32)), T // 512)
+    if g < 3:
+        return 1
+    L = ((T + g - 1) // g + 63) // 64 * 64
+    G = (T + L - 1) // L
+    return G if G >= 3 else 1
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1100, 128), (1, 1, 1535, 128), (1, 1, 1536, 128), (1, 1, 1600, 128),
+                                   (1, 16, 131072, 128), (1, 4, 8192, 64), (2, 16, 8192, 128), (4, 16, 8192, 128),
+                                   (1, 8, 16384, 64), (1, 2, 32768, 128)])
+def test_split_plan_and_workspace(shape):
+    B, H, T, d = shape
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    G = _plan(B * H, T, d, ncu)
+    want = 0 if G == 1 else (2 * (G - 1) + G) * B * H * d * d * 4
+    got = gdn_chunk_fwd_split_workspace(B, H, T, d, d, 64, torch.bfloat16)
+    _say("  plan", shape, "CUs", ncu, "G", G, "workspace", got)
+    assert got == want
