@@ -56,6 +56,35 @@ __host__ __device__ inline int64_t scan_blocks(int mode, int nseq, int G, int D)
   return (int64_t)nseq * per * (D / RPW);
 }
 
+// Loads one tile's inputs into registers, in their own element type (the
+// tile goes to LDS after the current one has been computed): keys, queries
+// and per-dimension gates (TILE x D, element e = tid + THREADS i), this
+// workgroup's value rows (TILE x RPW), scalar gates (threads below TILE).
+template <class E, int D, bool VEC>
+__device__ __forceinline__ void fetch_tile(E (&kreg)[TILE * D / THREADS], E (&qreg)[TILE * D / THREADS],
+                                           E (&vreg)[TILE * RPW / THREADS], float (&avreg)[VEC ? TILE * D / THREADS : 1],
+                                           float& areg, float& breg, const E* q, const E* k, const E* v,
+                                           const float* alpha, const float* beta, int64_t base, int64_t tt, int n,
+                                           int rg, int kind, int tid) {
+#pragma unroll
+  for (int i = 0; i < TILE * D / THREADS; ++i) {
+    const int e = tid + THREADS * i, t = e / D, c = e % D;
+    const bool in = t < n;
+    kreg[i] = in ? k[(base + tt + t) * D + c] : E(0);
+    qreg[i] = in ? q[(base + tt + t) * D + c] : E(0);
+    if constexpr (VEC) avreg[i] = in ? alpha[(base + tt + t) * D + c] : 1.f;
+  }
+#pragma unroll
+  for (int i = 0; i < TILE * RPW / THREADS; ++i) {
+    const int e = tid + THREADS * i, t = e / RPW, r = e % RPW;
+    vreg[i] = (t < n && kind != 1) ? v[(base + tt + t) * D + rg * RPW + r] : E(0);
+  }
+  if (tid < TILE) {
+    areg = (!VEC && tid < n) ? alpha[base + tt + tid] : 1.f;
+    breg = tid < n ? beta[base + tt + tid] : 0.f;
+  }
+}
+
 template <class E, int D, bool VEC = false>
 __global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
@@ -104,30 +133,40 @@ __global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
     for (int j = 0; j < CPT; ++j) s[j] = st[j];
   }
 
+  // Tiles are software-pipelined: the next tile's inputs are loaded into
+  // registers while the current one is computed, and go to LDS after it.
+  constexpr int NKQ = TILE * D / THREADS, NV = TILE * RPW / THREADS;
+  E kreg[NKQ], qreg[NKQ], vreg[NV];
+  float avreg[VEC ? NKQ : 1];
+  float areg = 1.f, breg = 0.f;
+  if (len > 0)
+    fetch_tile<E, D, VEC>(kreg, qreg, vreg, avreg, areg, breg, q, k, v, alpha, beta, base, 0,
+                          (int)(len < TILE ? len : TILE), rg, kind, tid);
   for (int64_t tt = 0; tt < len; tt += TILE) {
     const int n = (int)(len - tt < TILE ? len - tt : TILE);
     // stage the tile: keys, queries, this workgroup's value rows, gates
-    for (int e = tid; e < TILE * D; e += THREADS) {
-      const int t = e / D, c = e % D;
-      const bool in = t < n;
-      ks[t][c] = in ? Elem<E>::to_f32(k[(base + tt + t) * D + c]) : 0.f;
-      qs[t][c] = in ? Elem<E>::to_f32(q[(base + tt + t) * D + c]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < NKQ; ++i) {
+      const int e = tid + THREADS * i, t = e / D, c = e % D;
+      ks[t][c] = Elem<E>::to_f32(kreg[i]);
+      qs[t][c] = Elem<E>::to_f32(qreg[i]);
+      if constexpr (VEC) av[t][c] = avreg[i];
     }
-    for (int e = tid; e < TILE * RPW; e += THREADS) {
-      const int t = e / RPW, r = e % RPW;
-      vs[t][r] = (t < n && kind != 1) ? Elem<E>::to_f32(v[(base + tt + t) * D + rg * RPW + r]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + THREADS * i, t = e / RPW, r = e % RPW;
+      vs[t][r] = Elem<E>::to_f32(vreg[i]);
     }
     if (tid < TILE) {
-      as_[tid] = (!VEC && tid < n) ? alpha[base + tt + tid] : 1.f;
-      bs_[tid] = tid < n ? beta[base + tt + tid] : 0.f;
-    }
-    if constexpr (VEC) {
-      for (int e = tid; e < TILE * D; e += THREADS) {
-        const int t = e / D, c = e % D;
-        av[t][c] = t < n ? alpha[(base + tt + t) * D + c] : 1.f;
-      }
+      as_[tid] = areg;
+      bs_[tid] = breg;
     }
     __syncthreads();
+    if (tt + TILE < len) {
+      const int64_t nt = tt + TILE;
+      fetch_tile<E, D, VEC>(kreg, qreg, vreg, avreg, areg, breg, q, k, v, alpha, beta, base, nt,
+                            (int)(len - nt < TILE ? len - nt : TILE), rg, kind, tid);
+    }
     for (int t = 0; t < n; ++t) {
       const float a = as_[t], bt = bs_[t];
       float kr[CPT];
