@@ -1,0 +1,72 @@
+"""Host-side logic of bench.py, on the CPU: the algorithmic byte counts
+behind the roofline line, the rocprofv3 --pmc traffic summary and its
+source-hash guard, and the one-GPU guard of the command line."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+MiB = 1 << 20
+
+
+def test_algorithmic_bytes_of_the_main_workload():
+    # q, k, v: 3 x 128 MiB (bf16); alpha, beta: 2 x 2 MiB (fp32); o: 128 MiB
+    # (bf16); final state: 64 heads x 128 x 128 fp32 = 4 MiB; no initial state
+    assert bench.alg_bytes_main(4, 16, 8192, 128) == (3 * 128 + 2 * 2 + 128 + 4) * MiB
+
+
+def test_algorithmic_bytes_of_a_decode_step():
+    # the fp32 state is read and written once (2 x 256 MiB); per head q, k, v
+    # in (bf16), alpha, beta in (fp32) and o out (bf16)
+    heads = 256 * 16
+    per_head = 3 * 128 * 2 + 2 * 4 + 128 * 2
+    assert bench.alg_bytes_decode(256, 16, 128) == 2 * 256 * MiB + heads * per_head
+
+
+def _write_counters(d, counter, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "1_counter_collection.csv"), "w") as fh:
+        fh.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i, (name, value) in enumerate(rows):
+            fh.write('%d,"%s",%s,%r\n' % (i + 1, name, counter, value))
+
+
+def test_pmc_summary_scales_by_the_copy_and_averages_the_last_launches(tmp_path, monkeypatch):
+    out = tmp_path / "traffic.txt"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    copy_kib = 512 * 1024.0
+    # FETCH_SIZE reads half the copy's 512 MiB (scale 2); WRITE_SIZE reads it all
+    chunk = "void gdn::pipe::chunk_fwd_pipe_kernel<false>(...)"
+    early = [(chunk, 9.0e5)] * 5                      # before the clocks settle: ignored
+    last_fetch = [(chunk, 2.0e5 + 1000.0 * i) for i in range(bench.PMC_LAUNCHES)]
+    last_write = [(chunk, 1.3e5)] * bench.PMC_LAUNCHES
+    _write_counters(str(tmp_path / "f"), "FETCH_SIZE", [("copyBuffer", copy_kib / 2)] + early + last_fetch)
+    _write_counters(str(tmp_path / "w"), "WRITE_SIZE", [("copyBuffer", copy_kib)] + early + last_write)
+    bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"))
+    vals = {}
+    for line in out.read_text().splitlines():
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    mean_fetch = sum(v for _, v in last_fetch) / len(last_fetch)
+    assert float(vals["fetch_scale"]) == pytest.approx(2.0)
+    assert float(vals["write_scale"]) == pytest.approx(1.0)
+    assert int(vals["hbm_fetch_bytes"]) == int(mean_fetch * 1024 * 2)
+    assert int(vals["hbm_write_bytes"]) == int(1.3e5 * 1024)
+    assert vals["kernel_source_hash"] == bench.kernel_source_hash()
+    # the guard: the summary counts while the kernel sources are the ones it was taken on
+    assert bench.read_traffic() == int(vals["hbm_bytes_per_launch"])
+    out.write_text(out.read_text().replace(vals["kernel_source_hash"], "0" * 16))
+    assert bench.read_traffic() is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
