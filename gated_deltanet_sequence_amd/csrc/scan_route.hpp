@@ -56,32 +56,65 @@ __host__ __device__ inline int64_t scan_blocks(int mode, int nseq, int G, int D)
   return (int64_t)nseq * per * (D / RPW);
 }
 
-// Loads one tile's inputs into registers, in their own element type (the
-// tile goes to LDS after the current one has been computed): keys, queries
-// and per-dimension gates (TILE x D, element e = tid + THREADS i), this
-// workgroup's value rows (TILE x RPW), scalar gates (threads below TILE).
+// A tile's inputs are loaded in words of EPW elements: bf16 pairs as 32-bit
+// words (the compiler would otherwise pack two 16-bit loads into a register
+// as soon as they land, waiting for them), fp32 one element per word.
+template <class E> struct TileWord {
+  typedef float type;
+  static constexpr int EPW = 1;
+  static __device__ __forceinline__ float elem(float w, int) { return w; }
+};
+template <> struct TileWord<bf16_t> {
+  typedef uint32_t type;
+  static constexpr int EPW = 2;
+  static __device__ __forceinline__ float elem(uint32_t w, int h) {
+    return Elem<bf16_t>::to_f32((bf16_t)(w >> (16 * h)));
+  }
+};
+
+// Loads one tile's inputs into registers (the tile goes to LDS after the
+// current one has been computed): keys and queries (TILE x D, word
+// p = tid + THREADS i holds elements EPW p ..), per-dimension gates (element
+// tid + THREADS i), this workgroup's value rows (TILE x RPW, in words like
+// the keys), scalar gates (threads below TILE).  Every load is
+// unconditional: past the n tokens of a ragged tile it reads the last token
+// again, and the tile is masked when it goes to LDS.  (A conditional load
+// ends in a register copy that waits for it, which would serialize the
+// loads.)
 template <class E, int D, bool VEC>
-__device__ __forceinline__ void fetch_tile(E (&kreg)[TILE * D / THREADS], E (&qreg)[TILE * D / THREADS],
-                                           E (&vreg)[TILE * RPW / THREADS], float (&avreg)[VEC ? TILE * D / THREADS : 1],
-                                           float& areg, float& breg, const E* q, const E* k, const E* v,
-                                           const float* alpha, const float* beta, int64_t base, int64_t tt, int n,
-                                           int rg, int kind, int tid) {
+__device__ __forceinline__ void fetch_tile(typename TileWord<E>::type (&kreg)[TILE * D / THREADS / TileWord<E>::EPW],
+                                           typename TileWord<E>::type (&qreg)[TILE * D / THREADS / TileWord<E>::EPW],
+                                           typename TileWord<E>::type (&vreg)[TILE * RPW / THREADS / TileWord<E>::EPW],
+                                           float (&avreg)[VEC ? TILE * D / THREADS : 1], float& areg, float& breg,
+                                           const E* q, const E* k, const E* v, const float* alpha, const float* beta,
+                                           int64_t base, int64_t tt, int n, int rg, int tid) {
+  typedef typename TileWord<E>::type W;
+  constexpr int EPW = TileWord<E>::EPW;
 #pragma unroll
-  for (int i = 0; i < TILE * D / THREADS; ++i) {
-    const int e = tid + THREADS * i, t = e / D, c = e % D;
-    const bool in = t < n;
-    kreg[i] = in ? k[(base + tt + t) * D + c] : E(0);
-    qreg[i] = in ? q[(base + tt + t) * D + c] : E(0);
-    if constexpr (VEC) avreg[i] = in ? alpha[(base + tt + t) * D + c] : 1.f;
+  for (int i = 0; i < TILE * D / THREADS / EPW; ++i) {
+    const int e = EPW * (tid + THREADS * i), c = e % D;
+    const int t = e / D < n ? e / D : n - 1;
+    kreg[i] = *reinterpret_cast<const W*>(k + (base + tt + t) * D + c);
+    qreg[i] = *reinterpret_cast<const W*>(q + (base + tt + t) * D + c);
+  }
+  if constexpr (VEC) {
+#pragma unroll
+    for (int i = 0; i < TILE * D / THREADS; ++i) {
+      const int e = tid + THREADS * i, c = e % D;
+      const int t = e / D < n ? e / D : n - 1;
+      avreg[i] = alpha[(base + tt + t) * D + c];
+    }
   }
 #pragma unroll
-  for (int i = 0; i < TILE * RPW / THREADS; ++i) {
-    const int e = tid + THREADS * i, t = e / RPW, r = e % RPW;
-    vreg[i] = (t < n && kind != 1) ? v[(base + tt + t) * D + rg * RPW + r] : E(0);
+  for (int i = 0; i < TILE * RPW / THREADS / EPW; ++i) {
+    const int e = EPW * (tid + THREADS * i), r = e % RPW;
+    const int t = e / RPW < n ? e / RPW : n - 1;
+    vreg[i] = *reinterpret_cast<const W*>(v + (base + tt + t) * D + rg * RPW + r);
   }
   if (tid < TILE) {
-    areg = (!VEC && tid < n) ? alpha[base + tt + tid] : 1.f;
-    breg = tid < n ? beta[base + tt + tid] : 0.f;
+    const int t = tid < n ? tid : n - 1;
+    if constexpr (!VEC) areg = alpha[base + tt + t];
+    breg = beta[base + tt + t];
   }
 }
 
@@ -132,40 +165,57 @@ __global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
 #pragma unroll
     for (int j = 0; j < CPT; ++j) s[j] = st[j];
   }
+  // The start state is in registers before the tiles are: left pending, its
+  // loads would make the compiler wait for every load in flight (the next
+  // tile's too) at the first token of each tile.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
   // Tiles are software-pipelined: the next tile's inputs are loaded into
   // registers while the current one is computed, and go to LDS after it.
-  constexpr int NKQ = TILE * D / THREADS, NV = TILE * RPW / THREADS;
-  E kreg[NKQ], qreg[NKQ], vreg[NV];
-  float avreg[VEC ? NKQ : 1];
+  typedef typename TileWord<E>::type W;
+  constexpr int EPW = TileWord<E>::EPW;
+  constexpr int NKQ = TILE * D / THREADS / EPW, NV = TILE * RPW / THREADS / EPW;
+  W kreg[NKQ], qreg[NKQ], vreg[NV];
+  float avreg[VEC ? TILE * D / THREADS : 1];
   float areg = 1.f, breg = 0.f;
   if (len > 0)
     fetch_tile<E, D, VEC>(kreg, qreg, vreg, avreg, areg, breg, q, k, v, alpha, beta, base, 0,
-                          (int)(len < TILE ? len : TILE), rg, kind, tid);
+                          (int)(len < TILE ? len : TILE), rg, tid);
   for (int64_t tt = 0; tt < len; tt += TILE) {
     const int n = (int)(len - tt < TILE ? len - tt : TILE);
     // stage the tile: keys, queries, this workgroup's value rows, gates
 #pragma unroll
     for (int i = 0; i < NKQ; ++i) {
-      const int e = tid + THREADS * i, t = e / D, c = e % D;
-      ks[t][c] = Elem<E>::to_f32(kreg[i]);
-      qs[t][c] = Elem<E>::to_f32(qreg[i]);
-      if constexpr (VEC) av[t][c] = avreg[i];
+      const int e = EPW * (tid + THREADS * i), t = e / D, c = e % D;
+      const bool in = t < n;
+#pragma unroll
+      for (int h = 0; h < EPW; ++h) {
+        ks[t][c + h] = in ? TileWord<E>::elem(kreg[i], h) : 0.f;
+        qs[t][c + h] = in ? TileWord<E>::elem(qreg[i], h) : 0.f;
+      }
+    }
+    if constexpr (VEC) {
+#pragma unroll
+      for (int i = 0; i < TILE * D / THREADS; ++i) {
+        const int e = tid + THREADS * i, t = e / D, c = e % D;
+        av[t][c] = t < n ? avreg[i] : 1.f;
+      }
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int e = tid + THREADS * i, t = e / RPW, r = e % RPW;
-      vs[t][r] = Elem<E>::to_f32(vreg[i]);
+      const int e = EPW * (tid + THREADS * i), t = e / RPW, r = e % RPW;
+#pragma unroll
+      for (int h = 0; h < EPW; ++h) vs[t][r + h] = (t < n && kind != 1) ? TileWord<E>::elem(vreg[i], h) : 0.f;
     }
     if (tid < TILE) {
-      as_[tid] = areg;
-      bs_[tid] = breg;
+      as_[tid] = (!VEC && tid < n) ? areg : 1.f;
+      bs_[tid] = tid < n ? breg : 0.f;
     }
     __syncthreads();
     if (tt + TILE < len) {
       const int64_t nt = tt + TILE;
       fetch_tile<E, D, VEC>(kreg, qreg, vreg, avreg, areg, breg, q, k, v, alpha, beta, base, nt,
-                            (int)(len - nt < TILE ? len - nt : TILE), rg, kind, tid);
+                            (int)(len - nt < TILE ? len - nt : TILE), rg, tid);
     }
     for (int t = 0; t < n; ++t) {
       const float a = as_[t], bt = bs_[t];
