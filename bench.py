@@ -41,6 +41,8 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chunk_fwd_main.txt")
 KERNEL_SOURCES = ["gdn_common.hpp", "chunk_fwd_pipe.hpp", "gdn_api.hip"]
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_recurrent_step_decode.txt")
+DECODE_SOURCES = ["gdn_common.hpp", "recurrent_step.hpp", "gdn_api.hip"]
 
 
 def alg_bytes_main(B, H, T, d):
@@ -58,26 +60,28 @@ def alg_bytes_decode(N, H, d):
     return 2 * heads * d * d * 4 + heads * (3 * d * 2 + 2 * 4 + d * 2)
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=None):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (sources or KERNEL_SOURCES):
         with open(os.path.join(ROOT, "gated_deltanet_sequence_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None
-    when it is missing or was taken on different kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(path=None, sources=None):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary (by
+    default the main kernel's), or None when it is missing or was taken on
+    different kernel sources."""
+    path = path or TRAFFIC_FILE
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE, encoding="utf-8") as f:
+    with open(path, encoding="utf-8") as f:
         for line in f:
             if "=" in line and not line.lstrip().startswith("#"):
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_hash") != kernel_source_hash():
+    if vals.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     try:
         return int(float(vals["hbm_bytes_per_launch"]))
@@ -274,6 +278,8 @@ def time_decode(torch, dev, steps_override=None):
     from gated_deltanet_sequence_amd.binding import gdn_recurrent_step
     N, H, d, steps = DECODE["N"], DECODE["H"], DECODE["d"], DECODE["steps"]
     x = inputs.make_decode_inputs(N, H, d, steps, "bf16", seed=DECODE["seed"])
+    if steps_override is not None:
+        steps = min(steps, steps_override)
     state = x["s0"].to(dev)
     qs = [t.to(dev) for t in x["q"]]
     ks = [t.to(dev) for t in x["k"]]
@@ -309,7 +315,29 @@ def time_decode(torch, dev, steps_override=None):
             "tokens_per_s": N / (avg_ms * 1e-3), "ms_per_step": avg_ms,
             "step_ms_median": sorted(per)[steps // 2],
             "alg_bytes_per_step": byts, "achieved_GBs": byts / (avg_ms * 1e-3) / 1e9,
-            "hbm_frac": byts / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "hbm_frac": byts / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            # DRAM bytes per step from the committed rocprofv3 --pmc summary (null when
+            # it is missing or was taken on other kernel sources)
+            "traffic": read_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)}
+
+
+def host_info():
+    """The host the CPU figures come from: logical CPUs the OS reports, the CPUs
+    this process may run on, and the CPU model name."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"nproc": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": model}
 
 
 def cpu_baseline(x, o_gpu, sT_gpu):
@@ -322,7 +350,9 @@ def cpu_baseline(x, o_gpu, sT_gpu):
     f = inputs.to_f32_numpy
     q, k, v = f(x["q"]), f(x["k"]), f(x["v"])
     a, b = x["alpha"].numpy(), x["beta"].numpy()
-    cores = oracle.num_threads()
+    chains = MAIN["B"] * MAIN["H"]
+    # the oracle's OpenMP loop runs over the independent sequences
+    threads = min(oracle.num_threads(), chains)
     t0 = time.perf_counter()
     ro, rs = oracle.oracle_fwd(q, k, v, a, b, None)
     dt = time.perf_counter() - t0
@@ -331,17 +361,70 @@ def cpu_baseline(x, o_gpu, sT_gpu):
     eo = float(np.max(np.abs(go - ro)) / np.max(np.abs(ro)))
     es = float(np.max(np.abs(gs - rs)) / np.max(np.abs(rs)))
     tokens = MAIN["B"] * MAIN["T"]
-    return ({"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-             "sample": "the whole main workload (B=4,H=16,T=8192,d=128: 64 sequences x 8192 "
-                       "tokens), fp64 token loop, %.2f s" % dt},
-            {"max_rel_err_o": eo, "max_rel_err_final_state": es, "tol": 2e-2,
-             "pass": bool(eo <= 2e-2 and es <= 2e-2)})
+    res = {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": "the whole main workload (B=4,H=16,T=8192,d=128: 64 sequences x 8192 "
+                     "tokens), fp64 token loop, %.2f s" % dt,
+           "seconds": dt}
+    res.update(host_info())
+    return (res, {"max_rel_err_o": eo, "max_rel_err_final_state": es, "tol": 2e-2,
+                  "pass": bool(eo <= 2e-2 and es <= 2e-2)})
 
 
-def summarize_pmc(fetch_dir, write_dir):
-    """Write the traffic summary from two rocprofv3 --pmc runs of
-    `bench.py --pmc-pass` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch)."""
+def cpu_configs():
+    """The oracle timed on the host cores over the other workloads (the pages'
+    loop case, the long context and the 64 decode steps; the tiny workload
+    too): seconds, tokens/s and the threads its OpenMP loop used."""
+    import oracle
+    from gated_deltanet_sequence_amd import inputs
+    f = inputs.to_f32_numpy
+    out = {"host": host_info()}
+    for name, cfg, dtype in (("tiny", dict(B=1, H=1, T=256, d=64, seed=1, init_state=False), "f32"),
+                             ("loop_case", LOOP, "bf16"), ("long_context", LONG, "bf16")):
+        x = inputs.make_fwd_inputs(cfg["B"], cfg["H"], cfg["T"], cfg["d"], dtype, seed=cfg["seed"],
+                                   init_state=cfg["init_state"])
+        args = (f(x["q"]), f(x["k"]), f(x["v"]), x["alpha"].numpy(), x["beta"].numpy(),
+                x["s0"].numpy() if x.get("s0") is not None else None)
+        del x
+        t0 = time.perf_counter()
+        oracle.oracle_fwd(*args)
+        dt = time.perf_counter() - t0
+        out[name] = {"seconds": dt, "tokens_per_s": cfg["B"] * cfg["T"] / dt,
+                     "threads": min(oracle.num_threads(), cfg["B"] * cfg["H"])}
+        del args
+    N, H, d, steps = DECODE["N"], DECODE["H"], DECODE["d"], DECODE["steps"]
+    x = inputs.make_decode_inputs(N, H, d, steps, "bf16", seed=DECODE["seed"])
+    state = x["s0"].numpy().astype("float64")
+    cols = [(f(x["q"][t]), f(x["k"][t]), f(x["v"][t]), x["alpha"][t].numpy(), x["beta"][t].numpy())
+            for t in range(steps)]
+    del x
+    t0 = time.perf_counter()
+    for c in cols:
+        oracle.oracle_step(*c, state)
+    dt = time.perf_counter() - t0
+    out["decode"] = {"seconds": dt, "seconds_per_step": dt / steps, "tokens_per_s": N * steps / dt,
+                     "threads": min(oracle.num_threads(), N * H)}
+    return out
+
+
+PMC_TARGETS = {
+    # which: (kernel-name test, summary file, kernel sources, title, algorithmic bytes)
+    "main": (lambda n: "chunk_fwd" in n, "TRAFFIC_FILE", KERNEL_SOURCES,
+             "chunk_fwd_pipe_kernel, main workload (B=4,H=16,T=8192,d=128,C=64, bf16)",
+             lambda: alg_bytes_main(MAIN["B"], MAIN["H"], MAIN["T"], MAIN["d"])),
+    "decode": (lambda n: "recurrent_step" in n, "DECODE_TRAFFIC_FILE", DECODE_SOURCES,
+               "recurrent_step_kernel, decode step (256 sequences x H=16, d=128, fp32 state in place)",
+               lambda: alg_bytes_decode(DECODE["N"], DECODE["H"], DECODE["d"])),
+}
+
+
+def summarize_pmc(fetch_dir, write_dir, which="main"):
+    """Write the traffic summary of one kernel from two rocprofv3 --pmc runs of
+    `bench.py --pmc-pass WHICH` (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch).  Each counter is calibrated by what it reads for the plain
+    512 MiB device copy the pass makes first."""
     import csv
+    is_kernel, out_var, sources, title, alg_fn = PMC_TARGETS[which]
+    out_file = globals()[out_var]
 
     def read(d, counter):
         rows = []
@@ -356,45 +439,102 @@ def summarize_pmc(fetch_dir, write_dir):
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = read(d, counter)
-        copy = [v for n, v in rows if "chunk_fwd" not in n and "recurrent_step" not in n
-                and v > 100000]
+        copy = [v for n, v in rows if "gdn::" not in n and v > 100000]
         # the last launches of the pass, after the clocks have settled
-        chunk = [v for n, v in rows if "chunk_fwd" in n][-PMC_LAUNCHES:]
-        if not copy or not chunk:
-            raise SystemExit("no %s rows for the copy and chunk kernels in %s" % (counter, d))
-        out[counter] = (max(copy), sum(chunk) / len(chunk))
+        kern = [v for n, v in rows if "gdn::" in n and is_kernel(n)][-PMC_LAUNCHES:]
+        if not copy or not kern:
+            raise SystemExit("no %s rows for the copy and the %s kernel in %s" % (counter, which, d))
+        out[counter] = (max(copy), sum(kern) / len(kern))
     copy_kib = (1 << 29) / 1024.0  # the copy kernel moves 512 MiB each way
     f_fetch = copy_kib / out["FETCH_SIZE"][0]
     f_write = copy_kib / out["WRITE_SIZE"][0]
     fetch_b = out["FETCH_SIZE"][1] * 1024 * f_fetch
     write_b = out["WRITE_SIZE"][1] * 1024 * f_write
-    alg = alg_bytes_main(MAIN["B"], MAIN["H"], MAIN["T"], MAIN["d"])
+    alg = alg_fn()
     lines = [
-        "# HBM traffic of chunk_fwd_pipe_kernel, main workload (B=4,H=16,T=8192,d=128,C=64, bf16)",
+        "# HBM traffic of %s" % title,
         "# from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch):",
-        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -- python3 bench.py --pmc-pass" % fetch_dir,
-        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -- python3 bench.py --pmc-pass" % write_dir,
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -- python3 bench.py --pmc-pass %s" % (fetch_dir, which),
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -- python3 bench.py --pmc-pass %s" % (write_dir, which),
         "# (each pass runs the kernel for %.0f ms to settle the clocks, then %d more launches;" % (SETTLE_MS, PMC_LAUNCHES),
         "#  the figures below average those last %d launches)" % PMC_LAUNCHES,
-        "#   python3 bench.py --summarize-pmc %s %s" % (fetch_dir, write_dir),
+        "#   python3 bench.py --summarize-pmc %s %s --pmc-kernel %s" % (fetch_dir, write_dir, which),
         "# Each counter is scaled by (512 MiB / what it reads for a plain 512 MiB device copy",
         "# in the same run).",
         "copy_fetch_kib = %.1f" % out["FETCH_SIZE"][0],
         "copy_write_kib = %.1f" % out["WRITE_SIZE"][0],
         "fetch_scale = %.4f" % f_fetch,
         "write_scale = %.4f" % f_write,
-        "chunk_fetch_kib = %.1f" % out["FETCH_SIZE"][1],
-        "chunk_write_kib = %.1f" % out["WRITE_SIZE"][1],
+        "kernel_fetch_kib = %.1f" % out["FETCH_SIZE"][1],
+        "kernel_write_kib = %.1f" % out["WRITE_SIZE"][1],
         "hbm_fetch_bytes = %d" % fetch_b,
         "hbm_write_bytes = %d" % write_b,
         "hbm_bytes_per_launch = %d" % (fetch_b + write_b),
         "algorithmic_bytes_per_launch = %d" % alg,
         "traffic_over_algorithmic = %.3f" % ((fetch_b + write_b) / alg),
-        "kernel_source_hash = %s" % kernel_source_hash(),
+        "kernel_source_hash = %s" % kernel_source_hash(sources),
     ]
-    with open(TRAFFIC_FILE, "w", encoding="utf-8") as fh:
+    with open(out_file, "w", encoding="utf-8") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def summarize_trace(trace_dir, out_name, command, note="", tail=100):
+    """Write profiles/OUT_NAME.txt from a rocprofv3 --kernel-trace run: for every
+    kernel of the library and launch shape, the number of launches and the
+    mean, min and max duration, and the mean over the last `tail` launches
+    (the timed ones, when the run is bench.py's).  For the main chunk kernel
+    (256 workgroups) and the decode kernel it adds the fraction of the 8 TB/s
+    HBM peak that their algorithmic bytes give at that mean."""
+    import collections
+    import csv
+    paths = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not paths:
+        raise SystemExit("no *kernel_trace.csv under %s" % trace_dir)
+    rows = []
+    for p in paths:
+        with open(p, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    groups = collections.OrderedDict()
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "gdn::" not in name:
+            continue
+        short = name.split("(")[0].replace("void ", "")
+        wg = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
+        key = (short, wg, int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = ["# rocprofv3 kernel-trace summary (one MI355X); repository root as $REPO:",
+           "#   %s" % command,
+           "#   python3 bench.py --summarize-trace <that -d directory> %s --trace-cmd '<the command above>'%s"
+           % (out_name, (" --tail %d" % tail) if tail != 100 else "")]
+    out += ["# " + line for line in note.splitlines() if line.strip()]
+    out.append("# per kernel and launch shape: launches, mean, min and max duration, and the mean of")
+    out.append("# the last %d launches of that shape (us)" % tail)
+    out.append("%-58s %6s %7s %8s %10s %10s %10s %10s" % ("kernel", "wgs", "threads", "launches",
+                                                        "mean_us", "min_us", "max_us", "tail_us"))
+    derived = []
+    for (k, wg, th), v in groups.items():
+        t = v[-tail:]
+        tmean = sum(t) / len(t)
+        out.append("%-58s %6d %7d %8d %10.2f %10.2f %10.2f %10.2f" % (
+            k[:58], wg, th, len(v), sum(v) / len(v) / 1e3, min(v) / 1e3, max(v) / 1e3, tmean / 1e3))
+        alg = None
+        if "chunk_fwd_pipe_kernel<false>" in k and wg == 256:
+            alg, what = alg_bytes_main(MAIN["B"], MAIN["H"], MAIN["T"], MAIN["d"]), "main workload"
+        elif "recurrent_step_kernel" in k and wg == DECODE["N"] * DECODE["H"]:
+            alg, what = alg_bytes_decode(DECODE["N"], DECODE["H"], DECODE["d"]), "decode step"
+        if alg is not None:
+            derived += ["roofline of %s (%s, %d wgs): tail_average_ns = %d" % (k, what, wg, tmean),
+                        "  algorithmic_bytes_per_launch = %d" % alg,
+                        "  algorithmic_GBps_at_tail_average = %.1f" % (alg / tmean),
+                        "  fraction_of_8000_GBps = %.4f" % (alg / tmean / 8000.0)]
+    out += derived
+    path = os.path.join(ROOT, "profiles", out_name + ".txt")
+    with open(path, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(out) + "\n")
+    print("\n".join(out))
 
 
 def main():
@@ -412,13 +552,27 @@ def main():
                     help="skip the gated-linear-attention report")
     ap.add_argument("--no-routes", action="store_true",
                     help="skip the chunked / scan / per-token route comparison")
-    ap.add_argument("--pmc-pass", action="store_true",
-                    help="one 512 MiB copy plus two launches, for rocprofv3 --pmc runs")
+    ap.add_argument("--pmc-pass", nargs="?", const="main", choices=sorted(PMC_TARGETS),
+                    help="one 512 MiB copy, then the kernel (main chunk kernel, or the decode "
+                         "step) for the settling time and %d more launches, for rocprofv3 --pmc "
+                         "runs" % PMC_LAUNCHES)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--pmc-kernel", default="main", choices=sorted(PMC_TARGETS))
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_NAME"),
+                    help="write profiles/OUT_NAME.txt from a rocprofv3 --kernel-trace run")
+    ap.add_argument("--trace-cmd", default="", help="the profiling command, for the summary header")
+    ap.add_argument("--trace-note", default="", help="extra header lines for the summary")
+    ap.add_argument("--tail", type=int, default=100, help="launches averaged per shape (--summarize-trace)")
+    ap.add_argument("--cpu-configs", action="store_true",
+                    help="also time the oracle on the other workloads (loop case, long context, decode)")
     args = ap.parse_args()
 
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc)
+        summarize_pmc(*args.summarize_pmc, which=args.pmc_kernel)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, command=args.trace_cmd, note=args.trace_note,
+                        tail=args.tail)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: there is no multi-GPU path here "
@@ -437,7 +591,11 @@ def main():
         src = torch.empty(1 << 28, dtype=torch.float16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         dst.copy_(src)
-        time_chunk(torch, xd, steps=PMC_LAUNCHES, warmup=0)
+        del src, dst
+        if args.pmc_pass == "main":
+            time_chunk(torch, xd, steps=PMC_LAUNCHES, warmup=0)
+        else:
+            time_decode(torch, dev, steps_override=PMC_LAUNCHES)
         torch.cuda.synchronize()
         print("pmc pass done", flush=True)
         return
@@ -494,6 +652,8 @@ def main():
         res["routes"] = time_routes(torch, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"], res["parity"] = cpu_baseline(x, o, sT)
+    if args.cpu_configs:
+        res["cpu_oracle_other_workloads"] = cpu_configs()
     print(json.dumps(res), flush=True)
 
 

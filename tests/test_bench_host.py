@@ -70,3 +70,42 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def _write_trace(d, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "run_kernel_trace.csv"), "w") as fh:
+        fh.write("Kernel_Name,Grid_Size_X,Workgroup_Size_X,Start_Timestamp,End_Timestamp\n")
+        t = 0
+        for name, wgs, threads, dur in rows:
+            fh.write('"%s",%d,%d,%d,%d\n' % (name, wgs * threads, threads, t, t + dur))
+            t += dur + 1000
+
+
+def test_trace_summary_groups_by_kernel_and_shape_and_prices_the_main_launches(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    chunk = "void gdn::pipe::chunk_fwd_pipe_kernel<false>(unsigned short const*, int)"
+    rows = [(chunk, 256, 512, 300000)] * 50 + [(chunk, 256, 512, 200000)] * 100
+    rows += [(chunk, 8, 512, 150000)] * 3
+    rows += [("void at::native::copy_kernel(int)", 1024, 256, 5000)] * 2  # not the library's
+    _write_trace(str(tmp_path / "tr"), rows)
+    bench.summarize_trace(str(tmp_path / "tr"), "x", command="rocprofv3 --kernel-trace -- python3 bench.py")
+    text = (tmp_path / "profiles" / "x.txt").read_text()
+    assert "rocprofv3 --kernel-trace -- python3 bench.py" in text
+    assert "copy_kernel" not in text
+    lines = [l for l in text.splitlines() if l.startswith("gdn::pipe::chunk_fwd_pipe_kernel")]
+    assert len(lines) == 2
+    big = lines[0].split()
+    assert big[1:4] == ["256", "512", "150"]
+    # the tail mean covers the last 100 launches only; the mean all 150
+    assert float(big[-1]) == pytest.approx(200.0)
+    assert float(big[4]) == pytest.approx((50 * 300 + 100 * 200) / 150.0, abs=0.01)
+    frac = [l for l in text.splitlines() if "fraction_of_8000_GBps" in l][0]
+    alg = bench.alg_bytes_main(4, 16, 8192, 128)
+    assert float(frac.split("=")[1]) == pytest.approx(alg / 200000.0 / 8000.0, rel=1e-3)
+
+
+def test_host_info_names_the_cpu():
+    info = bench.host_info()
+    assert info["nproc"] >= 1 and isinstance(info["cpu_model"], str)
