@@ -16,7 +16,7 @@ from gated_deltanet_sequence_amd import inputs
 from gated_deltanet_sequence_amd.binding import (GDNError, gdn_chunk_fwd,
                                                  gdn_recurrent_step)
 
-from _helpers import TOL, maxrel, oracle_inputs, to_dev, to_np
+from _helpers import grouped_oracle_errors, TOL, maxrel, oracle_inputs, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -118,9 +118,16 @@ def test_config_main_full():
     check_against_oracle(x, dt, label="main")
 
 
-def test_config_long_sampled():
+def test_config_long_full():
+    """The long-context workload (B=1, H=16, T=131072, d=128, S0 ~ N(0,0.1)):
+    every sequence's output and final state against the oracle (run four
+    sequences at a time)."""
     x, dt = _cfg_inputs("long")
-    check_against_oracle(x, dt, chains=[0, 7, 15], label="long")
+    _say("case long, all 16 sequences, shape", tuple(x["q"].shape))
+    o, sT = run_gpu(x)
+    eo, es = grouped_oracle_errors(x, to_np(o), to_np(sT))
+    _say("  err o %.3e  err S_T %.3e  (tol %.0e)" % (eo, es, TOL[dt]))
+    assert eo <= TOL[dt] and es <= TOL[dt]
 
 
 def test_config_decode_full():
