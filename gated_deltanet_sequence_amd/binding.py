@@ -61,6 +61,8 @@ def load_library(path: str | None = None):
     lib.gdn_chunk_fwd_split.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
                                         p, ctypes.c_size_t, p]
     lib.gdn_chunk_fwd_split.restype = i32
+    lib.gdn_chunk_fwd_split_noalloc.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32, p]
+    lib.gdn_chunk_fwd_split_noalloc.restype = i32
     lib.gdn_chunk_fwd_split_workspace.argtypes = [i64, i64, i64, i64, i64, i64, i32]
     lib.gdn_chunk_fwd_split_workspace.restype = ctypes.c_size_t
     lib.gdn_recurrent_step.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, p]
@@ -234,6 +236,30 @@ def gdn_chunk_fwd_split(q, k, v, alpha, beta, initial_state=None, chunk_size: in
     if rc != GDN_OK:
         raise GDNError(rc, "gdn_chunk_fwd_split")
     return o, final_state
+
+
+def gdn_chunk_fwd_split_noalloc(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 64, *,
+                                o=None, final_state=None, output_final_state: bool = True, stream=None):
+    """gdn_chunk_fwd_split on the library's static per-GPU scratch instead of a
+    workspace (the C entry point allocates nothing; outputs are allocated here
+    only when not given).  Calls on one GPU must not overlap in time."""
+    B, H, T, dk, dv = _check_fwd_args(q, k, v, alpha, beta, initial_state)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    rc = lib.gdn_chunk_fwd_split_noalloc(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                         _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                                         _dev_ptr(initial_state, "initial_state"), _dev_ptr(o, "o"),
+                                         _dev_ptr(final_state, "final_state"), B, H, T, dk, dv,
+                                         int(chunk_size), _DTYPES[q.dtype], _stream_ptr(stream, q.device))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_chunk_fwd_split_noalloc")
+    return o, final_state
+
+
+SPLIT_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 def gdn_recurrent_step(q, k, v, alpha, beta, state, *, o=None, stream=None):

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gdn.h"
 #include "chunk_fwd.hpp"
 #include "chunk_fwd_pipe.hpp"
@@ -225,6 +227,70 @@ int check_fwd(const void* q, const void* k, const void* v, const float* alpha, c
 }
 }  // namespace
 
+namespace {
+// The three launches of the sequence-split pass on workspace ws (G >= 2).
+int split_launches(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                   const float* initial_state, void* o, float* final_state, int64_t nchain, int64_t T,
+                   int64_t dk, int64_t dv, int G, int64_t L, float* ws, hipStream_t stream) {
+  gdn::pipe::ChainMap cm{};
+  cm.nseq = (int)nchain;
+  cm.G = G;
+  cm.T = T;
+  cm.L = L;
+  cm.ws = ws;
+  // 1: per segment, the state from zero and the transition (first G-1 segments)
+  cm.mode = gdn::pipe::MAP_SPLIT_A;
+  int r = launch_chunk_pipe(q, k, v, alpha, beta, nullptr, o, nullptr, cm, dk, dv, stream);
+  if (r != GDN_OK) return r;
+  // 2: the start state of every segment
+  if (dk == 128)
+    hipLaunchKernelGGL(gdn::split::split_combine_kernel<128>, dim3((unsigned)(nchain * (128 / gdn::split::ROWS))),
+                       dim3(gdn::split::threads_for<128>()), 0, stream, initial_state, cm.ws, (int)nchain, G);
+  else
+    hipLaunchKernelGGL(gdn::split::split_combine_kernel<64>, dim3((unsigned)(nchain * (64 / gdn::split::ROWS))),
+                       dim3(gdn::split::threads_for<64>()), 0, stream, initial_state, cm.ws, (int)nchain, G);
+  if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
+  // 3: every segment from its start state, with output
+  cm.mode = gdn::pipe::MAP_SPLIT_C;
+  return launch_chunk_pipe(q, k, v, alpha, beta, nullptr, o, final_state, cm, dk, dv, stream);
+}
+
+// Scratch of gdn_chunk_fwd_split_noalloc: one copy in the memory of every
+// device the library runs on, held until the process ends.  Host code never
+// passes `scratch` itself to a kernel (on the host it is only a stand-in for
+// the symbol): the device address of each GPU's copy is looked up once per
+// device with hipGetSymbolAddress and kept in noalloc_ptr.
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex noalloc_mu;
+void* noalloc_ptr[NOALLOC_MAX_DEVICES] = {};
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[GDN_SPLIT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+// Device address of the current device's scratch (looked up on the first call
+// on that device, with that device current).
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return GDN_ERR_HIP;
+  }
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return GDN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(noalloc_mu);
+  if (!noalloc_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return GDN_ERR_HIP;
+    }
+    noalloc_ptr[dev] = p;
+  }
+  *out = noalloc_ptr[dev];
+  return GDN_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
@@ -369,28 +435,31 @@ int gdn_chunk_fwd_split(const void* q, const void* k, const void* v, const float
     for (const Range& r : others)
       if (overlaps(rw, r)) return GDN_ERR_INVALID_ARG;
   }
-  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  gdn::pipe::ChainMap cm{};
-  cm.nseq = (int)nchain;
-  cm.G = G;
-  cm.T = T;
-  cm.L = L;
-  cm.ws = static_cast<float*>(workspace);
-  // 1: per segment, the state from zero and the transition (first G-1 segments)
-  cm.mode = gdn::pipe::MAP_SPLIT_A;
-  int r = launch_chunk_pipe(q, k, v, alpha, beta, nullptr, o, nullptr, cm, dk, dv, stream);
+  return split_launches(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dk, dv, G, L,
+                        static_cast<float*>(workspace), static_cast<hipStream_t>(hip_stream));
+}
+
+int gdn_chunk_fwd_split_noalloc(const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, const float* initial_state, void* o, float* final_state,
+                                int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk_size,
+                                gdn_dtype dtype, void* hip_stream) {
+  const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
+                           chunk_size, dtype);
+  if (rc != GDN_OK) return rc;
+  if (dtype == GDN_BF16 && !pipe_len_ok(T, dk, dv)) return GDN_ERR_UNSUPPORTED;
+  const int64_t nchain = B * H;
+  int G = 1;
+  int64_t L = T;
+  if (dtype == GDN_BF16 && nchain > 0 && T > 0) split_plan(nchain, T, dv, G, L);
+  if (G < 2)
+    return gdn_chunk_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
+                         chunk_size, dtype, hip_stream);
+  if (split_ws_bytes(nchain, G, dk) > GDN_SPLIT_NOALLOC_SCRATCH_BYTES) return GDN_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  const int r = noalloc_scratch(&ws);
   if (r != GDN_OK) return r;
-  // 2: the start state of every segment
-  if (dk == 128)
-    hipLaunchKernelGGL(gdn::split::split_combine_kernel<128>, dim3((unsigned)(nchain * (128 / gdn::split::ROWS))),
-                       dim3(gdn::split::threads_for<128>()), 0, stream, initial_state, cm.ws, (int)nchain, G);
-  else
-    hipLaunchKernelGGL(gdn::split::split_combine_kernel<64>, dim3((unsigned)(nchain * (64 / gdn::split::ROWS))),
-                       dim3(gdn::split::threads_for<64>()), 0, stream, initial_state, cm.ws, (int)nchain, G);
-  if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
-  // 3: every segment from its start state, with output
-  cm.mode = gdn::pipe::MAP_SPLIT_C;
-  return launch_chunk_pipe(q, k, v, alpha, beta, nullptr, o, final_state, cm, dk, dv, stream);
+  return split_launches(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dk, dv, G, L,
+                        static_cast<float*>(ws), static_cast<hipStream_t>(hip_stream));
 }
 
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,

@@ -30,7 +30,8 @@
  *     never allocates, frees or synchronises.  Work is enqueued on
  *     `hip_stream` (a hipStream_t; NULL = the null stream) and the call
  *     returns once it is enqueued.  The library holds no state between calls
- *     and is safe to call from several host threads on different streams.
+ *     (except the per-GPU scratch of gdn_chunk_fwd_split_noalloc, below) and
+ *     is safe to call from several host threads on different streams.
  *   - Layouts are dense row-major exactly as written (no strides).  Every
  *     tensor pointer must be 16-byte aligned.
  *   - Arguments are validated before anything is launched; on any error no
@@ -190,6 +191,35 @@ int gdn_chunk_fwd_split(const void* q, const void* k, const void* v,
  * device (0: it would not split).  A host-side query; launches nothing. */
 size_t gdn_chunk_fwd_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk,
                                      int64_t dv, int64_t chunk_size, gdn_dtype dtype);
+
+/*
+ * gdn_chunk_fwd_split_noalloc — gdn_chunk_fwd_split for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, result, aliasing and
+ * errors as gdn_chunk_fwd_split, without the workspace: the segment states live
+ * in a static scratch array of GDN_SPLIT_NOALLOC_SCRATCH_BYTES that the library
+ * keeps in the memory of each GPU it runs on until the process ends.  The call
+ * allocates and frees nothing (on its first call on a device it only looks up
+ * that device's scratch address, with hipGetSymbolAddress).
+ *   - It uses the scratch of the device current on the calling thread;
+ *     hip_stream must belong to that device.
+ *   - A plan that needs more scratch than GDN_SPLIT_NOALLOC_SCRATCH_BYTES
+ *     returns GDN_ERR_UNSUPPORTED before anything is launched.  (With 256
+ *     compute units every plan fits: the workspace is bounded by about
+ *     (B*H + 3 * CUs / 8) * dk * dk * 4 bytes for dk = 128.)
+ *   - Every call on one GPU shares that GPU's scratch; its contents on entry
+ *     do not matter (each call writes every part it reads), but calls that
+ *     overlap in time on one GPU race and give wrong results: serialise them
+ *     (one stream, or events).
+ *   - When no split is planned (G = 1) the scratch is not touched and this is
+ *     gdn_chunk_fwd.
+ */
+#define GDN_SPLIT_NOALLOC_SCRATCH_BYTES (8u << 20)
+int gdn_chunk_fwd_split_noalloc(const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta,
+                                const float* initial_state, void* o, float* final_state,
+                                int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                                int64_t chunk_size, gdn_dtype dtype, void* hip_stream);
 
 /*
  * gdn_recurrent_step — one decode step: one new token for each of N*H

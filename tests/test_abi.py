@@ -172,3 +172,24 @@ def test_sequence_over_the_bf16_length_limit_is_rejected(lib):
     P = lambda x: ctypes.c_void_p(x)
     assert lib.gla_chunk_fwd(P(ptrs["q"]), P(ptrs["k"]), P(ptrs["v"]), P(ptrs["alpha"]), P(ptrs["beta"]),
                              None, P(ptrs["o"]), None, 1, 1, T, 128, 128, 64, 1, None) == binding.GDN_ERR_UNSUPPORTED
+
+
+def noalloc(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, alpha=A + 192 * MB, beta=A + 200 * MB,
+            s0=None, o=A + 256 * MB, sT=None, B=1, H=1, T=64, dk=64, dv=64, C=64, dtype=1):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gdn_chunk_fwd_split_noalloc(P(q), P(k), P(v), P(alpha), P(beta), P(s0), P(o), P(sT),
+                                           B, H, T, dk, dv, C, dtype, None)
+
+
+def test_noalloc_split_validates_before_any_device_call(lib):
+    # the same argument checks as gdn_chunk_fwd_split, all before the scratch
+    # is looked up or anything is launched
+    assert noalloc(lib, q=None) == binding.GDN_ERR_INVALID_ARG
+    assert noalloc(lib, B=-1) == binding.GDN_ERR_INVALID_ARG
+    assert noalloc(lib, dk=96, dv=96) == binding.GDN_ERR_UNSUPPORTED
+    assert noalloc(lib, C=32) == binding.GDN_ERR_UNSUPPORTED
+    assert noalloc(lib, v=A + 128 * MB + 8) == binding.GDN_ERR_ALIGNMENT
+    assert noalloc(lib, o=A + 64 * MB) == binding.GDN_ERR_INVALID_ARG     # o overlaps k
+    assert noalloc(lib, dtype=7) == binding.GDN_ERR_INVALID_ARG
+    # nothing to do: no sequences
+    assert noalloc(lib, B=0) == binding.GDN_OK
