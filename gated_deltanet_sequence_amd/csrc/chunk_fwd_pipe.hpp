@@ -347,6 +347,8 @@ struct StateRegs {
   f32x4 S[8];        // state tiles: value row lr, internal keys 16 jb + 4 lg + e
   f32x4 Oprev[4];    // Q S^T part of the previous chunk's output (per 16-token block)
   bf16x8_t Uprev[2]; // U of the previous chunk as kappa operands
+  bf16x8_t Kpre[2][4];  // key fragments of the next chunk's first two 16-token
+                        // blocks, read at the end of a period (delta rule)
 };
 
 // One period of a state wave: with FINISH, the output of chunk c - 1
@@ -374,9 +376,15 @@ __device__ __forceinline__ void read_p(const Smem& sm, const StateAddr& A, int64
     for (int pp = 0; pp <= rb / 2; ++pp) pf[rb][pp] = as_op(ld3<uint4>(pb[pp], rb * 2048));
 }
 
-template <bool FINISH, bool CHAIN, bool GLA>
+// PRE: the key fragments of blocks 0 and 1 of chunk c are in R.Kpre (read at
+// the end of the previous period, so that their LDS latency falls in the
+// barrier wait instead of delaying the first products of this period).
+// OUT = false: no output (the first launch of the sequence split, which
+// needs only the state): no Q S^T, no P U, no stores.
+template <bool FINISH_, bool CHAIN, bool GLA, bool PRE = false, bool OUT = true>
 __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, const StateAddr& A,
                                              StateRegs& R, int64_t c, int DV, int lane) {
+  constexpr bool FINISH = FINISH_ && OUT;
   const int lr = lane & 15, lg = lane >> 4;
   bf16x8_t pf[4][2];
   if constexpr (!CHAIN) {
@@ -414,9 +422,11 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   bf16x8_t fr[3][4];
   auto read_block = [&](int n) {
     if (GLA && n < 4) return;  // without the delta rule K S^T is not needed
+    if (!OUT && n >= 4) return;  // no output: Q is not needed
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp)
-      fr[n % 3][pp] = as_op(n < 4 ? ld3<uint4>(kf_b[pp], n * 4096) : ld3<uint4>(qf_b[pp], (n - 4) * 4096));
+      fr[n % 3][pp] = PRE && n < 2 ? R.Kpre[n][pp]
+                                   : as_op(n < 4 ? ld3<uint4>(kf_b[pp], n * 4096) : ld3<uint4>(qf_b[pp], (n - 4) * 4096));
   };
   // V and the gates of Y, read during the products of blocks 1..3
   uint2 vv[4];
@@ -471,10 +481,12 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
       if constexpr (FINISH) read_p(sm, A, c - 1, pf);
     }
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 ao = zero4();
+    if constexpr (OUT) {
+      f32x4 ao = zero4();
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) ao = mfma(Sop[pp], fr[(4 + rb) % 3][pp], ao);
-    O1[rb] = ao;
+      for (int pp = 0; pp < 4; ++pp) ao = mfma(Sop[pp], fr[(4 + rb) % 3][pp], ao);
+      O1[rb] = ao;
+    }
     if constexpr (GLA) {
       y[rb][0] = b4[rb].x * __uint_as_float(vv[rb].x << 16);
       y[rb][1] = b4[rb].y * __uint_as_float(vv[rb].x & 0xffff0000u);
@@ -489,9 +501,9 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     __builtin_amdgcn_sched_barrier(0);
   }
   const bf16x8_t Yop[2] = {pack_op(y[0], y[1]), pack_op(y[2], y[3])};
-  // the first K^T operands of the state update (ring of three slots, tile jb
-  // in slot jb % 3)
-  bf16x8_t kt[3][2];
+  // the first K^T operands of the state update (ring of four slots, tile jb
+  // in slot jb % 4, read three tiles ahead of its products)
+  bf16x8_t kt[4][2];
   auto read_kt = [&](int jb, bf16x8_t (&dst)[2]) {
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
@@ -501,6 +513,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   };
   read_kt(0, kt[0]);
   read_kt(1, kt[1]);
+  read_kt(2, kt[2]);
   __builtin_amdgcn_sched_barrier(0);
   // ---- U = Ti Y (Ti lower triangular: row block rb needs the 32-token blocks
   // pp <= rb/2, the upper 16x16 blocks inside them are zero) while O1 takes
@@ -516,7 +529,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
       for (int pp = 0; pp <= rb / 2; ++pp) acc = mfma(tf[rb][pp], Yop[pp], acc);
       U[rb] = acc;
     }
-    Onew[rb] = O1[rb] * eg[rb];
+    if constexpr (OUT) Onew[rb] = O1[rb] * eg[rb];
   }
   __builtin_amdgcn_sched_barrier(0);
   // ---- output of the previous chunk while the operands of U are packed:
@@ -531,12 +544,14 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
       Ofin[rb] = acc;
     }
   }
+  if constexpr (OUT) {
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) R.Oprev[rb] = Onew[rb];
+    for (int rb = 0; rb < 4; ++rb) R.Oprev[rb] = Onew[rb];
+  }
   bf16x8_t Uh[2];
 #pragma unroll
   for (int pp = 0; pp < 2; ++pp) {
-    R.Uprev[pp] = pack_op(U[2 * pp], U[2 * pp + 1]);
+    if constexpr (OUT) R.Uprev[pp] = pack_op(U[2 * pp], U[2 * pp + 1]);
     Uh[pp] = pack_op(U[2 * pp] * el[2 * pp], U[2 * pp + 1] * el[2 * pp + 1]);
   }
   if constexpr (FINISH) {
@@ -549,14 +564,26 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   __builtin_amdgcn_sched_barrier(0);
   // ---- S^T += K^T Uh with K^T from transposed reads: supplier lane (a, r) of
   // a 16-lane group addresses 4 key columns of token 4 lg + r.  The operands
-  // of tile jb + 2 are read while the products of tile jb run.
+  // of tile jb + 3 are read while the products of tile jb run; in the last
+  // tiles (delta rule) the key fragments of the next chunk's blocks 0 and 1
+  // are read instead.  The next chunk's keys are in LDS already (loaded three
+  // chunks ahead); after the last chunk the reads fetch unused values.
+  lptr kn_b[4];
+  if constexpr (!GLA) {
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) kn_b[pp] = lane_base(k_buf<GLA>(c + 1), A.frag[pp]);
+  }
 #pragma unroll
   for (int jb = 0; jb < 8; ++jb) {
-    if (jb < 6) read_kt(jb + 2, kt[(jb + 2) % 3]);
+    if (jb < 5) read_kt(jb + 3, kt[(jb + 3) % 4]);
+    if (!GLA && (jb == 5 || jb == 6)) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) R.Kpre[jb - 5][pp] = as_op(ld3<uint4>(kn_b[pp], (jb - 5) * 4096));
+    }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc = R.S[jb];
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) acc = mfma(kt[jb % 3][pp], Uh[pp], acc);
+    for (int pp = 0; pp < 2; ++pp) acc = mfma(kt[jb % 4][pp], Uh[pp], acc);
     R.S[jb] = acc;
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -618,10 +645,10 @@ __device__ __forceinline__ void prefetch_keys(const Seq& sq, int64_t c, int slic
   const uint32_t kq = (uint32_t)(c * C * sq.dk * 2) + (uint32_t)((32 * slice + (lane & 31)) * 128);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.k, (lds_void*)&lds_touch[0], 4, kq, 0, 0, 0);
 }
-__device__ __forceinline__ void prefetch_rest(const Seq& sq, int64_t c, int slice, int DV, int lane) {
+__device__ __forceinline__ void prefetch_rest(const Seq& sq, int64_t c, int slice, int DV, int lane, bool q_on = true) {
   lds_void* land = (lds_void*)&lds_touch[0];
   const uint32_t kq = (uint32_t)(c * C * sq.dk * 2) + (uint32_t)((32 * slice + (lane & 31)) * 128);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.q, land, 4, kq, 0, 0, 0);
+  if (q_on) __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.q, land, 4, kq, 0, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.v, land, 4, (uint32_t)((c * C + lane) * DV * 2), 0, 0, 0);
   const uint32_t g = (uint32_t)(c * C * 4 + (lane & 1) * 128);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(sq.a, land, 4, g, 0, 0, 0);
@@ -846,7 +873,7 @@ __device__ __forceinline__ void loader_prologue(Smem& sm, const Seq& sq, const D
 //   go through LDS (lds_gst) by LDS-DMA: in registers, the compiler would
 //   wait for every load before their use, since its count ignores LDS-DMA
 //   loads.
-template <bool GLA>
+template <bool GLA, bool OUT = true>
 __device__ __forceinline__ void loader_period(Smem& sm, const Seq& sq, const DmaAddr& D, int64_t p, int64_t nch,
                                               int DV, float& ga, float& gb, int lane) {
   constexpr int KA = KQ_AHEAD<GLA>;
@@ -859,7 +886,7 @@ __device__ __forceinline__ void loader_period(Smem& sm, const Seq& sq, const Dma
     }
     if (p + 1 >= 0 && p + 1 < nch) {
       dma_v(sq, D, p + 1, DV);
-      dma_rows(sq.q, q_buf<GLA>(p + 1), sq, D, p + 1);
+      if (OUT) dma_rows(sq.q, q_buf<GLA>(p + 1), sq, D, p + 1);
     }
     if (p + 3 >= 0 && p + 3 < nch) dma_rows(sq.k, k_buf<GLA>(p + 3), sq, D, p + 3);
     if (p + 3 < nch) build_gates(sm, ga, gb, p + 3, sq.T, lane);
@@ -1006,7 +1033,10 @@ __host__ __device__ inline int map_chains(const ChainMap& m) {
 // with L = 0 (so Ti = I) and U = Y = diag(beta) V: the L and inverse waves
 // stay idle, and the state waves compute neither K S^T nor the product by Ti.
 // The state chain is then only the decayed accumulation of U^T K.
-template <bool GLA>
+// OUT = false (delta rule only): the first launch of the sequence split,
+// which needs the segment states and no output; the P wave, the loads of Q
+// and the output products are left out.
+template <bool GLA, bool OUT = true>
 __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -1124,13 +1154,13 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     lds_barrier();
     lds_barrier();
     if (nch > 0) {
-      state_period<false, true, GLA>(sm, sq, A, R, 0, DV, lane);
+      state_period<false, true, GLA, false, OUT>(sm, sq, A, R, 0, DV, lane);
       lds_barrier();
       for (int64_t p = 1; p < nch; ++p) {
-        state_period<true, true, GLA>(sm, sq, A, R, p, DV, lane);
+        state_period<true, true, GLA, !GLA, OUT>(sm, sq, A, R, p, DV, lane);
         lds_barrier();
       }
-      state_period<true, false, GLA>(sm, sq, A, R, nch, DV, lane);
+      if (OUT) state_period<true, false, GLA>(sm, sq, A, R, nch, DV, lane);
     }
     lds_barrier();
     if (sT) {
@@ -1143,7 +1173,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     const StateAddr A = state_addr(lane, 0, DV);
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
-      if (p >= 0 && p < nch) build_p<GLA>(sm, A, p, lane);
+      if (OUT && p >= 0 && p < nch) build_p<GLA>(sm, A, p, lane);
       lds_barrier();
     }
   } else if (GLA && wave == W_L) {
@@ -1179,7 +1209,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     loader_prologue<GLA>(sm, sq, D, nch, ga, gb, lane);
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
-      loader_period<GLA>(sm, sq, D, p, nch, DV, ga, gb, lane);
+      loader_period<GLA, OUT>(sm, sq, D, p, nch, DV, ga, gb, lane);
       if constexpr (GLA)
         lds_barrier_keep_dma();  // this period's K loads stay in flight
       else
@@ -1211,7 +1241,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
         }
       } else {
         if (p + 5 < nch) prefetch_keys(sq, p + 5, slice, lane);
-        if (p + 3 < nch) prefetch_rest(sq, p + 3, slice, DV, lane);
+        if (p + 3 < nch) prefetch_rest(sq, p + 3, slice, DV, lane, OUT);
       }
       lds_barrier_keep_dma();
     }

@@ -71,10 +71,17 @@ int launch_chunk_pipe(const void* q, const void* k, const void* v, const float* 
   // one sequence's q, k or v must fit a 32-bit buffer range
   if (cm.T * dk * 2 > 0x7fffffff || cm.T * dv * 2 > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
   const int xcd_map = (nchain % 8) == 0;
-  hipLaunchKernelGGL(gdn::pipe::chunk_fwd_pipe_kernel<GLA>, dim3((unsigned)nblocks), dim3(64 * gdn::pipe::NWAVES), 0,
-                     stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                     static_cast<const bf16_t*>(v), alpha, beta, s0, static_cast<bf16_t*>(o), sT, cm,
-                     (int)dv, (int)dk, xcd_map);
+  // the first launch of the sequence split needs no output
+  if (!GLA && cm.mode == gdn::pipe::MAP_SPLIT_A)
+    hipLaunchKernelGGL((gdn::pipe::chunk_fwd_pipe_kernel<false, false>), dim3((unsigned)nblocks),
+                       dim3(64 * gdn::pipe::NWAVES), 0, stream, static_cast<const bf16_t*>(q),
+                       static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), alpha, beta, s0,
+                       static_cast<bf16_t*>(o), sT, cm, (int)dv, (int)dk, xcd_map);
+  else
+    hipLaunchKernelGGL(gdn::pipe::chunk_fwd_pipe_kernel<GLA>, dim3((unsigned)nblocks), dim3(64 * gdn::pipe::NWAVES),
+                       0, stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                       static_cast<const bf16_t*>(v), alpha, beta, s0, static_cast<bf16_t*>(o), sT, cm,
+                       (int)dv, (int)dk, xcd_map);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
