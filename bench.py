@@ -227,8 +227,9 @@ def time_routes(torch, dev, launches=5):
     token).  Mean times."""
     from gated_deltanet_sequence_amd import inputs
     from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd, gdn_chunk_fwd_split,
-                                                     gdn_chunk_fwd_split_workspace, gdn_recurrent_step,
-                                                     gdn_scan_fwd, gdn_scan_fwd_vecgate, gdn_scan_fwd_workspace)
+                                                     gdn_chunk_fwd_split_workspace, gdn_chunk_fwd_vecgate,
+                                                     gdn_recurrent_step, gdn_scan_fwd, gdn_scan_fwd_vecgate,
+                                                     gdn_scan_fwd_workspace)
     B, H, T, d = ROUTES["B"], ROUTES["H"], ROUTES["T"], ROUTES["d"]
     x = inputs.make_fwd_inputs(B, H, T, d, "bf16", seed=ROUTES["seed"])
     xd = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
@@ -237,14 +238,20 @@ def time_routes(torch, dev, launches=5):
                       dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     a = (xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None)
-    # the same gates repeated over the key dimension, for the per-dimension-gate route
+    # the same gates repeated over the key dimension, for the per-dimension-gate routes,
+    # and a gate drawn per key dimension (the same law) for the chunked one
     av = xd["alpha"][..., None].expand(-1, -1, -1, d).contiguous()
+    avd = inputs.make_vec_alpha(B, H, T, d, seed=ROUTES["seed"] + 100).to(dev)
     res = {"workload": "route comparison: B=1, H=8, T=16384, d_k=d_v=64, bf16 q/k/v, fp32 gates, zero S0"}
     for name, f in (("chunked", lambda: gdn_chunk_fwd(*a, 64, stream=stream)),
                     ("chunked_split", lambda: gdn_chunk_fwd_split(*a, 64, workspace=wsp, stream=stream)),
                     ("scan", lambda: gdn_scan_fwd(*a, workspace=ws, stream=stream)),
                     ("scan_vecgate", lambda: gdn_scan_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"],
-                                                                  None, workspace=ws, stream=stream))):
+                                                                  None, workspace=ws, stream=stream)),
+                    ("chunked_vecgate", lambda: gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"],
+                                                                      None, stream=stream)),
+                    ("chunked_vecgate_percolumn", lambda: gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], avd,
+                                                                                xd["beta"], None, stream=stream))):
         settle_clocks(torch, f)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)

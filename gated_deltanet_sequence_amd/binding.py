@@ -56,6 +56,8 @@ def load_library(path: str | None = None):
     lib.gdn_scan_fwd.restype = i32
     lib.gdn_scan_fwd_vecgate.argtypes = lib.gdn_scan_fwd.argtypes
     lib.gdn_scan_fwd_vecgate.restype = i32
+    lib.gdn_chunk_fwd_vecgate.argtypes = lib.gdn_chunk_fwd.argtypes
+    lib.gdn_chunk_fwd_vecgate.restype = i32
     lib.gdn_scan_fwd_workspace.argtypes = [i64, i64, i64, i64, i64, i32]
     lib.gdn_scan_fwd_workspace.restype = ctypes.c_size_t
     lib.gdn_chunk_fwd_split.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
@@ -202,6 +204,29 @@ def gdn_scan_fwd_vecgate(q, k, v, alpha, beta, initial_state=None, **kw):
     """gdn_scan_fwd with a per-dimension gate alpha [B,H,T,dk] (fp32) that
     decays the key columns of the state."""
     return gdn_scan_fwd(q, k, v, alpha, beta, initial_state, _vecgate=True, **kw)
+
+
+VECGATE_CHUNK = 32
+
+
+def gdn_chunk_fwd_vecgate(q, k, v, alpha, beta, initial_state=None, chunk_size: int = VECGATE_CHUNK, *,
+                          o=None, final_state=None, output_final_state: bool = True, stream=None):
+    """Chunked forward pass with a per-dimension gate alpha [B,H,T,dk] (fp32)
+    that decays the key columns of the state; bf16 q/k/v, 32-token chunks."""
+    B, H, T, dk, dv = _check_fwd_args(q, k, v, alpha, beta, initial_state, alpha_per_dim=True)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    rc = lib.gdn_chunk_fwd_vecgate(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                   _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                                   _dev_ptr(initial_state, "initial_state"), _dev_ptr(o, "o"),
+                                   _dev_ptr(final_state, "final_state"), B, H, T, dk, dv,
+                                   int(chunk_size), _DTYPES[q.dtype], _stream_ptr(stream, q.device))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_chunk_fwd_vecgate")
+    return o, final_state
 
 
 def gdn_chunk_fwd_split_workspace(B, H, T, dk, dv, chunk_size: int = 64, dtype=torch.bfloat16) -> int:

@@ -1,0 +1,414 @@
+// Chunked forward pass of the gated delta rule with a per-dimension gate,
+// bf16 inputs, d_k = d_v = 64 or 128, on gfx950.
+//
+// Sources (web pages, by title and section):
+//   [P1] "Gated DeltaNet GPU并行实现：拆解线性注意力循环的两种高效方案"
+//        §2.2 the forgetting gate may be a scalar or a vector (one factor per
+//        dimension); §3.2 chunked evaluation (dense products inside a chunk,
+//        serial state carry between chunks); §4.4 fp32 state, bf16 matmul
+//        inputs with fp32 accumulation.
+//
+// The recurrence.  alpha_t in [0,1]^{d_k} decays the key columns of the state:
+//     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+//     o_t = S_t q_t.
+//
+// Chunk algebra (derived from the token loop as for the scalar gate).  For a
+// chunk with start state S, let G_r[j] = sum_{s <= r} log2 alpha_s[j] (the
+// decay of key column j from the chunk start through token r) and write
+// x~ = 2^G o x for a token row x.  Then per token pair s <= r the decay
+// between them is 2^(G_r - G_s) per column, so
+//     A_qk[r][s] = q~_r . (2^-G_s o k_s),   A_kk[r][s] = k~_r . (2^-G_s o k_s)
+//     L = strictly-lower(diag(beta) A_kk),  Ti = (I + L)^-1,  P = lower(A_qk)
+//     U = Ti diag(beta) (V - K~ S^T)
+//     O = Q~ S^T + P U
+//     S' = S Diag(2^(G_C)) + U^T Kbar,   Kbar_s = 2^(G_C - G_s) o k_s.
+// The per-column decay of the scalar-gate masks moves into the operands: the
+// products stay plain matrix products (MFMA), the masks only zero the upper
+// triangle.  All factors are at most 1 except 2^-G_s, which is at most
+// 2^100 while the chunk decays by no more than 2^-100 in every column
+// (SAFE_MIN); then every factor and product lies in the normal fp32/bf16
+// range.  A chunk that decays more in some column (strong gates, a gate of
+// 0) forms A_qk and A_kk element by element from 2^(G_r - G_s) <= 1 instead
+// (slow, exact; such chunks carry almost nothing across anyway).
+//
+// Work split and layout as in chunk_fwd.hpp: one workgroup per (sequence,
+// 16-row value slice) walks all chunks; the fp32 state slice lives in MFMA
+// accumulators, a bf16 copy in LDS feeds the products; four waves in
+// phase-synchronous steps.  The chunk is 32 tokens: the fp32 table of G
+// (32 x d_k) and the four operand copies of q and k it needs per chunk then
+// fit in LDS next to the chunk matrices with room for two workgroups per CU.
+#pragma once
+
+#include "gdn_common.hpp"
+
+namespace gdn {
+namespace vec {
+
+constexpr int C = 32;      // tokens per chunk
+constexpr int DVS = 16;    // value rows per workgroup
+constexpr int NW = 4;      // waves
+constexpr int NT = NW * 64;
+constexpr float SAFE_MIN = -100.f;  // log2 of the least chunk decay the factored products take
+
+template <int DK>
+struct Smem {
+  static constexpr int LDK = DK + 8;  // bf16 rows of d_k, padded by 16 bytes
+  static constexpr int LDC = C + 8;   // bf16 rows of C, padded by 16 bytes
+  bf16_t Qs[C * LDK];    // 2^G o q, [token][dk]
+  bf16_t Kr[C * LDK];    // 2^G o k
+  bf16_t Kh[C * LDK];    // 2^-G o k (Gram columns); raw k in chunks on the exact path
+  bf16_t Qr[C * LDK];    // raw q (exact path)
+  bf16_t Kbt[DK * LDC];  // (2^(G_C - G) o k)^T, [dk][token]
+  bf16_t V[C * DVS];     // value slice, [token][dvs]
+  bf16_t S[DVS * LDK];   // operand copy of the state slice, [dv][dk]
+  bf16_t Yt[DVS * LDC];  // right-hand side of the triangular system, [dv][token]
+  bf16_t Ut[DVS * LDC];  // U^T
+  bf16_t Ti[C * LDC];    // (I + L)^-1, [token][token]
+  bf16_t Tt[C * LDC];    // its transpose while it is built
+  bf16_t Lb[C * LDC];    // L, operand copy
+  bf16_t P[C * LDC];     // lower(A_qk), [r][s]
+  bf16_t Mt[16 * LDC];   // partial product of the blocked inverse
+  float Ld[2][16][17];   // fp32 diagonal 16x16 blocks of L
+  float G[C * DK];       // log2-prefix of alpha per key column, [token][dk]
+  float beta[C];
+  float Ec[DK];          // 2^(G_C) per key column
+  int exactw[NW];        // per wave: a column of this chunk decays below 2^SAFE_MIN
+};
+
+template <int DK>
+__global__ __launch_bounds__(NT) void chunk_vec_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta,
+    const float* initial_state, bf16_t* __restrict__ o, float* final_state,
+    int nchain, int64_t Tlen, int DV, int xcd_map) {
+  using Sm = Smem<DK>;
+  using T = bf16_t;
+  constexpr int LDK = Sm::LDK;
+  constexpr int LDC = Sm::LDC;
+  constexpr int VEC = 8;                         // bf16 per 16-byte vector
+  constexpr int NQK = C * DK / VEC / NT;         // vectors per thread, q or k
+  constexpr int NVV = C * DVS / VEC;             // vectors of V (threads 0 .. NVV-1)
+  constexpr int IB = DVS / 16;
+  constexpr int JB = DK / 16;
+  constexpr int RB = C / 16;
+  constexpr int NST = (JB * IB + NW - 1) / NW;   // state tiles per wave
+  constexpr int NOT = (IB * RB + NW - 1) / NW;   // output tiles per wave
+  static_assert(NQK * NT * VEC == C * DK, "q/k vectors spread evenly");
+  static_assert(NVV <= NT && DK <= NT && C <= 64, "one thread per V vector, key column, token");
+  static_assert(RB == 2, "the blocked inverse below is for two 16-token blocks");
+
+  __shared__ Sm sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+
+  const int NS = DV / DVS;
+  int chain, slice;
+  {
+    const int w = blockIdx.x;
+    if (xcd_map) {
+      // the slices of one sequence land on one XCD and share its L2
+      const int x = w & 7, r = w >> 3;
+      slice = r % NS;
+      chain = (r / NS) * 8 + x;
+    } else {
+      chain = w / NS;
+      slice = w % NS;
+    }
+  }
+  if (chain >= nchain) return;
+
+  const T* qc = q + (int64_t)chain * Tlen * DK;
+  const T* kc = k + (int64_t)chain * Tlen * DK;
+  const T* vc = v + (int64_t)chain * Tlen * DV + slice * DVS;
+  const float* ac = alpha + (int64_t)chain * Tlen * DK;
+  const float* bc = beta + (int64_t)chain * Tlen;
+  T* oc = o + (int64_t)chain * Tlen * DV + slice * DVS;
+  const int64_t st_off = ((int64_t)chain * DV + (int64_t)slice * DVS) * DK;
+
+  // The upper blocks of the triangular buffers are never written and must
+  // read as zero.
+  for (int e = tid; e < C * LDC; e += NT) {
+    sm.Ti[e] = Elem<T>::from_f32(0.f);
+    sm.Tt[e] = Elem<T>::from_f32(0.f);
+    sm.P[e] = Elem<T>::from_f32(0.f);
+    sm.Lb[e] = Elem<T>::from_f32(0.f);
+  }
+
+  // State slice: S^T tiles [j-block][i-block] in MFMA accumulators.
+  f32x4 Sacc[NST];
+#pragma unroll
+  for (int m = 0; m < NST; ++m) {
+    const int t = wave + NW * m;
+    Sacc[m] = zero4();
+    if (t < JB * IB) {
+      const int jb = t / IB, ib = t % IB;
+      const int i = ib * 16 + lr, j = jb * 16 + 4 * lg;
+      if (initial_state) {
+        const float4 s4 = *reinterpret_cast<const float4*>(initial_state + st_off + (int64_t)i * DK + j);
+        Sacc[m] = f32x4{s4.x, s4.y, s4.z, s4.w};
+      }
+      store4<T>(&sm.S[i * LDK + j], Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
+    }
+  }
+
+  const int64_t nchunks = (Tlen + C - 1) / C;
+
+  // Register staging of the next chunk (prefetch): q, k vectors, a V vector,
+  // the gates of one key column over the chunk (thread j < DK) and beta of
+  // one token (thread r < C).  Tokens past the end read as zero q, k, v,
+  // alpha = 1 and beta = 0 (identity maps).
+  uint4 rq[NQK], rk[NQK], rv;
+  float ra[C], rbt;
+  auto load_chunk = [&](int64_t ch) {
+    const int64_t t0 = ch * C;
+#pragma unroll
+    for (int it = 0; it < NQK; ++it) {
+      const int vi = tid + NT * it;
+      const int r = vi / (DK / VEC), cg = vi % (DK / VEC);
+      const bool ok = t0 + r < Tlen;
+      const int64_t off = (t0 + r) * DK + cg * VEC;
+      rq[it] = ok ? *reinterpret_cast<const uint4*>(qc + off) : make_uint4(0, 0, 0, 0);
+      rk[it] = ok ? *reinterpret_cast<const uint4*>(kc + off) : make_uint4(0, 0, 0, 0);
+    }
+    {
+      const int r = tid / (DVS / VEC), cg = tid % (DVS / VEC);
+      const bool ok = tid < NVV && t0 + r < Tlen;
+      rv = ok ? *reinterpret_cast<const uint4*>(vc + (t0 + r) * DV + cg * VEC) : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < DK) {
+#pragma unroll
+      for (int r = 0; r < C; ++r) ra[r] = t0 + r < Tlen ? ac[(t0 + r) * DK + tid] : 1.f;
+    }
+    rbt = (tid < C && t0 + tid < Tlen) ? bc[t0 + tid] : 0.f;
+  };
+
+  if (nchunks > 0) load_chunk(0);
+
+  for (int64_t ch = 0; ch < nchunks; ++ch) {
+    __syncthreads();  // the previous chunk has finished with every buffer
+
+    // Gate table: thread j < DK walks column j over the chunk's tokens.
+    {
+      bool low = false;
+      if (tid < DK) {
+        float g = 0.f;
+#pragma unroll
+        for (int r = 0; r < C; ++r) {
+          g += fmaxf(fast_log2(ra[r]), LOG2_ALPHA_MIN);
+          sm.G[r * DK + tid] = g;
+        }
+        sm.Ec[tid] = fast_exp2(g);
+        low = g < SAFE_MIN;
+      }
+      const bool any = __builtin_amdgcn_ballot_w64(low) != 0;
+      if (lane == 0) sm.exactw[wave] = any ? 1 : 0;
+    }
+    if (tid < C) sm.beta[tid] = rbt;
+    if (tid < NVV) {
+      const int r = tid / (DVS / VEC), cg = tid % (DVS / VEC);
+      *reinterpret_cast<uint4*>(&sm.V[r * DVS + cg * VEC]) = rv;
+    }
+    __syncthreads();
+    bool exact = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) exact = exact || sm.exactw[w] != 0;
+
+    // Operands: 2^G o q, 2^G o k, 2^-G o k (raw q, k on the exact path), and
+    // (2^(G_C - G) o k)^T.
+#pragma unroll
+    for (int it = 0; it < NQK; ++it) {
+      const int vi = tid + NT * it;
+      const int r = vi / (DK / VEC), cg = vi % (DK / VEC);
+      const int j0 = cg * VEC;
+      const float4 g0 = *reinterpret_cast<const float4*>(&sm.G[r * DK + j0]);
+      const float4 g1 = *reinterpret_cast<const float4*>(&sm.G[r * DK + j0 + 4]);
+      const float4 c0 = *reinterpret_cast<const float4*>(&sm.G[(C - 1) * DK + j0]);
+      const float4 c1 = *reinterpret_cast<const float4*>(&sm.G[(C - 1) * DK + j0 + 4]);
+      const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const float gc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const T* qe = reinterpret_cast<const T*>(&rq[it]);
+      const T* ke = reinterpret_cast<const T*>(&rk[it]);
+      float qs[8], kr[8], kh[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qv = Elem<T>::to_f32(qe[e]), kv = Elem<T>::to_f32(ke[e]);
+        const float eg = fast_exp2(g[e]);
+        qs[e] = qv * eg;
+        kr[e] = kv * eg;
+        kh[e] = exact ? kv : kv * fast_exp2(-g[e]);
+        sm.Kbt[(j0 + e) * LDC + r] = Elem<T>::from_f32(kv * fast_exp2(gc[e] - g[e]));
+      }
+      *reinterpret_cast<uint4*>(&sm.Qs[r * LDK + j0]) =
+          make_uint4(pack_bf16x2(qs[0], qs[1]), pack_bf16x2(qs[2], qs[3]), pack_bf16x2(qs[4], qs[5]), pack_bf16x2(qs[6], qs[7]));
+      *reinterpret_cast<uint4*>(&sm.Kr[r * LDK + j0]) =
+          make_uint4(pack_bf16x2(kr[0], kr[1]), pack_bf16x2(kr[2], kr[3]), pack_bf16x2(kr[4], kr[5]), pack_bf16x2(kr[6], kr[7]));
+      *reinterpret_cast<uint4*>(&sm.Kh[r * LDK + j0]) =
+          make_uint4(pack_bf16x2(kh[0], kh[1]), pack_bf16x2(kh[2], kh[3]), pack_bf16x2(kh[4], kh[5]), pack_bf16x2(kh[6], kh[7]));
+      if (exact) *reinterpret_cast<uint4*>(&sm.Qr[r * LDK + j0]) = rq[it];
+    }
+    if (ch + 1 < nchunks) load_chunk(ch + 1);
+    __syncthreads();
+
+    // Gram products on the lower block triangle in [s][r] orientation (each
+    // lane holds four consecutive s of one row r):
+    //   L[r][s] = beta_r A_kk[r][s] (s < r),  P[r][s] = A_qk[r][s] (s <= r).
+    // Tiles u = 0..5: kind u / 3 (0: L, 1: P), block pair (sb, rb) =
+    // (0,0), (0,1), (1,1).
+    for (int u = wave; u < 6; u += NW) {
+      const int kind = u / 3, pr = u % 3;
+      const int rb = pr >= 1 ? 1 : 0, sb = pr == 1 ? 0 : rb;
+      const int r = rb * 16 + lr;
+      const int s0 = sb * 16 + 4 * lg;
+      float val[4];
+      if (!exact) {
+        const f32x4 acc = Mma<T>::template run<DK>(zero4(), &sm.Kh[sb * 16 * LDK], LDK,
+                                                   &(kind == 0 ? sm.Kr : sm.Qs)[rb * 16 * LDK], LDK, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = acc[e];
+      } else {
+        // A[r][s] = sum_j x_r[j] k_s[j] 2^(G_r[j] - G_s[j]), every factor <= 1
+        const T* xr = &(kind == 0 ? sm.Kh : sm.Qr)[r * LDK];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = s0 + e;
+          const T* ks = &sm.Kh[s * LDK];
+          float acc = 0.f;
+          if (s <= r) {
+            for (int j = 0; j < DK; ++j)
+              acc += Elem<T>::to_f32(xr[j]) * Elem<T>::to_f32(ks[j]) * fast_exp2(sm.G[r * DK + j] - sm.G[s * DK + j]);
+          }
+          val[e] = acc;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = s0 + e;
+        const bool in = kind == 0 ? (s < r) : (s <= r);
+        val[e] = in ? (kind == 0 ? sm.beta[r] : 1.f) * val[e] : 0.f;
+      }
+      T* dst = kind == 0 ? sm.Lb : sm.P;
+      store4<T>(&dst[r * LDC + s0], val[0], val[1], val[2], val[3]);
+      if (kind == 0 && sb == rb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.Ld[sb][r - rb * 16][s0 - sb * 16 + e] = val[e];
+      }
+    }
+    __syncthreads();
+
+    // Ti = (I + L)^-1, blocked: the two unit-lower 16x16 diagonal blocks by
+    // forward substitution in fp32 (lane = block, column) ...
+    if (wave == 0 && lane < 32) {
+      const int b = lane >> 4, c = lane & 15;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+        for (int s = 0; s < r; ++s) acc -= sm.Ld[b][r][s] * x[s];
+        x[r] = acc;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sm.Ti[(16 * b + r) * LDC + 16 * b + c] = Elem<T>::from_f32(x[r]);
+        sm.Tt[(16 * b + c) * LDC + 16 * b + r] = Elem<T>::from_f32(x[r]);
+      }
+    }
+    __syncthreads();
+    // ... then the off-diagonal block Ti[1][0] = -Ti[1][1] L[1][0] Ti[0][0].
+    if (wave == 0) {
+      const f32x4 acc = Mma<T>::template run<16>(zero4(), &sm.Lb[16 * LDC], LDC, &sm.Tt[0], LDC, lane);
+      store4<T>(&sm.Mt[lr * LDC + 4 * lg], acc[0], acc[1], acc[2], acc[3]);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const f32x4 acc = Mma<T>::template run<16>(zero4(), &sm.Ti[16 * LDC + 16], LDC, &sm.Mt[0], LDC, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.Ti[(16 + 4 * lg + e) * LDC + lr] = Elem<T>::from_f32(-acc[e]);
+    }
+    __syncthreads();
+
+    // Y = diag(beta) (V - K~ S^T) (tiles [r][i]) and the inter-chunk part of
+    // the output, S Q~^T (tiles [i][r], kept live).
+    for (int t = wave; t < RB * IB; t += NW) {
+      const int rb = t / IB, ib = t % IB;
+      const f32x4 acc = Mma<T>::template run<DK>(zero4(), &sm.Kr[rb * 16 * LDK], LDK,
+                                                 &sm.S[ib * 16 * LDK], LDK, lane);
+      const int i = ib * 16 + lr;
+      const int r0 = rb * 16 + 4 * lg;
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + e;
+        y[e] = sm.beta[r] * (Elem<T>::to_f32(sm.V[r * DVS + i]) - acc[e]);
+      }
+      store4<T>(&sm.Yt[i * LDC + r0], y[0], y[1], y[2], y[3]);
+    }
+    f32x4 Oacc[NOT];
+#pragma unroll
+    for (int m = 0; m < NOT; ++m) {
+      const int t = wave + NW * m;
+      Oacc[m] = zero4();
+      if (t < IB * RB) {
+        const int ib = t / RB, rb = t % RB;
+        Oacc[m] = Mma<T>::template run<DK>(zero4(), &sm.S[ib * 16 * LDK], LDK, &sm.Qs[rb * 16 * LDK], LDK, lane);
+      }
+    }
+    __syncthreads();
+
+    // U = Ti Y (tiles [r][i]), stored as U^T.
+    for (int t = wave; t < RB * IB; t += NW) {
+      const int rb = t / IB, ib = t % IB;
+      const f32x4 acc = Mma<T>::template run<C>(zero4(), &sm.Ti[rb * 16 * LDC], LDC, &sm.Yt[ib * 16 * LDC], LDC, lane);
+      const int i = ib * 16 + lr;
+      const int r0 = rb * 16 + 4 * lg;
+      store4<T>(&sm.Ut[i * LDC + r0], acc[0], acc[1], acc[2], acc[3]);
+    }
+    __syncthreads();
+
+    // O^T += U^T P^T and store; S^T <- Diag(2^(G_C)) S^T + Kbar^T U.
+#pragma unroll
+    for (int m = 0; m < NOT; ++m) {
+      const int t = wave + NW * m;
+      if (t < IB * RB) {
+        const int ib = t / RB, rb = t % RB;
+        Oacc[m] = Mma<T>::template run<C>(Oacc[m], &sm.Ut[ib * 16 * LDC], LDC, &sm.P[rb * 16 * LDC], LDC, lane);
+        const int64_t tok = ch * C + rb * 16 + lr;
+        if (tok < Tlen)
+          store4<T>(oc + tok * DV + ib * 16 + 4 * lg, Oacc[m][0], Oacc[m][1], Oacc[m][2], Oacc[m][3]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NST; ++m) {
+      const int t = wave + NW * m;
+      if (t < JB * IB) {
+        const int jb = t / IB, ib = t % IB;
+        const int i = ib * 16 + lr, j = jb * 16 + 4 * lg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sacc[m][e] *= sm.Ec[j + e];
+        Sacc[m] = Mma<T>::template run<C>(Sacc[m], &sm.Kbt[jb * 16 * LDC], LDC, &sm.Ut[ib * 16 * LDC], LDC, lane);
+        store4<T>(&sm.S[i * LDK + j], Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
+      }
+    }
+  }
+
+  // final state slice (fp32)
+  if (final_state) {
+#pragma unroll
+    for (int m = 0; m < NST; ++m) {
+      const int t = wave + NW * m;
+      if (t < JB * IB) {
+        const int jb = t / IB, ib = t % IB;
+        const int i = ib * 16 + lr, j = jb * 16 + 4 * lg;
+        *reinterpret_cast<float4*>(final_state + st_off + (int64_t)i * DK + j) =
+            make_float4(Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
+      }
+    }
+  }
+}
+
+}  // namespace vec
+}  // namespace gdn

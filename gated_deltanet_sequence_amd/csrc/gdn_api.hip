@@ -9,6 +9,7 @@
 #include "gdn.h"
 #include "chunk_fwd.hpp"
 #include "chunk_fwd_pipe.hpp"
+#include "chunk_vec.hpp"
 #include "recurrent_step.hpp"
 #include "split_combine.hpp"
 #include "scan_route.hpp"
@@ -401,6 +402,35 @@ int gdn_scan_fwd_vecgate(const void* q, const void* k, const void* v, const floa
                          void* workspace, size_t workspace_bytes, void* hip_stream) {
   return scan_fwd<true>(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv, dtype,
                         workspace, workspace_bytes, hip_stream);
+}
+
+int gdn_chunk_fwd_vecgate(const void* q, const void* k, const void* v, const float* alpha,
+                          const float* beta, const float* initial_state, void* o, float* final_state,
+                          int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk_size,
+                          gdn_dtype dtype, void* hip_stream) {
+  // the shared checks with the scalar path's chunk size; this route's own below
+  const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
+                           chunk_size > 0 ? 64 : chunk_size, dtype, false, true);
+  if (rc != GDN_OK) return rc;
+  if (chunk_size != gdn::vec::C || dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  const int64_t nchain = B * H;
+  if (nchain == 0) return GDN_OK;
+  if (T == 0 && !final_state) return GDN_OK;
+  const int64_t nblocks = nchain * (dv / gdn::vec::DVS);
+  if (nblocks > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+  const int xcd_map = (nchain % 8) == 0;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (dk == 128)
+    hipLaunchKernelGGL(gdn::vec::chunk_vec_kernel<128>, dim3((unsigned)nblocks), dim3(gdn::vec::NT), 0, stream,
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
+                       alpha, beta, initial_state, static_cast<bf16_t*>(o), final_state, (int)nchain, T, (int)dv,
+                       xcd_map);
+  else
+    hipLaunchKernelGGL(gdn::vec::chunk_vec_kernel<64>, dim3((unsigned)nblocks), dim3(gdn::vec::NT), 0, stream,
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
+                       alpha, beta, initial_state, static_cast<bf16_t*>(o), final_state, (int)nchain, T, (int)dv,
+                       xcd_map);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 size_t gdn_chunk_fwd_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,

@@ -80,6 +80,28 @@ def _gates(rng, shape, gate: str):
             torch.from_numpy(beta.astype(np.float32)).contiguous())
 
 
+def make_vec_alpha(B: int, H: int, T: int, d: int, seed: int, gate: str = "default") -> torch.Tensor:
+    """Per-dimension gate alpha [B,H,T,d] fp32: the scalar gate laws of
+    ``_gates`` drawn independently per token and key dimension from
+    ``numpy.random.default_rng(seed)`` ('default': exp(-softplus(z)); 'slow':
+    exp(-0.01 softplus(z)); 'fast': exp(-4 softplus(z)); 'resets': 0 where
+    z > 2.3, else exp(-softplus(z)))."""
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((B, H, T, d), dtype=np.float32)
+    sp = _softplus64(z)
+    if gate == "default":
+        alpha = np.exp(-sp)
+    elif gate == "slow":
+        alpha = np.exp(-0.01 * sp)
+    elif gate == "fast":
+        alpha = np.exp(-4.0 * sp)
+    elif gate == "resets":
+        alpha = np.where(z > 2.3, 0.0, np.exp(-sp))
+    else:
+        raise ValueError("gate must be one of 'default', 'slow', 'fast', 'resets'")
+    return torch.from_numpy(alpha.astype(np.float32)).contiguous()
+
+
 def make_fwd_inputs(B: int, H: int, T: int, d: int, dtype: str = "bf16",
                     seed: int = 0, init_state: bool = False,
                     gate: str = "default", dv: int | None = None) -> dict:

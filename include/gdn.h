@@ -150,6 +150,25 @@ int gdn_scan_fwd_vecgate(const void* q, const void* k, const void* v,
                          gdn_dtype dtype, void* workspace, size_t workspace_bytes,
                          void* hip_stream);
 
+/*
+ * gdn_chunk_fwd_vecgate — the per-dimension gate of gdn_scan_fwd_vecgate on
+ * the chunked route ([P1] §2.2 vector gate, §3.2 chunked evaluation): alpha
+ * is [B,H,T,dk] fp32, each entry in [0,1], decaying the key columns of the
+ * state,
+ *     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
+ * The per-column decay is folded into the chunk's key and query operands, so
+ * the chunk products stay dense MFMA products.  bf16 q/k/v only; chunk_size
+ * must be 32 (this route's chunk: its per-token, per-column decay table and
+ * the scaled operand copies fit the LDS at that size); otherwise
+ * GDN_ERR_UNSUPPORTED.  Other arguments, layouts, aliasing and errors as for
+ * gdn_chunk_fwd.  A gate under 2^-200 acts as 2^-200, as on the scalar path.
+ */
+int gdn_chunk_fwd_vecgate(const void* q, const void* k, const void* v,
+                          const float* alpha, const float* beta,
+                          const float* initial_state, void* o, float* final_state,
+                          int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                          int64_t chunk_size, gdn_dtype dtype, void* hip_stream);
+
 /* Workspace bytes gdn_scan_fwd needs for these sizes.  Host-only. */
 size_t gdn_scan_fwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
                               gdn_dtype dtype);

@@ -1,7 +1,7 @@
 """GPU parity of the delta rule with a per-dimension gate on the key columns
-(gdn_scan_fwd_vecgate, scan route) against its fp64 oracle
-(oracle_fwd_vecgate), with the workloads' bars (2e-2 bf16, 1e-4 fp32,
-max-abs-normwise on o and the final state).
+(gdn_scan_fwd_vecgate, scan route; gdn_chunk_fwd_vecgate, chunked route)
+against its fp64 oracle (oracle_fwd_vecgate), with the workloads' bars
+(2e-2 bf16, 1e-4 fp32, max-abs-normwise on o and the final state).
 
 Gates: alpha_t[j] = exp(-softplus(z)) drawn per token and key dimension from
 the seeded generator (the scalar-gate law of the workloads, per dimension);
@@ -12,7 +12,8 @@ import torch
 
 import oracle
 from gated_deltanet_sequence_amd import inputs
-from gated_deltanet_sequence_amd.binding import gdn_scan_fwd, gdn_scan_fwd_vecgate
+from gated_deltanet_sequence_amd.binding import (GDNError, gdn_chunk_fwd, gdn_chunk_fwd_vecgate, gdn_scan_fwd,
+                                                 gdn_scan_fwd_vecgate)
 
 from _helpers import TOL, maxrel, oracle_inputs, to_dev, to_np
 
@@ -62,3 +63,85 @@ def test_uniform_vecgate_matches_scalar_gate():
     o2, s2 = gdn_scan_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"])
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+# Chunked route (bf16, 32-token chunks).  Gates per dimension with the gate
+# laws of the workloads: default, slow (long memory), fast (every chunk
+# decays below 2^-100 in some column: the exact element-wise products) and
+# resets (a gate of 0 in ~1 % of the entries: the exact path for the chunks
+# that hold one).
+CHUNK_CASES = [
+    # B, H, T, d, initial state, gate
+    (1, 1, 1, 128, True, "default"),
+    (1, 2, 31, 64, False, "default"),
+    (2, 1, 33, 128, True, "default"),
+    (1, 3, 1000, 64, True, "default"),
+    (2, 2, 777, 128, True, "slow"),
+    (1, 2, 2048, 128, True, "slow"),
+    (1, 2, 300, 128, True, "fast"),
+    (2, 1, 500, 64, True, "resets"),
+    (1, 2, 640, 128, False, "resets"),
+    (8, 1, 256, 128, True, "default"),   # 8 sequences: XCD-grouped mapping
+]
+
+
+def run_chunk_vec(x):
+    xd = to_dev(x)
+    o, sT = gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"])
+    torch.cuda.synchronize()
+    return o, sT
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=lambda c: "B%dH%dT%dd%d_%s_%s" % (
+    c[0], c[1], c[2], c[3], "s0" if c[4] else "z", c[5]))
+def test_chunked_vecgate_against_oracle(case):
+    B, H, T, d, init, gate = case
+    print("case chunked vecgate", case, flush=True)
+    x = inputs.make_fwd_inputs(B, H, T, d, "bf16", seed=700 + T + d, init_state=init)
+    x["alpha"] = inputs.make_vec_alpha(B, H, T, d, seed=800 + T, gate=gate)
+    o, sT = run_chunk_vec(x)
+    (q, k, v, _, b), s0 = oracle_inputs(x)
+    ro, rs = oracle.oracle_fwd_vecgate(q, k, v, x["alpha"].numpy(), b, s0)
+    eo, es = maxrel(to_np(o), ro), maxrel(to_np(sT), rs)
+    print("  err o %.3e  err S_T %.3e (tol %.0e)" % (eo, es, TOL["bf16"]), flush=True)
+    assert np.all(np.isfinite(to_np(o))) and np.all(np.isfinite(to_np(sT)))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_chunked_vecgate_main_shape():
+    """The main workload's shape (B=4, H=16, T=8192, d=128) with a per-
+    dimension default gate, every output and the final state."""
+    B, H, T, d = 4, 16, 8192, 128
+    print("case chunked vecgate main shape", flush=True)
+    x = inputs.make_fwd_inputs(B, H, T, d, "bf16", seed=3)
+    x["alpha"] = inputs.make_vec_alpha(B, H, T, d, seed=33)
+    o, sT = run_chunk_vec(x)
+    (q, k, v, _, b), s0 = oracle_inputs(x)
+    ro, rs = oracle.oracle_fwd_vecgate(q, k, v, x["alpha"].numpy(), b, s0)
+    eo, es = maxrel(to_np(o), ro), maxrel(to_np(sT), rs)
+    print("  err o %.3e  err S_T %.3e" % (eo, es), flush=True)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_chunked_uniform_vecgate_matches_scalar_gate():
+    """A gate that is the same in every key column is the scalar gate: the
+    chunked vector-gate route against the scalar chunked route (both bf16,
+    different chunk sizes and decay bookkeeping: equal within the bar)."""
+    x = inputs.make_fwd_inputs(2, 2, 700, 128, "bf16", seed=52, init_state=True)
+    xd = to_dev(x)
+    av = xd["alpha"][..., None].expand(-1, -1, -1, 128).contiguous()
+    o1, s1 = gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"], xd["s0"])
+    o2, s2 = gdn_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"], 64)
+    torch.cuda.synchronize()
+    assert maxrel(to_np(o1), to_np(o2)) <= TOL["bf16"] and maxrel(to_np(s1), to_np(s2)) <= TOL["bf16"]
+
+
+def test_chunked_vecgate_rejects_other_chunk_sizes_and_fp32():
+    x = inputs.make_fwd_inputs(1, 1, 64, 64, "f32", seed=1)
+    x["alpha"] = inputs.make_vec_alpha(1, 1, 64, 64, seed=2)
+    xd = to_dev(x)
+    with pytest.raises(GDNError):
+        gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None)
+    xb = {n: (t.to(torch.bfloat16) if n in ("q", "k", "v") else t) for n, t in xd.items()}
+    with pytest.raises(GDNError):
+        gdn_chunk_fwd_vecgate(xb["q"], xb["k"], xb["v"], xb["alpha"], xb["beta"], None, 64)
