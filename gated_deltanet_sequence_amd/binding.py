@@ -212,7 +212,8 @@ VECGATE_CHUNK = 32
 def gdn_chunk_fwd_vecgate(q, k, v, alpha, beta, initial_state=None, chunk_size: int = VECGATE_CHUNK, *,
                           o=None, final_state=None, output_final_state: bool = True, stream=None):
     """Chunked forward pass with a per-dimension gate alpha [B,H,T,dk] (fp32)
-    that decays the key columns of the state; bf16 q/k/v, 32-token chunks."""
+    that decays the key columns of the state; bf16 or fp32 q/k/v, 32-token
+    chunks."""
     B, H, T, dk, dv = _check_fwd_args(q, k, v, alpha, beta, initial_state, alpha_per_dim=True)
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)

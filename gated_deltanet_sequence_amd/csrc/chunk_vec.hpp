@@ -1,12 +1,14 @@
-// Chunked forward pass of the gated delta rule with a per-dimension gate,
-// bf16 inputs, d_k = d_v = 64 or 128, on gfx950.
+// Chunked forward pass of the gated delta rule with a per-dimension gate (or
+// a scalar gate, as the special case of equal columns), bf16 or fp32 inputs,
+// d_k = d_v = 64 or 128, on gfx950.
 //
 // Sources (web pages, by title and section):
 //   [P1] "Gated DeltaNet GPU并行实现：拆解线性注意力循环的两种高效方案"
 //        §2.2 the forgetting gate may be a scalar or a vector (one factor per
 //        dimension); §3.2 chunked evaluation (dense products inside a chunk,
 //        serial state carry between chunks); §4.4 fp32 state, bf16 matmul
-//        inputs with fp32 accumulation.
+//        inputs with fp32 accumulation (fp32 inputs: fp32 products
+//        throughout).
 //
 // The recurrence.  alpha_t in [0,1]^{d_k} decays the key columns of the state:
 //     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
@@ -36,7 +38,13 @@
 // accumulators, a bf16 copy in LDS feeds the products; four waves in
 // phase-synchronous steps.  The chunk is 32 tokens: the fp32 table of G
 // (32 x d_k) and the four operand copies of q and k it needs per chunk then
-// fit in LDS next to the chunk matrices with room for two workgroups per CU.
+// fit in LDS next to the chunk matrices with room for two workgroups per CU
+// (bf16; fp32 operands take one workgroup per CU, 141 KB at d_k = 128).
+//
+// With a scalar gate (VG = false: alpha is [.., T] and every key column
+// decays alike) the same algebra holds with G_r[j] = g_r for all j; this is
+// the library's fp32 path at d = 128, where the 64-token generic kernel's
+// fp32 buffers exceed the LDS.
 #pragma once
 
 #include "gdn_common.hpp"
@@ -50,24 +58,25 @@ constexpr int NW = 4;      // waves
 constexpr int NT = NW * 64;
 constexpr float SAFE_MIN = -100.f;  // log2 of the least chunk decay the factored products take
 
-template <int DK>
+template <class T, int DK>
 struct Smem {
-  static constexpr int LDK = DK + 8;  // bf16 rows of d_k, padded by 16 bytes
-  static constexpr int LDC = C + 8;   // bf16 rows of C, padded by 16 bytes
-  bf16_t Qs[C * LDK];    // 2^G o q, [token][dk]
-  bf16_t Kr[C * LDK];    // 2^G o k
-  bf16_t Kh[C * LDK];    // 2^-G o k (Gram columns); raw k in chunks on the exact path
-  bf16_t Qr[C * LDK];    // raw q (exact path)
-  bf16_t Kbt[DK * LDC];  // (2^(G_C - G) o k)^T, [dk][token]
-  bf16_t V[C * DVS];     // value slice, [token][dvs]
-  bf16_t S[DVS * LDK];   // operand copy of the state slice, [dv][dk]
-  bf16_t Yt[DVS * LDC];  // right-hand side of the triangular system, [dv][token]
-  bf16_t Ut[DVS * LDC];  // U^T
-  bf16_t Ti[C * LDC];    // (I + L)^-1, [token][token]
-  bf16_t Tt[C * LDC];    // its transpose while it is built
-  bf16_t Lb[C * LDC];    // L, operand copy
-  bf16_t P[C * LDC];     // lower(A_qk), [r][s]
-  bf16_t Mt[16 * LDC];   // partial product of the blocked inverse
+  static constexpr int PAD = 16 / (int)sizeof(T);  // 16-byte row padding
+  static constexpr int LDK = DK + PAD;  // rows of d_k
+  static constexpr int LDC = C + PAD;   // rows of C
+  T Qs[C * LDK];    // 2^G o q, [token][dk]
+  T Kr[C * LDK];    // 2^G o k
+  T Kh[C * LDK];    // 2^-G o k (Gram columns); raw k in chunks on the exact path
+  T Qr[C * LDK];    // raw q (exact path)
+  T Kbt[DK * LDC];  // (2^(G_C - G) o k)^T, [dk][token]
+  T V[C * DVS];     // value slice, [token][dvs]
+  T S[DVS * LDK];   // operand copy of the state slice, [dv][dk]
+  T Yt[DVS * LDC];  // right-hand side of the triangular system, [dv][token]
+  T Ut[DVS * LDC];  // U^T
+  T Ti[C * LDC];    // (I + L)^-1, [token][token]
+  T Tt[C * LDC];    // its transpose while it is built
+  T Lb[C * LDC];    // L, operand copy
+  T P[C * LDC];     // lower(A_qk), [r][s]
+  T Mt[16 * LDC];   // partial product of the blocked inverse
   float Ld[2][16][17];   // fp32 diagonal 16x16 blocks of L
   float G[C * DK];       // log2-prefix of alpha per key column, [token][dk]
   float beta[C];
@@ -75,17 +84,26 @@ struct Smem {
   int exactw[NW];        // per wave: a column of this chunk decays below 2^SAFE_MIN
 };
 
-template <int DK>
+// Eight or four values -> one 16-byte vector of T.
+__device__ __forceinline__ void store_vec(bf16_t* p, const float (&x)[8]) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                            pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+}
+__device__ __forceinline__ void store_vec(float* p, const float (&x)[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+// VG: alpha is [.., T, DK] (per-dimension gate); otherwise [.., T] (scalar).
+template <class T, int DK, bool VG>
 __global__ __launch_bounds__(NT) void chunk_vec_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
-    const float* initial_state, bf16_t* __restrict__ o, float* final_state,
+    const float* initial_state, T* __restrict__ o, float* final_state,
     int nchain, int64_t Tlen, int DV, int xcd_map) {
-  using Sm = Smem<DK>;
-  using T = bf16_t;
+  using Sm = Smem<T, DK>;
   constexpr int LDK = Sm::LDK;
   constexpr int LDC = Sm::LDC;
-  constexpr int VEC = 8;                         // bf16 per 16-byte vector
+  constexpr int VEC = 16 / (int)sizeof(T);      // elements per 16-byte vector
   constexpr int NQK = C * DK / VEC / NT;         // vectors per thread, q or k
   constexpr int NVV = C * DVS / VEC;             // vectors of V (threads 0 .. NVV-1)
   constexpr int IB = DVS / 16;
@@ -124,7 +142,7 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
   const T* qc = q + (int64_t)chain * Tlen * DK;
   const T* kc = k + (int64_t)chain * Tlen * DK;
   const T* vc = v + (int64_t)chain * Tlen * DV + slice * DVS;
-  const float* ac = alpha + (int64_t)chain * Tlen * DK;
+  const float* ac = alpha + (int64_t)chain * Tlen * (VG ? DK : 1);
   const float* bc = beta + (int64_t)chain * Tlen;
   T* oc = o + (int64_t)chain * Tlen * DV + slice * DVS;
   const int64_t st_off = ((int64_t)chain * DV + (int64_t)slice * DVS) * DK;
@@ -181,7 +199,7 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
     }
     if (tid < DK) {
 #pragma unroll
-      for (int r = 0; r < C; ++r) ra[r] = t0 + r < Tlen ? ac[(t0 + r) * DK + tid] : 1.f;
+      for (int r = 0; r < C; ++r) ra[r] = t0 + r < Tlen ? ac[VG ? (t0 + r) * DK + tid : t0 + r] : 1.f;
     }
     rbt = (tid < C && t0 + tid < Tlen) ? bc[t0 + tid] : 0.f;
   };
@@ -224,17 +242,19 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
       const int vi = tid + NT * it;
       const int r = vi / (DK / VEC), cg = vi % (DK / VEC);
       const int j0 = cg * VEC;
-      const float4 g0 = *reinterpret_cast<const float4*>(&sm.G[r * DK + j0]);
-      const float4 g1 = *reinterpret_cast<const float4*>(&sm.G[r * DK + j0 + 4]);
-      const float4 c0 = *reinterpret_cast<const float4*>(&sm.G[(C - 1) * DK + j0]);
-      const float4 c1 = *reinterpret_cast<const float4*>(&sm.G[(C - 1) * DK + j0 + 4]);
-      const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-      const float gc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      float g[VEC], gc[VEC];
+#pragma unroll
+      for (int h = 0; h < VEC / 4; ++h) {
+        const float4 g4 = *reinterpret_cast<const float4*>(&sm.G[r * DK + j0 + 4 * h]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&sm.G[(C - 1) * DK + j0 + 4 * h]);
+        g[4 * h] = g4.x; g[4 * h + 1] = g4.y; g[4 * h + 2] = g4.z; g[4 * h + 3] = g4.w;
+        gc[4 * h] = c4.x; gc[4 * h + 1] = c4.y; gc[4 * h + 2] = c4.z; gc[4 * h + 3] = c4.w;
+      }
       const T* qe = reinterpret_cast<const T*>(&rq[it]);
       const T* ke = reinterpret_cast<const T*>(&rk[it]);
-      float qs[8], kr[8], kh[8];
+      float qs[VEC], kr[VEC], kh[VEC];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < VEC; ++e) {
         const float qv = Elem<T>::to_f32(qe[e]), kv = Elem<T>::to_f32(ke[e]);
         const float eg = fast_exp2(g[e]);
         qs[e] = qv * eg;
@@ -242,12 +262,9 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
         kh[e] = exact ? kv : kv * fast_exp2(-g[e]);
         sm.Kbt[(j0 + e) * LDC + r] = Elem<T>::from_f32(kv * fast_exp2(gc[e] - g[e]));
       }
-      *reinterpret_cast<uint4*>(&sm.Qs[r * LDK + j0]) =
-          make_uint4(pack_bf16x2(qs[0], qs[1]), pack_bf16x2(qs[2], qs[3]), pack_bf16x2(qs[4], qs[5]), pack_bf16x2(qs[6], qs[7]));
-      *reinterpret_cast<uint4*>(&sm.Kr[r * LDK + j0]) =
-          make_uint4(pack_bf16x2(kr[0], kr[1]), pack_bf16x2(kr[2], kr[3]), pack_bf16x2(kr[4], kr[5]), pack_bf16x2(kr[6], kr[7]));
-      *reinterpret_cast<uint4*>(&sm.Kh[r * LDK + j0]) =
-          make_uint4(pack_bf16x2(kh[0], kh[1]), pack_bf16x2(kh[2], kh[3]), pack_bf16x2(kh[4], kh[5]), pack_bf16x2(kh[6], kh[7]));
+      store_vec(&sm.Qs[r * LDK + j0], qs);
+      store_vec(&sm.Kr[r * LDK + j0], kr);
+      store_vec(&sm.Kh[r * LDK + j0], kh);
       if (exact) *reinterpret_cast<uint4*>(&sm.Qr[r * LDK + j0]) = rq[it];
     }
     if (ch + 1 < nchunks) load_chunk(ch + 1);

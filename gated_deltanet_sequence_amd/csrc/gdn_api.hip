@@ -192,7 +192,7 @@ const char* gdn_strerror(int code) {
   switch (code) {
     case GDN_OK: return "success";
     case GDN_ERR_INVALID_ARG: return "invalid argument (NULL pointer, negative size, bad dtype or overlapping output)";
-    case GDN_ERR_UNSUPPORTED: return "unsupported shape or chunk size (dk == dv in {64,128}, chunk_size 64; fp32 needs dk == 64)";
+    case GDN_ERR_UNSUPPORTED: return "unsupported shape or chunk size (dk == dv in {64,128}, chunk_size 64)";
     case GDN_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
     case GDN_ERR_HIP: return "HIP runtime error while launching";
     default: return "unknown gdn error code";
@@ -205,11 +205,10 @@ const char* gdn_version(void) { return "0.1.0"; }
 
 namespace {
 // Argument checks shared by the forward entry points: GDN_OK, or the error.
-// f32_any_width: fp32 inputs may have d = 128 too (the scan route).
 int check_fwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
               const float* initial_state, void* o, float* final_state, int64_t B, int64_t H,
               int64_t T, int64_t dk, int64_t dv, int64_t chunk_size, gdn_dtype dtype,
-              bool f32_any_width = false, bool alpha_per_dim = false) {
+              bool alpha_per_dim = false) {
   if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0 || chunk_size <= 0) return GDN_ERR_INVALID_ARG;
   if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
   if (too_large(B, H, T)) return GDN_ERR_UNSUPPORTED;
@@ -217,7 +216,6 @@ int check_fwd(const void* q, const void* k, const void* v, const float* alpha, c
   const bool has_tokens = nchain > 0 && T > 0;
   if (has_tokens && (!q || !k || !v || !alpha || !beta || !o)) return GDN_ERR_INVALID_ARG;
   if (dk != dv || (dk != 64 && dk != 128) || chunk_size != 64) return GDN_ERR_UNSUPPORTED;
-  if (dtype == GDN_F32 && dk != 64 && !f32_any_width) return GDN_ERR_UNSUPPORTED;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(alpha) || misaligned(beta) ||
       misaligned(initial_state) || misaligned(o) || misaligned(final_state))
     return GDN_ERR_ALIGNMENT;
@@ -299,6 +297,43 @@ int noalloc_scratch(void** out) {
 }
 }  // namespace
 
+namespace {
+// The 32-token chunk kernel of chunk_vec.hpp: the per-dimension gate (VG),
+// and the scalar gate for fp32 at d = 128.
+template <bool VG, class T, int DK>
+int launch_vec_t(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                 const float* initial_state, void* o, float* final_state, int64_t nchain, int64_t T_,
+                 int64_t dv, hipStream_t stream) {
+  const int64_t nblocks = nchain * (dv / gdn::vec::DVS);
+  if (nblocks > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+  const int xcd_map = (nchain % 8) == 0;
+  hipLaunchKernelGGL((gdn::vec::chunk_vec_kernel<T, DK, VG>), dim3((unsigned)nblocks), dim3(gdn::vec::NT), 0,
+                     stream, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), alpha,
+                     beta, initial_state, static_cast<T*>(o), final_state, (int)nchain, T_, (int)dv, xcd_map);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+template <bool VG>
+int launch_vec(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+               const float* initial_state, void* o, float* final_state, int64_t nchain, int64_t T,
+               int64_t dk, int64_t dv, gdn_dtype dtype, hipStream_t stream) {
+  if (nchain == 0) return GDN_OK;
+  if (T == 0 && !final_state) return GDN_OK;
+  if constexpr (!VG) {
+    // the scalar gate takes this kernel for fp32 at d = 128 only
+    (void)dk;
+    (void)dtype;
+    return launch_vec_t<false, float, 128>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv,
+                                           stream);
+  } else if (dtype == GDN_BF16) {
+    return dk == 128 ? launch_vec_t<true, bf16_t, 128>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv, stream)
+                     : launch_vec_t<true, bf16_t, 64>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv, stream);
+  } else {
+    return dk == 128 ? launch_vec_t<true, float, 128>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv, stream)
+                     : launch_vec_t<true, float, 64>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv, stream);
+  }
+}
+}  // namespace
+
 extern "C" {
 
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
@@ -316,6 +351,12 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
   if (dtype == GDN_BF16)
     return launch_chunk_pipe(q, k, v, alpha, beta, initial_state, o, final_state, seq_map(nchain, T),
                              dk, dv, stream);
+  // fp32 at d = 128: the 64-token kernel's fp32 buffers exceed the LDS, so
+  // the chunks are evaluated 32 tokens at a time (the result does not depend
+  // on the chunk size beyond rounding)
+  if (dk == 128)
+    return launch_vec<false>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dk, dv, dtype,
+                             stream);
   return launch_chunk<float, 64, 16, 64, 4>(q, k, v, alpha, beta, initial_state, o, final_state,
                                             nchain, T, dv, stream);
 }
@@ -355,7 +396,7 @@ int scan_fwd(const void* q, const void* k, const void* v, const float* alpha, co
              int64_t dk, int64_t dv, gdn_dtype dtype, void* workspace, size_t workspace_bytes,
              void* hip_stream) {
   const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
-                           64, dtype, true, VEC);
+                           64, dtype, VEC);
   if (rc != GDN_OK) return rc;
   const int64_t nseq = B * H;
   if (nseq == 0) return GDN_OK;
@@ -410,27 +451,11 @@ int gdn_chunk_fwd_vecgate(const void* q, const void* k, const void* v, const flo
                           gdn_dtype dtype, void* hip_stream) {
   // the shared checks with the scalar path's chunk size; this route's own below
   const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
-                           chunk_size > 0 ? 64 : chunk_size, dtype, false, true);
+                           chunk_size > 0 ? 64 : chunk_size, dtype, true);
   if (rc != GDN_OK) return rc;
-  if (chunk_size != gdn::vec::C || dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
-  const int64_t nchain = B * H;
-  if (nchain == 0) return GDN_OK;
-  if (T == 0 && !final_state) return GDN_OK;
-  const int64_t nblocks = nchain * (dv / gdn::vec::DVS);
-  if (nblocks > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
-  const int xcd_map = (nchain % 8) == 0;
-  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  if (dk == 128)
-    hipLaunchKernelGGL(gdn::vec::chunk_vec_kernel<128>, dim3((unsigned)nblocks), dim3(gdn::vec::NT), 0, stream,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
-                       alpha, beta, initial_state, static_cast<bf16_t*>(o), final_state, (int)nchain, T, (int)dv,
-                       xcd_map);
-  else
-    hipLaunchKernelGGL(gdn::vec::chunk_vec_kernel<64>, dim3((unsigned)nblocks), dim3(gdn::vec::NT), 0, stream,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
-                       alpha, beta, initial_state, static_cast<bf16_t*>(o), final_state, (int)nchain, T, (int)dv,
-                       xcd_map);
-  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  if (chunk_size != gdn::vec::C) return GDN_ERR_UNSUPPORTED;
+  return launch_vec<true>(q, k, v, alpha, beta, initial_state, o, final_state, B * H, T, dk, dv, dtype,
+                          static_cast<hipStream_t>(hip_stream));
 }
 
 size_t gdn_chunk_fwd_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,

@@ -80,7 +80,10 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *   chunk_size     tokens per chunk; the library supports 64.  T need not be a
  *                  multiple: the missing tokens of the last chunk act as
  *                  identity maps (alpha = 1, beta = 0) and produce no output.
- *   dk, dv         64 or 128, dk == dv.
+ *                  (fp32 inputs at d = 128 are evaluated 32 tokens at a time:
+ *                  the 64-token fp32 buffers exceed the LDS.  The result does
+ *                  not depend on the chunk size beyond rounding.)
+ *   dk, dv         64 or 128, dk == dv, for bf16 and fp32.
  *   T              >= 0.  T == 0 writes final_state = initial_state (or zeros).
  *                  For bf16, one sequence's q, k or v (T * d * 2 bytes) must be
  *                  under 2^31 bytes, else GDN_ERR_UNSUPPORTED.
@@ -157,9 +160,9 @@ int gdn_scan_fwd_vecgate(const void* q, const void* k, const void* v,
  * state,
  *     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
  * The per-column decay is folded into the chunk's key and query operands, so
- * the chunk products stay dense MFMA products.  bf16 q/k/v only; chunk_size
- * must be 32 (this route's chunk: its per-token, per-column decay table and
- * the scaled operand copies fit the LDS at that size); otherwise
+ * the chunk products stay dense MFMA products (bf16 or fp32, as q/k/v).
+ * chunk_size must be 32 (this route's chunk: its per-token, per-column decay
+ * table and the scaled operand copies fit the LDS at that size); otherwise
  * GDN_ERR_UNSUPPORTED.  Other arguments, layouts, aliasing and errors as for
  * gdn_chunk_fwd.  A gate under 2^-200 acts as 2^-200, as on the scalar path.
  */

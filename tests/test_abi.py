@@ -64,7 +64,7 @@ def step(lib, q=A, k=A + MB, v=A + 2 * MB, alpha=A + 3 * MB, beta=A + 4 * MB,
     (dict(beta=None), 1), (dict(o=None), 1),
     (dict(B=-1), 1), (dict(H=-2), 1), (dict(T=-1), 1), (dict(C=0), 1), (dict(dtype=7), 1),
     (dict(dk=32, dv=32), 2), (dict(dk=64, dv=128), 2), (dict(dk=256, dv=256), 2),
-    (dict(C=32), 2), (dict(C=128), 2), (dict(dtype=0, dk=128, dv=128), 2),
+    (dict(C=32), 2), (dict(C=128), 2),
     (dict(q=A + 8), 3), (dict(v=A + 128 * MB + 2), 3), (dict(o=A + 256 * MB + 4), 3),
     (dict(s0=A + 300 * MB + 8), 3), (dict(sT=A + 400 * MB + 12), 3),
     (dict(o=A + 112), 1),                  # output overlaps q
@@ -78,6 +78,7 @@ def test_chunk_fwd_rejects(lib, kw, code):
 def test_chunk_fwd_empty_is_noop(lib):
     # no sequences, or no tokens and no state to write: nothing is launched
     assert fwd(lib, B=0) == 0
+    assert fwd(lib, B=0, dtype=0, dk=128, dv=128) == 0   # fp32 at d = 128 passes the checks
     assert fwd(lib, H=0) == 0
     assert fwd(lib, T=0, sT=None) == 0
     assert fwd(lib, B=0, q=None, k=None, v=None, alpha=None, beta=None, o=None) == 0

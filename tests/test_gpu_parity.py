@@ -73,6 +73,17 @@ SMALL_CASES = [
     (1, 2, 500, 64, "f32", True, "resets"),
     (2, 2, 600, 128, "bf16", True, "beta2"),
     (1, 1, 400, 64, "f32", True, "beta2"),
+    # fp32 at d = 128 (32-token chunks inside): tails around the chunk edge,
+    # the XCD-grouped mapping, and every gate law
+    (1, 1, 1, 128, "f32", True, "default"),
+    (1, 2, 31, 128, "f32", False, "default"),
+    (2, 1, 33, 128, "f32", True, "default"),
+    (2, 2, 300, 128, "f32", True, "default"),
+    (8, 1, 100, 128, "f32", True, "default"),
+    (1, 2, 1024, 128, "f32", True, "slow"),
+    (1, 2, 300, 128, "f32", True, "fast"),
+    (1, 2, 500, 128, "f32", True, "resets"),
+    (1, 1, 400, 128, "f32", True, "beta2"),
 ]
 
 

@@ -116,6 +116,16 @@ def test_split_falls_back_to_plain_pass():
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_split_fp32_takes_plain_pass(d):
+    """fp32 inputs are never split: the split entry point is gdn_chunk_fwd."""
+    x = inputs.make_fwd_inputs(1, 2, 3000, d, "f32", seed=35 + d, init_state=True)
+    assert workspace(x) == 0
+    o1, s1 = run_split(x)
+    o2, s2 = run_plain(x)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
 def test_split_rejects_small_workspace():
     x = inputs.make_fwd_inputs(1, 2, 3000, 128, "bf16", seed=34)
     need = workspace(x)

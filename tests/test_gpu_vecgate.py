@@ -65,23 +65,28 @@ def test_uniform_vecgate_matches_scalar_gate():
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
-# Chunked route (bf16, 32-token chunks).  Gates per dimension with the gate
-# laws of the workloads: default, slow (long memory), fast (every chunk
-# decays below 2^-100 in some column: the exact element-wise products) and
-# resets (a gate of 0 in ~1 % of the entries: the exact path for the chunks
-# that hold one).
+# Chunked route (32-token chunks).  Gates per dimension with the gate laws
+# of the workloads: default, slow (long memory), fast (every chunk decays
+# below 2^-100 in some column: the exact element-wise products) and resets
+# (a gate of 0 in ~1 % of the entries: the exact path for the chunks that
+# hold one).
 CHUNK_CASES = [
-    # B, H, T, d, initial state, gate
-    (1, 1, 1, 128, True, "default"),
-    (1, 2, 31, 64, False, "default"),
-    (2, 1, 33, 128, True, "default"),
-    (1, 3, 1000, 64, True, "default"),
-    (2, 2, 777, 128, True, "slow"),
-    (1, 2, 2048, 128, True, "slow"),
-    (1, 2, 300, 128, True, "fast"),
-    (2, 1, 500, 64, True, "resets"),
-    (1, 2, 640, 128, False, "resets"),
-    (8, 1, 256, 128, True, "default"),   # 8 sequences: XCD-grouped mapping
+    # B, H, T, d, initial state, gate, dtype
+    (1, 1, 1, 128, True, "default", "bf16"),
+    (1, 2, 31, 64, False, "default", "bf16"),
+    (2, 1, 33, 128, True, "default", "bf16"),
+    (1, 3, 1000, 64, True, "default", "bf16"),
+    (2, 2, 777, 128, True, "slow", "bf16"),
+    (1, 2, 2048, 128, True, "slow", "bf16"),
+    (1, 2, 300, 128, True, "fast", "bf16"),
+    (2, 1, 500, 64, True, "resets", "bf16"),
+    (1, 2, 640, 128, False, "resets", "bf16"),
+    (8, 1, 256, 128, True, "default", "bf16"),   # 8 sequences: XCD-grouped mapping
+    (1, 1, 50, 64, True, "default", "f32"),
+    (2, 1, 900, 128, False, "default", "f32"),
+    (1, 2, 1200, 64, True, "slow", "f32"),
+    (1, 2, 300, 128, True, "fast", "f32"),
+    (1, 2, 640, 128, True, "resets", "f32"),
 ]
 
 
@@ -92,20 +97,20 @@ def run_chunk_vec(x):
     return o, sT
 
 
-@pytest.mark.parametrize("case", CHUNK_CASES, ids=lambda c: "B%dH%dT%dd%d_%s_%s" % (
-    c[0], c[1], c[2], c[3], "s0" if c[4] else "z", c[5]))
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=lambda c: "B%dH%dT%dd%d_%s_%s_%s" % (
+    c[0], c[1], c[2], c[3], "s0" if c[4] else "z", c[5], c[6]))
 def test_chunked_vecgate_against_oracle(case):
-    B, H, T, d, init, gate = case
+    B, H, T, d, init, gate, dtype = case
     print("case chunked vecgate", case, flush=True)
-    x = inputs.make_fwd_inputs(B, H, T, d, "bf16", seed=700 + T + d, init_state=init)
+    x = inputs.make_fwd_inputs(B, H, T, d, dtype, seed=700 + T + d, init_state=init)
     x["alpha"] = inputs.make_vec_alpha(B, H, T, d, seed=800 + T, gate=gate)
     o, sT = run_chunk_vec(x)
     (q, k, v, _, b), s0 = oracle_inputs(x)
     ro, rs = oracle.oracle_fwd_vecgate(q, k, v, x["alpha"].numpy(), b, s0)
     eo, es = maxrel(to_np(o), ro), maxrel(to_np(sT), rs)
-    print("  err o %.3e  err S_T %.3e (tol %.0e)" % (eo, es, TOL["bf16"]), flush=True)
+    print("  err o %.3e  err S_T %.3e (tol %.0e)" % (eo, es, TOL[dtype]), flush=True)
     assert np.all(np.isfinite(to_np(o))) and np.all(np.isfinite(to_np(sT)))
-    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
 def test_chunked_vecgate_main_shape():
@@ -136,12 +141,25 @@ def test_chunked_uniform_vecgate_matches_scalar_gate():
     assert maxrel(to_np(o1), to_np(o2)) <= TOL["bf16"] and maxrel(to_np(s1), to_np(s2)) <= TOL["bf16"]
 
 
-def test_chunked_vecgate_rejects_other_chunk_sizes_and_fp32():
-    x = inputs.make_fwd_inputs(1, 1, 64, 64, "f32", seed=1)
-    x["alpha"] = inputs.make_vec_alpha(1, 1, 64, 64, seed=2)
+def test_chunked_vecgate_rejects_other_chunk_sizes():
+    for dtype in ("f32", "bf16"):
+        x = inputs.make_fwd_inputs(1, 1, 64, 64, dtype, seed=1)
+        x["alpha"] = inputs.make_vec_alpha(1, 1, 64, 64, seed=2)
+        xd = to_dev(x)
+        for C in (16, 64):
+            with pytest.raises(GDNError):
+                gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None, C)
+
+
+def test_chunked_uniform_vecgate_matches_scalar_gate_fp32():
+    """fp32 at d = 128: the scalar-gate path runs the same 32-token kernel
+    with one gate per token, the vector-gate path with that gate repeated over
+    the key columns; the decay tables hold the same values, so the two agree
+    bit for bit."""
+    x = inputs.make_fwd_inputs(2, 2, 500, 128, "f32", seed=53, init_state=True)
     xd = to_dev(x)
-    with pytest.raises(GDNError):
-        gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None)
-    xb = {n: (t.to(torch.bfloat16) if n in ("q", "k", "v") else t) for n, t in xd.items()}
-    with pytest.raises(GDNError):
-        gdn_chunk_fwd_vecgate(xb["q"], xb["k"], xb["v"], xb["alpha"], xb["beta"], None, 64)
+    av = xd["alpha"][..., None].expand(-1, -1, -1, 128).contiguous()
+    o1, s1 = gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"], xd["s0"])
+    o2, s2 = gdn_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"], 64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
