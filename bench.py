@@ -24,6 +24,7 @@ from __future__ import annotations
 import argparse
 import glob
 import hashlib
+import re
 import json
 import os
 import sys
@@ -40,9 +41,11 @@ DECODE = dict(N=256, H=16, d=128, steps=64, seed=5)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chunk_fwd_main.txt")
-KERNEL_SOURCES = ["gdn_common.hpp", "chunk_fwd_pipe.hpp", "gdn_api.hip"]
+# Sources whose text identifies a measured kernel: whole files, or
+# "file:function" for one function of a file (a kernel's launch code).
+KERNEL_SOURCES = ["gdn_common.hpp", "chunk_fwd_pipe.hpp", "gdn_api.hip:launch_chunk_pipe", "gdn_api.hip:seq_map"]
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_recurrent_step_decode.txt")
-DECODE_SOURCES = ["gdn_common.hpp", "recurrent_step.hpp", "gdn_api.hip"]
+DECODE_SOURCES = ["gdn_common.hpp", "recurrent_step.hpp", "gdn_api.hip:launch_step"]
 
 
 def alg_bytes_main(B, H, T, d):
@@ -60,11 +63,29 @@ def alg_bytes_decode(N, H, d):
     return 2 * heads * d * d * 4 + heads * (3 * d * 2 + 2 * 4 + d * 2)
 
 
-def kernel_source_hash(sources=None):
+def source_text(entry, read=None):
+    """Text of a KERNEL_SOURCES entry: a whole file, or for "file:function"
+    the function's definition (from its first line at column 0 to the first
+    closing brace at column 0)."""
+    f, _, fn = entry.partition(":")
+    if read is None:
+        with open(os.path.join(ROOT, "gated_deltanet_sequence_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+    else:
+        text = read(f)
+    if not fn:
+        return text
+    m = re.search(r"^\S[^\n]*\b%s\(" % re.escape(fn), text, re.M)
+    if m is None:
+        raise ValueError("no definition of %s in %s" % (fn, f))
+    end = text.index("\n}\n", m.start())
+    return text[m.start():end + 3]
+
+
+def kernel_source_hash(sources=None, read=None):
     h = hashlib.sha256()
-    for f in (sources or KERNEL_SOURCES):
-        with open(os.path.join(ROOT, "gated_deltanet_sequence_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for e in (sources or KERNEL_SOURCES):
+        h.update(source_text(e, read).encode("utf-8"))
     return h.hexdigest()[:16]
 
 
@@ -479,6 +500,7 @@ def summarize_pmc(fetch_dir, write_dir, which="main"):
         "hbm_bytes_per_launch = %d" % (fetch_b + write_b),
         "algorithmic_bytes_per_launch = %d" % alg,
         "traffic_over_algorithmic = %.3f" % ((fetch_b + write_b) / alg),
+        "# kernel_source_hash: sha256 (first 16 hex digits) of %s" % ", ".join(sources),
         "kernel_source_hash = %s" % kernel_source_hash(sources),
     ]
     with open(out_file, "w", encoding="utf-8") as fh:
