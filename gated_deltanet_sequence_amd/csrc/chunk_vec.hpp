@@ -57,9 +57,21 @@ constexpr int DVS = 16;    // value rows per workgroup
 constexpr int NW = 4;      // waves
 constexpr int NT = NW * 64;
 constexpr float SAFE_MIN = -100.f;  // log2 of the least chunk decay the factored products take
+constexpr int LDR = 20;    // row stride (floats) of the fp32 diagonal blocks of L
+
+// Order this wave's earlier LDS accesses before its later ones (one wave
+// hands data to other lanes of itself through LDS): the LDS unit runs one
+// wave's instructions in order, so draining the counter suffices; the
+// empty asm keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <class T, int DK>
-struct Smem {
+struct __attribute__((aligned(16))) Smem {
   static constexpr int PAD = 16 / (int)sizeof(T);  // 16-byte row padding
   static constexpr int LDK = DK + PAD;  // rows of d_k
   static constexpr int LDC = C + PAD;   // rows of C
@@ -77,8 +89,9 @@ struct Smem {
   T Lb[C * LDC];    // L, operand copy
   T P[C * LDC];     // lower(A_qk), [r][s]
   T Mt[16 * LDC];   // partial product of the blocked inverse
-  float Ld[2][16][17];   // fp32 diagonal 16x16 blocks of L
-  float G[C * DK];       // log2-prefix of alpha per key column, [token][dk]
+  float Ld[2][16][LDR];  // fp32 diagonal 16x16 blocks of L (rows 16-byte aligned)
+  float tot[NT / DK][DK];  // gate scan: log2 sums of each token group per column
+  float G[C * (DK + 4)]; // log2-prefix of alpha per key column, [token][dk], rows padded by 16 bytes
   float beta[C];
   float Ec[DK];          // 2^(G_C) per key column
   int exactw[NW];        // per wave: a column of this chunk decays below 2^SAFE_MIN
@@ -103,6 +116,7 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
   using Sm = Smem<T, DK>;
   constexpr int LDK = Sm::LDK;
   constexpr int LDC = Sm::LDC;
+  constexpr int LDG = DK + 4;                    // row stride of the gate table
   constexpr int VEC = 16 / (int)sizeof(T);      // elements per 16-byte vector
   constexpr int NQK = C * DK / VEC / NT;         // vectors per thread, q or k
   constexpr int NVV = C * DVS / VEC;             // vectors of V (threads 0 .. NVV-1)
@@ -110,10 +124,12 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
   constexpr int JB = DK / 16;
   constexpr int RB = C / 16;
   constexpr int NST = (JB * IB + NW - 1) / NW;   // state tiles per wave
-  constexpr int NOT = (IB * RB + NW - 1) / NW;   // output tiles per wave
   static_assert(NQK * NT * VEC == C * DK, "q/k vectors spread evenly");
   static_assert(NVV <= NT && DK <= NT && C <= 64, "one thread per V vector, key column, token");
   static_assert(RB == 2, "the blocked inverse below is for two 16-token blocks");
+  static_assert(IB * RB == 2 && NW == 4, "wave roles below: one Y wave, two output waves");
+  constexpr int NG = NT / DK;                    // token groups of the gate scan
+  constexpr int TPG = C / NG;                    // tokens per group
 
   __shared__ Sm sm;
 
@@ -176,32 +192,35 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
   const int64_t nchunks = (Tlen + C - 1) / C;
 
   // Register staging of the next chunk (prefetch): q, k vectors, a V vector,
-  // the gates of one key column over the chunk (thread j < DK) and beta of
-  // one token (thread r < C).  Tokens past the end read as zero q, k, v,
-  // alpha = 1 and beta = 0 (identity maps).
+  // the gates of one key column over one group of TPG tokens and beta of one
+  // token.  Every load is unconditional, so that it stays in flight until its
+  // use in the next chunk: tokens past the end reread the last token, and the
+  // uses below mask them (zero q, k, v, alpha = 1, beta = 0: identity maps).
+  const int gj = tid % DK, gg = tid / DK;  // gate column and token group of this thread
   uint4 rq[NQK], rk[NQK], rv;
-  float ra[C], rbt;
+  float ra[TPG], rbt;
+  auto tok = [&](int64_t t) { return t < Tlen ? t : Tlen - 1; };  // clamped token index
   auto load_chunk = [&](int64_t ch) {
     const int64_t t0 = ch * C;
 #pragma unroll
     for (int it = 0; it < NQK; ++it) {
       const int vi = tid + NT * it;
-      const int r = vi / (DK / VEC), cg = vi % (DK / VEC);
-      const bool ok = t0 + r < Tlen;
-      const int64_t off = (t0 + r) * DK + cg * VEC;
-      rq[it] = ok ? *reinterpret_cast<const uint4*>(qc + off) : make_uint4(0, 0, 0, 0);
-      rk[it] = ok ? *reinterpret_cast<const uint4*>(kc + off) : make_uint4(0, 0, 0, 0);
+      const int r = vi % C, cg = vi / C;  // token fastest (see the operands below)
+      const int64_t off = tok(t0 + r) * DK + cg * VEC;
+      rq[it] = *reinterpret_cast<const uint4*>(qc + off);
+      rk[it] = *reinterpret_cast<const uint4*>(kc + off);
     }
     {
-      const int r = tid / (DVS / VEC), cg = tid % (DVS / VEC);
-      const bool ok = tid < NVV && t0 + r < Tlen;
-      rv = ok ? *reinterpret_cast<const uint4*>(vc + (t0 + r) * DV + cg * VEC) : make_uint4(0, 0, 0, 0);
+      const int vi = tid % NVV;
+      const int r = vi / (DVS / VEC), cg = vi % (DVS / VEC);
+      rv = *reinterpret_cast<const uint4*>(vc + tok(t0 + r) * DV + cg * VEC);
     }
-    if (tid < DK) {
 #pragma unroll
-      for (int r = 0; r < C; ++r) ra[r] = t0 + r < Tlen ? ac[VG ? (t0 + r) * DK + tid : t0 + r] : 1.f;
+    for (int i = 0; i < TPG; ++i) {
+      const int64_t t = tok(t0 + gg * TPG + i);
+      ra[i] = ac[VG ? t * DK + gj : t];
     }
-    rbt = (tid < C && t0 + tid < Tlen) ? bc[t0 + tid] : 0.f;
+    rbt = bc[tok(t0 + tid % C)];
   };
 
   if (nchunks > 0) load_chunk(0);
@@ -209,26 +228,39 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
   for (int64_t ch = 0; ch < nchunks; ++ch) {
     __syncthreads();  // the previous chunk has finished with every buffer
 
-    // Gate table: thread j < DK walks column j over the chunk's tokens.
+    // Gate table, as a scan over the chunk's tokens per key column: thread
+    // (group gg, column gj) sums log2 alpha over its TPG tokens; the sums of
+    // the earlier groups are added once every group's total is in LDS.
+    float gl[TPG];
     {
-      bool low = false;
-      if (tid < DK) {
-        float g = 0.f;
+      float g = 0.f;
 #pragma unroll
-        for (int r = 0; r < C; ++r) {
-          g += fmaxf(fast_log2(ra[r]), LOG2_ALPHA_MIN);
-          sm.G[r * DK + tid] = g;
-        }
-        sm.Ec[tid] = fast_exp2(g);
-        low = g < SAFE_MIN;
+      for (int i = 0; i < TPG; ++i) {
+        g += fmaxf(fast_log2(ch * C + gg * TPG + i < Tlen ? ra[i] : 1.f), LOG2_ALPHA_MIN);
+        gl[i] = g;
+      }
+      sm.tot[gg][gj] = g;
+    }
+    if (tid < C) sm.beta[tid] = ch * C + tid < Tlen ? rbt : 0.f;
+    if (tid < NVV) {
+      const int r = tid / (DVS / VEC), cg = tid % (DVS / VEC);
+      *reinterpret_cast<uint4*>(&sm.V[r * DVS + cg * VEC]) = ch * C + r < Tlen ? rv : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+    {
+      float off = 0.f;
+#pragma unroll
+      for (int h = 0; h < NG - 1; ++h) off += h < gg ? sm.tot[h][gj] : 0.f;
+#pragma unroll
+      for (int i = 0; i < TPG; ++i) sm.G[(gg * TPG + i) * LDG + gj] = gl[i] + off;
+      bool low = false;
+      if (gg == NG - 1) {
+        const float gC = gl[TPG - 1] + off;
+        sm.Ec[gj] = fast_exp2(gC);
+        low = gC < SAFE_MIN;
       }
       const bool any = __builtin_amdgcn_ballot_w64(low) != 0;
       if (lane == 0) sm.exactw[wave] = any ? 1 : 0;
-    }
-    if (tid < C) sm.beta[tid] = rbt;
-    if (tid < NVV) {
-      const int r = tid / (DVS / VEC), cg = tid % (DVS / VEC);
-      *reinterpret_cast<uint4*>(&sm.V[r * DVS + cg * VEC]) = rv;
     }
     __syncthreads();
     bool exact = false;
@@ -236,36 +268,56 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
     for (int w = 0; w < NW; ++w) exact = exact || sm.exactw[w] != 0;
 
     // Operands: 2^G o q, 2^G o k, 2^-G o k (raw q, k on the exact path), and
-    // (2^(G_C - G) o k)^T.
+    // (2^(G_C - G) o k)^T (as 2^-G 2^(G_C) when the factors are in range).
+    // A thread holds VEC keys of one token, with the token fastest over the
+    // lanes: the transposed writes of K^T are then consecutive elements
+    // (conflict-free), and the padded rows of G and of the operand copies
+    // keep the row-wise accesses conflict-free too.
 #pragma unroll
     for (int it = 0; it < NQK; ++it) {
       const int vi = tid + NT * it;
-      const int r = vi / (DK / VEC), cg = vi % (DK / VEC);
+      const int r = vi % C, cg = vi / C;
       const int j0 = cg * VEC;
       float g[VEC], gc[VEC];
 #pragma unroll
       for (int h = 0; h < VEC / 4; ++h) {
-        const float4 g4 = *reinterpret_cast<const float4*>(&sm.G[r * DK + j0 + 4 * h]);
-        const float4 c4 = *reinterpret_cast<const float4*>(&sm.G[(C - 1) * DK + j0 + 4 * h]);
+        const float4 g4 = *reinterpret_cast<const float4*>(&sm.G[r * LDG + j0 + 4 * h]);
+        const float4 c4 = exact ? *reinterpret_cast<const float4*>(&sm.G[(C - 1) * LDG + j0 + 4 * h])
+                                : *reinterpret_cast<const float4*>(&sm.Ec[j0 + 4 * h]);
         g[4 * h] = g4.x; g[4 * h + 1] = g4.y; g[4 * h + 2] = g4.z; g[4 * h + 3] = g4.w;
         gc[4 * h] = c4.x; gc[4 * h + 1] = c4.y; gc[4 * h + 2] = c4.z; gc[4 * h + 3] = c4.w;
       }
-      const T* qe = reinterpret_cast<const T*>(&rq[it]);
-      const T* ke = reinterpret_cast<const T*>(&rk[it]);
+      const bool live = ch * C + r < Tlen;
+      const uint4 zq = live ? rq[it] : make_uint4(0, 0, 0, 0);
+      const uint4 zk = live ? rk[it] : make_uint4(0, 0, 0, 0);
+      const T* qe = reinterpret_cast<const T*>(&zq);
+      const T* ke = reinterpret_cast<const T*>(&zk);
       float qs[VEC], kr[VEC], kh[VEC];
+      if (!exact) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float qv = Elem<T>::to_f32(qe[e]), kv = Elem<T>::to_f32(ke[e]);
-        const float eg = fast_exp2(g[e]);
-        qs[e] = qv * eg;
-        kr[e] = kv * eg;
-        kh[e] = exact ? kv : kv * fast_exp2(-g[e]);
-        sm.Kbt[(j0 + e) * LDC + r] = Elem<T>::from_f32(kv * fast_exp2(gc[e] - g[e]));
+        for (int e = 0; e < VEC; ++e) {
+          const float qv = Elem<T>::to_f32(qe[e]), kv = Elem<T>::to_f32(ke[e]);
+          const float eg = fast_exp2(g[e]), ei = fast_exp2(-g[e]);
+          qs[e] = qv * eg;
+          kr[e] = kv * eg;
+          kh[e] = kv * ei;
+          sm.Kbt[(j0 + e) * LDC + r] = Elem<T>::from_f32(kh[e] * gc[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float qv = Elem<T>::to_f32(qe[e]), kv = Elem<T>::to_f32(ke[e]);
+          const float eg = fast_exp2(g[e]);
+          qs[e] = qv * eg;
+          kr[e] = kv * eg;
+          kh[e] = kv;
+          sm.Kbt[(j0 + e) * LDC + r] = Elem<T>::from_f32(kv * fast_exp2(gc[e] - g[e]));
+        }
+        *reinterpret_cast<uint4*>(&sm.Qr[r * LDK + j0]) = zq;
       }
       store_vec(&sm.Qs[r * LDK + j0], qs);
       store_vec(&sm.Kr[r * LDK + j0], kr);
       store_vec(&sm.Kh[r * LDK + j0], kh);
-      if (exact) *reinterpret_cast<uint4*>(&sm.Qr[r * LDK + j0]) = rq[it];
     }
     if (ch + 1 < nchunks) load_chunk(ch + 1);
     __syncthreads();
@@ -280,6 +332,7 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
       const int rb = pr >= 1 ? 1 : 0, sb = pr == 1 ? 0 : rb;
       const int r = rb * 16 + lr;
       const int s0 = sb * 16 + 4 * lg;
+      const float rowf = kind == 0 ? sm.beta[r] : 1.f;  // read before the products, unconditionally
       float val[4];
       if (!exact) {
         const f32x4 acc = Mma<T>::template run<DK>(zero4(), &sm.Kh[sb * 16 * LDK], LDK,
@@ -296,7 +349,7 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
           float acc = 0.f;
           if (s <= r) {
             for (int j = 0; j < DK; ++j)
-              acc += Elem<T>::to_f32(xr[j]) * Elem<T>::to_f32(ks[j]) * fast_exp2(sm.G[r * DK + j] - sm.G[s * DK + j]);
+              acc += Elem<T>::to_f32(xr[j]) * Elem<T>::to_f32(ks[j]) * fast_exp2(sm.G[r * LDG + j] - sm.G[s * LDG + j]);
           }
           val[e] = acc;
         }
@@ -304,80 +357,99 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s = s0 + e;
-        const bool in = kind == 0 ? (s < r) : (s <= r);
-        val[e] = in ? (kind == 0 ? sm.beta[r] : 1.f) * val[e] : 0.f;
+        const bool in = s < r + kind;  // L: s < r, P: s <= r
+        val[e] = in ? rowf * val[e] : 0.f;
       }
       T* dst = kind == 0 ? sm.Lb : sm.P;
       store4<T>(&dst[r * LDC + s0], val[0], val[1], val[2], val[3]);
-      if (kind == 0 && sb == rb) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm.Ld[sb][r - rb * 16][s0 - sb * 16 + e] = val[e];
-      }
+      if (kind == 0 && sb == rb)
+        *reinterpret_cast<float4*>(&sm.Ld[sb][r - rb * 16][s0 - sb * 16]) = make_float4(val[0], val[1], val[2], val[3]);
     }
     __syncthreads();
 
-    // Ti = (I + L)^-1, blocked: the two unit-lower 16x16 diagonal blocks by
-    // forward substitution in fp32 (lane = block, column) ...
-    if (wave == 0 && lane < 32) {
-      const int b = lane >> 4, c = lane & 15;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == c) ? 1.f : 0.f;
-#pragma unroll
-        for (int s = 0; s < r; ++s) acc -= sm.Ld[b][r][s] * x[s];
-        x[r] = acc;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sm.Ti[(16 * b + r) * LDC + 16 * b + c] = Elem<T>::from_f32(x[r]);
-        sm.Tt[(16 * b + c) * LDC + 16 * b + r] = Elem<T>::from_f32(x[r]);
-      }
-    }
-    __syncthreads();
-    // ... then the off-diagonal block Ti[1][0] = -Ti[1][1] L[1][0] Ti[0][0].
+    f32x4 Oacc = zero4();
     if (wave == 0) {
-      const f32x4 acc = Mma<T>::template run<16>(zero4(), &sm.Lb[16 * LDC], LDC, &sm.Tt[0], LDC, lane);
-      store4<T>(&sm.Mt[lr * LDC + 4 * lg], acc[0], acc[1], acc[2], acc[3]);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const f32x4 acc = Mma<T>::template run<16>(zero4(), &sm.Ti[16 * LDC + 16], LDC, &sm.Mt[0], LDC, lane);
+      // Ti = (I + L)^-1, blocked, on this wave alone: the two unit-lower 16x16
+      // diagonal blocks by forward substitution in fp32 (lane = block,
+      // column; each band of four L columns read as float4 rows one band
+      // ahead) ...
+      if (lane < 32) {
+        const int b = lane >> 4, c = lane & 15;
+        const float* Lr = &sm.Ld[b][0][0];
+        float x[16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.Ti[(16 + 4 * lg + e) * LDC + lr] = Elem<T>::from_f32(-acc[e]);
-    }
-    __syncthreads();
-
-    // Y = diag(beta) (V - K~ S^T) (tiles [r][i]) and the inter-chunk part of
-    // the output, S Q~^T (tiles [i][r], kept live).
-    for (int t = wave; t < RB * IB; t += NW) {
-      const int rb = t / IB, ib = t % IB;
-      const f32x4 acc = Mma<T>::template run<DK>(zero4(), &sm.Kr[rb * 16 * LDK], LDK,
-                                                 &sm.S[ib * 16 * LDK], LDK, lane);
-      const int i = ib * 16 + lr;
-      const int r0 = rb * 16 + 4 * lg;
-      float y[4];
+        for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+        float4 lq[2][16];
+        auto band_read = [&](int Q, float4 (&dst)[16]) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = r0 + e;
-        y[e] = sm.beta[r] * (Elem<T>::to_f32(sm.V[r * DVS + i]) - acc[e]);
+          for (int r = 4 * Q + 1; r < 16; ++r) dst[r] = *reinterpret_cast<const float4*>(Lr + r * LDR + 4 * Q);
+        };
+        auto band = [&](int Q, const float4 (&l)[16]) {
+#pragma unroll
+          for (int s = 4 * Q; s < 4 * Q + 4; ++s) {
+#pragma unroll
+            for (int r = s + 1; r < 16; ++r) {
+              const float4 l4 = l[r];
+              const float lrs = (s & 3) == 0 ? l4.x : (s & 3) == 1 ? l4.y : (s & 3) == 2 ? l4.z : l4.w;
+              x[r] = fmaf(-lrs, x[s], x[r]);
+            }
+          }
+        };
+        band_read(0, lq[0]);
+        band_read(1, lq[1]);
+        band(0, lq[0]);
+        band_read(2, lq[0]);
+        band(1, lq[1]);
+        band_read(3, lq[1]);
+        band(2, lq[0]);
+        band(3, lq[1]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sm.Ti[(16 * b + r) * LDC + 16 * b + c] = Elem<T>::from_f32(x[r]);
+          sm.Tt[(16 * b + c) * LDC + 16 * b + r] = Elem<T>::from_f32(x[r]);
+        }
       }
-      store4<T>(&sm.Yt[i * LDC + r0], y[0], y[1], y[2], y[3]);
-    }
-    f32x4 Oacc[NOT];
-#pragma unroll
-    for (int m = 0; m < NOT; ++m) {
-      const int t = wave + NW * m;
-      Oacc[m] = zero4();
-      if (t < IB * RB) {
-        const int ib = t / RB, rb = t % RB;
-        Oacc[m] = Mma<T>::template run<DK>(zero4(), &sm.S[ib * 16 * LDK], LDK, &sm.Qs[rb * 16 * LDK], LDK, lane);
+      wave_lds_sync();
+      // ... then the off-diagonal block Ti[1][0] = -Ti[1][1] L[1][0] Ti[0][0].
+      {
+        const f32x4 acc = Mma<T>::template run<16>(zero4(), &sm.Lb[16 * LDC], LDC, &sm.Tt[0], LDC, lane);
+        store4<T>(&sm.Mt[lr * LDC + 4 * lg], acc[0], acc[1], acc[2], acc[3]);
       }
+      wave_lds_sync();
+      {
+        const f32x4 acc = Mma<T>::template run<16>(zero4(), &sm.Ti[16 * LDC + 16], LDC, &sm.Mt[0], LDC, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.Ti[(16 + 4 * lg + e) * LDC + lr] = Elem<T>::from_f32(-acc[e]);
+      }
+    } else if (wave == 1) {
+      // Y = diag(beta) (V - K~ S^T), tiles [r][i], meanwhile.
+#pragma unroll
+      for (int t = 0; t < RB * IB; ++t) {
+        const int rb = t / IB, ib = t % IB;
+        const f32x4 acc = Mma<T>::template run<DK>(zero4(), &sm.Kr[rb * 16 * LDK], LDK,
+                                                   &sm.S[ib * 16 * LDK], LDK, lane);
+        const int i = ib * 16 + lr;
+        const int r0 = rb * 16 + 4 * lg;
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = r0 + e;
+          y[e] = sm.beta[r] * (Elem<T>::to_f32(sm.V[r * DVS + i]) - acc[e]);
+        }
+        store4<T>(&sm.Yt[i * LDC + r0], y[0], y[1], y[2], y[3]);
+      }
+    } else {
+      // the inter-chunk part of the output, S Q~^T (tile [i][r] of this
+      // output wave, kept live until the output is finished)
+      const int t = wave - 2;
+      const int ib = t / RB, rb = t % RB;
+      Oacc = Mma<T>::template run<DK>(zero4(), &sm.S[ib * 16 * LDK], LDK, &sm.Qs[rb * 16 * LDK], LDK, lane);
     }
     __syncthreads();
 
     // U = Ti Y (tiles [r][i]), stored as U^T.
-    for (int t = wave; t < RB * IB; t += NW) {
+    if (wave < RB * IB) {
+      const int t = wave;
       const int rb = t / IB, ib = t % IB;
       const f32x4 acc = Mma<T>::template run<C>(zero4(), &sm.Ti[rb * 16 * LDC], LDC, &sm.Yt[ib * 16 * LDC], LDC, lane);
       const int i = ib * 16 + lr;
@@ -386,17 +458,14 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
     }
     __syncthreads();
 
-    // O^T += U^T P^T and store; S^T <- Diag(2^(G_C)) S^T + Kbar^T U.
-#pragma unroll
-    for (int m = 0; m < NOT; ++m) {
-      const int t = wave + NW * m;
-      if (t < IB * RB) {
-        const int ib = t / RB, rb = t % RB;
-        Oacc[m] = Mma<T>::template run<C>(Oacc[m], &sm.Ut[ib * 16 * LDC], LDC, &sm.P[rb * 16 * LDC], LDC, lane);
-        const int64_t tok = ch * C + rb * 16 + lr;
-        if (tok < Tlen)
-          store4<T>(oc + tok * DV + ib * 16 + 4 * lg, Oacc[m][0], Oacc[m][1], Oacc[m][2], Oacc[m][3]);
-      }
+    // O^T += U^T P^T and store (output waves); S^T <- Diag(2^(G_C)) S^T +
+    // Kbar^T U (every wave, its state tiles).
+    if (wave >= 2) {
+      const int t = wave - 2;
+      const int ib = t / RB, rb = t % RB;
+      Oacc = Mma<T>::template run<C>(Oacc, &sm.Ut[ib * 16 * LDC], LDC, &sm.P[rb * 16 * LDC], LDC, lane);
+      const int64_t tk = ch * C + rb * 16 + lr;
+      if (tk < Tlen) store4<T>(oc + tk * DV + ib * 16 + 4 * lg, Oacc[0], Oacc[1], Oacc[2], Oacc[3]);
     }
 #pragma unroll
     for (int m = 0; m < NST; ++m) {
