@@ -11,7 +11,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn.so")
 
 SOURCES = ["gdn_api.hip"]
-HEADERS = ["gdn_common.hpp", "chunk_fwd.hpp", "chunk_fwd_pipe.hpp", "chunk_vec.hpp", "recurrent_step.hpp", "split_combine.hpp", "scan_route.hpp"]
+HEADERS = ["gdn_common.hpp", "chunk_fwd_pipe.hpp", "chunk_vec.hpp", "recurrent_step.hpp", "split_combine.hpp", "scan_route.hpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -13,7 +13,8 @@
 //        tiles so they overlap; §4.4 fp32 state, bf16 matmul operands with
 //        fp32 accumulation.
 //
-// Chunk algebra (as in chunk_fwd.hpp): for a chunk with start state S,
+// Chunk algebra (derived by unrolling the per-token update inside a chunk;
+// [P1] §2.1-2.3): for a chunk with start state S,
 //   g = log2-prefix of alpha, D_rs = 2^(g_r - g_s) (s <= r)
 //   L = strictly-lower(diag(beta) (D o K K^T)),   Ti = (I + L)^-1
 //   P = (D o Q K^T) on s <= r

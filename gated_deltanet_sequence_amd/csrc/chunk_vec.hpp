@@ -33,18 +33,20 @@
 // 0) forms A_qk and A_kk element by element from 2^(G_r - G_s) <= 1 instead
 // (slow, exact; such chunks carry almost nothing across anyway).
 //
-// Work split and layout as in chunk_fwd.hpp: one workgroup per (sequence,
-// 16-row value slice) walks all chunks; the fp32 state slice lives in MFMA
-// accumulators, a bf16 copy in LDS feeds the products; four waves in
-// phase-synchronous steps.  The chunk is 32 tokens: the fp32 table of G
-// (32 x d_k) and the four operand copies of q and k it needs per chunk then
-// fit in LDS next to the chunk matrices with room for two workgroups per CU
-// (bf16; fp32 operands take one workgroup per CU, 141 KB at d_k = 128).
+// Work split: rows of S (value dimensions) evolve independently, so one
+// workgroup owns a 16-row value slice of one sequence and walks all its
+// chunks; the S-independent chunk products are recomputed by each slice's
+// workgroup.  The fp32 state slice lives in MFMA accumulators, a copy in the
+// input type in LDS feeds the products; four waves in seven barrier-separated
+// steps per chunk.  The chunk is 32 tokens: the fp32 table of G (32 x d_k)
+// and the four operand copies of q and k it needs per chunk then fit in LDS
+// next to the chunk matrices (bf16: 53 KB at d_k = 64, 85 KB at 128; fp32:
+// 142 KB at d_k = 128).
 //
 // With a scalar gate (VG = false: alpha is [.., T] and every key column
-// decays alike) the same algebra holds with G_r[j] = g_r for all j; this is
-// the library's fp32 path at d = 128, where the 64-token generic kernel's
-// fp32 buffers exceed the LDS.
+// decays alike) the same algebra holds with G_r[j] = g_r for all j; that
+// instance is the library's path for fp32 inputs (a 64-token chunk's fp32
+// buffers would exceed the LDS at d_k = 128).
 #pragma once
 
 #include "gdn_common.hpp"

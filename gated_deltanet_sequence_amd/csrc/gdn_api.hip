@@ -7,7 +7,6 @@
 #include <mutex>
 
 #include "gdn.h"
-#include "chunk_fwd.hpp"
 #include "chunk_fwd_pipe.hpp"
 #include "chunk_vec.hpp"
 #include "recurrent_step.hpp"
@@ -45,21 +44,6 @@ bool overlaps(Range a, Range b) {
   if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
   return a0 < b0 + (uintptr_t)b.bytes && b0 < a0 + (uintptr_t)a.bytes;
-}
-
-template <class E, int DK, int DVS, int C, int NW>
-int launch_chunk(const void* q, const void* k, const void* v, const float* alpha,
-                 const float* beta, const float* s0, void* o, float* sT, int64_t nchain,
-                 int64_t T, int64_t dv, hipStream_t stream) {
-  const int ns = (int)(dv / DVS);
-  const int64_t nblocks = nchain * ns;
-  if (nblocks > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
-  const int xcd_map = (nchain % 8) == 0;
-  hipLaunchKernelGGL((gdn::chunk_fwd_kernel<E, DK, DVS, C, NW>), dim3((unsigned)nblocks),
-                     dim3(NW * 64), 0, stream, static_cast<const E*>(q), static_cast<const E*>(k),
-                     static_cast<const E*>(v), alpha, beta, s0, static_cast<E*>(o), sT,
-                     (int)nchain, T, (int)dv, xcd_map);
-  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 template <bool GLA = false>
@@ -299,7 +283,7 @@ int noalloc_scratch(void** out) {
 
 namespace {
 // The 32-token chunk kernel of chunk_vec.hpp: the per-dimension gate (VG),
-// and the scalar gate for fp32 at d = 128.
+// and the scalar gate for fp32 inputs.
 template <bool VG, class T, int DK>
 int launch_vec_t(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                  const float* initial_state, void* o, float* final_state, int64_t nchain, int64_t T_,
@@ -319,11 +303,10 @@ int launch_vec(const void* q, const void* k, const void* v, const float* alpha, 
   if (nchain == 0) return GDN_OK;
   if (T == 0 && !final_state) return GDN_OK;
   if constexpr (!VG) {
-    // the scalar gate takes this kernel for fp32 at d = 128 only
-    (void)dk;
+    // the scalar gate takes this kernel for fp32 inputs only
     (void)dtype;
-    return launch_vec_t<false, float, 128>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv,
-                                           stream);
+    return dk == 128 ? launch_vec_t<false, float, 128>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv, stream)
+                     : launch_vec_t<false, float, 64>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv, stream);
   } else if (dtype == GDN_BF16) {
     return dk == 128 ? launch_vec_t<true, bf16_t, 128>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv, stream)
                      : launch_vec_t<true, bf16_t, 64>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv, stream);
@@ -351,14 +334,10 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
   if (dtype == GDN_BF16)
     return launch_chunk_pipe(q, k, v, alpha, beta, initial_state, o, final_state, seq_map(nchain, T),
                              dk, dv, stream);
-  // fp32 at d = 128: the 64-token kernel's fp32 buffers exceed the LDS, so
-  // the chunks are evaluated 32 tokens at a time (the result does not depend
-  // on the chunk size beyond rounding)
-  if (dk == 128)
-    return launch_vec<false>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dk, dv, dtype,
-                             stream);
-  return launch_chunk<float, 64, 16, 64, 4>(q, k, v, alpha, beta, initial_state, o, final_state,
-                                            nchain, T, dv, stream);
+  // fp32: chunks of 32 tokens (64-token fp32 buffers exceed the LDS at
+  // d = 128); the result does not depend on the chunk size beyond rounding
+  return launch_vec<false>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dk, dv, dtype,
+                           stream);
 }
 
 int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,

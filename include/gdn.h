@@ -80,8 +80,8 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *   chunk_size     tokens per chunk; the library supports 64.  T need not be a
  *                  multiple: the missing tokens of the last chunk act as
  *                  identity maps (alpha = 1, beta = 0) and produce no output.
- *                  (fp32 inputs at d = 128 are evaluated 32 tokens at a time:
- *                  the 64-token fp32 buffers exceed the LDS.  The result does
+ *                  (fp32 inputs are evaluated 32 tokens at a time: 64-token
+ *                  fp32 buffers exceed the LDS at d = 128.  The result does
  *                  not depend on the chunk size beyond rounding.)
  *   dk, dv         64 or 128, dk == dv, for bf16 and fp32.
  *   T              >= 0.  T == 0 writes final_state = initial_state (or zeros).
