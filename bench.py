@@ -6,7 +6,7 @@ d_k=d_v=128, C=64, bf16 q/k/v, fp32 gates, zero initial state, fp32 final
 state), inputs resident in HBM before the timed region.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--no-decode] [--no-long] [--no-loop] [--no-gla] [--no-routes]
+                  [--no-decode] [--no-long] [--no-loop] [--no-gla] [--no-vecgate] [--no-routes]
                   [--pmc-pass]
   python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   (writes the HBM-traffic
                   summary under profiles/ from two rocprofv3 --pmc runs)
@@ -82,10 +82,18 @@ def source_text(entry, read=None):
     return text[m.start():end + 3]
 
 
+def code_only(text):
+    """Source text without comments and with whitespace runs collapsed, so
+    that a measurement stays tied to the code, not to its comments."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(sources=None, read=None):
     h = hashlib.sha256()
     for e in (sources or KERNEL_SOURCES):
-        h.update(source_text(e, read).encode("utf-8"))
+        h.update(code_only(source_text(e, read)).encode("utf-8"))
     return h.hexdigest()[:16]
 
 
@@ -235,6 +243,37 @@ def time_gla(torch, xd, launches=50):
     alg = alg_bytes_main(B, H, T, d)
     return {"workload": "gated linear attention (no delta rule) on the main workload's inputs",
             "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def time_vecgate(torch, xd, launches=10):
+    """The chunked per-dimension-gate route (gdn_chunk_fwd_vecgate) on the main
+    workload's q, k, v, beta with a gate drawn per token and key dimension
+    (the workloads' gate law): mean launch time and its HBM-roofline fraction
+    (its algorithmic bytes count the [B,H,T,d_k] fp32 gate)."""
+    from gated_deltanet_sequence_amd import inputs
+    from gated_deltanet_sequence_amd.binding import gdn_chunk_fwd_vecgate
+    B, H, T, d = xd["q"].shape
+    av = inputs.make_vec_alpha(B, H, T, d, seed=MAIN["seed"] + 200).to(xd["q"].device)
+    o = torch.empty_like(xd["v"])
+    sT = torch.empty((B, H, d, d), dtype=torch.float32, device=xd["q"].device)
+    stream = torch.cuda.current_stream()
+    f = lambda: gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"], None,
+                                      o=o, final_state=sT, stream=stream)
+    settle_clocks(torch, f)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(launches):
+        f()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    alg = alg_bytes_main(B, H, T, d) + B * H * T * (d - 1) * 4  # the gate is d_k floats per token, not one
+    del av
+    return {"workload": "per-dimension gate, chunked route (32-token chunks), on the main workload's shape: "
+                        "B=4, H=16, T=8192, d_k=d_v=128, bf16 q/k/v, fp32 alpha [B,H,T,d_k]",
+            "ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "alg_bytes": alg,
             "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
@@ -500,7 +539,8 @@ def summarize_pmc(fetch_dir, write_dir, which="main"):
         "hbm_bytes_per_launch = %d" % (fetch_b + write_b),
         "algorithmic_bytes_per_launch = %d" % alg,
         "traffic_over_algorithmic = %.3f" % ((fetch_b + write_b) / alg),
-        "# kernel_source_hash: sha256 (first 16 hex digits) of %s" % ", ".join(sources),
+        "# kernel_source_hash: sha256 (first 16 hex digits) of the code (comments and whitespace runs removed) of %s"
+        % ", ".join(sources),
         "kernel_source_hash = %s" % kernel_source_hash(sources),
     ]
     with open(out_file, "w", encoding="utf-8") as fh:
@@ -579,6 +619,8 @@ def main():
                     help="skip the loop-case (sequence-split) report")
     ap.add_argument("--no-gla", action="store_true",
                     help="skip the gated-linear-attention report")
+    ap.add_argument("--no-vecgate", action="store_true",
+                    help="skip the per-dimension-gate route on the main workload's shape")
     ap.add_argument("--no-routes", action="store_true",
                     help="skip the chunked / scan / per-token route comparison")
     ap.add_argument("--pmc-pass", nargs="?", const="main", choices=sorted(PMC_TARGETS),
@@ -677,6 +719,8 @@ def main():
         res["loop_case"] = time_split(torch, dev, LOOP, launches=100)
     if not args.no_gla:
         res["gla"] = time_gla(torch, xd)
+    if not args.no_vecgate:
+        res["vecgate"] = time_vecgate(torch, xd)
     if not args.no_routes:
         res["routes"] = time_routes(torch, dev)
     if not args.no_cpu_baseline:

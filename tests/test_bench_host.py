@@ -109,3 +109,19 @@ def test_trace_summary_groups_by_kernel_and_shape_and_prices_the_main_launches(t
 def test_host_info_names_the_cpu():
     info = bench.host_info()
     assert info["nproc"] >= 1 and isinstance(info["cpu_model"], str)
+
+
+def test_kernel_hash_follows_code_not_comments():
+    """The traffic summaries stay valid across comment edits of a kernel and
+    are voided by any change of its code."""
+    base = "int f(int a) {  // sum\n  return a + 1; /* one */\n}\n"
+    read = lambda text: (lambda f: text)
+    h0 = bench.kernel_source_hash(["x.hpp"], read(base))
+    assert bench.kernel_source_hash(["x.hpp"], read(base.replace("// sum", "// the sum\n  "))) == h0
+    assert bench.kernel_source_hash(["x.hpp"], read(base.replace("/* one */", ""))) == h0
+    assert bench.kernel_source_hash(["x.hpp"], read(base.replace("a + 1", "a + 2"))) != h0
+    # one function of a file: edits elsewhere in the file do not matter
+    two = base + "int g(int b) {\n  return b;\n}\n"
+    hf = bench.kernel_source_hash(["x.hip:f"], read(two))
+    assert bench.kernel_source_hash(["x.hip:f"], read(two.replace("return b;", "return b * 2;"))) == hf
+    assert bench.kernel_source_hash(["x.hip:f"], read(two.replace("a + 1", "a - 1"))) != hf

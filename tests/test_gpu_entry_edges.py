@@ -1,5 +1,5 @@
-"""Edge cases of the sequence-split, scan, vector-gate and GLA entry points
-on the GPU: zero tokens (the final state is the initial one, or zero), no
+"""Edge cases of the sequence-split, scan, vector-gate (scan and chunked),
+GLA and fp32 chunked entry points on the GPU: zero tokens (the final state is the initial one, or zero), no
 sequences, fewer tokens than one chunk or block, and a final state that
 aliases the initial state.  Results are compared with the fp64 oracles or
 with exact expectations."""
@@ -9,8 +9,8 @@ import torch
 
 import oracle
 from gated_deltanet_sequence_amd import inputs
-from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd_split, gdn_scan_fwd, gdn_scan_fwd_vecgate,
-                                                 gla_chunk_fwd)
+from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd, gdn_chunk_fwd_split, gdn_chunk_fwd_vecgate,
+                                                 gdn_scan_fwd, gdn_scan_fwd_vecgate, gla_chunk_fwd)
 
 from _helpers import TOL, maxrel, oracle_inputs, to_dev, to_np
 
@@ -27,6 +27,11 @@ ENTRIES = {
     "scan_vecgate": lambda xd: gdn_scan_fwd_vecgate(xd["q"], xd["k"], xd["v"], _vec(xd["alpha"], xd["q"].shape[3]),
                                                     xd["beta"], xd["s0"]),
     "gla": lambda xd: gla_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"], 64),
+    "chunk_vecgate": lambda xd: gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], _vec(xd["alpha"], xd["q"].shape[3]),
+                                                      xd["beta"], xd["s0"]),
+    # the same bf16-rounded inputs as fp32: the fp32 chunked path
+    "fp32": lambda xd: gdn_chunk_fwd(xd["q"].float(), xd["k"].float(), xd["v"].float(), xd["alpha"], xd["beta"],
+                                     xd["s0"], 64),
 }
 
 
@@ -51,18 +56,19 @@ def test_no_sequences(name):
     assert o.numel() == 0 and sT.numel() == 0
 
 
-@pytest.mark.parametrize("name", ["split", "scan", "scan_vecgate"])
-@pytest.mark.parametrize("T", [1, 17, 63])
+@pytest.mark.parametrize("name", ["split", "scan", "scan_vecgate", "chunk_vecgate", "fp32"])
+@pytest.mark.parametrize("T", [1, 17, 31, 33, 63])
 def test_short_sequences_match_oracle(name, T):
     x = inputs.make_fwd_inputs(1, 2, T, 64, "bf16", seed=63 + T, init_state=True)
     o, sT = ENTRIES[name](to_dev(x))
     torch.cuda.synchronize()
     (q, k, v, a, b), s0 = oracle_inputs(x)
     ro, rs = oracle.oracle_fwd(q, k, v, a, b, s0)
-    assert maxrel(to_np(o), ro) <= TOL["bf16"] and maxrel(to_np(sT), rs) <= TOL["bf16"]
+    tol = TOL["f32"] if name == "fp32" else TOL["bf16"]
+    assert maxrel(to_np(o), ro) <= tol and maxrel(to_np(sT), rs) <= tol
 
 
-@pytest.mark.parametrize("name", ["scan", "gla"])
+@pytest.mark.parametrize("name", ["scan", "gla", "chunk_vecgate", "fp32"])
 def test_final_state_aliases_initial_state(name):
     x = inputs.make_fwd_inputs(1, 2, 700, 128, "bf16", seed=64, init_state=True)
     xd = to_dev(x)
@@ -71,8 +77,14 @@ def test_final_state_aliases_initial_state(name):
     s = xd["s0"].clone()
     if name == "scan":
         o, s2 = gdn_scan_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], s, final_state=s)
-    else:
+    elif name == "gla":
         o, s2 = gla_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], s, 64, final_state=s)
+    elif name == "chunk_vecgate":
+        o, s2 = gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], _vec(xd["alpha"], 128), xd["beta"], s,
+                                      final_state=s)
+    else:
+        o, s2 = gdn_chunk_fwd(xd["q"].float(), xd["k"].float(), xd["v"].float(), xd["alpha"], xd["beta"], s, 64,
+                              final_state=s)
     torch.cuda.synchronize()
     assert s2.data_ptr() == s.data_ptr()
     assert torch.equal(o, ref_o) and torch.equal(s, ref_s)
