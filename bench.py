@@ -288,6 +288,8 @@ def time_routes(torch, dev, launches=5):
     from gated_deltanet_sequence_amd import inputs
     from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd, gdn_chunk_fwd_split,
                                                      gdn_chunk_fwd_split_workspace, gdn_chunk_fwd_vecgate,
+                                                     gdn_chunk_fwd_vecgate_split,
+                                                     gdn_chunk_fwd_vecgate_split_workspace,
                                                      gdn_recurrent_step, gdn_scan_fwd, gdn_scan_fwd_vecgate,
                                                      gdn_scan_fwd_workspace)
     B, H, T, d = ROUTES["B"], ROUTES["H"], ROUTES["T"], ROUTES["d"]
@@ -295,6 +297,8 @@ def time_routes(torch, dev, launches=5):
     xd = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
     ws = torch.empty(gdn_scan_fwd_workspace(B, H, T, d, d, torch.bfloat16), dtype=torch.uint8, device=dev)
     wsp = torch.empty(max(gdn_chunk_fwd_split_workspace(B, H, T, d, d, 64, torch.bfloat16), 16),
+                      dtype=torch.uint8, device=dev)
+    wsv = torch.empty(max(gdn_chunk_fwd_vecgate_split_workspace(B, H, T, d, d, 32, torch.bfloat16), 16),
                       dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     a = (xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None)
@@ -311,7 +315,10 @@ def time_routes(torch, dev, launches=5):
                     ("chunked_vecgate", lambda: gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"],
                                                                       None, stream=stream)),
                     ("chunked_vecgate_percolumn", lambda: gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], avd,
-                                                                                xd["beta"], None, stream=stream))):
+                                                                                xd["beta"], None, stream=stream)),
+                    ("chunked_vecgate_split", lambda: gdn_chunk_fwd_vecgate_split(xd["q"], xd["k"], xd["v"], avd,
+                                                                                  xd["beta"], None, workspace=wsv,
+                                                                                  stream=stream))):
         settle_clocks(torch, f)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)

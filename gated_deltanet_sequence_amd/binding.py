@@ -58,6 +58,11 @@ def load_library(path: str | None = None):
     lib.gdn_scan_fwd_vecgate.restype = i32
     lib.gdn_chunk_fwd_vecgate.argtypes = lib.gdn_chunk_fwd.argtypes
     lib.gdn_chunk_fwd_vecgate.restype = i32
+    lib.gdn_chunk_fwd_vecgate_split.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
+                                                p, ctypes.c_size_t, p]
+    lib.gdn_chunk_fwd_vecgate_split.restype = i32
+    lib.gdn_chunk_fwd_vecgate_split_workspace.argtypes = [i64, i64, i64, i64, i64, i64, i32]
+    lib.gdn_chunk_fwd_vecgate_split_workspace.restype = ctypes.c_size_t
     lib.gdn_scan_fwd_workspace.argtypes = [i64, i64, i64, i64, i64, i32]
     lib.gdn_scan_fwd_workspace.restype = ctypes.c_size_t
     lib.gdn_chunk_fwd_split.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
@@ -227,6 +232,41 @@ def gdn_chunk_fwd_vecgate(q, k, v, alpha, beta, initial_state=None, chunk_size: 
                                    int(chunk_size), _DTYPES[q.dtype], _stream_ptr(stream, q.device))
     if rc != GDN_OK:
         raise GDNError(rc, "gdn_chunk_fwd_vecgate")
+    return o, final_state
+
+
+def gdn_chunk_fwd_vecgate_split_workspace(B, H, T, dk, dv, chunk_size: int = VECGATE_CHUNK,
+                                          dtype=torch.bfloat16) -> int:
+    """Bytes of workspace gdn_chunk_fwd_vecgate_split needs on the current device (0: no split)."""
+    return int(load_library().gdn_chunk_fwd_vecgate_split_workspace(B, H, T, dk, dv, int(chunk_size),
+                                                                    _DTYPES[dtype]))
+
+
+def gdn_chunk_fwd_vecgate_split(q, k, v, alpha, beta, initial_state=None, chunk_size: int = VECGATE_CHUNK, *,
+                                o=None, final_state=None, output_final_state: bool = True,
+                                workspace=None, stream=None):
+    """gdn_chunk_fwd_vecgate with every sequence split into segments that run
+    in parallel (for few, long sequences).  Same arguments and result; the
+    workspace (a uint8 GPU tensor) is allocated here when not given."""
+    B, H, T, dk, dv = _check_fwd_args(q, k, v, alpha, beta, initial_state, alpha_per_dim=True)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    need = gdn_chunk_fwd_vecgate_split_workspace(B, H, T, dk, dv, chunk_size, q.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    rc = lib.gdn_chunk_fwd_vecgate_split(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                         _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                                         _dev_ptr(initial_state, "initial_state"), _dev_ptr(o, "o"),
+                                         _dev_ptr(final_state, "final_state"), B, H, T, dk, dv,
+                                         int(chunk_size), _DTYPES[q.dtype],
+                                         _dev_ptr(workspace, "workspace"), ws_bytes,
+                                         _stream_ptr(stream, q.device))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_chunk_fwd_vecgate_split")
     return o, final_state
 
 

@@ -50,6 +50,7 @@
 #pragma once
 
 #include "gdn_common.hpp"
+#include "chunk_fwd_pipe.hpp"  // ChainMap: the chain -> (sequence, token range) map of the sequence split
 
 namespace gdn {
 namespace vec {
@@ -109,12 +110,19 @@ __device__ __forceinline__ void store_vec(float* p, const float (&x)[4]) {
 }
 
 // VG: alpha is [.., T, DK] (per-dimension gate); otherwise [.., T] (scalar).
+// cm maps workgroups to (sequence, token range) chains as for the pipelined
+// kernel (gdn::pipe::ChainMap): whole sequences (MAP_SEQ), or the first and
+// the last launch of the sequence split (MAP_SPLIT_A: segment states from a
+// zero start and segment transitions from the identity with V read as zero,
+// no output; MAP_SPLIT_C: every segment from its start state in cm.ws).  The
+// per-token maps stay affine with a per-dimension gate, so the split and its
+// combine step are the same.
 template <class T, int DK, bool VG>
 __global__ __launch_bounds__(NT) void chunk_vec_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* initial_state, T* __restrict__ o, float* final_state,
-    int nchain, int64_t Tlen, int DV, int xcd_map) {
+    gdn::pipe::ChainMap cm, int DV, int xcd_map) {
   using Sm = Smem<T, DK>;
   constexpr int LDK = Sm::LDK;
   constexpr int LDC = Sm::LDC;
@@ -155,15 +163,43 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
       slice = w % NS;
     }
   }
-  if (chain >= nchain) return;
+  if (chain >= gdn::pipe::map_chains(cm)) return;
 
-  const T* qc = q + (int64_t)chain * Tlen * DK;
-  const T* kc = k + (int64_t)chain * Tlen * DK;
-  const T* vc = v + (int64_t)chain * Tlen * DV + slice * DVS;
-  const float* ac = alpha + (int64_t)chain * Tlen * (VG ? DK : 1);
-  const float* bc = beta + (int64_t)chain * Tlen;
-  T* oc = o + (int64_t)chain * Tlen * DV + slice * DVS;
-  const int64_t st_off = ((int64_t)chain * DV + (int64_t)slice * DVS) * DK;
+  // this chain's sequence, token range, start and end state, and whether it
+  // reads V and writes output
+  const int64_t dd = (int64_t)DK * DV;  // floats per state
+  int seq = chain;
+  int64_t t0 = 0, Tlen = cm.T;
+  bool v_on = true, o_on = true, s0_ident = false;
+  const float* s0 = initial_state ? initial_state + (int64_t)chain * dd : nullptr;
+  float* sT = final_state ? final_state + (int64_t)chain * dd : nullptr;
+  if (cm.mode == gdn::pipe::MAP_SPLIT_A) {
+    const int per = cm.nseq * (cm.G - 1);
+    const int kind = chain / per, r = chain % per;
+    seq = r / (cm.G - 1);
+    t0 = (int64_t)(r % (cm.G - 1)) * cm.L;
+    Tlen = cm.L;
+    o_on = false;
+    v_on = kind == 0;
+    s0_ident = kind == 1;
+    s0 = nullptr;
+    sT = cm.ws + ((int64_t)kind * per + r) * dd;
+  } else if (cm.mode == gdn::pipe::MAP_SPLIT_C) {
+    seq = chain / cm.G;
+    const int g = chain % cm.G;
+    t0 = (int64_t)g * cm.L;
+    Tlen = g == cm.G - 1 ? cm.T - t0 : cm.L;
+    s0 = cm.ws + (2 * (int64_t)cm.nseq * (cm.G - 1) + (int64_t)seq * cm.G + g) * dd;
+    sT = g == cm.G - 1 && final_state ? final_state + (int64_t)seq * dd : nullptr;
+  }
+  const int64_t tok0 = (int64_t)seq * cm.T + t0;  // first token in memory
+  const T* qc = q + tok0 * DK;
+  const T* kc = k + tok0 * DK;
+  const T* vc = v + tok0 * DV + slice * DVS;
+  const float* ac = alpha + tok0 * (VG ? DK : 1);
+  const float* bc = beta + tok0;
+  T* oc = o + tok0 * DV + slice * DVS;
+  const int64_t st_off = (int64_t)slice * DVS * DK;  // this slice's rows within s0 / sT
 
   // The upper blocks of the triangular buffers are never written and must
   // read as zero.
@@ -183,8 +219,11 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
     if (t < JB * IB) {
       const int jb = t / IB, ib = t % IB;
       const int i = ib * 16 + lr, j = jb * 16 + 4 * lg;
-      if (initial_state) {
-        const float4 s4 = *reinterpret_cast<const float4*>(initial_state + st_off + (int64_t)i * DK + j);
+      if (s0_ident) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sacc[m][e] = slice * DVS + i == j + e ? 1.f : 0.f;
+      } else if (s0) {
+        const float4 s4 = *reinterpret_cast<const float4*>(s0 + st_off + (int64_t)i * DK + j);
         Sacc[m] = f32x4{s4.x, s4.y, s4.z, s4.w};
       }
       store4<T>(&sm.S[i * LDK + j], Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
@@ -246,7 +285,7 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
     if (tid < C) sm.beta[tid] = ch * C + tid < Tlen ? rbt : 0.f;
     if (tid < NVV) {
       const int r = tid / (DVS / VEC), cg = tid % (DVS / VEC);
-      *reinterpret_cast<uint4*>(&sm.V[r * DVS + cg * VEC]) = ch * C + r < Tlen ? rv : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&sm.V[r * DVS + cg * VEC]) = v_on && ch * C + r < Tlen ? rv : make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
     {
@@ -440,7 +479,7 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
         }
         store4<T>(&sm.Yt[i * LDC + r0], y[0], y[1], y[2], y[3]);
       }
-    } else {
+    } else if (o_on) {
       // the inter-chunk part of the output, S Q~^T (tile [i][r] of this
       // output wave, kept live until the output is finished)
       const int t = wave - 2;
@@ -462,7 +501,7 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
 
     // O^T += U^T P^T and store (output waves); S^T <- Diag(2^(G_C)) S^T +
     // Kbar^T U (every wave, its state tiles).
-    if (wave >= 2) {
+    if (wave >= 2 && o_on) {
       const int t = wave - 2;
       const int ib = t / RB, rb = t % RB;
       Oacc = Mma<T>::template run<C>(Oacc, &sm.Ut[ib * 16 * LDC], LDC, &sm.P[rb * 16 * LDC], LDC, lane);
@@ -484,14 +523,14 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
   }
 
   // final state slice (fp32)
-  if (final_state) {
+  if (sT) {
 #pragma unroll
     for (int m = 0; m < NST; ++m) {
       const int t = wave + NW * m;
       if (t < JB * IB) {
         const int jb = t / IB, ib = t % IB;
         const int i = ib * 16 + lr, j = jb * 16 + 4 * lg;
-        *reinterpret_cast<float4*>(final_state + st_off + (int64_t)i * DK + j) =
+        *reinterpret_cast<float4*>(sT + st_off + (int64_t)i * DK + j) =
             make_float4(Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
       }
     }

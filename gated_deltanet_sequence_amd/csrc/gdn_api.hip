@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "gdn.h"
 #include "chunk_fwd_pipe.hpp"
@@ -283,37 +284,105 @@ int noalloc_scratch(void** out) {
 
 namespace {
 // The 32-token chunk kernel of chunk_vec.hpp: the per-dimension gate (VG),
-// and the scalar gate for fp32 inputs.
+// and the scalar gate for fp32 inputs.  vec_dispatch calls f(T{}, DK) with
+// the element type and key width of the instantiation that serves dtype, dk.
+template <bool VG, class F>
+int vec_dispatch(gdn_dtype dtype, int64_t dk, F&& f) {
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
+  if (!VG || dtype == GDN_F32) return dk == 128 ? f(float{}, D128{}) : f(float{}, D64{});
+  return dk == 128 ? f(bf16_t{}, D128{}) : f(bf16_t{}, D64{});
+}
+
 template <bool VG, class T, int DK>
 int launch_vec_t(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
-                 const float* initial_state, void* o, float* final_state, int64_t nchain, int64_t T_,
+                 const float* initial_state, void* o, float* final_state, const gdn::pipe::ChainMap& cm,
                  int64_t dv, hipStream_t stream) {
+  const int64_t nchain = gdn::pipe::map_chains(cm);
   const int64_t nblocks = nchain * (dv / gdn::vec::DVS);
   if (nblocks > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
   const int xcd_map = (nchain % 8) == 0;
   hipLaunchKernelGGL((gdn::vec::chunk_vec_kernel<T, DK, VG>), dim3((unsigned)nblocks), dim3(gdn::vec::NT), 0,
                      stream, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), alpha,
-                     beta, initial_state, static_cast<T*>(o), final_state, (int)nchain, T_, (int)dv, xcd_map);
+                     beta, initial_state, static_cast<T*>(o), final_state, cm, (int)dv, xcd_map);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 template <bool VG>
 int launch_vec(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
-               const float* initial_state, void* o, float* final_state, int64_t nchain, int64_t T,
+               const float* initial_state, void* o, float* final_state, const gdn::pipe::ChainMap& cm,
                int64_t dk, int64_t dv, gdn_dtype dtype, hipStream_t stream) {
-  if (nchain == 0) return GDN_OK;
-  if (T == 0 && !final_state) return GDN_OK;
-  if constexpr (!VG) {
-    // the scalar gate takes this kernel for fp32 inputs only
-    (void)dtype;
-    return dk == 128 ? launch_vec_t<false, float, 128>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv, stream)
-                     : launch_vec_t<false, float, 64>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv, stream);
-  } else if (dtype == GDN_BF16) {
-    return dk == 128 ? launch_vec_t<true, bf16_t, 128>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv, stream)
-                     : launch_vec_t<true, bf16_t, 64>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv, stream);
-  } else {
-    return dk == 128 ? launch_vec_t<true, float, 128>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv, stream)
-                     : launch_vec_t<true, float, 64>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dv, stream);
+  return vec_dispatch<VG>(dtype, dk, [&](auto t, auto dkc) {
+    return launch_vec_t<VG, decltype(t), decltype(dkc)::value>(q, k, v, alpha, beta, initial_state, o, final_state,
+                                                               cm, dv, stream);
+  });
+}
+
+// Segments of the vector-gate split: as split_plan, but the first launch
+// may hold as many workgroups as the kernel's occupancy puts on the device
+// at once (two per CU at d = 64 in bf16, one otherwise), and segments are
+// multiples of the 32-token chunk.
+template <bool VG>
+void vec_split_plan(int64_t nseq, int64_t T, int64_t dk, int64_t dv, gdn_dtype dtype, int& G, int64_t& L) {
+  G = 1;
+  L = T;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) {
+    (void)hipGetLastError();
+    return;
   }
+  const int per_cu = vec_dispatch<VG>(dtype, dk, [&](auto t, auto dkc) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(&gdn::vec::chunk_vec_kernel<decltype(t), decltype(dkc)::value, VG>),
+            gdn::vec::NT, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      n = 1;
+    }
+    return n > 0 ? n : 1;
+  });
+  const int64_t ns = dv / gdn::vec::DVS;
+  int64_t g = 1 + (int64_t)ncu * per_cu / (2 * nseq * ns);
+  g = g < T / MIN_SEG ? g : T / MIN_SEG;
+  if (g < 3) return;
+  const int64_t C = gdn::vec::C;
+  L = ((T + g - 1) / g + C - 1) / C * C;
+  G = (int)((T + L - 1) / L);
+  if (G < 3) {
+    G = 1;
+    L = T;
+  }
+}
+
+// The combine step of a sequence split: the start state of every segment.
+int launch_combine(int64_t dk, const float* initial_state, float* ws, int64_t nchain, int G, hipStream_t stream) {
+  if (dk == 128)
+    hipLaunchKernelGGL(gdn::split::split_combine_kernel<128>, dim3((unsigned)(nchain * (128 / gdn::split::ROWS))),
+                       dim3(gdn::split::threads_for<128>()), 0, stream, initial_state, ws, (int)nchain, G);
+  else
+    hipLaunchKernelGGL(gdn::split::split_combine_kernel<64>, dim3((unsigned)(nchain * (64 / gdn::split::ROWS))),
+                       dim3(gdn::split::threads_for<64>()), 0, stream, initial_state, ws, (int)nchain, G);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+// The three launches of the vector-gate split on workspace ws (G >= 2).
+int vec_split_launches(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                       const float* initial_state, void* o, float* final_state, int64_t nchain, int64_t T,
+                       int64_t dk, int64_t dv, gdn_dtype dtype, int G, int64_t L, float* ws,
+                       hipStream_t stream) {
+  gdn::pipe::ChainMap cm{};
+  cm.nseq = (int)nchain;
+  cm.G = G;
+  cm.T = T;
+  cm.L = L;
+  cm.ws = ws;
+  cm.mode = gdn::pipe::MAP_SPLIT_A;
+  int r = launch_vec<true>(q, k, v, alpha, beta, nullptr, o, nullptr, cm, dk, dv, dtype, stream);
+  if (r != GDN_OK) return r;
+  r = launch_combine(dk, initial_state, ws, nchain, G, stream);
+  if (r != GDN_OK) return r;
+  cm.mode = gdn::pipe::MAP_SPLIT_C;
+  return launch_vec<true>(q, k, v, alpha, beta, nullptr, o, final_state, cm, dk, dv, dtype, stream);
 }
 }  // namespace
 
@@ -336,8 +405,8 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
                              dk, dv, stream);
   // fp32: chunks of 32 tokens (64-token fp32 buffers exceed the LDS at
   // d = 128); the result does not depend on the chunk size beyond rounding
-  return launch_vec<false>(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dk, dv, dtype,
-                           stream);
+  return launch_vec<false>(q, k, v, alpha, beta, initial_state, o, final_state, seq_map(nchain, T), dk, dv,
+                           dtype, stream);
 }
 
 int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
@@ -433,8 +502,53 @@ int gdn_chunk_fwd_vecgate(const void* q, const void* k, const void* v, const flo
                            chunk_size > 0 ? 64 : chunk_size, dtype, true);
   if (rc != GDN_OK) return rc;
   if (chunk_size != gdn::vec::C) return GDN_ERR_UNSUPPORTED;
-  return launch_vec<true>(q, k, v, alpha, beta, initial_state, o, final_state, B * H, T, dk, dv, dtype,
+  const int64_t nchain = B * H;
+  if (nchain == 0 || (T == 0 && !final_state)) return GDN_OK;
+  return launch_vec<true>(q, k, v, alpha, beta, initial_state, o, final_state, seq_map(nchain, T), dk, dv, dtype,
                           static_cast<hipStream_t>(hip_stream));
+}
+
+size_t gdn_chunk_fwd_vecgate_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                                             int64_t chunk_size, gdn_dtype dtype) {
+  if (B <= 0 || H <= 0 || T <= 0 || dk != dv || (dk != 64 && dk != 128) || chunk_size != gdn::vec::C ||
+      (dtype != GDN_BF16 && dtype != GDN_F32) || too_large(B, H, T))
+    return 0;
+  int G;
+  int64_t L;
+  vec_split_plan<true>(B * H, T, dk, dv, dtype, G, L);
+  return split_ws_bytes(B * H, G, dk);
+}
+
+int gdn_chunk_fwd_vecgate_split(const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, const float* initial_state, void* o, float* final_state,
+                                int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk_size,
+                                gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
+                           chunk_size > 0 ? 64 : chunk_size, dtype, true);
+  if (rc != GDN_OK) return rc;
+  if (chunk_size != gdn::vec::C) return GDN_ERR_UNSUPPORTED;
+  const int64_t nchain = B * H;
+  int G = 1;
+  int64_t L = T;
+  if (nchain > 0 && T > 0) vec_split_plan<true>(nchain, T, dk, dv, dtype, G, L);
+  if (G < 2)
+    return gdn_chunk_fwd_vecgate(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv, chunk_size,
+                                 dtype, hip_stream);
+  const size_t need = split_ws_bytes(nchain, G, dk);
+  if (!workspace || workspace_bytes < need) return GDN_ERR_INVALID_ARG;
+  if (misaligned(workspace)) return GDN_ERR_ALIGNMENT;
+  {
+    const Range rw{workspace, (int64_t)need};
+    const int64_t esz = dtype == GDN_BF16 ? 2 : 4;
+    const Range others[] = {{q, nchain * T * dk * esz}, {k, nchain * T * dk * esz},
+                            {v, nchain * T * dv * esz}, {o, nchain * T * dv * esz},
+                            {alpha, nchain * T * dk * 4}, {beta, nchain * T * 4},
+                            {initial_state, nchain * dv * dk * 4}, {final_state, nchain * dv * dk * 4}};
+    for (const Range& r : others)
+      if (overlaps(rw, r)) return GDN_ERR_INVALID_ARG;
+  }
+  return vec_split_launches(q, k, v, alpha, beta, initial_state, o, final_state, nchain, T, dk, dv, dtype, G, L,
+                            static_cast<float*>(workspace), static_cast<hipStream_t>(hip_stream));
 }
 
 size_t gdn_chunk_fwd_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,

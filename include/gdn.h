@@ -172,6 +172,38 @@ int gdn_chunk_fwd_vecgate(const void* q, const void* k, const void* v,
                           int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
                           int64_t chunk_size, gdn_dtype dtype, void* hip_stream);
 
+/*
+ * gdn_chunk_fwd_vecgate_split — gdn_chunk_fwd_vecgate for workloads with few
+ * sequences: every sequence is cut into G segments that run in parallel and
+ * are joined by composing their affine maps ([P1] §2.3, §3.3), exactly as in
+ * gdn_chunk_fwd_split (the per-token maps stay affine with a per-dimension
+ * gate): the segments' states from a zero start and their transitions, then
+ * the segments' start states (fp32), then every segment from its start state.
+ * G is chosen from B*H, T, the device's CU count and the kernel's occupancy;
+ * when fewer than 3 segments would do, G is 1 and this is
+ * gdn_chunk_fwd_vecgate itself (the workspace is not touched).
+ *
+ *   workspace        device memory owned by the caller, at least
+ *                    gdn_chunk_fwd_vecgate_split_workspace(...) bytes (0 when
+ *                    no split is planned; NULL is then accepted), 16-byte
+ *                    aligned, overlapping no other argument; its contents on
+ *                    entry do not matter.  Calls sharing a workspace must not
+ *                    overlap in time.
+ * Other arguments, layouts, aliasing and errors as for gdn_chunk_fwd_vecgate;
+ * a missing or too small workspace returns GDN_ERR_INVALID_ARG.
+ */
+int gdn_chunk_fwd_vecgate_split(const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta,
+                                const float* initial_state, void* o, float* final_state,
+                                int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                                int64_t chunk_size, gdn_dtype dtype, void* workspace,
+                                size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes gdn_chunk_fwd_vecgate_split needs on the current device
+ * (0: no split).  Host-only; also 0 for arguments the entry point rejects. */
+size_t gdn_chunk_fwd_vecgate_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk,
+                                             int64_t dv, int64_t chunk_size, gdn_dtype dtype);
+
 /* Workspace bytes gdn_scan_fwd needs for these sizes.  Host-only. */
 size_t gdn_scan_fwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
                               gdn_dtype dtype);

@@ -194,3 +194,25 @@ def test_noalloc_split_validates_before_any_device_call(lib):
     assert noalloc(lib, dtype=7) == binding.GDN_ERR_INVALID_ARG
     # nothing to do: no sequences
     assert noalloc(lib, B=0) == binding.GDN_OK
+
+
+def test_vecgate_split_rejects_invalid_arguments_and_sizes_workspace(lib):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def vs(B=1, H=1, T=64, dk=64, dv=64, C=32, dtype=1, q=A, o=A + 256 * MB, alpha=A + 192 * MB):
+        return lib.gdn_chunk_fwd_vecgate_split(P(q), P(A + 64 * MB), P(A + 128 * MB), P(alpha),
+                                               P(A + 240 * MB), None, P(o), None, B, H, T, dk, dv, C, dtype,
+                                               None, 0, None)
+    assert vs(B=-1) == binding.GDN_ERR_INVALID_ARG
+    assert vs(dtype=5) == binding.GDN_ERR_INVALID_ARG
+    assert vs(q=None) == binding.GDN_ERR_INVALID_ARG
+    assert vs(C=64) == binding.GDN_ERR_UNSUPPORTED          # this route's chunk is 32 tokens
+    assert vs(dk=96, dv=96) == binding.GDN_ERR_UNSUPPORTED
+    assert vs(q=A + 4) == binding.GDN_ERR_ALIGNMENT
+    assert vs(o=A) == binding.GDN_ERR_INVALID_ARG            # output overlaps q
+    assert vs(B=0) == 0                                      # nothing to do
+    f = lib.gdn_chunk_fwd_vecgate_split_workspace
+    assert f(1, 8, 16384, 64, 64, 64, 1) == 0               # unsupported chunk size
+    assert f(1, 8, 16384, 96, 96, 32, 1) == 0               # unsupported width
+    assert f(0, 8, 16384, 64, 64, 32, 1) == 0               # nothing to do
+    assert f(1, 8, 16384, 64, 64, 32, 1) >= 0               # no GPU here: 0; on a GPU: > 0

@@ -12,7 +12,9 @@ import torch
 
 import oracle
 from gated_deltanet_sequence_amd import inputs
-from gated_deltanet_sequence_amd.binding import (GDNError, gdn_chunk_fwd, gdn_chunk_fwd_vecgate, gdn_scan_fwd,
+from gated_deltanet_sequence_amd.binding import (GDNError, gdn_chunk_fwd, gdn_chunk_fwd_vecgate,
+                                                 gdn_chunk_fwd_vecgate_split,
+                                                 gdn_chunk_fwd_vecgate_split_workspace, gdn_scan_fwd,
                                                  gdn_scan_fwd_vecgate)
 
 from _helpers import TOL, maxrel, oracle_inputs, to_dev, to_np
@@ -163,3 +165,72 @@ def test_chunked_uniform_vecgate_matches_scalar_gate_fp32():
     o2, s2 = gdn_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"], 64)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+# Sequence split of the chunked vector-gate route: few sequences, long
+# enough for at least three segments (the workspace query says whether the
+# split engages).  Against the oracle, at the bars above.
+SPLIT_CASES = [
+    # B, H, T, d, dtype, initial state, gate
+    (1, 8, 16384, 64, "bf16", False, "default"),   # the pages' route-comparison shape
+    (1, 2, 8192, 128, "bf16", True, "slow"),
+    (2, 1, 3000, 128, "bf16", True, "fast"),
+    (1, 2, 4096, 64, "f32", True, "resets"),
+    (1, 1, 2000, 128, "f32", True, "default"),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "B%dH%dT%dd%d_%s_%s_%s" % (
+    c[0], c[1], c[2], c[3], c[4], "s0" if c[5] else "z", c[6]))
+def test_chunked_vecgate_split_against_oracle(case):
+    B, H, T, d, dtype, init, gate = case
+    x = inputs.make_fwd_inputs(B, H, T, d, dtype, seed=900 + T + d, init_state=init)
+    x["alpha"] = inputs.make_vec_alpha(B, H, T, d, seed=950 + T, gate=gate)
+    ws = gdn_chunk_fwd_vecgate_split_workspace(B, H, T, d, d, 32, x["q"].dtype)
+    print("case chunked vecgate split", case, "workspace", ws, flush=True)
+    assert ws > 0, "the split is expected to engage for this shape"
+    xd = to_dev(x)
+    o, sT = gdn_chunk_fwd_vecgate_split(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"])
+    torch.cuda.synchronize()
+    (q, k, v, _, b), s0 = oracle_inputs(x)
+    ro, rs = oracle.oracle_fwd_vecgate(q, k, v, x["alpha"].numpy(), b, s0)
+    eo, es = maxrel(to_np(o), ro), maxrel(to_np(sT), rs)
+    print("  err o %.3e  err S_T %.3e (tol %.0e)" % (eo, es, TOL[dtype]), flush=True)
+    assert np.all(np.isfinite(to_np(o))) and np.all(np.isfinite(to_np(sT)))
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_chunked_vecgate_split_falls_back_and_aliases():
+    """With many sequences no split is planned (workspace 0) and the entry
+    point is the plain chunked route, bit for bit; a final state aliasing the
+    initial state gives the same result as separate buffers."""
+    x = inputs.make_fwd_inputs(8, 8, 512, 64, "bf16", seed=71, init_state=True)
+    x["alpha"] = inputs.make_vec_alpha(8, 8, 512, 64, seed=72)
+    assert gdn_chunk_fwd_vecgate_split_workspace(8, 8, 512, 64, 64, 32, torch.bfloat16) == 0
+    xd = to_dev(x)
+    o1, s1 = gdn_chunk_fwd_vecgate_split(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"])
+    o2, s2 = gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+    y = inputs.make_fwd_inputs(1, 2, 6000, 64, "bf16", seed=73, init_state=True)
+    y["alpha"] = inputs.make_vec_alpha(1, 2, 6000, 64, seed=74)
+    assert gdn_chunk_fwd_vecgate_split_workspace(1, 2, 6000, 64, 64, 32, torch.bfloat16) > 0
+    yd = to_dev(y)
+    ref_o, ref_s = gdn_chunk_fwd_vecgate_split(yd["q"], yd["k"], yd["v"], yd["alpha"], yd["beta"], yd["s0"])
+    s = yd["s0"].clone()
+    o, s3 = gdn_chunk_fwd_vecgate_split(yd["q"], yd["k"], yd["v"], yd["alpha"], yd["beta"], s, final_state=s)
+    torch.cuda.synchronize()
+    assert s3.data_ptr() == s.data_ptr()
+    assert torch.equal(o, ref_o) and torch.equal(s, ref_s)
+
+
+def test_chunked_vecgate_split_rejects_small_workspace():
+    x = inputs.make_fwd_inputs(1, 2, 6000, 64, "bf16", seed=75)
+    x["alpha"] = inputs.make_vec_alpha(1, 2, 6000, 64, seed=76)
+    need = gdn_chunk_fwd_vecgate_split_workspace(1, 2, 6000, 64, 64, 32, torch.bfloat16)
+    assert need > 0
+    xd = to_dev(x)
+    ws = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(GDNError):
+        gdn_chunk_fwd_vecgate_split(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None, workspace=ws)
