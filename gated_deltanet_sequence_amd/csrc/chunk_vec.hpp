@@ -356,7 +356,7 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
         }
         *reinterpret_cast<uint4*>(&sm.Qr[r * LDK + j0]) = zq;
       }
-      store_vec(&sm.Qs[r * LDK + j0], qs);
+      if (o_on) store_vec(&sm.Qs[r * LDK + j0], qs);
       store_vec(&sm.Kr[r * LDK + j0], kr);
       store_vec(&sm.Kh[r * LDK + j0], kh);
     }
@@ -368,7 +368,8 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
     //   L[r][s] = beta_r A_kk[r][s] (s < r),  P[r][s] = A_qk[r][s] (s <= r).
     // Tiles u = 0..5: kind u / 3 (0: L, 1: P), block pair (sb, rb) =
     // (0,0), (0,1), (1,1).
-    for (int u = wave; u < 6; u += NW) {
+    // (without output only the L tiles: P and the query operands go unused)
+    for (int u = wave; u < (o_on ? 6 : 3); u += NW) {
       const int kind = u / 3, pr = u % 3;
       const int rb = pr >= 1 ? 1 : 0, sb = pr == 1 ? 0 : rb;
       const int r = rb * 16 + lr;
