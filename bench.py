@@ -252,29 +252,35 @@ def time_vecgate(torch, xd, launches=10):
     (the workloads' gate law): mean launch time and its HBM-roofline fraction
     (its algorithmic bytes count the [B,H,T,d_k] fp32 gate)."""
     from gated_deltanet_sequence_amd import inputs
-    from gated_deltanet_sequence_amd.binding import gdn_chunk_fwd_vecgate
+    from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd_vecgate, gdn_scan_fwd_vecgate,
+                                                     gdn_scan_fwd_workspace)
     B, H, T, d = xd["q"].shape
     av = inputs.make_vec_alpha(B, H, T, d, seed=MAIN["seed"] + 200).to(xd["q"].device)
     o = torch.empty_like(xd["v"])
     sT = torch.empty((B, H, d, d), dtype=torch.float32, device=xd["q"].device)
+    ws = torch.empty(gdn_scan_fwd_workspace(B, H, T, d, d, torch.bfloat16), dtype=torch.uint8, device=xd["q"].device)
     stream = torch.cuda.current_stream()
-    f = lambda: gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"], None,
-                                      o=o, final_state=sT, stream=stream)
-    settle_clocks(torch, f)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(launches):
-        f()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / launches
+    times = {}
+    for name, f in (("chunked", lambda: gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"], None,
+                                                              o=o, final_state=sT, stream=stream)),
+                    ("scan", lambda: gdn_scan_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"], None,
+                                                          o=o, final_state=sT, workspace=ws, stream=stream))):
+        settle_clocks(torch, f)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) / launches
+    ms = times["chunked"]
     alg = alg_bytes_main(B, H, T, d) + B * H * T * (d - 1) * 4  # the gate is d_k floats per token, not one
-    del av
+    del av, ws
     return {"workload": "per-dimension gate, chunked route (32-token chunks), on the main workload's shape: "
                         "B=4, H=16, T=8192, d_k=d_v=128, bf16 q/k/v, fp32 alpha [B,H,T,d_k]",
             "ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "alg_bytes": alg,
-            "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "scan_route_ms": times["scan"]}
 
 
 ROUTES = dict(B=1, H=8, T=16384, d=64, seed=6)

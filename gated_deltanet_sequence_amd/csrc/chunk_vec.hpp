@@ -240,28 +240,35 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
   const int gj = tid % DK, gg = tid / DK;  // gate column and token group of this thread
   uint4 rq[NQK], rk[NQK], rv;
   float ra[TPG], rbt;
-  auto tok = [&](int64_t t) { return t < Tlen ? t : Tlen - 1; };  // clamped token index
   auto load_chunk = [&](int64_t ch) {
+    // chunk base pointers (uniform) and 32-bit offsets; rows past the end
+    // are clamped to the chunk's last valid row
     const int64_t t0 = ch * C;
+    const int rmax = (int)(Tlen - 1 - t0 < C - 1 ? Tlen - 1 - t0 : C - 1);
+    const T* qb = qc + t0 * DK;
+    const T* kb = kc + t0 * DK;
+    const T* vb = vc + t0 * DV;
+    const float* ab = ac + t0 * (VG ? DK : 1);
+    const float* bb = bc + t0;
 #pragma unroll
     for (int it = 0; it < NQK; ++it) {
       const int vi = tid + NT * it;
       const int r = vi % C, cg = vi / C;  // token fastest (see the operands below)
-      const int64_t off = tok(t0 + r) * DK + cg * VEC;
-      rq[it] = *reinterpret_cast<const uint4*>(qc + off);
-      rk[it] = *reinterpret_cast<const uint4*>(kc + off);
+      const int off = min(r, rmax) * DK + cg * VEC;
+      rq[it] = *reinterpret_cast<const uint4*>(qb + off);
+      rk[it] = *reinterpret_cast<const uint4*>(kb + off);
     }
     {
       const int vi = tid % NVV;
       const int r = vi / (DVS / VEC), cg = vi % (DVS / VEC);
-      rv = *reinterpret_cast<const uint4*>(vc + tok(t0 + r) * DV + cg * VEC);
+      rv = *reinterpret_cast<const uint4*>(vb + min(r, rmax) * DV + cg * VEC);
     }
 #pragma unroll
     for (int i = 0; i < TPG; ++i) {
-      const int64_t t = tok(t0 + gg * TPG + i);
-      ra[i] = ac[VG ? t * DK + gj : t];
+      const int rr = min(gg * TPG + i, rmax);
+      ra[i] = ab[VG ? rr * DK + gj : rr];
     }
-    rbt = bc[tok(t0 + tid % C)];
+    rbt = bb[min(tid % C, rmax)];
   };
 
   if (nchunks > 0) load_chunk(0);
@@ -368,8 +375,10 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
     //   L[r][s] = beta_r A_kk[r][s] (s < r),  P[r][s] = A_qk[r][s] (s <= r).
     // Tiles u = 0..5: kind u / 3 (0: L, 1: P), block pair (sb, rb) =
     // (0,0), (0,1), (1,1).
-    // (without output only the L tiles: P and the query operands go unused)
-    for (int u = wave; u < (o_on ? 6 : 3); u += NW) {
+    // The three L tiles run here, on waves 0..2; the three P tiles (needed
+    // only by the output) run in the next step on the waves that are not
+    // building the inverse, and not at all without output.
+    auto gram_tile = [&](int u) {
       const int kind = u / 3, pr = u % 3;
       const int rb = pr >= 1 ? 1 : 0, sb = pr == 1 ? 0 : rb;
       const int r = rb * 16 + lr;
@@ -406,7 +415,8 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
       store4<T>(&dst[r * LDC + s0], val[0], val[1], val[2], val[3]);
       if (kind == 0 && sb == rb)
         *reinterpret_cast<float4*>(&sm.Ld[sb][r - rb * 16][s0 - sb * 16]) = make_float4(val[0], val[1], val[2], val[3]);
-    }
+    };
+    if (wave < 3) gram_tile(wave);
     __syncthreads();
 
     f32x4 Oacc = zero4();
@@ -480,12 +490,14 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
         }
         store4<T>(&sm.Yt[i * LDC + r0], y[0], y[1], y[2], y[3]);
       }
+      if (o_on) gram_tile(5);
     } else if (o_on) {
       // the inter-chunk part of the output, S Q~^T (tile [i][r] of this
       // output wave, kept live until the output is finished)
       const int t = wave - 2;
       const int ib = t / RB, rb = t % RB;
       Oacc = Mma<T>::template run<DK>(zero4(), &sm.S[ib * 16 * LDK], LDK, &sm.Qs[rb * 16 * LDK], LDK, lane);
+      gram_tile(3 + t);
     }
     __syncthreads();
 
