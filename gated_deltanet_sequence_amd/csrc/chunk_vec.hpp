@@ -456,23 +456,33 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
         band(2, lq[0]);
         band(3, lq[1]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sm.Ti[(16 * b + r) * LDC + 16 * b + c] = Elem<T>::from_f32(x[r]);
-          sm.Tt[(16 * b + c) * LDC + 16 * b + r] = Elem<T>::from_f32(x[r]);
+        for (int r = 0; r < 16; ++r) sm.Ti[(16 * b + r) * LDC + 16 * b + c] = Elem<T>::from_f32(x[r]);
+        // column c of the block is row 16 b + c of Ti^T: 16 consecutive elements
+#pragma unroll
+        for (int h = 0; h < 16 / VEC; ++h) {
+          float xv[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) xv[e] = x[VEC * h + e];
+          store_vec(&sm.Tt[(16 * b + c) * LDC + 16 * b + VEC * h], xv);
         }
       }
       wave_lds_sync();
       // ... then the off-diagonal block Ti[1][0] = -Ti[1][1] L[1][0] Ti[0][0].
-      {
-        const f32x4 acc = Mma<T>::template run<16>(zero4(), &sm.Lb[16 * LDC], LDC, &sm.Tt[0], LDC, lane);
-        store4<T>(&sm.Mt[lr * LDC + 4 * lg], acc[0], acc[1], acc[2], acc[3]);
+      const f32x4 m = Mma<T>::template run<16>(zero4(), &sm.Lb[16 * LDC], LDC, &sm.Tt[0], LDC, lane);
+      f32x4 acc;
+      if constexpr (sizeof(T) == 2) {
+        // M = L[1][0] Ti[0][0] is in the accumulator layout, which is the B
+        // operand layout of the 16-deep product: no round trip through LDS
+        const i16x4_t av = __builtin_bit_cast(i16x4_t, *reinterpret_cast<const uint2*>(&sm.Ti[(16 + lr) * LDC + 16 + 4 * lg]));
+        const i16x4_t bv = __builtin_bit_cast(i16x4_t, make_uint2(pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])));
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, zero4(), 0, 0, 0);
+      } else {
+        store4<T>(&sm.Mt[lr * LDC + 4 * lg], m[0], m[1], m[2], m[3]);
+        wave_lds_sync();
+        acc = Mma<T>::template run<16>(zero4(), &sm.Ti[16 * LDC + 16], LDC, &sm.Mt[0], LDC, lane);
       }
-      wave_lds_sync();
-      {
-        const f32x4 acc = Mma<T>::template run<16>(zero4(), &sm.Ti[16 * LDC + 16], LDC, &sm.Mt[0], LDC, lane);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.Ti[(16 + 4 * lg + e) * LDC + lr] = Elem<T>::from_f32(-acc[e]);
-      }
+      for (int e = 0; e < 4; ++e) sm.Ti[(16 + 4 * lg + e) * LDC + lr] = Elem<T>::from_f32(-acc[e]);
     } else if (wave == 1) {
       // Y = diag(beta) (V - K~ S^T), tiles [r][i], meanwhile.
 #pragma unroll
