@@ -1,0 +1,99 @@
+"""A seeded sweep of random shapes over every forward entry point, against
+the fp64 oracles at the workloads' bars (2e-2 bf16, 1e-4 fp32; max-abs-
+normwise on o and the final state).
+
+The shapes are drawn once from numpy.random.default_rng(2026): batch, heads,
+a length from 1 to 900 tokens (mostly not a multiple of any chunk), d = 64
+or 128, bf16 or fp32, with or without an initial state, and one of the gate
+laws (default, slow, fast, resets, beta2); eight more cases draw one or two
+sequences of 1,600 to 6,000 tokens, long enough for the split entry points
+to plan segments.  Each case names the entry point
+it runs: the plain chunked pass, the sequence split, the blocked scan, the
+chunked per-dimension gate (plain and split), and gated linear attention."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_deltanet_sequence_amd import inputs
+from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd, gdn_chunk_fwd_split, gdn_chunk_fwd_vecgate,
+                                                 gdn_chunk_fwd_vecgate_split, gdn_scan_fwd, gla_chunk_fwd)
+
+from _helpers import TOL, maxrel, oracle_inputs, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+ENTRIES = ["chunk", "split", "scan", "vecgate", "vecgate_split", "gla"]
+GATES = ["default", "slow", "fast", "resets", "beta2"]
+
+
+def _draw_cases(n=36):
+    rng = np.random.default_rng(2026)
+    cases = []
+    for i in range(n):
+        entry = ENTRIES[i % len(ENTRIES)]
+        dtype = "bf16" if entry == "gla" or rng.random() < 0.7 else "f32"
+        gate = GATES[int(rng.integers(len(GATES)))]
+        if entry.startswith("vecgate") and gate == "beta2":
+            gate = "default"            # the per-dimension gate laws have no beta variant
+        cases.append((entry, int(rng.integers(1, 4)), int(rng.integers(1, 6)), int(rng.integers(1, 901)),
+                      int(rng.choice([64, 128])), dtype, bool(rng.random() < 0.5), gate, 3000 + i))
+    return cases
+
+
+def _draw_long_cases(n=8):
+    """Few, longer sequences, so that the two split entry points plan segments."""
+    rng = np.random.default_rng(2027)
+    cases = []
+    for i in range(n):
+        entry = ("split", "vecgate_split")[i % 2]
+        dtype = "bf16" if entry == "split" or rng.random() < 0.6 else "f32"
+        gate = GATES[int(rng.integers(4))]
+        cases.append((entry, 1, int(rng.integers(1, 3)), int(rng.integers(1600, 6001)),
+                      int(rng.choice([64, 128])), dtype, bool(rng.random() < 0.5), gate, 4000 + i))
+    return cases
+
+
+CASES = _draw_cases() + _draw_long_cases()
+
+
+def _run(entry, xd, av):
+    a = (xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"])
+    if entry == "chunk":
+        return gdn_chunk_fwd(*a, 64)
+    if entry == "split":
+        return gdn_chunk_fwd_split(*a, 64)
+    if entry == "scan":
+        return gdn_scan_fwd(*a)
+    if entry == "gla":
+        return gla_chunk_fwd(*a, 64)
+    va = (xd["q"], xd["k"], xd["v"], av, xd["beta"], xd["s0"])
+    return gdn_chunk_fwd_vecgate(*va) if entry == "vecgate" else gdn_chunk_fwd_vecgate_split(*va)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "%s_B%dH%dT%dd%d_%s_%s_%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], "s0" if c[6] else "z", c[7]))
+def test_random_shape_against_oracle(case):
+    entry, B, H, T, d, dtype, init, gate, seed = case
+    print("case sweep", case, flush=True)
+    vec = entry.startswith("vecgate")
+    x = inputs.make_fwd_inputs(B, H, T, d, dtype, seed=seed, init_state=init,
+                               gate="default" if vec else gate)
+    av = None
+    if vec:
+        x["alpha"] = inputs.make_vec_alpha(B, H, T, d, seed=seed + 1, gate=gate)
+    xd = to_dev(x)
+    av = xd["alpha"] if vec else None
+    o, sT = _run(entry, xd, av)
+    torch.cuda.synchronize()
+    (q, k, v, al, b), s0 = oracle_inputs(x)
+    if entry == "gla":
+        ro, rs = oracle.oracle_gla_fwd(q, k, v, al, b, s0)
+    elif vec:
+        ro, rs = oracle.oracle_fwd_vecgate(q, k, v, al, b, s0)
+    else:
+        ro, rs = oracle.oracle_fwd(q, k, v, al, b, s0)
+    eo, es = maxrel(to_np(o), ro), maxrel(to_np(sT), rs)
+    print("  err o %.3e  err S_T %.3e (tol %.0e)" % (eo, es, TOL[dtype]), flush=True)
+    assert np.all(np.isfinite(to_np(o))) and np.all(np.isfinite(to_np(sT)))
+    assert eo <= TOL[dtype] and es <= TOL[dtype]

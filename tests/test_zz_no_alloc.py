@@ -59,3 +59,43 @@ def test_noalloc_split_matches_the_workspace_split_on_consecutive_calls():
         assert torch.equal(s1, s2), "case %d: final state differs" % i
         del x, o1, s1, o2, s2
         torch.cuda.empty_cache()
+
+
+def test_noalloc_split_replays_from_a_captured_graph():
+    """Callers that cannot allocate include code under graph capture.  The
+    allocation-free split is captured into a HIP graph once and replayed three
+    times; between the replays an eager call with another plan overwrites the
+    shared scratch and the outputs are poisoned.  Every replay must equal the
+    eager call bit for bit (nothing in the scratch has to start at zero)."""
+    dev = torch.device("cuda:0")
+    B, H, T, d = 1, 4, 8192, 64           # the pages' loop case: a 16-segment plan
+    assert gdn_chunk_fwd_split_workspace(B, H, T, d, d, 64, torch.bfloat16) > 0
+    x = _inputs(B, H, T, d, True, 200, dev)
+    a = (x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["s0"], 64)
+    o_ref = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev)
+    s_ref = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    gdn_chunk_fwd_split_noalloc(*a, o=o_ref, final_state=s_ref)   # eager; also looks up the scratch
+    torch.cuda.synchronize()
+    # another plan that writes the same scratch between the replays
+    y = _inputs(1, 2, 16384, 128, True, 201, dev)
+    b = (y["q"], y["k"], y["v"], y["alpha"], y["beta"], y["s0"], 64)
+    assert gdn_chunk_fwd_split_workspace(1, 2, 16384, 128, 128, 64, torch.bfloat16) > 0
+    o_y = torch.empty((1, 2, 16384, 128), dtype=torch.bfloat16, device=dev)
+    s_y = torch.empty((1, 2, 128, 128), dtype=torch.float32, device=dev)
+
+    o = torch.empty_like(o_ref)
+    s = torch.empty_like(s_ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gdn_chunk_fwd_split_noalloc(*a, o=o, final_state=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        print("graph replay", rep, flush=True)
+        o.fill_(float("nan"))
+        s.fill_(float("nan"))
+        gdn_chunk_fwd_split_noalloc(*b, o=o_y, final_state=s_y)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), "replay %d: o differs" % rep
+        assert torch.equal(s, s_ref), "replay %d: final state differs" % rep
