@@ -131,7 +131,7 @@ def _check_fwd_args(q, k, v, alpha, beta, initial_state, alpha_per_dim=False):
 
 def gdn_chunk_fwd(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 64, *,
                   o=None, final_state=None, output_final_state: bool = True, stream=None):
-    """Chunked forward pass.  q, k [B,H,T,dk], v [B,H,T,dv] (bf16 or fp32);
+    """Chunked forward pass (chunk_size 64, or 32).  q, k [B,H,T,dk], v [B,H,T,dv] (bf16 or fp32);
     alpha, beta [B,H,T] fp32; initial_state [B,H,dv,dk] fp32 or None.
 
     Returns (o [B,H,T,dv] in the input dtype, final_state [B,H,dv,dk] fp32 or

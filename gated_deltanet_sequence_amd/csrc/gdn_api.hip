@@ -177,7 +177,7 @@ const char* gdn_strerror(int code) {
   switch (code) {
     case GDN_OK: return "success";
     case GDN_ERR_INVALID_ARG: return "invalid argument (NULL pointer, negative size, bad dtype or overlapping output)";
-    case GDN_ERR_UNSUPPORTED: return "unsupported shape or chunk size (dk == dv in {64,128}, chunk_size 64)";
+    case GDN_ERR_UNSUPPORTED: return "unsupported shape or chunk size (dk == dv in {64,128}; chunk_size 64, or 32 where documented)";
     case GDN_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
     case GDN_ERR_HIP: return "HIP runtime error while launching";
     default: return "unknown gdn error code";
@@ -284,13 +284,14 @@ int noalloc_scratch(void** out) {
 
 namespace {
 // The 32-token chunk kernel of chunk_vec.hpp: the per-dimension gate (VG),
-// and the scalar gate for fp32 inputs.  vec_dispatch calls f(T{}, DK) with
-// the element type and key width of the instantiation that serves dtype, dk.
+// and the scalar gate for fp32 inputs and for a requested chunk size of 32.
+// vec_dispatch calls f(T{}, DK) with the element type and key width of the
+// instantiation that serves dtype, dk.
 template <bool VG, class F>
 int vec_dispatch(gdn_dtype dtype, int64_t dk, F&& f) {
   using D64 = std::integral_constant<int, 64>;
   using D128 = std::integral_constant<int, 128>;
-  if (!VG || dtype == GDN_F32) return dk == 128 ? f(float{}, D128{}) : f(float{}, D64{});
+  if (dtype == GDN_F32) return dk == 128 ? f(float{}, D128{}) : f(float{}, D64{});
   return dk == 128 ? f(bf16_t{}, D128{}) : f(bf16_t{}, D64{});
 }
 
@@ -392,19 +393,22 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
                   const float* beta, const float* initial_state, void* o, float* final_state,
                   int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk_size,
                   gdn_dtype dtype, void* hip_stream) {
+  // chunk sizes: 64, and 32 (the 32-token kernel)
+  const bool c32 = chunk_size == gdn::vec::C;
   const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
-                           chunk_size, dtype);
+                           c32 ? 64 : chunk_size, dtype);
   if (rc != GDN_OK) return rc;
-  if (dtype == GDN_BF16 && !pipe_len_ok(T, dk, dv)) return GDN_ERR_UNSUPPORTED;
+  if (dtype == GDN_BF16 && !c32 && !pipe_len_ok(T, dk, dv)) return GDN_ERR_UNSUPPORTED;
   const int64_t nchain = B * H;
   if (nchain == 0) return GDN_OK;
   if (T == 0 && !final_state) return GDN_OK;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  if (dtype == GDN_BF16)
+  if (dtype == GDN_BF16 && !c32)
     return launch_chunk_pipe(q, k, v, alpha, beta, initial_state, o, final_state, seq_map(nchain, T),
                              dk, dv, stream);
-  // fp32: chunks of 32 tokens (64-token fp32 buffers exceed the LDS at
-  // d = 128); the result does not depend on the chunk size beyond rounding
+  // fp32 (at either chunk size: 64-token fp32 buffers exceed the LDS at
+  // d = 128, and the result does not depend on the chunk size beyond
+  // rounding) and chunk size 32: chunks of 32 tokens
   return launch_vec<false>(q, k, v, alpha, beta, initial_state, o, final_state, seq_map(nchain, T), dk, dv,
                            dtype, stream);
 }

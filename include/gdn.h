@@ -77,12 +77,14 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *   final_state    [B,H,dv,dk] fp32    OUT: S_T, or NULL to skip it.
  *                                      May alias initial_state (each workgroup
  *                                      reads its part of S_0 before writing).
- *   chunk_size     tokens per chunk; the library supports 64.  T need not be a
- *                  multiple: the missing tokens of the last chunk act as
- *                  identity maps (alpha = 1, beta = 0) and produce no output.
- *                  (fp32 inputs are evaluated 32 tokens at a time: 64-token
- *                  fp32 buffers exceed the LDS at d = 128.  The result does
- *                  not depend on the chunk size beyond rounding.)
+ *   chunk_size     tokens per chunk: 64 (the pipelined bf16 kernel; the fast
+ *                  path), or 32 (the 32-token kernel, bf16 or fp32).  T need
+ *                  not be a multiple: the missing tokens of the last chunk act
+ *                  as identity maps (alpha = 1, beta = 0) and produce no
+ *                  output.  (fp32 inputs are evaluated 32 tokens at a time for
+ *                  either size: 64-token fp32 buffers exceed the LDS at
+ *                  d = 128.  The result does not depend on the chunk size
+ *                  beyond rounding.)  Other sizes return GDN_ERR_UNSUPPORTED.
  *   dk, dv         64 or 128, dk == dv, for bf16 and fp32.
  *   T              >= 0.  T == 0 writes final_state = initial_state (or zeros).
  *                  For bf16, one sequence's q, k or v (T * d * 2 bytes) must be

@@ -64,7 +64,7 @@ def step(lib, q=A, k=A + MB, v=A + 2 * MB, alpha=A + 3 * MB, beta=A + 4 * MB,
     (dict(beta=None), 1), (dict(o=None), 1),
     (dict(B=-1), 1), (dict(H=-2), 1), (dict(T=-1), 1), (dict(C=0), 1), (dict(dtype=7), 1),
     (dict(dk=32, dv=32), 2), (dict(dk=64, dv=128), 2), (dict(dk=256, dv=256), 2),
-    (dict(C=32), 2), (dict(C=128), 2),
+    (dict(C=16), 2), (dict(C=48), 2), (dict(C=128), 2),
     (dict(q=A + 8), 3), (dict(v=A + 128 * MB + 2), 3), (dict(o=A + 256 * MB + 4), 3),
     (dict(s0=A + 300 * MB + 8), 3), (dict(sT=A + 400 * MB + 12), 3),
     (dict(o=A + 112), 1),                  # output overlaps q

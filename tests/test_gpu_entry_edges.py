@@ -1,5 +1,5 @@
 """Edge cases of the sequence-split, scan, vector-gate (scan and chunked),
-GLA and fp32 chunked entry points on the GPU: zero tokens (the final state is the initial one, or zero), no
+GLA, fp32 chunked and 32-token chunked entry points on the GPU: zero tokens (the final state is the initial one, or zero), no
 sequences, fewer tokens than one chunk or block, and a final state that
 aliases the initial state.  Results are compared with the fp64 oracles or
 with exact expectations."""
@@ -29,6 +29,8 @@ ENTRIES = {
     "gla": lambda xd: gla_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"], 64),
     "chunk_vecgate": lambda xd: gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], _vec(xd["alpha"], xd["q"].shape[3]),
                                                       xd["beta"], xd["s0"]),
+    # chunk_size 32: the 32-token kernel on the bf16 inputs
+    "c32": lambda xd: gdn_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"], 32),
     # the same bf16-rounded inputs as fp32: the fp32 chunked path
     "fp32": lambda xd: gdn_chunk_fwd(xd["q"].float(), xd["k"].float(), xd["v"].float(), xd["alpha"], xd["beta"],
                                      xd["s0"], 64),
@@ -56,7 +58,7 @@ def test_no_sequences(name):
     assert o.numel() == 0 and sT.numel() == 0
 
 
-@pytest.mark.parametrize("name", ["split", "scan", "scan_vecgate", "chunk_vecgate", "fp32"])
+@pytest.mark.parametrize("name", ["split", "scan", "scan_vecgate", "chunk_vecgate", "c32", "fp32"])
 @pytest.mark.parametrize("T", [1, 17, 31, 33, 63])
 def test_short_sequences_match_oracle(name, T):
     x = inputs.make_fwd_inputs(1, 2, T, 64, "bf16", seed=63 + T, init_state=True)
@@ -68,7 +70,7 @@ def test_short_sequences_match_oracle(name, T):
     assert maxrel(to_np(o), ro) <= tol and maxrel(to_np(sT), rs) <= tol
 
 
-@pytest.mark.parametrize("name", ["scan", "gla", "chunk_vecgate", "fp32"])
+@pytest.mark.parametrize("name", ["scan", "gla", "chunk_vecgate", "c32", "fp32"])
 def test_final_state_aliases_initial_state(name):
     x = inputs.make_fwd_inputs(1, 2, 700, 128, "bf16", seed=64, init_state=True)
     xd = to_dev(x)
@@ -82,6 +84,8 @@ def test_final_state_aliases_initial_state(name):
     elif name == "chunk_vecgate":
         o, s2 = gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], _vec(xd["alpha"], 128), xd["beta"], s,
                                       final_state=s)
+    elif name == "c32":
+        o, s2 = gdn_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], s, 32, final_state=s)
     else:
         o, s2 = gdn_chunk_fwd(xd["q"].float(), xd["k"].float(), xd["v"].float(), xd["alpha"], xd["beta"], s, 64,
                               final_state=s)

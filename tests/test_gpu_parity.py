@@ -33,9 +33,9 @@ def run_gpu(x, chunk=64, **kw):
     return o, sT
 
 
-def check_against_oracle(x, dtype, chains=None, label=""):
-    _say("case", label, "shape", tuple(x["q"].shape), "dtype", dtype)
-    o, sT = run_gpu(x)
+def check_against_oracle(x, dtype, chains=None, label="", chunk=64):
+    _say("case", label, "shape", tuple(x["q"].shape), "dtype", dtype, "chunk", chunk)
+    o, sT = run_gpu(x, chunk)
     (q, k, v, a, b), s0 = oracle_inputs(x, chains)
     ro, rs = oracle.oracle_fwd(q, k, v, a, b, s0)
     go, gs = to_np(o), to_np(sT)
@@ -93,6 +93,48 @@ def test_chunk_fwd_small(case):
     B, H, T, d, dtype, init, gate = case
     x = inputs.make_fwd_inputs(B, H, T, d, dtype, seed=100 + T + d, init_state=init, gate=gate)
     check_against_oracle(x, dtype, label="small")
+
+
+# chunk_size 32 (the 32-token kernel, both dtypes): tails around the chunk
+# edge, several chunks, the XCD-grouped mapping, and every gate law
+C32_CASES = [
+    (1, 1, 1, 64, "bf16", True, "default"),
+    (1, 2, 31, 128, "bf16", False, "default"),
+    (2, 1, 33, 64, "bf16", True, "default"),
+    (2, 2, 300, 128, "bf16", True, "default"),
+    (8, 1, 100, 128, "bf16", True, "default"),
+    (1, 2, 1024, 128, "bf16", True, "slow"),
+    (1, 2, 300, 64, "bf16", True, "fast"),
+    (1, 2, 500, 128, "bf16", True, "resets"),
+    (1, 1, 400, 128, "bf16", True, "beta2"),
+    (1, 2, 95, 64, "f32", True, "default"),
+    (2, 2, 200, 128, "f32", True, "resets"),
+]
+
+
+@pytest.mark.parametrize("case", C32_CASES, ids=lambda c: "B%dH%dT%dd%d_%s_%s_%s" % (
+    c[0], c[1], c[2], c[3], c[4], "s0" if c[5] else "z", c[6]))
+def test_chunk_fwd_c32(case):
+    B, H, T, d, dtype, init, gate = case
+    x = inputs.make_fwd_inputs(B, H, T, d, dtype, seed=300 + T + d, init_state=init, gate=gate)
+    check_against_oracle(x, dtype, label="c32", chunk=32)
+
+
+def test_chunk_sizes_agree():
+    """The chunk size only reorders the rounding: 32- and 64-token chunks give
+    the same result to the dtype's tolerance, and the fp32 path (evaluated 32
+    tokens at a time for either size) is bit-identical across the two."""
+    for dtype in ("bf16", "f32"):
+        x = inputs.make_fwd_inputs(2, 2, 333, 128, dtype, seed=77, init_state=True)
+        o64, s64 = run_gpu(x, 64)
+        o32, s32 = run_gpu(x, 32)
+        a, b = to_np(o64), to_np(o32)
+        eo = maxrel(b, a)
+        es = maxrel(to_np(s32), to_np(s64))
+        _say("chunk 32 vs 64", dtype, "err o %.3e  err S_T %.3e" % (eo, es))
+        assert eo <= TOL[dtype] and es <= TOL[dtype]
+        if dtype == "f32":
+            assert torch.equal(o64, o32) and torch.equal(s64, s32)
 
 
 # The bf16 kernel keeps K of four consecutive chunks in LDS (loaded three
@@ -255,7 +297,7 @@ def test_binding_rejects_bad_inputs():
     with pytest.raises(ValueError):
         gdn_chunk_fwd(x["q"].transpose(2, 3), x["k"], x["v"], x["alpha"], x["beta"])
     with pytest.raises(GDNError) as ei:
-        gdn_chunk_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], None, 32)
+        gdn_chunk_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], None, 48)
     assert ei.value.code == 2
     with pytest.raises(ValueError):
         gdn_chunk_fwd(x["q"].cpu(), x["k"], x["v"], x["alpha"], x["beta"])

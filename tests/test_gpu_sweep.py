@@ -7,7 +7,8 @@ a length from 1 to 900 tokens (mostly not a multiple of any chunk), d = 64
 or 128, bf16 or fp32, with or without an initial state, and one of the gate
 laws (default, slow, fast, resets, beta2); eight more cases draw one or two
 sequences of 1,600 to 6,000 tokens, long enough for the split entry points
-to plan segments.  Each case names the entry point
+to plan segments, and six more run the plain chunked pass at chunk_size 32
+(numpy.random.default_rng(2028)).  Each case names the entry point
 it runs: the plain chunked pass, the sequence split, the blocked scan, the
 chunked per-dimension gate (plain and split), and gated linear attention."""
 import numpy as np
@@ -54,13 +55,23 @@ def _draw_long_cases(n=8):
     return cases
 
 
-CASES = _draw_cases() + _draw_long_cases()
+def _draw_c32_cases(n=6):
+    """The plain chunked pass at chunk_size 32."""
+    rng = np.random.default_rng(2028)
+    return [("chunk32", int(rng.integers(1, 4)), int(rng.integers(1, 6)), int(rng.integers(1, 901)),
+             int(rng.choice([64, 128])), "bf16" if rng.random() < 0.7 else "f32", bool(rng.random() < 0.5),
+             GATES[int(rng.integers(len(GATES)))], 5000 + i) for i in range(n)]
+
+
+CASES = _draw_cases() + _draw_long_cases() + _draw_c32_cases()
 
 
 def _run(entry, xd, av):
     a = (xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"])
     if entry == "chunk":
         return gdn_chunk_fwd(*a, 64)
+    if entry == "chunk32":
+        return gdn_chunk_fwd(*a, 32)
     if entry == "split":
         return gdn_chunk_fwd_split(*a, 64)
     if entry == "scan":
