@@ -97,11 +97,9 @@ def kernel_source_hash(sources=None, read=None):
     return h.hexdigest()[:16]
 
 
-def read_traffic(path=None, sources=None):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary (by
-    default the main kernel's), or None when it is missing or was taken on
-    different kernel sources."""
-    path = path or TRAFFIC_FILE
+def read_summary(path, key, sources=None):
+    """A value from a committed rocprofv3 --pmc summary, or None when the file
+    is missing or was taken on different kernel sources."""
     if not os.path.exists(path):
         return None
     vals = {}
@@ -109,13 +107,20 @@ def read_traffic(path=None, sources=None):
         for line in f:
             if "=" in line and not line.lstrip().startswith("#"):
                 k, v = line.split("=", 1)
-                vals[k.strip()] = v.strip()
+                vals[k.strip()] = v.split("(")[0].strip()
     if vals.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     try:
-        return int(float(vals["hbm_bytes_per_launch"]))
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
+
+
+def read_traffic(path=None, sources=None):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary (by
+    default the main kernel's), or None (see read_summary)."""
+    v = read_summary(path or TRAFFIC_FILE, "hbm_bytes_per_launch", sources)
+    return None if v is None else int(v)
 
 
 def main_inputs(torch, dev):
@@ -561,6 +566,67 @@ def summarize_pmc(fetch_dir, write_dir, which="main"):
     print("\n".join(lines))
 
 
+# Instruction counters of the main chunk kernel, one rocprofv3 --pmc run per
+# group (each group within one pass's hardware counter limits).
+ACTIVITY_GROUPS = (("MfmaUtil", "MfmaFlopsBF16"),
+                   ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"))
+ACTIVITY_FILE = os.path.join(ROOT, "profiles", "activity_chunk_fwd_main.txt")
+
+
+def summarize_activity(dirs):
+    """Write the MFMA and LDS activity summary of the main chunk kernel from
+    rocprofv3 --pmc runs of `bench.py --pmc-pass main`, one per group of
+    ACTIVITY_GROUPS: each counter averaged over the last launches of the pass."""
+    import csv
+    vals = {}
+    for d in dirs:
+        rows = []
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path, newline="") as fh:
+                for r in csv.DictReader(fh):
+                    if "gdn::" in r["Kernel_Name"] and "chunk_fwd" in r["Kernel_Name"]:
+                        rows.append((int(r["Dispatch_Id"]), r["Counter_Name"], float(r["Counter_Value"])))
+        by = {}
+        for disp, name, v in rows:
+            by.setdefault(name, {}).setdefault(disp, 0.0)
+            by[name][disp] += v
+        for name, per in by.items():
+            last = [per[k] for k in sorted(per)][-PMC_LAUNCHES:]
+            vals[name] = sum(last) / len(last)
+    missing = [c for g in ACTIVITY_GROUPS for c in g if c not in vals]
+    if missing:
+        raise SystemExit("no rows for %s in %s" % (", ".join(missing), " ".join(dirs)))
+    B, H, T, d, C = MAIN["B"], MAIN["H"], MAIN["T"], MAIN["d"], MAIN["C"]
+    alg_f = alg_flops_main(B, H, T, d, C)
+    lines = ["# MFMA and LDS activity of chunk_fwd_pipe_kernel, main workload (B=4,H=16,T=8192,d=128,C=64, bf16)",
+             "# from rocprofv3 --pmc runs of bench.py --pmc-pass main (the kernel for %.0f ms to settle" % SETTLE_MS,
+             "# the clocks, then %d more launches; each figure is the mean over those last launches):" % PMC_LAUNCHES]
+    for g, d_ in zip(ACTIVITY_GROUPS, dirs):
+        lines.append("#   rocprofv3 --pmc %s --output-format csv -d %s -- python3 bench.py --pmc-pass main"
+                     % (" ".join(g), d_))
+    lines.append("#   python3 bench.py --summarize-activity %s" % " ".join(dirs))
+    for g in ACTIVITY_GROUPS:
+        for c in g:
+            lines.append("%s = %.1f" % (c, vals[c]))
+    lines += [
+        "# derived",
+        "mfma_bf16_flops_per_launch = %d" % vals["MfmaFlopsBF16"],
+        "algorithmic_flops_per_launch = %d  (full C x C tiles)" % alg_f,
+        "mfma_flops_over_algorithmic = %.3f" % (vals["MfmaFlopsBF16"] / alg_f),
+        "mfma_busy_percent_of_simd_cycles = %.1f  (MfmaUtil)" % vals["MfmaUtil"],
+        "flops_per_mfma_instruction = %.0f" % (vals["MfmaFlopsBF16"] / vals["SQ_INSTS_MFMA"]),
+        "valu_instructions_per_mfma = %.2f  (SQ_INSTS_VALU counts MFMAs too)"
+        % (vals["SQ_INSTS_VALU"] / vals["SQ_INSTS_MFMA"]),
+        "lds_bank_conflict_cycles_over_lds_active = %.3f" % (vals["SQ_LDS_BANK_CONFLICT"] / vals["SQ_LDS_IDX_ACTIVE"]),
+        "# kernel_source_hash: sha256 (first 16 hex digits) of the code (comments and whitespace runs removed) of %s"
+        % ", ".join(KERNEL_SOURCES),
+        "kernel_source_hash = %s" % kernel_source_hash(KERNEL_SOURCES),
+    ]
+    with open(ACTIVITY_FILE, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_trace(trace_dir, out_name, command, note="", tail=100):
     """Write profiles/OUT_NAME.txt from a rocprofv3 --kernel-trace run: for every
     kernel of the library and launch shape, the number of launches and the
@@ -642,6 +708,8 @@ def main():
                          "runs" % PMC_LAUNCHES)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pmc-kernel", default="main", choices=sorted(PMC_TARGETS))
+    ap.add_argument("--summarize-activity", nargs=len(ACTIVITY_GROUPS), metavar="PMC_DIR",
+                    help="write the MFMA / LDS activity summary from one --pmc run per counter group")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_NAME"),
                     help="write profiles/OUT_NAME.txt from a rocprofv3 --kernel-trace run")
     ap.add_argument("--trace-cmd", default="", help="the profiling command, for the summary header")
@@ -653,6 +721,9 @@ def main():
 
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, which=args.pmc_kernel)
+        return
+    if args.summarize_activity:
+        summarize_activity(args.summarize_activity)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, command=args.trace_cmd, note=args.trace_note,
@@ -721,7 +792,11 @@ def main():
                      "launch_ms_median": pct(0.5), "launch_ms_p10": pct(0.1),
                      "launch_ms_p90": pct(0.9), "timed_launches": len(kms),
                      "mfma_achieved_TFLOPs": alg_f / (avg_k * 1e-3) / 1e12,
-                     "mfma_frac": alg_f / (avg_k * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+                     "mfma_frac": alg_f / (avg_k * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                     # rocprofv3 counters (profiles/activity_chunk_fwd_main.txt; None once the
+                     # kernel sources differ from those the counters were taken on)
+                     "mfma_busy_pct_counter": read_summary(ACTIVITY_FILE, "mfma_busy_percent_of_simd_cycles"),
+                     "mfma_bf16_flops_counter": read_summary(ACTIVITY_FILE, "mfma_bf16_flops_per_launch")},
         "token_heads_per_s": B * H * T / (ms_per_step * 1e-3),
     }
     if not args.no_decode:
