@@ -348,7 +348,7 @@ struct StateRegs {
   f32x4 S[8];        // state tiles: value row lr, internal keys 16 jb + 4 lg + e
   f32x4 Oprev[4];    // Q S^T part of the previous chunk's output (per 16-token block)
   bf16x8_t Uprev[2]; // U of the previous chunk as kappa operands
-  bf16x8_t Kpre[2][4];  // key fragments of the next chunk's first two 16-token
+  bf16x8_t Kpre[3][4];  // key fragments of the next chunk's first three 16-token
                         // blocks, read at the end of a period (delta rule)
 };
 
@@ -377,9 +377,11 @@ __device__ __forceinline__ void read_p(const Smem& sm, const StateAddr& A, int64
     for (int pp = 0; pp <= rb / 2; ++pp) pf[rb][pp] = as_op(ld3<uint4>(pb[pp], rb * 2048));
 }
 
-// PRE: the key fragments of blocks 0 and 1 of chunk c are in R.Kpre (read at
-// the end of the previous period, so that their LDS latency falls in the
-// barrier wait instead of delaying the first products of this period).
+// PRE: the key fragments of blocks 0, 1 and 2 of chunk c are in R.Kpre (read
+// at the end of the previous period, so that their LDS latency falls in the
+// barrier wait instead of delaying the first products of this period: at the
+// start of a period every wave issues its LDS reads at once, and the state
+// waves' reads queue behind the others').
 // OUT = false: no output (the first launch of the sequence split, which
 // needs only the state): no Q S^T, no P U, no stores.
 template <bool FINISH_, bool CHAIN, bool GLA, bool PRE = false, bool OUT = true>
@@ -426,7 +428,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     if (!OUT && n >= 4) return;  // no output: Q is not needed
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp)
-      fr[n % 3][pp] = PRE && n < 2 ? R.Kpre[n][pp]
+      fr[n % 3][pp] = PRE && n < 3 ? R.Kpre[n][pp]
                                    : as_op(n < 4 ? ld3<uint4>(kf_b[pp], n * 4096) : ld3<uint4>(qf_b[pp], (n - 4) * 4096));
   };
   // V and the gates of Y, read during the products of blocks 1..3
@@ -566,8 +568,8 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   // ---- S^T += K^T Uh with K^T from transposed reads: supplier lane (a, r) of
   // a 16-lane group addresses 4 key columns of token 4 lg + r.  The operands
   // of tile jb + 3 are read while the products of tile jb run; in the last
-  // tiles (delta rule) the key fragments of the next chunk's blocks 0 and 1
-  // are read instead.  The next chunk's keys are in LDS already (loaded three
+  // tiles (delta rule) the key fragments of the next chunk's blocks 0, 1 and
+  // 2 are read instead.  The next chunk's keys are in LDS already (loaded three
   // chunks ahead); after the last chunk the reads fetch unused values.
   lptr kn_b[4];
   if constexpr (!GLA) {
@@ -577,9 +579,9 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
 #pragma unroll
   for (int jb = 0; jb < 8; ++jb) {
     if (jb < 5) read_kt(jb + 3, kt[(jb + 3) % 4]);
-    if (!GLA && (jb == 5 || jb == 6)) {
+    if (!GLA && jb >= 4 && jb <= 6) {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) R.Kpre[jb - 5][pp] = as_op(ld3<uint4>(kn_b[pp], (jb - 5) * 4096));
+      for (int pp = 0; pp < 4; ++pp) R.Kpre[jb - 4][pp] = as_op(ld3<uint4>(kn_b[pp], (jb - 4) * 4096));
     }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc = R.S[jb];
@@ -1174,6 +1176,10 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     const StateAddr A = state_addr(lane, 0, DV);
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
+      // With the delta rule the P wave has slack: it starts its LDS reads
+      // about 500 cycles into the period, behind those of the state waves,
+      // whose chain is longer (without it, P is as long as the state waves).
+      if constexpr (!GLA) __builtin_amdgcn_s_sleep(8);
       if (OUT && p >= 0 && p < nch) build_p<GLA>(sm, A, p, lane);
       lds_barrier();
     }
