@@ -40,8 +40,9 @@
 // input type in LDS feeds the products; four waves in seven barrier-separated
 // steps per chunk.  The chunk is 32 tokens: the fp32 table of G (32 x d_k)
 // and the four operand copies of q and k it needs per chunk then fit in LDS
-// next to the chunk matrices (bf16: 53 KB at d_k = 64, 85 KB at 128; fp32:
-// 142 KB at d_k = 128).
+// next to the chunk matrices (bf16: 48.8 KB at d_k = 64, 80.8 KB at 128;
+// fp32: 137 KB at d_k = 128).  Under 80 KB, two workgroups share a CU (the
+// bf16 instances ask the compiler for two waves per SIMD).
 //
 // With a scalar gate (VG = false: alpha is [.., T] and every key column
 // decays alike) the same algebra holds with G_r[j] = g_r for all j; that
@@ -78,6 +79,7 @@ struct __attribute__((aligned(16))) Smem {
   static constexpr int PAD = 16 / (int)sizeof(T);  // 16-byte row padding
   static constexpr int LDK = DK + PAD;  // rows of d_k
   static constexpr int LDC = C + PAD;   // rows of C
+  static constexpr int VEC16 = 16 / (int)sizeof(T);
   T Qs[C * LDK];    // 2^G o q, [token][dk]
   T Kr[C * LDK];    // 2^G o k
   T Kh[C * LDK];    // 2^-G o k (Gram columns); raw k in chunks on the exact path
@@ -85,15 +87,18 @@ struct __attribute__((aligned(16))) Smem {
   T Kbt[DK * LDC];  // (2^(G_C - G) o k)^T, [dk][token]
   T V[C * DVS];     // value slice, [token][dvs]
   T S[DVS * LDK];   // operand copy of the state slice, [dv][dk]
-  T Yt[DVS * LDC];  // right-hand side of the triangular system, [dv][token]
+  union {
+    T Yt[DVS * LDC];  // right-hand side of the triangular system, [dv][token]
+    float tot[NT / DK][DK];  // gate scan: log2 sums of each token group per column
+                             // (dead by the time Yt is written, and Yt by the next scan)
+  };
   T Ut[DVS * LDC];  // U^T
   T Ti[C * LDC];    // (I + L)^-1, [token][token]
-  T Tt[C * LDC];    // its transpose while it is built
   T Lb[C * LDC];    // L, operand copy
   T P[C * LDC];     // lower(A_qk), [r][s]
-  T Mt[16 * LDC];   // partial product of the blocked inverse
+  T Mt[sizeof(T) == 2 ? VEC16 : 16 * LDC];  // partial product of the blocked inverse (fp32;
+                                            // bf16 keeps it in registers)
   float Ld[2][16][LDR];  // fp32 diagonal 16x16 blocks of L (rows 16-byte aligned)
-  float tot[NT / DK][DK];  // gate scan: log2 sums of each token group per column
   float G[C * (DK + 4)]; // log2-prefix of alpha per key column, [token][dk], rows padded by 16 bytes
   float beta[C];
   float Ec[DK];          // 2^(G_C) per key column
@@ -118,7 +123,7 @@ __device__ __forceinline__ void store_vec(float* p, const float (&x)[4]) {
 // per-token maps stay affine with a per-dimension gate, so the split and its
 // combine step are the same.
 template <class T, int DK, bool VG>
-__global__ __launch_bounds__(NT) void chunk_vec_kernel(
+__global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
     const float* initial_state, T* __restrict__ o, float* final_state,
@@ -205,7 +210,6 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
   // read as zero.
   for (int e = tid; e < C * LDC; e += NT) {
     sm.Ti[e] = Elem<T>::from_f32(0.f);
-    sm.Tt[e] = Elem<T>::from_f32(0.f);
     sm.P[e] = Elem<T>::from_f32(0.f);
     sm.Lb[e] = Elem<T>::from_f32(0.f);
   }
@@ -457,18 +461,23 @@ __global__ __launch_bounds__(NT) void chunk_vec_kernel(
         band(3, lq[1]);
 #pragma unroll
         for (int r = 0; r < 16; ++r) sm.Ti[(16 * b + r) * LDC + 16 * b + c] = Elem<T>::from_f32(x[r]);
-        // column c of the block is row 16 b + c of Ti^T: 16 consecutive elements
+        // column c of Ti[0][0] is row c of its transpose: 16 consecutive
+        // elements, written over the diagonal block L[0][0] of the operand
+        // copy of L, which only the forward substitution (from the fp32
+        // copy) needed
+        if (b == 0) {
 #pragma unroll
-        for (int h = 0; h < 16 / VEC; ++h) {
-          float xv[VEC];
+          for (int h = 0; h < 16 / VEC; ++h) {
+            float xv[VEC];
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) xv[e] = x[VEC * h + e];
-          store_vec(&sm.Tt[(16 * b + c) * LDC + 16 * b + VEC * h], xv);
+            for (int e = 0; e < VEC; ++e) xv[e] = x[VEC * h + e];
+            store_vec(&sm.Lb[c * LDC + VEC * h], xv);
+          }
         }
       }
       wave_lds_sync();
       // ... then the off-diagonal block Ti[1][0] = -Ti[1][1] L[1][0] Ti[0][0].
-      const f32x4 m = Mma<T>::template run<16>(zero4(), &sm.Lb[16 * LDC], LDC, &sm.Tt[0], LDC, lane);
+      const f32x4 m = Mma<T>::template run<16>(zero4(), &sm.Lb[16 * LDC], LDC, &sm.Lb[0], LDC, lane);
       f32x4 acc;
       if constexpr (sizeof(T) == 2) {
         // M = L[1][0] Ti[0][0] is in the accumulator layout, which is the B
