@@ -100,9 +100,10 @@ T_MAX = (2 ** 31 - 1) // (128 * 2)  # longest bf16 sequence at d = 128: q, k, v 
 def test_maximum_sequence_length_tail_matches_oracle():
     """The longest sequence the bf16 path takes at d = 128 (8,388,607 tokens;
     buffer offsets up to 2^31 - 1 bytes), on the plain and the sequence-split
-    entry points.  alpha = 0 at token t0 wipes the state (up to the 2^-200
-    clamp of log2 alpha), so the outputs from t0 on and the final state equal
-    the oracle's run over the tokens from t0 on, from a zero state."""
+    entry points and at chunk_size 32 (the 32-token kernel).  alpha = 0 at
+    token t0 wipes the state (up to the 2^-200 clamp of log2 alpha), so the
+    outputs from t0 on and the final state equal the oracle's run over the
+    tokens from t0 on, from a zero state."""
     from gated_deltanet_sequence_amd.binding import gdn_chunk_fwd, gdn_chunk_fwd_split
     T, d = T_MAX, 128
     print("case max length T", T, "d", d, flush=True)
@@ -114,7 +115,9 @@ def test_maximum_sequence_length_tail_matches_oracle():
     ro, rs = oracle.oracle_fwd(q, k, v, a, b, None)
     for name, run in (("plain", lambda: gdn_chunk_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], None, 64)),
                       ("split", lambda: gdn_chunk_fwd_split(x["q"], x["k"], x["v"], x["alpha"], x["beta"],
-                                                            None, 64))):
+                                                            None, 64)),
+                      ("chunk_size 32", lambda: gdn_chunk_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                                                              None, 32))):
         print("  entry", name, flush=True)
         o, sT = run()
         torch.cuda.synchronize()
