@@ -63,6 +63,10 @@ def load_library(path: str | None = None):
     lib.gdn_chunk_fwd_vecgate_split.restype = i32
     lib.gdn_chunk_fwd_vecgate_split_workspace.argtypes = [i64, i64, i64, i64, i64, i64, i32]
     lib.gdn_chunk_fwd_vecgate_split_workspace.restype = ctypes.c_size_t
+    lib.gdn_chunk_fwd_vecgate_2pass.argtypes = lib.gdn_chunk_fwd_vecgate_split.argtypes
+    lib.gdn_chunk_fwd_vecgate_2pass.restype = i32
+    lib.gdn_chunk_fwd_vecgate_2pass_workspace.argtypes = [i64, i64, i64, i64, i64, i64, i32]
+    lib.gdn_chunk_fwd_vecgate_2pass_workspace.restype = ctypes.c_size_t
     lib.gdn_scan_fwd_workspace.argtypes = [i64, i64, i64, i64, i64, i32]
     lib.gdn_scan_fwd_workspace.restype = ctypes.c_size_t
     lib.gdn_chunk_fwd_split.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
@@ -232,6 +236,42 @@ def gdn_chunk_fwd_vecgate(q, k, v, alpha, beta, initial_state=None, chunk_size: 
                                    int(chunk_size), _DTYPES[q.dtype], _stream_ptr(stream, q.device))
     if rc != GDN_OK:
         raise GDNError(rc, "gdn_chunk_fwd_vecgate")
+    return o, final_state
+
+
+def gdn_chunk_fwd_vecgate_2pass_workspace(B, H, T, dk, dv, chunk_size: int = VECGATE_CHUNK,
+                                          dtype=torch.bfloat16) -> int:
+    """Bytes of workspace with which gdn_chunk_fwd_vecgate_2pass uses its largest tile."""
+    return int(load_library().gdn_chunk_fwd_vecgate_2pass_workspace(B, H, T, dk, dv, int(chunk_size),
+                                                                    _DTYPES[dtype]))
+
+
+def gdn_chunk_fwd_vecgate_2pass(q, k, v, alpha, beta, initial_state=None, chunk_size: int = VECGATE_CHUNK, *,
+                                o=None, final_state=None, output_final_state: bool = True,
+                                workspace=None, stream=None):
+    """gdn_chunk_fwd_vecgate in two passes (the state-independent chunk work
+    once per chunk, into workspace records; then the state products per value
+    slice).  Same arguments and result; the workspace (a uint8 GPU tensor) is
+    allocated here when not given."""
+    B, H, T, dk, dv = _check_fwd_args(q, k, v, alpha, beta, initial_state, alpha_per_dim=True)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = gdn_chunk_fwd_vecgate_2pass_workspace(B, H, T, dk, dv, chunk_size, q.dtype)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    lib = load_library()
+    rc = lib.gdn_chunk_fwd_vecgate_2pass(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                         _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                                         _dev_ptr(initial_state, "initial_state"), _dev_ptr(o, "o"),
+                                         _dev_ptr(final_state, "final_state"), B, H, T, dk, dv,
+                                         int(chunk_size), _DTYPES[q.dtype],
+                                         _dev_ptr(workspace, "workspace"), ws_bytes,
+                                         _stream_ptr(stream, q.device))
+    if rc != GDN_OK:
+        raise GDNError(rc, "gdn_chunk_fwd_vecgate_2pass")
     return o, final_state
 
 

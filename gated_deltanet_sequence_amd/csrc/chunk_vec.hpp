@@ -114,6 +114,30 @@ __device__ __forceinline__ void store_vec(float* p, const float (&x)[4]) {
   *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
+// Two-pass evaluation (gdn_chunk_fwd_vecgate_2pass).  The S-independent part
+// of a chunk (gate scan, scaled operands, L, (I+L)^-1, P) does not depend on
+// the value slice, yet the single-pass kernel repeats it in every slice's
+// workgroup.  The first pass (the PREP instance of chunk_vec_kernel, one
+// workgroup per chunk) computes it once per chunk and writes the buffers the
+// state products need, verbatim in their LDS layout, to a record in the
+// caller's workspace; the second pass (vec_state_kernel) walks the chunks of
+// every value slice from those records.
+constexpr int MAP_PREP = 3;  // ChainMap mode of the PREP instance (cm.L: first
+                             // token of the tile, cm.G: chunks per sequence in
+                             // the tile, cm.ws: the records)
+template <class T, int DK>
+struct VecRec {
+  using Sm = Smem<T, DK>;
+  static constexpr int QS = 0;                                             // 2^G o q     [C][LDK]
+  static constexpr int KR = QS + C * Sm::LDK * (int)sizeof(T);             // 2^G o k     [C][LDK]
+  static constexpr int KBT = KR + C * Sm::LDK * (int)sizeof(T);            // Kbar^T      [DK][LDC]
+  static constexpr int TI = KBT + DK * Sm::LDC * (int)sizeof(T);           // (I + L)^-1  [C][LDC]
+  static constexpr int PM = TI + C * Sm::LDC * (int)sizeof(T);             // P           [C][LDC]
+  static constexpr int EC = PM + C * Sm::LDC * (int)sizeof(T);             // 2^(G_C)     [DK] fp32
+  static constexpr int BETA = EC + DK * 4;                                 // beta        [C] fp32
+  static constexpr int BYTES = (BETA + C * 4 + 1023) / 1024 * 1024;        // whole KiB
+};
+
 // VG: alpha is [.., T, DK] (per-dimension gate); otherwise [.., T] (scalar).
 // cm maps workgroups to (sequence, token range) chains as for the pipelined
 // kernel (gdn::pipe::ChainMap): whole sequences (MAP_SEQ), or the first and
@@ -122,7 +146,10 @@ __device__ __forceinline__ void store_vec(float* p, const float (&x)[4]) {
 // no output; MAP_SPLIT_C: every segment from its start state in cm.ws).  The
 // per-token maps stay affine with a per-dimension gate, so the split and its
 // combine step are the same.
-template <class T, int DK, bool VG>
+// PREP: the first pass of the two-pass evaluation (cm.mode == MAP_PREP): one
+// workgroup per chunk of the tile, no state, no output; the chunk's record is
+// written to cm.ws.
+template <class T, int DK, bool VG, bool PREP = false>
 __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -156,7 +183,10 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
 
   const int NS = DV / DVS;
   int chain, slice;
-  {
+  if constexpr (PREP) {
+    chain = blockIdx.x;
+    slice = 0;
+  } else {
     const int w = blockIdx.x;
     if (xcd_map) {
       // the slices of one sequence land on one XCD and share its L2
@@ -178,7 +208,15 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
   bool v_on = true, o_on = true, s0_ident = false;
   const float* s0 = initial_state ? initial_state + (int64_t)chain * dd : nullptr;
   float* sT = final_state ? final_state + (int64_t)chain * dd : nullptr;
-  if (cm.mode == gdn::pipe::MAP_SPLIT_A) {
+  if constexpr (PREP) {
+    // chain = (sequence, chunk of the tile); 1 .. C tokens
+    seq = chain / cm.G;
+    t0 = cm.L + (int64_t)(chain % cm.G) * C;
+    Tlen = cm.T - t0 < C ? cm.T - t0 : C;
+    v_on = false;
+    s0 = nullptr;
+    sT = nullptr;
+  } else if (cm.mode == gdn::pipe::MAP_SPLIT_A) {
     const int per = cm.nseq * (cm.G - 1);
     const int kind = chain / per, r = chain % per;
     seq = r / (cm.G - 1);
@@ -492,6 +530,8 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) sm.Ti[(16 + 4 * lg + e) * LDC + lr] = Elem<T>::from_f32(-acc[e]);
+    } else if (PREP && wave == 1) {
+      gram_tile(5);
     } else if (wave == 1) {
       // Y = diag(beta) (V - K~ S^T), tiles [r][i], meanwhile.
 #pragma unroll
@@ -515,10 +555,30 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
       // output wave, kept live until the output is finished)
       const int t = wave - 2;
       const int ib = t / RB, rb = t % RB;
-      Oacc = Mma<T>::template run<DK>(zero4(), &sm.S[ib * 16 * LDK], LDK, &sm.Qs[rb * 16 * LDK], LDK, lane);
+      if constexpr (!PREP)
+        Oacc = Mma<T>::template run<DK>(zero4(), &sm.S[ib * 16 * LDK], LDK, &sm.Qs[rb * 16 * LDK], LDK, lane);
       gram_tile(3 + t);
     }
     __syncthreads();
+
+    if constexpr (PREP) {
+      // the chunk's record: the buffers the state products read, verbatim
+      using R = VecRec<T, DK>;
+      char* rec = reinterpret_cast<char*>(cm.ws) + (int64_t)chain * R::BYTES;
+      auto put = [&](int off, const void* src, int bytes) {
+        const uint4* s16 = reinterpret_cast<const uint4*>(src);
+        uint4* d16 = reinterpret_cast<uint4*>(rec + off);
+        for (int e = tid; e < bytes / 16; e += NT) d16[e] = s16[e];
+      };
+      put(R::QS, sm.Qs, (int)sizeof(sm.Qs));
+      put(R::KR, sm.Kr, (int)sizeof(sm.Kr));
+      put(R::KBT, sm.Kbt, (int)sizeof(sm.Kbt));
+      put(R::TI, sm.Ti, (int)sizeof(sm.Ti));
+      put(R::PM, sm.P, (int)sizeof(sm.P));
+      put(R::EC, sm.Ec, (int)sizeof(sm.Ec));
+      put(R::BETA, sm.beta, (int)sizeof(sm.beta));
+      return;
+    }
 
     // U = Ti Y (tiles [r][i]), stored as U^T.
     if (wave < RB * IB) {
@@ -563,6 +623,208 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
         const int jb = t / IB, ib = t % IB;
         const int i = ib * 16 + lr, j = jb * 16 + 4 * lg;
         *reinterpret_cast<float4*>(sT + st_off + (int64_t)i * DK + j) =
+            make_float4(Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
+      }
+    }
+  }
+}
+
+// Register staging of the second pass: a record as NR 16-byte vectors per
+// thread (N16 in all), and one V vector.  (Native vectors: an array of the
+// uint4 structs under a guard was kept in scratch memory.)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <int NR, int N16>
+__device__ __forceinline__ void rec_load(u32x4 (&rr)[NR], const char* src, int tid) {
+  const u32x4* s16 = reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+  for (int n = 0; n < NR; ++n) {
+    const int e = tid + NT * n;
+    if (N16 % NT == 0 || e < N16) rr[n] = s16[e];
+  }
+}
+template <int NR, int N16, class T>
+__device__ __forceinline__ void rec_stage(const u32x4 (&rr)[NR], u32x4 rv, char* dst, T* vdst, int tid, bool has_v) {
+  u32x4* d16 = reinterpret_cast<u32x4*>(dst);
+#pragma unroll
+  for (int n = 0; n < NR; ++n) {
+    const int e = tid + NT * n;
+    if (N16 % NT == 0 || e < N16) d16[e] = rr[n];
+  }
+  if (has_v) reinterpret_cast<u32x4*>(vdst)[tid] = rv;
+}
+template <class T>
+__device__ __forceinline__ u32x4 v_load(const T* vc, int c, int r, int col, int64_t Tlen, int DV, bool has_v) {
+  const int64_t tk = (int64_t)c * C + r;
+  return has_v && tk < Tlen ? *reinterpret_cast<const u32x4*>(vc + tk * DV + col) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Second pass of the two-pass evaluation: one workgroup per (sequence,
+// 16-row value slice) walks the chunks [c0, c0 + nct) of the tile from their
+// records (rec: [sequence][chunk of the tile] records of VecRec<T, DK>::BYTES)
+// with the state slice in MFMA accumulators.  Per chunk, three barrier-
+// separated steps: Y = diag(beta) (V - K~ S^T) (waves 0, 1) beside the inter-
+// chunk output S Q~^T (waves 2, 3); U = Ti Y (waves 0, 1); the output
+// O = S Q~^T + P U (waves 2, 3) and the state update (every wave).  The next
+// chunk's record and V are loaded into registers while a chunk is computed
+// and written to the other of two LDS record buffers in its last step.
+// s0 (NULL: zero) is read before sT (NULL: not stored) is written, by the
+// same workgroup, so they may alias.
+template <class T, int DK>
+__global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void vec_state_kernel(
+    const T* __restrict__ v, const char* __restrict__ rec, const float* s0, T* __restrict__ o,
+    float* sT, int nseq, int64_t Tseq, int64_t c0, int nct, int DV, int xcd_map) {
+  using Sm = Smem<T, DK>;
+  using R = VecRec<T, DK>;
+  constexpr int LDK = Sm::LDK;
+  constexpr int LDC = Sm::LDC;
+  constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int NVV = C * DVS / VEC;             // 16-byte vectors of V (threads 0 .. NVV-1)
+  constexpr int N16 = R::BYTES / 16;             // 16-byte vectors of a record
+  constexpr int NR = (N16 + NT - 1) / NT;        // per thread
+  constexpr int JB = DK / 16;
+  constexpr int IB = DVS / 16;
+  constexpr int RB = C / 16;
+  constexpr int NST = (JB * IB + NW - 1) / NW;
+  static_assert(IB == 1 && RB == 2 && NW == 4, "wave roles below: two Y waves, two output waves");
+  static_assert(NVV <= NT, "one thread per V vector");
+
+  __shared__ __attribute__((aligned(16))) char recb[2][R::BYTES];
+  __shared__ __attribute__((aligned(16))) T Vb[2][C * DVS];
+  __shared__ __attribute__((aligned(16))) T Ssh[DVS * LDK];  // operand copy of the state slice
+  __shared__ __attribute__((aligned(16))) T Yt[DVS * LDC];
+  __shared__ __attribute__((aligned(16))) T Ut[DVS * LDC];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+
+  const int NS = DV / DVS;
+  int seq, slice;
+  {
+    const int w = blockIdx.x;
+    if (xcd_map) {
+      const int x = w & 7, r = w >> 3;
+      slice = r % NS;
+      seq = (r / NS) * 8 + x;
+    } else {
+      seq = w / NS;
+      slice = w % NS;
+    }
+  }
+  if (seq >= nseq) return;
+  const int64_t dd = (int64_t)DK * DV;
+  const int64_t st_off = (int64_t)seq * dd + (int64_t)slice * DVS * DK;
+  const int64_t tok0 = (int64_t)seq * Tseq + c0 * C;  // first token of the tile in memory
+  const int64_t Tlen = Tseq - c0 * C;                  // tokens of the sequence from there
+  const T* vc = v + tok0 * DV + slice * DVS;
+  T* oc = o + tok0 * DV + slice * DVS;
+  const char* rc = rec + (int64_t)seq * nct * R::BYTES;
+
+  f32x4 Sacc[NST];
+#pragma unroll
+  for (int m = 0; m < NST; ++m) {
+    const int t = wave + NW * m;
+    Sacc[m] = zero4();
+    if (t < JB * IB) {
+      const int jb = t / IB, ib = t % IB;
+      const int i = ib * 16 + lr, j = jb * 16 + 4 * lg;
+      if (s0) {
+        const float4 s4 = *reinterpret_cast<const float4*>(s0 + st_off + (int64_t)i * DK + j);
+        Sacc[m] = f32x4{s4.x, s4.y, s4.z, s4.w};
+      }
+      store4<T>(&Ssh[i * LDK + j], Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
+    }
+  }
+
+  // register staging of a chunk's record and V slice (V rows past the end of
+  // the sequence are written as zero)
+  u32x4 rr[NR], rv = u32x4{0u, 0u, 0u, 0u};
+  // V vector of this thread in chunk c: token c*C + vr, columns vcg*VEC ..
+  const int vr = tid / (DVS / VEC), vcg = tid % (DVS / VEC);
+  if (nct > 0) {
+    rec_load<NR, N16>(rr, rc, tid);
+    rv = v_load<T>(vc, 0, vr, vcg * VEC, Tlen, DV, tid < NVV);
+    rec_stage<NR, N16>(rr, rv, recb[0], Vb[0], tid, tid < NVV);
+  }
+  if (nct > 1) {
+    rec_load<NR, N16>(rr, rc + R::BYTES, tid);
+    rv = v_load<T>(vc, 1, vr, vcg * VEC, Tlen, DV, tid < NVV);
+  }
+
+  for (int c = 0; c < nct; ++c) {
+    const int b = c & 1;
+    const T* Qs = reinterpret_cast<const T*>(recb[b] + R::QS);
+    const T* Kr = reinterpret_cast<const T*>(recb[b] + R::KR);
+    const T* Kbt = reinterpret_cast<const T*>(recb[b] + R::KBT);
+    const T* Ti = reinterpret_cast<const T*>(recb[b] + R::TI);
+    const T* Pm = reinterpret_cast<const T*>(recb[b] + R::PM);
+    const float* Ec = reinterpret_cast<const float*>(recb[b] + R::EC);
+    const float* be = reinterpret_cast<const float*>(recb[b] + R::BETA);
+    __syncthreads();  // this chunk's record, V and the state copy are in LDS
+
+    f32x4 Oacc = zero4();
+    if (wave < 2) {
+      // Y = diag(beta) (V - K~ S^T), tile [r][i] with rb = wave
+      const int rb = wave;
+      const f32x4 acc = Mma<T>::template run<DK>(zero4(), &Kr[rb * 16 * LDK], LDK, &Ssh[0], LDK, lane);
+      const int r0 = rb * 16 + 4 * lg;
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = be[r0 + e] * (Elem<T>::to_f32(Vb[b][(r0 + e) * DVS + lr]) - acc[e]);
+      store4<T>(&Yt[lr * LDC + r0], y[0], y[1], y[2], y[3]);
+    } else {
+      // S Q~^T, tile [i][r] with rb = wave - 2, kept live until the output is finished
+      Oacc = Mma<T>::template run<DK>(zero4(), &Ssh[0], LDK, &Qs[(wave - 2) * 16 * LDK], LDK, lane);
+    }
+    __syncthreads();
+
+    // U = Ti Y (tile [r][i] with rb = wave), stored as U^T
+    if (wave < 2) {
+      const int rb = wave;
+      const f32x4 acc = Mma<T>::template run<C>(zero4(), &Ti[rb * 16 * LDC], LDC, &Yt[0], LDC, lane);
+      store4<T>(&Ut[lr * LDC + rb * 16 + 4 * lg], acc[0], acc[1], acc[2], acc[3]);
+    }
+    __syncthreads();
+
+    // the output (waves 2, 3) and the state update (every wave); the next
+    // chunk's record goes to the other buffer
+    if (wave >= 2) {
+      const int rb = wave - 2;
+      Oacc = Mma<T>::template run<C>(Oacc, &Ut[0], LDC, &Pm[rb * 16 * LDC], LDC, lane);
+      const int64_t tk = (int64_t)c * C + rb * 16 + lr;
+      if (tk < Tlen) store4<T>(oc + tk * DV + 4 * lg, Oacc[0], Oacc[1], Oacc[2], Oacc[3]);
+    }
+#pragma unroll
+    for (int m = 0; m < NST; ++m) {
+      const int t = wave + NW * m;
+      if (t < JB * IB) {
+        const int jb = t / IB;
+        const int j = jb * 16 + 4 * lg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sacc[m][e] *= Ec[j + e];
+        Sacc[m] = Mma<T>::template run<C>(Sacc[m], &Kbt[jb * 16 * LDC], LDC, &Ut[0], LDC, lane);
+        store4<T>(&Ssh[lr * LDK + j], Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
+      }
+    }
+    if (c + 1 < nct) {
+      rec_stage<NR, N16>(rr, rv, recb[b ^ 1], Vb[b ^ 1], tid, tid < NVV);
+      if (c + 2 < nct) {
+        rec_load<NR, N16>(rr, rc + (int64_t)(c + 2) * R::BYTES, tid);
+        rv = v_load<T>(vc, c + 2, vr, vcg * VEC, Tlen, DV, tid < NVV);
+      }
+    }
+  }
+
+  if (sT) {
+#pragma unroll
+    for (int m = 0; m < NST; ++m) {
+      const int t = wave + NW * m;
+      if (t < JB * IB) {
+        const int jb = t / IB;
+        const int j = jb * 16 + 4 * lg;
+        *reinterpret_cast<float4*>(sT + st_off + (int64_t)lr * DK + j) =
             make_float4(Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
       }
     }

@@ -385,6 +385,56 @@ int vec_split_launches(const void* q, const void* k, const void* v, const float*
   cm.mode = gdn::pipe::MAP_SPLIT_C;
   return launch_vec<true>(q, k, v, alpha, beta, nullptr, o, final_state, cm, dk, dv, dtype, stream);
 }
+
+// Two-pass per-dimension gate.  The workspace holds the state carried from
+// one tile of chunks to the next (B*H*dk*dv floats), then the records of one
+// tile (B*H*tile records).  A tile is at most VEC2P_TILE chunks per sequence:
+// at the main workload's shape its records (138 MB) fit the 256 MB Infinity
+// Cache, where the second pass finds them.
+constexpr int64_t VEC2P_TILE = 64;
+
+int64_t vec2p_rec_bytes(int64_t dk, gdn_dtype dtype) {
+  return vec_dispatch<true>(dtype, dk, [](auto t, auto dkc) {
+    return (int)gdn::vec::VecRec<decltype(t), decltype(dkc)::value>::BYTES;
+  });
+}
+
+template <class T, int DK>
+int vec2p_launches_t(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                     const float* initial_state, void* o, float* final_state, int64_t nseq, int64_t Tseq,
+                     int64_t dv, char* ws, int64_t tile, hipStream_t stream) {
+  float* carry = reinterpret_cast<float*>(ws);
+  char* rec = ws + nseq * DK * dv * 4;
+  const int64_t nch = (Tseq + gdn::vec::C - 1) / gdn::vec::C;
+  const int64_t nstate = nseq * (dv / gdn::vec::DVS);
+  if (nseq * tile > 0x7fffffff || nstate > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+  const int xcd_map = (nseq % 8) == 0;
+  int64_t c0 = 0;
+  do {
+    const int64_t n = tile < nch - c0 ? tile : nch - c0;  // 0 when there are no chunks
+    if (n > 0) {
+      gdn::pipe::ChainMap cm{};
+      cm.mode = gdn::vec::MAP_PREP;
+      cm.nseq = (int)nseq;
+      cm.G = (int)n;
+      cm.T = Tseq;
+      cm.L = c0 * gdn::vec::C;
+      cm.ws = reinterpret_cast<float*>(rec);
+      hipLaunchKernelGGL((gdn::vec::chunk_vec_kernel<T, DK, true, true>), dim3((unsigned)(nseq * n)),
+                         dim3(gdn::vec::NT), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
+                         static_cast<const T*>(v), alpha, beta, nullptr, static_cast<T*>(o), nullptr, cm, (int)dv, 0);
+      if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
+    }
+    const float* in = c0 == 0 ? initial_state : carry;
+    float* out = c0 + n >= nch ? final_state : carry;
+    hipLaunchKernelGGL((gdn::vec::vec_state_kernel<T, DK>), dim3((unsigned)nstate), dim3(gdn::vec::NT), 0, stream,
+                       static_cast<const T*>(v), rec, in, static_cast<T*>(o), out, (int)nseq, Tseq, c0, (int)n,
+                       (int)dv, xcd_map);
+    if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
+    c0 += n;
+  } while (c0 < nch);
+  return GDN_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -510,6 +560,52 @@ int gdn_chunk_fwd_vecgate(const void* q, const void* k, const void* v, const flo
   if (nchain == 0 || (T == 0 && !final_state)) return GDN_OK;
   return launch_vec<true>(q, k, v, alpha, beta, initial_state, o, final_state, seq_map(nchain, T), dk, dv, dtype,
                           static_cast<hipStream_t>(hip_stream));
+}
+
+size_t gdn_chunk_fwd_vecgate_2pass_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                                             int64_t chunk_size, gdn_dtype dtype) {
+  if (B <= 0 || H <= 0 || T < 0 || dk != dv || (dk != 64 && dk != 128) || chunk_size != gdn::vec::C ||
+      (dtype != GDN_BF16 && dtype != GDN_F32) || too_large(B, H, T))
+    return 0;
+  const int64_t nch = (T + gdn::vec::C - 1) / gdn::vec::C;
+  const int64_t tile = nch < VEC2P_TILE ? (nch > 0 ? nch : 1) : VEC2P_TILE;
+  return (size_t)(B * H * (dk * dv * 4 + tile * vec2p_rec_bytes(dk, dtype)));
+}
+
+int gdn_chunk_fwd_vecgate_2pass(const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, const float* initial_state, void* o, float* final_state,
+                                int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk_size,
+                                gdn_dtype dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
+                           chunk_size > 0 ? 64 : chunk_size, dtype, true);
+  if (rc != GDN_OK) return rc;
+  if (chunk_size != gdn::vec::C) return GDN_ERR_UNSUPPORTED;
+  const int64_t nseq = B * H;
+  if (nseq == 0 || (T == 0 && !final_state)) return GDN_OK;
+  const int64_t rec = vec2p_rec_bytes(dk, dtype);
+  const int64_t carry = nseq * dk * dv * 4;
+  const int64_t nch = (T + gdn::vec::C - 1) / gdn::vec::C;
+  if (!workspace || (int64_t)workspace_bytes < carry + nseq * rec) return GDN_ERR_INVALID_ARG;
+  if (misaligned(workspace)) return GDN_ERR_ALIGNMENT;
+  int64_t tile = ((int64_t)workspace_bytes - carry) / (nseq * rec);
+  if (tile > VEC2P_TILE) tile = VEC2P_TILE;
+  if (tile > nch) tile = nch;
+  {
+    const Range rw{workspace, carry + (tile > 0 ? tile : 1) * nseq * rec};
+    const int64_t esz = dtype == GDN_BF16 ? 2 : 4;
+    const Range others[] = {{q, nseq * T * dk * esz}, {k, nseq * T * dk * esz},
+                            {v, nseq * T * dv * esz}, {o, nseq * T * dv * esz},
+                            {alpha, nseq * T * dk * 4}, {beta, nseq * T * 4},
+                            {initial_state, nseq * dv * dk * 4}, {final_state, nseq * dv * dk * 4}};
+    for (const Range& r : others)
+      if (overlaps(rw, r)) return GDN_ERR_INVALID_ARG;
+  }
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(workspace);
+  return vec_dispatch<true>(dtype, dk, [&](auto t, auto dkc) {
+    return vec2p_launches_t<decltype(t), decltype(dkc)::value>(q, k, v, alpha, beta, initial_state, o, final_state,
+                                                              nseq, T, dv, ws, tile, stream);
+  });
 }
 
 size_t gdn_chunk_fwd_vecgate_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,

@@ -206,6 +206,42 @@ int gdn_chunk_fwd_vecgate_split(const void* q, const void* k, const void* v,
 size_t gdn_chunk_fwd_vecgate_split_workspace(int64_t B, int64_t H, int64_t T, int64_t dk,
                                              int64_t dv, int64_t chunk_size, gdn_dtype dtype);
 
+/*
+ * gdn_chunk_fwd_vecgate_2pass — the same result as gdn_chunk_fwd_vecgate
+ * ([P1] §2.2 per-dimension gate, §3.2 chunked evaluation), in two passes
+ * over tiles of at most 64 chunks (2048 tokens) per sequence:
+ *   1. per chunk, once: the gate prefix, the scaled operand copies of q and
+ *      k, L, (I+L)^-1 and P, written to a record in the workspace;
+ *   2. per 16-row value slice: the state-dependent products of every chunk
+ *      of the tile, from the records.
+ * The single-pass kernel repeats step 1 in the workgroup of every value
+ * slice; here it is done once per chunk, at the cost of writing and reading
+ * the records.  The state passes from tile to tile through the workspace.
+ *
+ *   workspace        device memory owned by the caller, at least
+ *                    B*H*(dk*dv*4 + R) bytes for a record size R (one chunk
+ *                    per tile); gdn_chunk_fwd_vecgate_2pass_workspace(...)
+ *                    gives the size for the largest tile, and a larger
+ *                    workspace is not used beyond it.  16-byte aligned,
+ *                    overlapping no other argument; its contents on entry do
+ *                    not matter.  Calls sharing a workspace must not overlap
+ *                    in time.
+ * Other arguments, layouts, aliasing (final_state may be initial_state) and
+ * errors as for gdn_chunk_fwd_vecgate (chunk_size 32); a missing or too
+ * small workspace returns GDN_ERR_INVALID_ARG.
+ */
+int gdn_chunk_fwd_vecgate_2pass(const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta,
+                                const float* initial_state, void* o, float* final_state,
+                                int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                                int64_t chunk_size, gdn_dtype dtype, void* workspace,
+                                size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes with which gdn_chunk_fwd_vecgate_2pass uses its largest
+ * tile for these sizes.  Host-only; 0 for arguments it rejects. */
+size_t gdn_chunk_fwd_vecgate_2pass_workspace(int64_t B, int64_t H, int64_t T, int64_t dk,
+                                             int64_t dv, int64_t chunk_size, gdn_dtype dtype);
+
 /* Workspace bytes gdn_scan_fwd needs for these sizes.  Host-only. */
 size_t gdn_scan_fwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
                               gdn_dtype dtype);

@@ -216,3 +216,36 @@ def test_vecgate_split_rejects_invalid_arguments_and_sizes_workspace(lib):
     assert f(1, 8, 16384, 96, 96, 32, 1) == 0               # unsupported width
     assert f(0, 8, 16384, 64, 64, 32, 1) == 0               # nothing to do
     assert f(1, 8, 16384, 64, 64, 32, 1) >= 0               # no GPU here: 0; on a GPU: > 0
+
+
+def test_vecgate_2pass_rejects_invalid_arguments_and_sizes_workspace(lib):
+    """The two-pass route's checks, all before any device call, and its
+    workspace size: the carried state (B*H*dk*dv floats) plus one record per
+    chunk of the largest tile (at most 64 chunks per sequence); a record holds
+    the scaled q and k, Kbar^T, (I+L)^-1, P, 2^(G_C) and beta of a 32-token
+    chunk in their LDS layout, rounded up to whole KiB."""
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    WS = A + 512 * MB
+
+    def tp(B=1, H=1, T=64, dk=64, dv=64, C=32, dtype=1, q=A, o=A + 256 * MB, ws=WS, wsb=64 * MB):
+        return lib.gdn_chunk_fwd_vecgate_2pass(P(q), P(A + 64 * MB), P(A + 128 * MB), P(A + 192 * MB),
+                                               P(A + 240 * MB), None, P(o), None, B, H, T, dk, dv, C, dtype,
+                                               P(ws), wsb, None)
+    assert tp(B=-1) == binding.GDN_ERR_INVALID_ARG
+    assert tp(q=None) == binding.GDN_ERR_INVALID_ARG
+    assert tp(C=64) == binding.GDN_ERR_UNSUPPORTED
+    assert tp(dk=96, dv=96) == binding.GDN_ERR_UNSUPPORTED
+    assert tp(ws=None) == binding.GDN_ERR_INVALID_ARG
+    assert tp(wsb=64 * 64 * 4 + 20480 - 1) == binding.GDN_ERR_INVALID_ARG   # under one record per sequence
+    assert tp(ws=WS + 8) == binding.GDN_ERR_ALIGNMENT
+    assert tp(ws=A + 64 * MB) == binding.GDN_ERR_INVALID_ARG               # workspace overlaps k
+    assert tp(B=0) == 0
+    f = lib.gdn_chunk_fwd_vecgate_2pass_workspace
+    rec = {(1, 64): 20480, (1, 128): 33792, (0, 64): 36864, (0, 128): 62464}
+    for (dt, d), r in rec.items():
+        assert f(1, 1, 1000, d, d, 32, dt) == d * d * 4 + 32 * r              # 32 chunks: one tile
+        assert f(4, 16, 8192, d, d, 32, dt) == 64 * (d * d * 4 + 64 * r)      # tiles of 64 chunks
+        assert f(1, 1, 0, d, d, 32, dt) == d * d * 4 + r
+    assert f(1, 1, 1000, 64, 64, 64, 1) == 0
+    assert f(1, 1, 1000, 96, 96, 32, 1) == 0
+    assert f(0, 1, 1000, 64, 64, 32, 1) == 0

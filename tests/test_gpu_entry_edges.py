@@ -1,5 +1,6 @@
 """Edge cases of the sequence-split, scan, vector-gate (scan and chunked),
-GLA, fp32 chunked and 32-token chunked entry points on the GPU: zero tokens (the final state is the initial one, or zero), no
+GLA, fp32 chunked, 32-token chunked and two-pass per-dimension-gate entry
+points on the GPU: zero tokens (the final state is the initial one, or zero), no
 sequences, fewer tokens than one chunk or block, and a final state that
 aliases the initial state.  Results are compared with the fp64 oracles or
 with exact expectations."""
@@ -10,6 +11,7 @@ import torch
 import oracle
 from gated_deltanet_sequence_amd import inputs
 from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd, gdn_chunk_fwd_split, gdn_chunk_fwd_vecgate,
+                                                 gdn_chunk_fwd_vecgate_2pass,
                                                  gdn_scan_fwd, gdn_scan_fwd_vecgate, gla_chunk_fwd)
 
 from _helpers import TOL, maxrel, oracle_inputs, to_dev, to_np
@@ -29,6 +31,9 @@ ENTRIES = {
     "gla": lambda xd: gla_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"], 64),
     "chunk_vecgate": lambda xd: gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], _vec(xd["alpha"], xd["q"].shape[3]),
                                                       xd["beta"], xd["s0"]),
+    "chunk_vecgate_2pass": lambda xd: gdn_chunk_fwd_vecgate_2pass(xd["q"], xd["k"], xd["v"],
+                                                                  _vec(xd["alpha"], xd["q"].shape[3]), xd["beta"],
+                                                                  xd["s0"]),
     # chunk_size 32: the 32-token kernel on the bf16 inputs
     "c32": lambda xd: gdn_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"], 32),
     # the same bf16-rounded inputs as fp32: the fp32 chunked path
@@ -58,7 +63,8 @@ def test_no_sequences(name):
     assert o.numel() == 0 and sT.numel() == 0
 
 
-@pytest.mark.parametrize("name", ["split", "scan", "scan_vecgate", "chunk_vecgate", "c32", "fp32"])
+@pytest.mark.parametrize("name", ["split", "scan", "scan_vecgate", "chunk_vecgate", "chunk_vecgate_2pass", "c32",
+                                  "fp32"])
 @pytest.mark.parametrize("T", [1, 17, 31, 33, 63])
 def test_short_sequences_match_oracle(name, T):
     x = inputs.make_fwd_inputs(1, 2, T, 64, "bf16", seed=63 + T, init_state=True)
@@ -70,7 +76,7 @@ def test_short_sequences_match_oracle(name, T):
     assert maxrel(to_np(o), ro) <= tol and maxrel(to_np(sT), rs) <= tol
 
 
-@pytest.mark.parametrize("name", ["scan", "gla", "chunk_vecgate", "c32", "fp32"])
+@pytest.mark.parametrize("name", ["scan", "gla", "chunk_vecgate", "chunk_vecgate_2pass", "c32", "fp32"])
 def test_final_state_aliases_initial_state(name):
     x = inputs.make_fwd_inputs(1, 2, 700, 128, "bf16", seed=64, init_state=True)
     xd = to_dev(x)
@@ -84,6 +90,9 @@ def test_final_state_aliases_initial_state(name):
     elif name == "chunk_vecgate":
         o, s2 = gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], _vec(xd["alpha"], 128), xd["beta"], s,
                                       final_state=s)
+    elif name == "chunk_vecgate_2pass":
+        o, s2 = gdn_chunk_fwd_vecgate_2pass(xd["q"], xd["k"], xd["v"], _vec(xd["alpha"], 128), xd["beta"], s,
+                                            final_state=s)
     elif name == "c32":
         o, s2 = gdn_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], s, 32, final_state=s)
     else:
