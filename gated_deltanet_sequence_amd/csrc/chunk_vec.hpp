@@ -124,7 +124,11 @@ __device__ __forceinline__ void store_vec(float* p, const float (&x)[4]) {
 // every value slice from those records.
 constexpr int MAP_PREP = 3;  // ChainMap mode of the PREP instance (cm.L: first
                              // token of the tile, cm.G: chunks per sequence in
-                             // the tile, cm.ws: the records)
+                             // the tile, cm.ws: the records; the grid holds
+                             // cm.nseq * ng workgroups, each taking one of ng
+                             // groups of consecutive chunks of a sequence, so
+                             // that the next chunk's inputs load while one is
+                             // computed)
 template <class T, int DK>
 struct VecRec {
   using Sm = Smem<T, DK>;
@@ -208,11 +212,16 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
   bool v_on = true, o_on = true, s0_ident = false;
   const float* s0 = initial_state ? initial_state + (int64_t)chain * dd : nullptr;
   float* sT = final_state ? final_state + (int64_t)chain * dd : nullptr;
+  int prep_first = 0;  // PREP: the first chunk of this workgroup within the tile
   if constexpr (PREP) {
-    // chain = (sequence, chunk of the tile); 1 .. C tokens
-    seq = chain / cm.G;
-    t0 = cm.L + (int64_t)(chain % cm.G) * C;
-    Tlen = cm.T - t0 < C ? cm.T - t0 : C;
+    // chain = (sequence, group of consecutive chunks of the tile)
+    const int ng = (int)gridDim.x / cm.nseq;
+    const int gsz = (cm.G + ng - 1) / ng;
+    seq = chain / ng;
+    prep_first = (chain % ng) * gsz;
+    const int nc = max(0, min(gsz, cm.G - prep_first));
+    t0 = cm.L + (int64_t)prep_first * C;
+    Tlen = max((int64_t)0, min((int64_t)nc * C, cm.T - t0));
     v_on = false;
     s0 = nullptr;
     sT = nullptr;
@@ -564,7 +573,7 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
     if constexpr (PREP) {
       // the chunk's record: the buffers the state products read, verbatim
       using R = VecRec<T, DK>;
-      char* rec = reinterpret_cast<char*>(cm.ws) + (int64_t)chain * R::BYTES;
+      char* rec = reinterpret_cast<char*>(cm.ws) + ((int64_t)seq * cm.G + prep_first + ch) * R::BYTES;
       auto put = [&](int off, const void* src, int bytes) {
         const uint4* s16 = reinterpret_cast<const uint4*>(src);
         uint4* d16 = reinterpret_cast<uint4*>(rec + off);
@@ -577,7 +586,7 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
       put(R::PM, sm.P, (int)sizeof(sm.P));
       put(R::EC, sm.Ec, (int)sizeof(sm.Ec));
       put(R::BETA, sm.beta, (int)sizeof(sm.beta));
-      return;
+      continue;
     }
 
     // U = Ti Y (tiles [r][i]), stored as U^T.
@@ -630,27 +639,26 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
 }
 
 // Register staging of the second pass: a record as NR 16-byte vectors per
-// thread (N16 in all), and one V vector.  (Native vectors: an array of the
-// uint4 structs under a guard was kept in scratch memory.)
+// thread of NTH (N16 in all), and one V vector.  (Native vectors: an array of
+// the uint4 structs under a guard was kept in scratch memory.)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-template <int NR, int N16>
+template <int NR, int N16, int NTH>
 __device__ __forceinline__ void rec_load(u32x4 (&rr)[NR], const char* src, int tid) {
   const u32x4* s16 = reinterpret_cast<const u32x4*>(src);
 #pragma unroll
   for (int n = 0; n < NR; ++n) {
-    const int e = tid + NT * n;
-    if (N16 % NT == 0 || e < N16) rr[n] = s16[e];
+    const int e = tid + NTH * n;
+    if (N16 % NTH == 0 || e < N16) rr[n] = s16[e];
   }
 }
-template <int NR, int N16, class T>
-__device__ __forceinline__ void rec_stage(const u32x4 (&rr)[NR], u32x4 rv, char* dst, T* vdst, int tid, bool has_v) {
+template <int NR, int N16, int NTH>
+__device__ __forceinline__ void rec_stage(const u32x4 (&rr)[NR], char* dst, int tid) {
   u32x4* d16 = reinterpret_cast<u32x4*>(dst);
 #pragma unroll
   for (int n = 0; n < NR; ++n) {
-    const int e = tid + NT * n;
-    if (N16 % NT == 0 || e < N16) d16[e] = rr[n];
+    const int e = tid + NTH * n;
+    if (N16 % NTH == 0 || e < N16) d16[e] = rr[n];
   }
-  if (has_v) reinterpret_cast<u32x4*>(vdst)[tid] = rv;
 }
 template <class T>
 __device__ __forceinline__ u32x4 v_load(const T* vc, int c, int r, int col, int64_t Tlen, int DV, bool has_v) {
@@ -658,62 +666,68 @@ __device__ __forceinline__ u32x4 v_load(const T* vc, int c, int r, int col, int6
   return has_v && tk < Tlen ? *reinterpret_cast<const u32x4*>(vc + tk * DV + col) : u32x4{0u, 0u, 0u, 0u};
 }
 
-// Second pass of the two-pass evaluation: one workgroup per (sequence,
-// 16-row value slice) walks the chunks [c0, c0 + nct) of the tile from their
-// records (rec: [sequence][chunk of the tile] records of VecRec<T, DK>::BYTES)
-// with the state slice in MFMA accumulators.  Per chunk, three barrier-
-// separated steps: Y = diag(beta) (V - K~ S^T) (waves 0, 1) beside the inter-
-// chunk output S Q~^T (waves 2, 3); U = Ti Y (waves 0, 1); the output
-// O = S Q~^T + P U (waves 2, 3) and the state update (every wave).  The next
-// chunk's record and V are loaded into registers while a chunk is computed
-// and written to the other of two LDS record buffers in its last step.
-// s0 (NULL: zero) is read before sT (NULL: not stored) is written, by the
-// same workgroup, so they may alias.
-template <class T, int DK>
-__global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void vec_state_kernel(
+// Second pass of the two-pass evaluation: one workgroup per (sequence, SL
+// consecutive 16-row value slices) walks the chunks [c0, c0 + nct) of the
+// tile from their records (rec: [sequence][chunk of the tile] records of
+// VecRec<T, DK>::BYTES), each slice's state in the MFMA accumulators of its
+// own four waves; the slices of a workgroup share the records in LDS.  Per
+// chunk, three barrier-separated steps: Y = diag(beta) (V - K~ S^T) (waves
+// 0, 1 of a slice) beside the inter-chunk output S Q~^T (waves 2, 3); U = Ti Y
+// (waves 0, 1); the output O = S Q~^T + P U (waves 2, 3) and the state update
+// (every wave).  The next chunk's record and V are loaded into registers
+// while a chunk is computed and written to the other of two LDS record
+// buffers in its last step.  s0 (NULL: zero) is read before sT (NULL: not
+// stored) is written, by the same workgroup, so they may alias.
+template <class T, int DK, int SL>
+__global__ __launch_bounds__(NT * SL, SL == 1 && sizeof(T) == 2 ? 2 : 1) void vec_state_kernel(
     const T* __restrict__ v, const char* __restrict__ rec, const float* s0, T* __restrict__ o,
     float* sT, int nseq, int64_t Tseq, int64_t c0, int nct, int DV, int xcd_map) {
   using Sm = Smem<T, DK>;
   using R = VecRec<T, DK>;
+  constexpr int NTH = NT * SL;
   constexpr int LDK = Sm::LDK;
   constexpr int LDC = Sm::LDC;
   constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int NVV = C * DVS / VEC;             // 16-byte vectors of V (threads 0 .. NVV-1)
+  constexpr int NVV = C * DVS / VEC;             // 16-byte vectors of one slice's V
   constexpr int N16 = R::BYTES / 16;             // 16-byte vectors of a record
-  constexpr int NR = (N16 + NT - 1) / NT;        // per thread
+  constexpr int NR = (N16 + NTH - 1) / NTH;      // per thread
   constexpr int JB = DK / 16;
   constexpr int IB = DVS / 16;
   constexpr int RB = C / 16;
   constexpr int NST = (JB * IB + NW - 1) / NW;
   static_assert(IB == 1 && RB == 2 && NW == 4, "wave roles below: two Y waves, two output waves");
-  static_assert(NVV <= NT, "one thread per V vector");
+  static_assert(NVV <= NT, "one thread of the slice's waves per V vector");
 
   __shared__ __attribute__((aligned(16))) char recb[2][R::BYTES];
-  __shared__ __attribute__((aligned(16))) T Vb[2][C * DVS];
-  __shared__ __attribute__((aligned(16))) T Ssh[DVS * LDK];  // operand copy of the state slice
-  __shared__ __attribute__((aligned(16))) T Yt[DVS * LDC];
-  __shared__ __attribute__((aligned(16))) T Ut[DVS * LDC];
+  __shared__ __attribute__((aligned(16))) T Vb[2][SL][C * DVS];
+  __shared__ __attribute__((aligned(16))) T Ssh[SL][DVS * LDK];  // operand copy of each state slice
+  __shared__ __attribute__((aligned(16))) T Yt[SL][DVS * LDC];
+  __shared__ __attribute__((aligned(16))) T Ut[SL][DVS * LDC];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = wave_all / NW;    // slice of this wave within the workgroup
+  const int wave = wave_all % NW; // role within the slice
+  const int ts = tid % NT;        // thread within the slice's waves
   const int lr = lane & 15;
   const int lg = lane >> 4;
 
-  const int NS = DV / DVS;
-  int seq, slice;
+  const int NSG = DV / (DVS * SL);  // slice groups per sequence
+  int seq, sg;
   {
     const int w = blockIdx.x;
     if (xcd_map) {
       const int x = w & 7, r = w >> 3;
-      slice = r % NS;
-      seq = (r / NS) * 8 + x;
+      sg = r % NSG;
+      seq = (r / NSG) * 8 + x;
     } else {
-      seq = w / NS;
-      slice = w % NS;
+      seq = w / NSG;
+      sg = w % NSG;
     }
   }
   if (seq >= nseq) return;
+  const int slice = sg * SL + h;
   const int64_t dd = (int64_t)DK * DV;
   const int64_t st_off = (int64_t)seq * dd + (int64_t)slice * DVS * DK;
   const int64_t tok0 = (int64_t)seq * Tseq + c0 * C;  // first token of the tile in memory
@@ -721,6 +735,9 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void vec_state_kernel(
   const T* vc = v + tok0 * DV + slice * DVS;
   T* oc = o + tok0 * DV + slice * DVS;
   const char* rc = rec + (int64_t)seq * nct * R::BYTES;
+  T* Sh = Ssh[h];
+  T* Yh = Yt[h];
+  T* Uh = Ut[h];
 
   f32x4 Sacc[NST];
 #pragma unroll
@@ -728,29 +745,29 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void vec_state_kernel(
     const int t = wave + NW * m;
     Sacc[m] = zero4();
     if (t < JB * IB) {
-      const int jb = t / IB, ib = t % IB;
-      const int i = ib * 16 + lr, j = jb * 16 + 4 * lg;
+      const int j = t * 16 + 4 * lg;
       if (s0) {
-        const float4 s4 = *reinterpret_cast<const float4*>(s0 + st_off + (int64_t)i * DK + j);
+        const float4 s4 = *reinterpret_cast<const float4*>(s0 + st_off + (int64_t)lr * DK + j);
         Sacc[m] = f32x4{s4.x, s4.y, s4.z, s4.w};
       }
-      store4<T>(&Ssh[i * LDK + j], Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
+      store4<T>(&Sh[lr * LDK + j], Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
     }
   }
 
-  // register staging of a chunk's record and V slice (V rows past the end of
-  // the sequence are written as zero)
+  // register staging of a chunk's record (all threads) and of each slice's
+  // V (V rows past the end of the sequence are written as zero)
   u32x4 rr[NR], rv = u32x4{0u, 0u, 0u, 0u};
-  // V vector of this thread in chunk c: token c*C + vr, columns vcg*VEC ..
-  const int vr = tid / (DVS / VEC), vcg = tid % (DVS / VEC);
+  const bool has_v = ts < NVV;
+  const int vr = ts / (DVS / VEC), vcg = ts % (DVS / VEC);  // token, 16-byte column group of this V vector
   if (nct > 0) {
-    rec_load<NR, N16>(rr, rc, tid);
-    rv = v_load<T>(vc, 0, vr, vcg * VEC, Tlen, DV, tid < NVV);
-    rec_stage<NR, N16>(rr, rv, recb[0], Vb[0], tid, tid < NVV);
+    rec_load<NR, N16, NTH>(rr, rc, tid);
+    rv = v_load<T>(vc, 0, vr, vcg * VEC, Tlen, DV, has_v);
+    rec_stage<NR, N16, NTH>(rr, recb[0], tid);
+    if (has_v) reinterpret_cast<u32x4*>(Vb[0][h])[ts] = rv;
   }
   if (nct > 1) {
-    rec_load<NR, N16>(rr, rc + R::BYTES, tid);
-    rv = v_load<T>(vc, 1, vr, vcg * VEC, Tlen, DV, tid < NVV);
+    rec_load<NR, N16, NTH>(rr, rc + R::BYTES, tid);
+    rv = v_load<T>(vc, 1, vr, vcg * VEC, Tlen, DV, has_v);
   }
 
   for (int c = 0; c < nct; ++c) {
@@ -762,29 +779,30 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void vec_state_kernel(
     const T* Pm = reinterpret_cast<const T*>(recb[b] + R::PM);
     const float* Ec = reinterpret_cast<const float*>(recb[b] + R::EC);
     const float* be = reinterpret_cast<const float*>(recb[b] + R::BETA);
-    __syncthreads();  // this chunk's record, V and the state copy are in LDS
+    const T* Vh = Vb[b][h];
+    __syncthreads();  // this chunk's record, V and the state copies are in LDS
 
     f32x4 Oacc = zero4();
     if (wave < 2) {
       // Y = diag(beta) (V - K~ S^T), tile [r][i] with rb = wave
       const int rb = wave;
-      const f32x4 acc = Mma<T>::template run<DK>(zero4(), &Kr[rb * 16 * LDK], LDK, &Ssh[0], LDK, lane);
+      const f32x4 acc = Mma<T>::template run<DK>(zero4(), &Kr[rb * 16 * LDK], LDK, Sh, LDK, lane);
       const int r0 = rb * 16 + 4 * lg;
       float y[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = be[r0 + e] * (Elem<T>::to_f32(Vb[b][(r0 + e) * DVS + lr]) - acc[e]);
-      store4<T>(&Yt[lr * LDC + r0], y[0], y[1], y[2], y[3]);
+      for (int e = 0; e < 4; ++e) y[e] = be[r0 + e] * (Elem<T>::to_f32(Vh[(r0 + e) * DVS + lr]) - acc[e]);
+      store4<T>(&Yh[lr * LDC + r0], y[0], y[1], y[2], y[3]);
     } else {
       // S Q~^T, tile [i][r] with rb = wave - 2, kept live until the output is finished
-      Oacc = Mma<T>::template run<DK>(zero4(), &Ssh[0], LDK, &Qs[(wave - 2) * 16 * LDK], LDK, lane);
+      Oacc = Mma<T>::template run<DK>(zero4(), Sh, LDK, &Qs[(wave - 2) * 16 * LDK], LDK, lane);
     }
     __syncthreads();
 
     // U = Ti Y (tile [r][i] with rb = wave), stored as U^T
     if (wave < 2) {
       const int rb = wave;
-      const f32x4 acc = Mma<T>::template run<C>(zero4(), &Ti[rb * 16 * LDC], LDC, &Yt[0], LDC, lane);
-      store4<T>(&Ut[lr * LDC + rb * 16 + 4 * lg], acc[0], acc[1], acc[2], acc[3]);
+      const f32x4 acc = Mma<T>::template run<C>(zero4(), &Ti[rb * 16 * LDC], LDC, Yh, LDC, lane);
+      store4<T>(&Uh[lr * LDC + rb * 16 + 4 * lg], acc[0], acc[1], acc[2], acc[3]);
     }
     __syncthreads();
 
@@ -792,7 +810,7 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void vec_state_kernel(
     // chunk's record goes to the other buffer
     if (wave >= 2) {
       const int rb = wave - 2;
-      Oacc = Mma<T>::template run<C>(Oacc, &Ut[0], LDC, &Pm[rb * 16 * LDC], LDC, lane);
+      Oacc = Mma<T>::template run<C>(Oacc, Uh, LDC, &Pm[rb * 16 * LDC], LDC, lane);
       const int64_t tk = (int64_t)c * C + rb * 16 + lr;
       if (tk < Tlen) store4<T>(oc + tk * DV + 4 * lg, Oacc[0], Oacc[1], Oacc[2], Oacc[3]);
     }
@@ -800,19 +818,19 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void vec_state_kernel(
     for (int m = 0; m < NST; ++m) {
       const int t = wave + NW * m;
       if (t < JB * IB) {
-        const int jb = t / IB;
-        const int j = jb * 16 + 4 * lg;
+        const int j = t * 16 + 4 * lg;
 #pragma unroll
         for (int e = 0; e < 4; ++e) Sacc[m][e] *= Ec[j + e];
-        Sacc[m] = Mma<T>::template run<C>(Sacc[m], &Kbt[jb * 16 * LDC], LDC, &Ut[0], LDC, lane);
-        store4<T>(&Ssh[lr * LDK + j], Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
+        Sacc[m] = Mma<T>::template run<C>(Sacc[m], &Kbt[t * 16 * LDC], LDC, Uh, LDC, lane);
+        store4<T>(&Sh[lr * LDK + j], Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
       }
     }
     if (c + 1 < nct) {
-      rec_stage<NR, N16>(rr, rv, recb[b ^ 1], Vb[b ^ 1], tid, tid < NVV);
+      rec_stage<NR, N16, NTH>(rr, recb[b ^ 1], tid);
+      if (has_v) reinterpret_cast<u32x4*>(Vb[b ^ 1][h])[ts] = rv;
       if (c + 2 < nct) {
-        rec_load<NR, N16>(rr, rc + (int64_t)(c + 2) * R::BYTES, tid);
-        rv = v_load<T>(vc, c + 2, vr, vcg * VEC, Tlen, DV, tid < NVV);
+        rec_load<NR, N16, NTH>(rr, rc + (int64_t)(c + 2) * R::BYTES, tid);
+        rv = v_load<T>(vc, c + 2, vr, vcg * VEC, Tlen, DV, has_v);
       }
     }
   }
@@ -822,8 +840,7 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void vec_state_kernel(
     for (int m = 0; m < NST; ++m) {
       const int t = wave + NW * m;
       if (t < JB * IB) {
-        const int jb = t / IB;
-        const int j = jb * 16 + 4 * lg;
+        const int j = t * 16 + 4 * lg;
         *reinterpret_cast<float4*>(sT + st_off + (int64_t)lr * DK + j) =
             make_float4(Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
       }

@@ -388,10 +388,12 @@ int vec_split_launches(const void* q, const void* k, const void* v, const float*
 
 // Two-pass per-dimension gate.  The workspace holds the state carried from
 // one tile of chunks to the next (B*H*dk*dv floats), then the records of one
-// tile (B*H*tile records).  A tile is at most VEC2P_TILE chunks per sequence:
-// at the main workload's shape its records (138 MB) fit the 256 MB Infinity
-// Cache, where the second pass finds them.
-constexpr int64_t VEC2P_TILE = 64;
+// tile (B*H*tile records).  A tile is at most VEC2P_TILE chunks per sequence
+// (8192 tokens; the main workload's shape in one tile, 553 MB of records).
+// Measured at that shape: tiles of 64, 128, 256 chunks took 0.542, 0.524 and
+// 0.511 ms, longer tiles the same; at B=1, H=8, T=16384, d=64: 0.456, 0.411,
+// 0.384 ms, and 0.373 ms for 512.
+constexpr int64_t VEC2P_TILE = 256;
 
 int64_t vec2p_rec_bytes(int64_t dk, gdn_dtype dtype) {
   return vec_dispatch<true>(dtype, dk, [](auto t, auto dkc) {
@@ -406,7 +408,16 @@ int vec2p_launches_t(const void* q, const void* k, const void* v, const float* a
   float* carry = reinterpret_cast<float*>(ws);
   char* rec = ws + nseq * DK * dv * 4;
   const int64_t nch = (Tseq + gdn::vec::C - 1) / gdn::vec::C;
-  const int64_t nstate = nseq * (dv / gdn::vec::DVS);
+  // Two value slices per workgroup of the second pass (sharing the records
+  // in LDS) when that still fills the device: at the main workload's shape
+  // 0.63 -> 0.55 ms; with fewer sequences one slice per workgroup is faster
+  // (B=1, H=8, T=16384, d=64: 0.45 vs 0.55 ms).
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    (void)hipGetLastError();
+  const int sl = ncu > 0 && nseq * (dv / gdn::vec::DVS) >= 2 * (int64_t)ncu ? 2 : 1;
+  const int64_t nstate = nseq * (dv / (gdn::vec::DVS * sl));
   if (nseq * tile > 0x7fffffff || nstate > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
   const int xcd_map = (nseq % 8) == 0;
   int64_t c0 = 0;
@@ -420,16 +431,25 @@ int vec2p_launches_t(const void* q, const void* k, const void* v, const float* a
       cm.T = Tseq;
       cm.L = c0 * gdn::vec::C;
       cm.ws = reinterpret_cast<float*>(rec);
-      hipLaunchKernelGGL((gdn::vec::chunk_vec_kernel<T, DK, true, true>), dim3((unsigned)(nseq * n)),
+      // groups of consecutive chunks per sequence: about as many workgroups
+      // as the device holds at once (two per CU), each walking its chunks
+      int64_t ng = ncu > 0 ? 2 * (int64_t)ncu / nseq : n;
+      ng = ng < 1 ? 1 : ng > n ? n : ng;
+      hipLaunchKernelGGL((gdn::vec::chunk_vec_kernel<T, DK, true, true>), dim3((unsigned)(nseq * ng)),
                          dim3(gdn::vec::NT), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
                          static_cast<const T*>(v), alpha, beta, nullptr, static_cast<T*>(o), nullptr, cm, (int)dv, 0);
       if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
     }
     const float* in = c0 == 0 ? initial_state : carry;
     float* out = c0 + n >= nch ? final_state : carry;
-    hipLaunchKernelGGL((gdn::vec::vec_state_kernel<T, DK>), dim3((unsigned)nstate), dim3(gdn::vec::NT), 0, stream,
-                       static_cast<const T*>(v), rec, in, static_cast<T*>(o), out, (int)nseq, Tseq, c0, (int)n,
-                       (int)dv, xcd_map);
+    if (sl == 2)
+      hipLaunchKernelGGL((gdn::vec::vec_state_kernel<T, DK, 2>), dim3((unsigned)nstate), dim3(gdn::vec::NT * 2), 0,
+                         stream, static_cast<const T*>(v), rec, in, static_cast<T*>(o), out, (int)nseq, Tseq, c0,
+                         (int)n, (int)dv, xcd_map);
+    else
+      hipLaunchKernelGGL((gdn::vec::vec_state_kernel<T, DK, 1>), dim3((unsigned)nstate), dim3(gdn::vec::NT), 0,
+                         stream, static_cast<const T*>(v), rec, in, static_cast<T*>(o), out, (int)nseq, Tseq, c0,
+                         (int)n, (int)dv, xcd_map);
     if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
     c0 += n;
   } while (c0 < nch);

@@ -221,7 +221,7 @@ def test_vecgate_split_rejects_invalid_arguments_and_sizes_workspace(lib):
 def test_vecgate_2pass_rejects_invalid_arguments_and_sizes_workspace(lib):
     """The two-pass route's checks, all before any device call, and its
     workspace size: the carried state (B*H*dk*dv floats) plus one record per
-    chunk of the largest tile (at most 64 chunks per sequence); a record holds
+    chunk of the largest tile (at most 256 chunks per sequence); a record holds
     the scaled q and k, Kbar^T, (I+L)^-1, P, 2^(G_C) and beta of a 32-token
     chunk in their LDS layout, rounded up to whole KiB."""
     P = lambda x: None if x is None else ctypes.c_void_p(x)
@@ -244,7 +244,8 @@ def test_vecgate_2pass_rejects_invalid_arguments_and_sizes_workspace(lib):
     rec = {(1, 64): 20480, (1, 128): 33792, (0, 64): 36864, (0, 128): 62464}
     for (dt, d), r in rec.items():
         assert f(1, 1, 1000, d, d, 32, dt) == d * d * 4 + 32 * r              # 32 chunks: one tile
-        assert f(4, 16, 8192, d, d, 32, dt) == 64 * (d * d * 4 + 64 * r)      # tiles of 64 chunks
+        assert f(4, 16, 8192, d, d, 32, dt) == 64 * (d * d * 4 + 256 * r)     # one tile of 256 chunks
+        assert f(1, 2, 20000, d, d, 32, dt) == 2 * (d * d * 4 + 256 * r)      # 625 chunks: tiles of 256
         assert f(1, 1, 0, d, d, 32, dt) == d * d * 4 + r
     assert f(1, 1, 1000, 64, 64, 64, 1) == 0
     assert f(1, 1, 1000, 96, 96, 32, 1) == 0

@@ -24,10 +24,15 @@ CASES = [
     (2, 1, 33, 128, True, "default", "bf16"),
     (1, 3, 1000, 64, True, "default", "bf16"),
     (2, 2, 777, 128, True, "slow", "bf16"),
-    (1, 2, 5000, 128, True, "slow", "bf16"),    # 157 chunks: three tiles of at most 64
+    (1, 2, 12000, 128, True, "slow", "bf16"),   # 375 chunks: two tiles of at most 256
     (1, 2, 300, 128, True, "fast", "bf16"),
-    (2, 1, 2500, 64, True, "resets", "bf16"),   # two tiles
+    (2, 1, 2500, 64, True, "resets", "bf16"),
     (8, 1, 256, 128, True, "default", "bf16"),  # 8 sequences: XCD-grouped mapping
+    # enough value slices to fill the device twice: two slices per workgroup
+    # of the second pass
+    (8, 8, 100, 128, True, "default", "bf16"),
+    (8, 16, 70, 64, True, "resets", "bf16"),
+    (8, 8, 40, 128, True, "default", "f32"),
     (1, 1, 50, 64, True, "default", "f32"),
     (2, 1, 2100, 128, False, "default", "f32"),
     (1, 2, 1200, 64, True, "slow", "f32"),
@@ -39,6 +44,11 @@ def _inputs(B, H, T, d, dtype, init, gate, seed):
     x = inputs.make_fwd_inputs(B, H, T, d, dtype, seed=seed, init_state=init)
     x["alpha"] = inputs.make_vec_alpha(B, H, T, d, seed=seed + 100, gate=gate)
     return x
+
+
+def _record_bytes(d, dtype=torch.bfloat16):
+    # the workspace of one sequence and one chunk: the carried state and one record
+    return gdn_chunk_fwd_vecgate_2pass_workspace(1, 1, 32, d, d, 32, dtype) - d * d * 4
 
 
 def _run2(xd, **kw):
@@ -67,16 +77,15 @@ def test_2pass_against_oracle_and_single_pass(case):
 
 
 def test_2pass_tile_length_does_not_change_the_result():
-    """Workspaces for tiles of 1, 3 and 64 chunks (B=2, H=2, T=3000: 94 chunks)
+    """Workspaces for tiles of 1, 3, 64 and 94 chunks (B=2, H=2, T=3000: 94 chunks)
     give the same outputs and final state bit for bit; the state passes from
     tile to tile through the workspace in fp32."""
     B, H, T, d = 2, 2, 3000, 128
     x = _inputs(B, H, T, d, "bf16", True, "default", seed=1901)
     xd = to_dev(x)
-    full = gdn_chunk_fwd_vecgate_2pass_workspace(B, H, T, d, d, 32, torch.bfloat16)
-    rec = (full - B * H * d * d * 4) // (B * H * 64)
+    rec = _record_bytes(d)
     ref = None
-    for tile in (1, 3, 64):
+    for tile in (1, 3, 64, 94):
         ws = torch.empty(B * H * (d * d * 4 + tile * rec), dtype=torch.uint8, device="cuda")
         print("  tile", tile, "workspace", ws.numel(), flush=True)
         o, sT = _run2(xd, workspace=ws)
@@ -110,8 +119,7 @@ def test_2pass_aliasing_and_errors():
     torch.cuda.synchronize()
     assert s2.data_ptr() == s.data_ptr()
     assert torch.equal(o, ref_o) and torch.equal(s, ref_s)
-    need = gdn_chunk_fwd_vecgate_2pass_workspace(1, 2, 2500, 64, 64, 32, torch.bfloat16)
-    rec = (need - 2 * 64 * 64 * 4) // (2 * 64)
+    rec = _record_bytes(64)
     small = torch.empty(2 * (64 * 64 * 4 + rec) - 16, dtype=torch.uint8, device="cuda")
     with pytest.raises(GDNError) as ei:
         gdn_chunk_fwd_vecgate_2pass(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None, workspace=small)
