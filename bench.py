@@ -252,21 +252,28 @@ def time_gla(torch, xd, launches=50):
 
 
 def time_vecgate(torch, xd, launches=10):
-    """The chunked per-dimension-gate route (gdn_chunk_fwd_vecgate) on the main
-    workload's q, k, v, beta with a gate drawn per token and key dimension
-    (the workloads' gate law): mean launch time and its HBM-roofline fraction
-    (its algorithmic bytes count the [B,H,T,d_k] fp32 gate)."""
+    """The chunked per-dimension-gate routes on the main workload's q, k, v,
+    beta with a gate drawn per token and key dimension (the workloads' gate
+    law): mean times of the two-pass route (gdn_chunk_fwd_vecgate_2pass, the
+    reported one, with its HBM-roofline fraction; its algorithmic bytes count
+    the [B,H,T,d_k] fp32 gate), the single-pass route and the scan route."""
     from gated_deltanet_sequence_amd import inputs
-    from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd_vecgate, gdn_scan_fwd_vecgate,
+    from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd_vecgate, gdn_chunk_fwd_vecgate_2pass,
+                                                     gdn_chunk_fwd_vecgate_2pass_workspace, gdn_scan_fwd_vecgate,
                                                      gdn_scan_fwd_workspace)
     B, H, T, d = xd["q"].shape
     av = inputs.make_vec_alpha(B, H, T, d, seed=MAIN["seed"] + 200).to(xd["q"].device)
     o = torch.empty_like(xd["v"])
     sT = torch.empty((B, H, d, d), dtype=torch.float32, device=xd["q"].device)
     ws = torch.empty(gdn_scan_fwd_workspace(B, H, T, d, d, torch.bfloat16), dtype=torch.uint8, device=xd["q"].device)
+    n2 = gdn_chunk_fwd_vecgate_2pass_workspace(B, H, T, d, d, 32, torch.bfloat16)
+    ws2 = torch.empty(n2, dtype=torch.uint8, device=xd["q"].device)
     stream = torch.cuda.current_stream()
     times = {}
-    for name, f in (("chunked", lambda: gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"], None,
+    for name, f in (("two_pass", lambda: gdn_chunk_fwd_vecgate_2pass(xd["q"], xd["k"], xd["v"], av, xd["beta"],
+                                                                     None, o=o, final_state=sT, workspace=ws2,
+                                                                     stream=stream)),
+                    ("chunked", lambda: gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"], None,
                                                               o=o, final_state=sT, stream=stream)),
                     ("scan", lambda: gdn_scan_fwd_vecgate(xd["q"], xd["k"], xd["v"], av, xd["beta"], None,
                                                           o=o, final_state=sT, workspace=ws, stream=stream))):
@@ -279,13 +286,14 @@ def time_vecgate(torch, xd, launches=10):
         e1.record(stream)
         torch.cuda.synchronize()
         times[name] = e0.elapsed_time(e1) / launches
-    ms = times["chunked"]
+    ms = times["two_pass"]
     alg = alg_bytes_main(B, H, T, d) + B * H * T * (d - 1) * 4  # the gate is d_k floats per token, not one
-    del av, ws
-    return {"workload": "per-dimension gate, chunked route (32-token chunks), on the main workload's shape: "
-                        "B=4, H=16, T=8192, d_k=d_v=128, bf16 q/k/v, fp32 alpha [B,H,T,d_k]",
+    del av, ws, ws2
+    return {"workload": "per-dimension gate, two-pass chunked route (32-token chunks), on the main workload's "
+                        "shape: B=4, H=16, T=8192, d_k=d_v=128, bf16 q/k/v, fp32 alpha [B,H,T,d_k]",
             "ms": ms, "tokens_per_s": B * T / (ms * 1e-3), "alg_bytes": alg,
-            "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "scan_route_ms": times["scan"]}
+            "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "workspace_bytes": n2,
+            "single_pass_ms": times["chunked"], "scan_route_ms": times["scan"]}
 
 
 ROUTES = dict(B=1, H=8, T=16384, d=64, seed=6)
@@ -299,6 +307,8 @@ def time_routes(torch, dev, launches=5):
     from gated_deltanet_sequence_amd import inputs
     from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd, gdn_chunk_fwd_split,
                                                      gdn_chunk_fwd_split_workspace, gdn_chunk_fwd_vecgate,
+                                                     gdn_chunk_fwd_vecgate_2pass,
+                                                     gdn_chunk_fwd_vecgate_2pass_workspace,
                                                      gdn_chunk_fwd_vecgate_split,
                                                      gdn_chunk_fwd_vecgate_split_workspace,
                                                      gdn_recurrent_step, gdn_scan_fwd, gdn_scan_fwd_vecgate,
@@ -310,6 +320,8 @@ def time_routes(torch, dev, launches=5):
     wsp = torch.empty(max(gdn_chunk_fwd_split_workspace(B, H, T, d, d, 64, torch.bfloat16), 16),
                       dtype=torch.uint8, device=dev)
     wsv = torch.empty(max(gdn_chunk_fwd_vecgate_split_workspace(B, H, T, d, d, 32, torch.bfloat16), 16),
+                      dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(gdn_chunk_fwd_vecgate_2pass_workspace(B, H, T, d, d, 32, torch.bfloat16),
                       dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     a = (xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], None)
@@ -329,6 +341,9 @@ def time_routes(torch, dev, launches=5):
                                                                                 xd["beta"], None, stream=stream)),
                     ("chunked_vecgate_split", lambda: gdn_chunk_fwd_vecgate_split(xd["q"], xd["k"], xd["v"], avd,
                                                                                   xd["beta"], None, workspace=wsv,
+                                                                                  stream=stream)),
+                    ("chunked_vecgate_2pass", lambda: gdn_chunk_fwd_vecgate_2pass(xd["q"], xd["k"], xd["v"], avd,
+                                                                                  xd["beta"], None, workspace=ws2,
                                                                                   stream=stream))):
         settle_clocks(torch, f)
         e0 = torch.cuda.Event(enable_timing=True)
