@@ -754,23 +754,33 @@ __global__ __launch_bounds__(NT * SL, SL == 1 && sizeof(T) == 2 ? 2 : 1) void ve
     }
   }
 
-  // register staging of a chunk's record (all threads) and of each slice's
-  // V (V rows past the end of the sequence are written as zero)
-  u32x4 rr[NR], rv = u32x4{0u, 0u, 0u, 0u};
+  // register staging of the records (all threads) and of each slice's V (V
+  // rows past the end of the sequence are written as zero), two chunks ahead:
+  // while chunk c is computed, the records of chunks c+1 (set A) and c+2 (set
+  // B) are in flight; at its end, c+1 goes to LDS and c+3 is requested into
+  // the set that held it.  The loop is unrolled by two so that the two
+  // register sets stay static.
+  u32x4 rA[NR], rB[NR], vA = u32x4{0u, 0u, 0u, 0u}, vB = u32x4{0u, 0u, 0u, 0u};
   const bool has_v = ts < NVV;
   const int vr = ts / (DVS / VEC), vcg = ts % (DVS / VEC);  // token, 16-byte column group of this V vector
   if (nct > 0) {
-    rec_load<NR, N16, NTH>(rr, rc, tid);
-    rv = v_load<T>(vc, 0, vr, vcg * VEC, Tlen, DV, has_v);
-    rec_stage<NR, N16, NTH>(rr, recb[0], tid);
-    if (has_v) reinterpret_cast<u32x4*>(Vb[0][h])[ts] = rv;
+    rec_load<NR, N16, NTH>(rA, rc, tid);
+    vA = v_load<T>(vc, 0, vr, vcg * VEC, Tlen, DV, has_v);
+    rec_stage<NR, N16, NTH>(rA, recb[0], tid);
+    if (has_v) reinterpret_cast<u32x4*>(Vb[0][h])[ts] = vA;
   }
   if (nct > 1) {
-    rec_load<NR, N16, NTH>(rr, rc + R::BYTES, tid);
-    rv = v_load<T>(vc, 1, vr, vcg * VEC, Tlen, DV, has_v);
+    rec_load<NR, N16, NTH>(rA, rc + R::BYTES, tid);
+    vA = v_load<T>(vc, 1, vr, vcg * VEC, Tlen, DV, has_v);
+  }
+  if (nct > 2) {
+    rec_load<NR, N16, NTH>(rB, rc + 2 * R::BYTES, tid);
+    vB = v_load<T>(vc, 2, vr, vcg * VEC, Tlen, DV, has_v);
   }
 
-  for (int c = 0; c < nct; ++c) {
+  // one chunk: its products, then the next record from set `nx` to LDS and
+  // the record three chunks ahead into `nx`
+  auto chunk = [&](int c, u32x4 (&nx)[NR], u32x4& nv) {
     const int b = c & 1;
     const T* Qs = reinterpret_cast<const T*>(recb[b] + R::QS);
     const T* Kr = reinterpret_cast<const T*>(recb[b] + R::KR);
@@ -826,13 +836,17 @@ __global__ __launch_bounds__(NT * SL, SL == 1 && sizeof(T) == 2 ? 2 : 1) void ve
       }
     }
     if (c + 1 < nct) {
-      rec_stage<NR, N16, NTH>(rr, recb[b ^ 1], tid);
-      if (has_v) reinterpret_cast<u32x4*>(Vb[b ^ 1][h])[ts] = rv;
-      if (c + 2 < nct) {
-        rec_load<NR, N16, NTH>(rr, rc + (int64_t)(c + 2) * R::BYTES, tid);
-        rv = v_load<T>(vc, c + 2, vr, vcg * VEC, Tlen, DV, has_v);
+      rec_stage<NR, N16, NTH>(nx, recb[b ^ 1], tid);
+      if (has_v) reinterpret_cast<u32x4*>(Vb[b ^ 1][h])[ts] = nv;
+      if (c + 3 < nct) {
+        rec_load<NR, N16, NTH>(nx, rc + (int64_t)(c + 3) * R::BYTES, tid);
+        nv = v_load<T>(vc, c + 3, vr, vcg * VEC, Tlen, DV, has_v);
       }
     }
+  };
+  for (int c = 0; c < nct; c += 2) {
+    chunk(c, rA, vA);
+    if (c + 1 < nct) chunk(c + 1, rB, vB);
   }
 
   if (sT) {
