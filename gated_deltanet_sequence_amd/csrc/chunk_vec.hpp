@@ -666,10 +666,14 @@ __device__ __forceinline__ u32x4 v_load(const T* vc, int c, int r, int col, int6
   return has_v && tk < Tlen ? *reinterpret_cast<const u32x4*>(vc + tk * DV + col) : u32x4{0u, 0u, 0u, 0u};
 }
 
-// Second pass of the two-pass evaluation: one workgroup per (sequence, SL
-// consecutive 16-row value slices) walks the chunks [c0, c0 + nct) of the
-// tile from their records (rec: [sequence][chunk of the tile] records of
-// VecRec<T, DK>::BYTES), each slice's state in the MFMA accumulators of its
+// Second pass of the two-pass evaluation: one workgroup per (chain, SL
+// consecutive 16-row value slices), a chain being a sequence's chunks
+// [c0, c0 + nct) of the tile or, in a sequence split (cm), one segment of
+// them, walks its chunks from their records (rec: [sequence][chunk of the
+// tile] records of VecRec<T, DK>::BYTES; in a split the segment states from
+// a zero start and the segment transitions from the identity with V read as
+// zero, then every segment from its start state, with cm.ws laid out as for
+// the single-pass split), each slice's state in the MFMA accumulators of its
 // own four waves; the slices of a workgroup share the records in LDS.  Per
 // chunk, three barrier-separated steps: Y = diag(beta) (V - K~ S^T) (waves
 // 0, 1 of a slice) beside the inter-chunk output S Q~^T (waves 2, 3); U = Ti Y
@@ -681,7 +685,7 @@ __device__ __forceinline__ u32x4 v_load(const T* vc, int c, int r, int col, int6
 template <class T, int DK, int SL>
 __global__ __launch_bounds__(NT * SL, SL == 1 && sizeof(T) == 2 ? 2 : 1) void vec_state_kernel(
     const T* __restrict__ v, const char* __restrict__ rec, const float* s0, T* __restrict__ o,
-    float* sT, int nseq, int64_t Tseq, int64_t c0, int nct, int DV, int xcd_map) {
+    float* sT, int nseq, int64_t Tseq, int64_t c0, int nct, int DV, int xcd_map, gdn::pipe::ChainMap cm) {
   using Sm = Smem<T, DK>;
   using R = VecRec<T, DK>;
   constexpr int NTH = NT * SL;
@@ -714,27 +718,55 @@ __global__ __launch_bounds__(NT * SL, SL == 1 && sizeof(T) == 2 ? 2 : 1) void ve
   const int lg = lane >> 4;
 
   const int NSG = DV / (DVS * SL);  // slice groups per sequence
-  int seq, sg;
+  int chain, sg;
   {
     const int w = blockIdx.x;
     if (xcd_map) {
       const int x = w & 7, r = w >> 3;
       sg = r % NSG;
-      seq = (r / NSG) * 8 + x;
+      chain = (r / NSG) * 8 + x;
     } else {
-      seq = w / NSG;
+      chain = w / NSG;
       sg = w % NSG;
     }
   }
-  if (seq >= nseq) return;
+  if (chain >= gdn::pipe::map_chains(cm)) return;
   const int slice = sg * SL + h;
   const int64_t dd = (int64_t)DK * DV;
-  const int64_t st_off = (int64_t)seq * dd + (int64_t)slice * DVS * DK;
-  const int64_t tok0 = (int64_t)seq * Tseq + c0 * C;  // first token of the tile in memory
-  const int64_t Tlen = Tseq - c0 * C;                  // tokens of the sequence from there
+
+  // this chain's sequence, chunks of the tile, start and end state, and
+  // whether it reads V and writes output (cm.mode as for chunk_vec_kernel:
+  // whole sequences, or the first and last launch of a sequence split, whose
+  // segments are cm.L tokens; the tile then holds the whole sequence)
+  int seq = chain, cf = 0, ncc = nct;
+  bool v_on = true, o_on = true, ident = false;
+  const float* s0c = s0 ? s0 + (int64_t)chain * dd : nullptr;
+  float* sTc = sT ? sT + (int64_t)chain * dd : nullptr;
+  if (cm.mode == gdn::pipe::MAP_SPLIT_A) {
+    const int per = nseq * (cm.G - 1);
+    const int kind = chain / per, r = chain % per;
+    seq = r / (cm.G - 1);
+    ncc = (int)(cm.L / C);
+    cf = (r % (cm.G - 1)) * ncc;
+    o_on = false;
+    v_on = kind == 0;
+    ident = kind == 1;
+    s0c = nullptr;
+    sTc = cm.ws + ((int64_t)kind * per + r) * dd;
+  } else if (cm.mode == gdn::pipe::MAP_SPLIT_C) {
+    seq = chain / cm.G;
+    const int g = chain % cm.G;
+    cf = g * (int)(cm.L / C);
+    ncc = g == cm.G - 1 ? nct - cf : (int)(cm.L / C);
+    s0c = cm.ws + (2 * (int64_t)nseq * (cm.G - 1) + (int64_t)seq * cm.G + g) * dd;
+    sTc = g == cm.G - 1 && sT ? sT + (int64_t)seq * dd : nullptr;
+  }
+  const int64_t st_off = (int64_t)slice * DVS * DK;          // this slice's rows within a state
+  const int64_t tok0 = (int64_t)seq * Tseq + (c0 + cf) * C;  // first token of the chain in memory
+  const int64_t Tlen = Tseq - (c0 + cf) * C;                 // tokens of the sequence from there
   const T* vc = v + tok0 * DV + slice * DVS;
   T* oc = o + tok0 * DV + slice * DVS;
-  const char* rc = rec + (int64_t)seq * nct * R::BYTES;
+  const char* rc = rec + ((int64_t)seq * nct + cf) * R::BYTES;
   T* Sh = Ssh[h];
   T* Yh = Yt[h];
   T* Uh = Ut[h];
@@ -746,8 +778,11 @@ __global__ __launch_bounds__(NT * SL, SL == 1 && sizeof(T) == 2 ? 2 : 1) void ve
     Sacc[m] = zero4();
     if (t < JB * IB) {
       const int j = t * 16 + 4 * lg;
-      if (s0) {
-        const float4 s4 = *reinterpret_cast<const float4*>(s0 + st_off + (int64_t)lr * DK + j);
+      if (ident) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sacc[m][e] = slice * DVS + lr == j + e ? 1.f : 0.f;
+      } else if (s0c) {
+        const float4 s4 = *reinterpret_cast<const float4*>(s0c + st_off + (int64_t)lr * DK + j);
         Sacc[m] = f32x4{s4.x, s4.y, s4.z, s4.w};
       }
       store4<T>(&Sh[lr * LDK + j], Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
@@ -761,21 +796,22 @@ __global__ __launch_bounds__(NT * SL, SL == 1 && sizeof(T) == 2 ? 2 : 1) void ve
   // the set that held it.  The loop is unrolled by two so that the two
   // register sets stay static.
   u32x4 rA[NR], rB[NR], vA = u32x4{0u, 0u, 0u, 0u}, vB = u32x4{0u, 0u, 0u, 0u};
-  const bool has_v = ts < NVV;
+  const bool has_v = ts < NVV;       // this thread stages a V vector
+  const bool read_v = has_v && v_on;  // ... read from v (else zero)
   const int vr = ts / (DVS / VEC), vcg = ts % (DVS / VEC);  // token, 16-byte column group of this V vector
-  if (nct > 0) {
+  if (ncc > 0) {
     rec_load<NR, N16, NTH>(rA, rc, tid);
-    vA = v_load<T>(vc, 0, vr, vcg * VEC, Tlen, DV, has_v);
+    vA = v_load<T>(vc, 0, vr, vcg * VEC, Tlen, DV, read_v);
     rec_stage<NR, N16, NTH>(rA, recb[0], tid);
     if (has_v) reinterpret_cast<u32x4*>(Vb[0][h])[ts] = vA;
   }
-  if (nct > 1) {
+  if (ncc > 1) {
     rec_load<NR, N16, NTH>(rA, rc + R::BYTES, tid);
-    vA = v_load<T>(vc, 1, vr, vcg * VEC, Tlen, DV, has_v);
+    vA = v_load<T>(vc, 1, vr, vcg * VEC, Tlen, DV, read_v);
   }
-  if (nct > 2) {
+  if (ncc > 2) {
     rec_load<NR, N16, NTH>(rB, rc + 2 * R::BYTES, tid);
-    vB = v_load<T>(vc, 2, vr, vcg * VEC, Tlen, DV, has_v);
+    vB = v_load<T>(vc, 2, vr, vcg * VEC, Tlen, DV, read_v);
   }
 
   // one chunk: its products, then the next record from set `nx` to LDS and
@@ -822,7 +858,7 @@ __global__ __launch_bounds__(NT * SL, SL == 1 && sizeof(T) == 2 ? 2 : 1) void ve
       const int rb = wave - 2;
       Oacc = Mma<T>::template run<C>(Oacc, Uh, LDC, &Pm[rb * 16 * LDC], LDC, lane);
       const int64_t tk = (int64_t)c * C + rb * 16 + lr;
-      if (tk < Tlen) store4<T>(oc + tk * DV + 4 * lg, Oacc[0], Oacc[1], Oacc[2], Oacc[3]);
+      if (o_on && tk < Tlen) store4<T>(oc + tk * DV + 4 * lg, Oacc[0], Oacc[1], Oacc[2], Oacc[3]);
     }
 #pragma unroll
     for (int m = 0; m < NST; ++m) {
@@ -835,27 +871,27 @@ __global__ __launch_bounds__(NT * SL, SL == 1 && sizeof(T) == 2 ? 2 : 1) void ve
         store4<T>(&Sh[lr * LDK + j], Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
       }
     }
-    if (c + 1 < nct) {
+    if (c + 1 < ncc) {
       rec_stage<NR, N16, NTH>(nx, recb[b ^ 1], tid);
       if (has_v) reinterpret_cast<u32x4*>(Vb[b ^ 1][h])[ts] = nv;
-      if (c + 3 < nct) {
+      if (c + 3 < ncc) {
         rec_load<NR, N16, NTH>(nx, rc + (int64_t)(c + 3) * R::BYTES, tid);
-        nv = v_load<T>(vc, c + 3, vr, vcg * VEC, Tlen, DV, has_v);
+        nv = v_load<T>(vc, c + 3, vr, vcg * VEC, Tlen, DV, read_v);
       }
     }
   };
-  for (int c = 0; c < nct; c += 2) {
+  for (int c = 0; c < ncc; c += 2) {
     chunk(c, rA, vA);
-    if (c + 1 < nct) chunk(c + 1, rB, vB);
+    if (c + 1 < ncc) chunk(c + 1, rB, vB);
   }
 
-  if (sT) {
+  if (sTc) {
 #pragma unroll
     for (int m = 0; m < NST; ++m) {
       const int t = wave + NW * m;
       if (t < JB * IB) {
         const int j = t * 16 + 4 * lg;
-        *reinterpret_cast<float4*>(sT + st_off + (int64_t)lr * DK + j) =
+        *reinterpret_cast<float4*>(sTc + st_off + (int64_t)lr * DK + j) =
             make_float4(Sacc[m][0], Sacc[m][1], Sacc[m][2], Sacc[m][3]);
       }
     }

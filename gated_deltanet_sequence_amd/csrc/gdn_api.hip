@@ -401,59 +401,155 @@ int64_t vec2p_rec_bytes(int64_t dk, gdn_dtype dtype) {
   });
 }
 
+int device_cus() {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return ncu;
+}
+
+// The first pass over chunks [c0, c0 + n) of every sequence: groups of
+// consecutive chunks per sequence, about as many workgroups as the device
+// holds at once (two per CU), each walking its chunks.
+template <class T, int DK>
+int vec2p_prep(const void* q, const void* k, const void* v, const float* alpha, const float* beta, void* o,
+               int64_t nseq, int64_t Tseq, int64_t dv, char* rec, int64_t c0, int64_t n, int ncu,
+               hipStream_t stream) {
+  gdn::pipe::ChainMap cm{};
+  cm.mode = gdn::vec::MAP_PREP;
+  cm.nseq = (int)nseq;
+  cm.G = (int)n;
+  cm.T = Tseq;
+  cm.L = c0 * gdn::vec::C;
+  cm.ws = reinterpret_cast<float*>(rec);
+  int64_t ng = ncu > 0 ? 2 * (int64_t)ncu / nseq : n;
+  ng = ng < 1 ? 1 : ng > n ? n : ng;
+  if (nseq * ng > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((gdn::vec::chunk_vec_kernel<T, DK, true, true>), dim3((unsigned)(nseq * ng)),
+                     dim3(gdn::vec::NT), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
+                     static_cast<const T*>(v), alpha, beta, nullptr, static_cast<T*>(o), nullptr, cm, (int)dv, 0);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+// The second pass over the chains of cm (cm.nseq = the sequences) with sl
+// value slices per workgroup.
+template <class T, int DK>
+int vec2p_state(int sl, const void* v, const char* rec, const float* in, void* o, float* out, int64_t nseq,
+                int64_t Tseq, int64_t c0, int64_t n, int64_t dv, const gdn::pipe::ChainMap& cm,
+                hipStream_t stream) {
+  const int64_t nchain = gdn::pipe::map_chains(cm);
+  const int64_t nblocks = nchain * (dv / (gdn::vec::DVS * sl));
+  if (nblocks > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+  const int xcd_map = (nchain % 8) == 0;
+  if (sl == 2)
+    hipLaunchKernelGGL((gdn::vec::vec_state_kernel<T, DK, 2>), dim3((unsigned)nblocks), dim3(gdn::vec::NT * 2), 0,
+                       stream, static_cast<const T*>(v), rec, in, static_cast<T*>(o), out, (int)nseq, Tseq, c0,
+                       (int)n, (int)dv, xcd_map, cm);
+  else
+    hipLaunchKernelGGL((gdn::vec::vec_state_kernel<T, DK, 1>), dim3((unsigned)nblocks), dim3(gdn::vec::NT), 0,
+                       stream, static_cast<const T*>(v), rec, in, static_cast<T*>(o), out, (int)nseq, Tseq, c0,
+                       (int)n, (int)dv, xcd_map, cm);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+// Sequence split of the two-pass route (few sequences: the second pass is a
+// chain of T/32 chunks per workgroup): as for the single-pass split, the
+// first G-1 segments from a zero start and from the identity (V read as
+// zero), the combine step, then every segment from its start state.  The
+// records of the whole sequences are written once by the first pass.  G is
+// the largest value whose first launch fits the device at the second pass's
+// occupancy, with segments of at least VEC2P_MIN_SEG tokens; below 3, no split.
+constexpr int64_t VEC2P_MIN_SEG = 256;
+void vec2p_split_plan(int64_t nseq, int64_t T, int64_t dk, int64_t dv, gdn_dtype dtype, int& G, int64_t& L) {
+  G = 1;
+  L = T;
+  const int ncu = device_cus();
+  if (ncu <= 0) return;
+  const int per_cu = vec_dispatch<true>(dtype, dk, [&](auto t, auto dkc) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(&gdn::vec::vec_state_kernel<decltype(t), decltype(dkc)::value, 1>),
+            gdn::vec::NT, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      n = 0;
+    }
+    return n;
+  });
+  if (per_cu <= 0) return;
+  const int64_t ns = dv / gdn::vec::DVS;
+  int64_t g = 1 + (int64_t)per_cu * ncu / (2 * nseq * ns);
+  g = g < T / VEC2P_MIN_SEG ? g : T / VEC2P_MIN_SEG;
+  if (g < 3) return;
+  const int64_t C = gdn::vec::C;
+  L = ((T + g - 1) / g + C - 1) / C * C;
+  G = (int)((T + L - 1) / L);
+  if (G < 3) {
+    G = 1;
+    L = T;
+  }
+}
+
 template <class T, int DK>
 int vec2p_launches_t(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                      const float* initial_state, void* o, float* final_state, int64_t nseq, int64_t Tseq,
-                     int64_t dv, char* ws, int64_t tile, hipStream_t stream) {
+                     int64_t dv, char* ws, int64_t tile, int G, int64_t L, hipStream_t stream) {
+  const int64_t nch = (Tseq + gdn::vec::C - 1) / gdn::vec::C;
+  const int ncu = device_cus();
+  if (G >= 3) {
+    // split: ws = the split's states, then the records of every chunk
+    float* sws = reinterpret_cast<float*>(ws);
+    char* rec = ws + split_ws_bytes(nseq, G, DK);
+    int r = vec2p_prep<T, DK>(q, k, v, alpha, beta, o, nseq, Tseq, dv, rec, 0, nch, ncu, stream);
+    if (r != GDN_OK) return r;
+    gdn::pipe::ChainMap cm{};
+    cm.nseq = (int)nseq;
+    cm.G = G;
+    cm.T = Tseq;
+    cm.L = L;
+    cm.ws = sws;
+    cm.mode = gdn::pipe::MAP_SPLIT_A;
+    r = vec2p_state<T, DK>(1, v, rec, nullptr, o, nullptr, nseq, Tseq, 0, nch, dv, cm, stream);
+    if (r != GDN_OK) return r;
+    r = launch_combine(DK, initial_state, sws, nseq, G, stream);
+    if (r != GDN_OK) return r;
+    cm.mode = gdn::pipe::MAP_SPLIT_C;
+    return vec2p_state<T, DK>(1, v, rec, nullptr, o, final_state, nseq, Tseq, 0, nch, dv, cm, stream);
+  }
+  // tiles: ws = the carried state, then the records of one tile.  Two value
+  // slices per workgroup of the second pass (sharing the records in LDS) when
+  // that still fills the device: at the main workload's shape 0.63 -> 0.55
+  // ms; with fewer sequences one slice per workgroup is faster (B=1, H=8,
+  // T=16384, d=64: 0.45 vs 0.55 ms).
   float* carry = reinterpret_cast<float*>(ws);
   char* rec = ws + nseq * DK * dv * 4;
-  const int64_t nch = (Tseq + gdn::vec::C - 1) / gdn::vec::C;
-  // Two value slices per workgroup of the second pass (sharing the records
-  // in LDS) when that still fills the device: at the main workload's shape
-  // 0.63 -> 0.55 ms; with fewer sequences one slice per workgroup is faster
-  // (B=1, H=8, T=16384, d=64: 0.45 vs 0.55 ms).
-  int dev = 0, ncu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    (void)hipGetLastError();
   const int sl = ncu > 0 && nseq * (dv / gdn::vec::DVS) >= 2 * (int64_t)ncu ? 2 : 1;
-  const int64_t nstate = nseq * (dv / (gdn::vec::DVS * sl));
-  if (nseq * tile > 0x7fffffff || nstate > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
-  const int xcd_map = (nseq % 8) == 0;
+  gdn::pipe::ChainMap cm{};
+  cm.mode = gdn::pipe::MAP_SEQ;
+  cm.nseq = (int)nseq;
   int64_t c0 = 0;
   do {
     const int64_t n = tile < nch - c0 ? tile : nch - c0;  // 0 when there are no chunks
     if (n > 0) {
-      gdn::pipe::ChainMap cm{};
-      cm.mode = gdn::vec::MAP_PREP;
-      cm.nseq = (int)nseq;
-      cm.G = (int)n;
-      cm.T = Tseq;
-      cm.L = c0 * gdn::vec::C;
-      cm.ws = reinterpret_cast<float*>(rec);
-      // groups of consecutive chunks per sequence: about as many workgroups
-      // as the device holds at once (two per CU), each walking its chunks
-      int64_t ng = ncu > 0 ? 2 * (int64_t)ncu / nseq : n;
-      ng = ng < 1 ? 1 : ng > n ? n : ng;
-      hipLaunchKernelGGL((gdn::vec::chunk_vec_kernel<T, DK, true, true>), dim3((unsigned)(nseq * ng)),
-                         dim3(gdn::vec::NT), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
-                         static_cast<const T*>(v), alpha, beta, nullptr, static_cast<T*>(o), nullptr, cm, (int)dv, 0);
-      if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
+      const int r = vec2p_prep<T, DK>(q, k, v, alpha, beta, o, nseq, Tseq, dv, rec, c0, n, ncu, stream);
+      if (r != GDN_OK) return r;
     }
     const float* in = c0 == 0 ? initial_state : carry;
     float* out = c0 + n >= nch ? final_state : carry;
-    if (sl == 2)
-      hipLaunchKernelGGL((gdn::vec::vec_state_kernel<T, DK, 2>), dim3((unsigned)nstate), dim3(gdn::vec::NT * 2), 0,
-                         stream, static_cast<const T*>(v), rec, in, static_cast<T*>(o), out, (int)nseq, Tseq, c0,
-                         (int)n, (int)dv, xcd_map);
-    else
-      hipLaunchKernelGGL((gdn::vec::vec_state_kernel<T, DK, 1>), dim3((unsigned)nstate), dim3(gdn::vec::NT), 0,
-                         stream, static_cast<const T*>(v), rec, in, static_cast<T*>(o), out, (int)nseq, Tseq, c0,
-                         (int)n, (int)dv, xcd_map);
-    if (hipGetLastError() != hipSuccess) return GDN_ERR_HIP;
+    const int r = vec2p_state<T, DK>(sl, v, rec, in, o, out, nseq, Tseq, c0, n, dv, cm, stream);
+    if (r != GDN_OK) return r;
     c0 += n;
   } while (c0 < nch);
   return GDN_OK;
+}
+
+// Workspace of the two-pass route: with a split, the split's states and the
+// records of whole sequences; else the carried state and one tile's records.
+int64_t vec2p_split_bytes(int64_t nseq, int64_t T, int G, int64_t dk, gdn_dtype dtype) {
+  const int64_t nch = (T + gdn::vec::C - 1) / gdn::vec::C;
+  return (int64_t)split_ws_bytes(nseq, G, dk) + nseq * nch * vec2p_rec_bytes(dk, dtype);
 }
 }  // namespace
 
@@ -589,7 +685,15 @@ size_t gdn_chunk_fwd_vecgate_2pass_workspace(int64_t B, int64_t H, int64_t T, in
     return 0;
   const int64_t nch = (T + gdn::vec::C - 1) / gdn::vec::C;
   const int64_t tile = nch < VEC2P_TILE ? (nch > 0 ? nch : 1) : VEC2P_TILE;
-  return (size_t)(B * H * (dk * dv * 4 + tile * vec2p_rec_bytes(dk, dtype)));
+  int64_t need = B * H * (dk * dv * 4 + tile * vec2p_rec_bytes(dk, dtype));
+  int G = 1;
+  int64_t L = T;
+  if (T > 0) vec2p_split_plan(B * H, T, dk, dv, dtype, G, L);
+  if (G >= 3) {
+    const int64_t split = vec2p_split_bytes(B * H, T, G, dk, dtype);
+    need = split > need ? split : need;
+  }
+  return (size_t)need;
 }
 
 int gdn_chunk_fwd_vecgate_2pass(const void* q, const void* k, const void* v, const float* alpha,
@@ -607,11 +711,22 @@ int gdn_chunk_fwd_vecgate_2pass(const void* q, const void* k, const void* v, con
   const int64_t nch = (T + gdn::vec::C - 1) / gdn::vec::C;
   if (!workspace || (int64_t)workspace_bytes < carry + nseq * rec) return GDN_ERR_INVALID_ARG;
   if (misaligned(workspace)) return GDN_ERR_ALIGNMENT;
-  int64_t tile = ((int64_t)workspace_bytes - carry) / (nseq * rec);
-  if (tile > VEC2P_TILE) tile = VEC2P_TILE;
-  if (tile > nch) tile = nch;
+  // a split when planned and the workspace holds it, else tiles
+  int G = 1;
+  int64_t L = T;
+  if (T > 0) vec2p_split_plan(nseq, T, dk, dv, dtype, G, L);
+  int64_t used = 0, tile = 0;
+  if (G >= 3 && vec2p_split_bytes(nseq, T, G, dk, dtype) <= (int64_t)workspace_bytes) {
+    used = vec2p_split_bytes(nseq, T, G, dk, dtype);
+  } else {
+    G = 1;
+    tile = ((int64_t)workspace_bytes - carry) / (nseq * rec);
+    if (tile > VEC2P_TILE) tile = VEC2P_TILE;
+    if (tile > nch) tile = nch;
+    used = carry + (tile > 0 ? tile : 1) * nseq * rec;
+  }
   {
-    const Range rw{workspace, carry + (tile > 0 ? tile : 1) * nseq * rec};
+    const Range rw{workspace, used};
     const int64_t esz = dtype == GDN_BF16 ? 2 : 4;
     const Range others[] = {{q, nseq * T * dk * esz}, {k, nseq * T * dk * esz},
                             {v, nseq * T * dv * esz}, {o, nseq * T * dv * esz},
@@ -624,7 +739,7 @@ int gdn_chunk_fwd_vecgate_2pass(const void* q, const void* k, const void* v, con
   char* ws = static_cast<char*>(workspace);
   return vec_dispatch<true>(dtype, dk, [&](auto t, auto dkc) {
     return vec2p_launches_t<decltype(t), decltype(dkc)::value>(q, k, v, alpha, beta, initial_state, o, final_state,
-                                                              nseq, T, dv, ws, tile, stream);
+                                                              nseq, T, dv, ws, tile, G, L, stream);
   });
 }
 

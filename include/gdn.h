@@ -217,6 +217,11 @@ size_t gdn_chunk_fwd_vecgate_split_workspace(int64_t B, int64_t H, int64_t T, in
  * The single-pass kernel repeats step 1 in the workgroup of every value
  * slice; here it is done once per chunk, at the cost of writing and reading
  * the records.  The state passes from tile to tile through the workspace.
+ * With few sequences (B*H*dv/16 small against the CU count) and a workspace
+ * that holds the records of whole sequences, step 2 splits every sequence
+ * into segments as gdn_chunk_fwd_split does ([P1] §3.3), joined through their
+ * affine state maps; the result then differs from the unsplit one by
+ * rounding only.
  *
  *   workspace        device memory owned by the caller, at least
  *                    B*H*(dk*dv*4 + R) bytes for a record size R (one chunk
@@ -237,8 +242,9 @@ int gdn_chunk_fwd_vecgate_2pass(const void* q, const void* k, const void* v,
                                 int64_t chunk_size, gdn_dtype dtype, void* workspace,
                                 size_t workspace_bytes, void* hip_stream);
 
-/* Workspace bytes with which gdn_chunk_fwd_vecgate_2pass uses its largest
- * tile for these sizes.  Host-only; 0 for arguments it rejects. */
+/* Workspace bytes with which gdn_chunk_fwd_vecgate_2pass uses its best plan
+ * for these sizes on the current device (the sequence split where one is
+ * planned, else the largest tile).  Host-only; 0 for arguments it rejects. */
 size_t gdn_chunk_fwd_vecgate_2pass_workspace(int64_t B, int64_t H, int64_t T, int64_t dk,
                                              int64_t dv, int64_t chunk_size, gdn_dtype dtype);
 

@@ -1,9 +1,11 @@
 """GPU parity of the two-pass chunked route with a per-dimension gate
 (gdn_chunk_fwd_vecgate_2pass) against the fp64 oracle (oracle_fwd_vecgate),
 with the workloads' bars (2e-2 bf16, 1e-4 fp32, max-abs-normwise on o and
-the final state).  The two passes compute the same products in the same
-order as the single-pass route, so they also match it bit for bit, and the
-tile length (set by the workspace size) does not change the result."""
+the final state).  Without a sequence split the two passes compute the same
+products in the same order as the single-pass route, so they also match it
+bit for bit, and the tile length (set by the workspace size) does not change
+the result.  With few sequences the route splits them into segments (when
+the workspace holds the split), which changes the rounding only."""
 import numpy as np
 import pytest
 import torch
@@ -24,7 +26,7 @@ CASES = [
     (2, 1, 33, 128, True, "default", "bf16"),
     (1, 3, 1000, 64, True, "default", "bf16"),
     (2, 2, 777, 128, True, "slow", "bf16"),
-    (1, 2, 12000, 128, True, "slow", "bf16"),   # 375 chunks: two tiles of at most 256
+    (1, 2, 12000, 128, True, "slow", "bf16"),   # 375 chunks: split, and unsplit two tiles of at most 256
     (1, 2, 300, 128, True, "fast", "bf16"),
     (2, 1, 2500, 64, True, "resets", "bf16"),
     (8, 1, 256, 128, True, "default", "bf16"),  # 8 sequences: XCD-grouped mapping
@@ -37,6 +39,11 @@ CASES = [
     (2, 1, 2100, 128, False, "default", "f32"),
     (1, 2, 1200, 64, True, "slow", "f32"),
     (1, 2, 640, 128, True, "resets", "f32"),
+    # few long sequences: sequence split where the device plans one
+    (1, 2, 6000, 64, True, "default", "bf16"),
+    (1, 1, 9000, 128, True, "slow", "bf16"),
+    (2, 1, 4000, 64, False, "fast", "f32"),
+    (1, 2, 3333, 128, True, "resets", "f32"),
 ]
 
 
@@ -49,6 +56,13 @@ def _inputs(B, H, T, d, dtype, init, gate, seed):
 def _record_bytes(d, dtype=torch.bfloat16):
     # the workspace of one sequence and one chunk: the carried state and one record
     return gdn_chunk_fwd_vecgate_2pass_workspace(1, 1, 32, d, d, 32, dtype) - d * d * 4
+
+
+def _tiled_bytes(B, H, T, d, dtype):
+    """Workspace of the tiled (unsplit) plan; the query returns more exactly
+    when a sequence split is planned."""
+    nch = (T + 31) // 32
+    return B * H * (d * d * 4 + max(1, min(nch, 256)) * _record_bytes(d, dtype))
 
 
 def _run2(xd, **kw):
@@ -64,16 +78,23 @@ def test_2pass_against_oracle_and_single_pass(case):
     print("case vecgate 2pass", case, flush=True)
     x = _inputs(B, H, T, d, dtype, init, gate, seed=1700 + T + d)
     xd = to_dev(x)
-    o, sT = _run2(xd)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tiled = _tiled_bytes(B, H, T, d, tdt)
+    split = gdn_chunk_fwd_vecgate_2pass_workspace(B, H, T, d, d, 32, tdt) > tiled
     (q, k, v, _, b), s0 = oracle_inputs(x)
     ro, rs = oracle.oracle_fwd_vecgate(q, k, v, x["alpha"].numpy(), b, s0)
-    eo, es = maxrel(to_np(o), ro), maxrel(to_np(sT), rs)
-    print("  err o %.3e  err S_T %.3e (tol %.0e)" % (eo, es, TOL[dtype]), flush=True)
-    assert np.all(np.isfinite(to_np(o))) and np.all(np.isfinite(to_np(sT)))
-    assert eo <= TOL[dtype] and es <= TOL[dtype]
     o1, s1 = gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"])
-    torch.cuda.synchronize()
-    assert torch.equal(o, o1) and torch.equal(sT, s1)
+    # the planned route (a split where planned), then the tiled plan
+    for ws_bytes in ([None, tiled] if split else [None]):
+        ws = None if ws_bytes is None else torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        o, sT = _run2(xd, workspace=ws)
+        eo, es = maxrel(to_np(o), ro), maxrel(to_np(sT), rs)
+        print("  %s: err o %.3e  err S_T %.3e (tol %.0e)" % ("split" if split and ws is None else "tiles", eo, es,
+                                                             TOL[dtype]), flush=True)
+        assert np.all(np.isfinite(to_np(o))) and np.all(np.isfinite(to_np(sT)))
+        assert eo <= TOL[dtype] and es <= TOL[dtype]
+        if not (split and ws is None):
+            assert torch.equal(o, o1) and torch.equal(sT, s1)
 
 
 def test_2pass_tile_length_does_not_change_the_result():
@@ -113,12 +134,16 @@ def test_2pass_main_shape_matches_single_pass():
 def test_2pass_aliasing_and_errors():
     x = _inputs(1, 2, 2500, 64, "bf16", True, "default", seed=1911)
     xd = to_dev(x)
-    ref_o, ref_s = _run2(xd)
-    s = xd["s0"].clone()
-    o, s2 = gdn_chunk_fwd_vecgate_2pass(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], s, final_state=s)
-    torch.cuda.synchronize()
-    assert s2.data_ptr() == s.data_ptr()
-    assert torch.equal(o, ref_o) and torch.equal(s, ref_s)
+    # the planned route (a split on a GPU with enough CUs) and the tiled one
+    for ws_bytes in (None, _tiled_bytes(1, 2, 2500, 64, torch.bfloat16)):
+        ws = None if ws_bytes is None else torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        ref_o, ref_s = _run2(xd, workspace=ws)
+        s = xd["s0"].clone()
+        o, s2 = gdn_chunk_fwd_vecgate_2pass(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], s, final_state=s,
+                                            workspace=ws)
+        torch.cuda.synchronize()
+        assert s2.data_ptr() == s.data_ptr()
+        assert torch.equal(o, ref_o) and torch.equal(s, ref_s)
     rec = _record_bytes(64)
     small = torch.empty(2 * (64 * 64 * 4 + rec) - 16, dtype=torch.uint8, device="cuda")
     with pytest.raises(GDNError) as ei:
