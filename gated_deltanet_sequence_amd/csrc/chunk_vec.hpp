@@ -117,8 +117,8 @@ __device__ __forceinline__ void store_vec(float* p, const float (&x)[4]) {
 // Two-pass evaluation (gdn_chunk_fwd_vecgate_2pass).  The S-independent part
 // of a chunk (gate scan, scaled operands, L, (I+L)^-1, P) does not depend on
 // the value slice, yet the single-pass kernel repeats it in every slice's
-// workgroup.  The first pass (the PREP instance of chunk_vec_kernel, one
-// workgroup per chunk) computes it once per chunk and writes the buffers the
+// workgroup.  The first pass (the PREP instance of chunk_vec_kernel) computes
+// it once per chunk and writes the buffers the
 // state products need, verbatim in their LDS layout, to a record in the
 // caller's workspace; the second pass (vec_state_kernel) walks the chunks of
 // every value slice from those records.
@@ -150,9 +150,9 @@ struct VecRec {
 // no output; MAP_SPLIT_C: every segment from its start state in cm.ws).  The
 // per-token maps stay affine with a per-dimension gate, so the split and its
 // combine step are the same.
-// PREP: the first pass of the two-pass evaluation (cm.mode == MAP_PREP): one
-// workgroup per chunk of the tile, no state, no output; the chunk's record is
-// written to cm.ws.
+// PREP: the first pass of the two-pass evaluation (cm.mode == MAP_PREP): a
+// workgroup walks one group of consecutive chunks of a sequence in the tile,
+// with no state and no output, and writes each chunk's record to cm.ws.
 template <class T, int DK, bool VG, bool PREP = false>
 __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
