@@ -74,6 +74,10 @@ constexpr int DVS = 32;   // value columns per workgroup
 // once), so the second state wave has a SIMD of its own.
 constexpr int NWAVES = 8;
 constexpr int W_P = 2, W_L = 3, W_PREFETCH = 4, W_IDLE = 5, W_LOADER = 6, W_INV = 7;
+// Without the delta rule the P wave builds the first PSPLIT tiles of P and
+// the idle inverse slot (SIMD 3) the rest (2.4 % faster than all ten on the
+// P wave, which shares SIMD 2 with the loader).
+constexpr int PSPLIT = 5;
 constexpr int TTS = 72;   // row stride (elements) of Ti^T
 constexpr int LDR = 20;   // row stride (floats) of the fp32 diagonal blocks of L
 
@@ -664,9 +668,9 @@ __device__ __forceinline__ void prefetch_rest(const Seq& sq, int64_t c, int slic
 constexpr int TILE_RB[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
 constexpr int TILE_SB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
-// P of chunk c.  Tiles are software-pipelined: the products of tile t + 1 are
-// issued before the decay, mask and store of tile t.
-template <bool GLA>
+// Tiles TB .. TE-1 of P of chunk c.  Tiles are software-pipelined: the
+// products of tile t + 1 are issued before the decay, mask and store of tile t.
+template <bool GLA, int TB = 0, int TE = 10>
 __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const int buf = (int)(c & 1);
@@ -687,7 +691,7 @@ __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c,
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) kf[b][pp] = as_op(ld3<uint4>(kf_b[pp], b * 4096));
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < (TB == 0 ? 2 : 4); ++b)
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) qf[b][pp] = as_op(ld3<uint4>(qf_b[pp], b * 4096));
   // decay of element (s, r): 2^(g_r - g_C) 2^(g_C - g_s) when split, else
@@ -709,15 +713,15 @@ __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c,
   };
   auto run = [&](auto SPLIT) {
     f32x4 acc[2];
-    acc[0] = tile(0);
+    acc[TB & 1] = tile(TB);
 #pragma unroll
-    for (int t = 0; t < 10; ++t) {
+    for (int t = TB; t < TE; ++t) {
       const int rb = TILE_RB[t], sb = TILE_SB[t];
-      if (sb == 0 && rb >= 1 && rb < 3) {
+      if (TB == 0 && sb == 0 && rb >= 1 && rb < 3) {
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) qf[rb + 1][pp] = as_op(ld3<uint4>(qf_b[pp], (rb + 1) * 4096));
       }
-      if (t + 1 < 10) acc[(t + 1) & 1] = tile(t + 1);
+      if (t + 1 < TE) acc[(t + 1) & 1] = tile(t + 1);
       __builtin_amdgcn_sched_barrier(0);
       const f32x4 a = acc[t & 1];
       const float g[4] = {gs4[sb].x, gs4[sb].y, gs4[sb].z, gs4[sb].w};
@@ -1180,7 +1184,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
       // about 500 cycles into the period, behind those of the state waves,
       // whose chain is longer (without it, P is as long as the state waves).
       if constexpr (!GLA) __builtin_amdgcn_s_sleep(8);
-      if (OUT && p >= 0 && p < nch) build_p<GLA>(sm, A, p, lane);
+      if (OUT && p >= 0 && p < nch) build_p<GLA, 0, GLA ? PSPLIT : 10>(sm, A, p, lane);
       lds_barrier();
     }
   } else if (GLA && wave == W_L) {
@@ -1221,6 +1225,14 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
         lds_barrier_keep_dma();  // this period's K loads stay in flight
       else
         lds_barrier();
+    }
+  } else if (GLA && wave == W_INV) {
+    // without the delta rule this slot builds the last tiles of P
+    const StateAddr A = state_addr(lane, 0, DV);
+    lds_barrier();
+    for (int64_t p = -2; p <= nch; ++p) {
+      if (p >= 0 && p < nch) build_p<GLA, PSPLIT, 10>(sm, A, p, lane);
+      lds_barrier();
     }
   } else if (wave == W_INV) {
     // The inverse is the longest role of a period and shares its SIMD with the
