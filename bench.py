@@ -410,6 +410,7 @@ def time_decode(torch, dev, steps_override=None):
     per = [ev[t].elapsed_time(ev[t + 1]) for t in range(steps)]
     avg_ms = ev[0].elapsed_time(ev[steps]) / steps
     byts = alg_bytes_decode(N, H, d)
+    variants = {} if steps_override is not None else time_decode_variants(torch, dev, x, qs, ks, vs, bes, o)
     return {"workload": "decode: 256 sequences x H=16, d_k=d_v=128, fp32 state [256,16,128,128] "
                         "updated in place, bf16 q/k/v, 64 consecutive steps",
             "tokens_per_s": N / (avg_ms * 1e-3), "ms_per_step": avg_ms,
@@ -418,7 +419,43 @@ def time_decode(torch, dev, steps_override=None):
             "hbm_frac": byts / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             # DRAM bytes per step from the committed rocprofv3 --pmc summary (null when
             # it is missing or was taken on other kernel sources)
-            "traffic": read_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)}
+            "traffic": read_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES),
+            **variants}
+
+
+def time_decode_variants(torch, dev, x, qs, ks, vs, bes, o, launches=64):
+    """The decode steps with a per-dimension gate and without the delta rule on
+    the decode workload's shape, each over 64 steps on a copy of S0 (eight
+    per-dimension gates drawn once and cycled; the scalar gates of the
+    workload)."""
+    from gated_deltanet_sequence_amd import inputs
+    from gated_deltanet_sequence_amd.binding import gdn_recurrent_step_vecgate, gla_recurrent_step
+    N, H, d, steps = DECODE["N"], DECODE["H"], DECODE["d"], DECODE["steps"]
+    av = inputs.make_vec_alpha(N, H, 8, d, seed=DECODE["seed"] + 100).to(dev)
+    avs = [av[:, :, t].contiguous() for t in range(8)]
+    als = [t.to(dev) for t in x["alpha"]]
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn, alphas, gate_bytes in (("vecgate", gdn_recurrent_step_vecgate, avs, N * H * (d - 1) * 4),
+                                         ("gla", gla_recurrent_step, als, 0)):
+        state = x["s0"].to(dev)
+        for t in range(4):
+            fn(qs[t], ks[t], vs[t], alphas[t % len(alphas)], bes[t], state, o=o, stream=stream)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(launches):
+            t = i % steps
+            fn(qs[t], ks[t], vs[t], alphas[t % len(alphas)], bes[t], state, o=o, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        byts = alg_bytes_decode(N, H, d) + gate_bytes
+        res[name + "_step"] = {"ms_per_step": ms, "tokens_per_s": N / (ms * 1e-3),
+                               "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del state
+    return res
 
 
 def host_info():
@@ -675,19 +712,26 @@ def summarize_trace(trace_dir, out_name, command, note="", tail=100):
     out += ["# " + line for line in note.splitlines() if line.strip()]
     out.append("# per kernel and launch shape: launches, mean, min and max duration, and the mean of")
     out.append("# the last %d launches of that shape (us)" % tail)
-    out.append("%-58s %6s %7s %8s %10s %10s %10s %10s" % ("kernel", "wgs", "threads", "launches",
+    out.append("%-66s %6s %7s %8s %10s %10s %10s %10s" % ("kernel", "wgs", "threads", "launches",
                                                         "mean_us", "min_us", "max_us", "tail_us"))
     derived = []
     for (k, wg, th), v in groups.items():
         t = v[-tail:]
         tmean = sum(t) / len(t)
-        out.append("%-58s %6d %7d %8d %10.2f %10.2f %10.2f %10.2f" % (
-            k[:58], wg, th, len(v), sum(v) / len(v) / 1e3, min(v) / 1e3, max(v) / 1e3, tmean / 1e3))
+        out.append("%-66s %6d %7d %8d %10.2f %10.2f %10.2f %10.2f" % (
+            k[:66], wg, th, len(v), sum(v) / len(v) / 1e3, min(v) / 1e3, max(v) / 1e3, tmean / 1e3))
         alg = None
         if "chunk_fwd_pipe_kernel<false, true>" in k and wg == 256:
             alg, what = alg_bytes_main(MAIN["B"], MAIN["H"], MAIN["T"], MAIN["d"]), "main workload"
         elif "recurrent_step_kernel" in k and wg == DECODE["N"] * DECODE["H"]:
+            # the last template argument is the gate kind: 0 scalar, 1 per
+            # dimension (dk - 1 more gate floats per head), 2 no delta rule
             alg, what = alg_bytes_decode(DECODE["N"], DECODE["H"], DECODE["d"]), "decode step"
+            if k.endswith(", 1>"):
+                alg += DECODE["N"] * DECODE["H"] * (DECODE["d"] - 1) * 4
+                what = "decode step, per-dimension gate"
+            elif k.endswith(", 2>"):
+                what = "decode step, gated linear attention"
         if alg is not None:
             derived += ["roofline of %s (%s, %d wgs): tail_average_ns = %d" % (k, what, wg, tmean),
                         "  algorithmic_bytes_per_launch = %d" % alg,

@@ -8,7 +8,14 @@ The binding is imported lazily so that the input generator can be used on
 machines without the library or a GPU.
 """
 
-__all__ = ["gdn_chunk_fwd", "gdn_recurrent_step", "GDNError", "load_library", "version"]
+__all__ = [
+    "gdn_chunk_fwd", "gdn_chunk_fwd_split", "gdn_chunk_fwd_split_workspace", "gdn_chunk_fwd_split_noalloc",
+    "gdn_scan_fwd", "gdn_scan_fwd_workspace", "gdn_scan_fwd_vecgate",
+    "gdn_chunk_fwd_vecgate", "gdn_chunk_fwd_vecgate_split", "gdn_chunk_fwd_vecgate_split_workspace",
+    "gdn_chunk_fwd_vecgate_2pass", "gdn_chunk_fwd_vecgate_2pass_workspace",
+    "gla_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_step_vecgate", "gla_recurrent_step",
+    "GDNError", "load_library", "strerror", "version",
+]
 
 
 def __getattr__(name):

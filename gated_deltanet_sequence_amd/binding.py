@@ -76,8 +76,9 @@ def load_library(path: str | None = None):
     lib.gdn_chunk_fwd_split_noalloc.restype = i32
     lib.gdn_chunk_fwd_split_workspace.argtypes = [i64, i64, i64, i64, i64, i64, i32]
     lib.gdn_chunk_fwd_split_workspace.restype = ctypes.c_size_t
-    lib.gdn_recurrent_step.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, p]
-    lib.gdn_recurrent_step.restype = i32
+    for fn in (lib.gdn_recurrent_step, lib.gdn_recurrent_step_vecgate, lib.gla_recurrent_step):
+        fn.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, p]
+        fn.restype = i32
     lib.gdn_strerror.argtypes = [i32]
     lib.gdn_strerror.restype = ctypes.c_char_p
     lib.gdn_version.argtypes = []
@@ -368,9 +369,7 @@ def gdn_chunk_fwd_split_noalloc(q, k, v, alpha, beta, initial_state=None, chunk_
 SPLIT_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
-def gdn_recurrent_step(q, k, v, alpha, beta, state, *, o=None, stream=None):
-    """One decode step.  q, k [N,H,dk], v [N,H,dv] (bf16 or fp32); alpha, beta
-    [N,H] fp32; state [N,H,dv,dk] fp32, updated IN PLACE.  Returns o [N,H,dv]."""
+def _step(name, q, k, v, alpha, beta, state, o, stream, vec_gate):
     if q.dtype not in _DTYPES:
         raise TypeError("q/k/v must be bfloat16 or float32")
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -379,18 +378,37 @@ def gdn_recurrent_step(q, k, v, alpha, beta, state, *, o=None, stream=None):
         raise ValueError("q, k must be [N,H,dk] and v [N,H,dv]")
     N, H, dk = q.shape
     dv = v.shape[2]
-    for name, t in (("alpha", alpha), ("beta", beta)):
-        if t.dtype != torch.float32 or tuple(t.shape) != (N, H):
-            raise ValueError("%s must be fp32 [N,H]" % name)
+    a_shape = (N, H, dk) if vec_gate else (N, H)
+    if alpha.dtype != torch.float32 or tuple(alpha.shape) != a_shape:
+        raise ValueError("alpha must be fp32 [%s]" % ("N,H,dk" if vec_gate else "N,H"))
+    if beta.dtype != torch.float32 or tuple(beta.shape) != (N, H):
+        raise ValueError("beta must be fp32 [N,H]")
     if state.dtype != torch.float32 or tuple(state.shape) != (N, H, dv, dk):
         raise ValueError("state must be fp32 [N,H,dv,dk]")
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     lib = load_library()
-    rc = lib.gdn_recurrent_step(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                                _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
-                                _dev_ptr(state, "state"), _dev_ptr(o, "o"), N, H, dk, dv,
-                                _DTYPES[q.dtype], _stream_ptr(stream, q.device))
+    rc = getattr(lib, name)(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                            _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                            _dev_ptr(state, "state"), _dev_ptr(o, "o"), N, H, dk, dv,
+                            _DTYPES[q.dtype], _stream_ptr(stream, q.device))
     if rc != GDN_OK:
-        raise GDNError(rc, "gdn_recurrent_step")
+        raise GDNError(rc, name)
     return o
+
+
+def gdn_recurrent_step(q, k, v, alpha, beta, state, *, o=None, stream=None):
+    """One decode step.  q, k [N,H,dk], v [N,H,dv] (bf16 or fp32); alpha, beta
+    [N,H] fp32; state [N,H,dv,dk] fp32, updated IN PLACE.  Returns o [N,H,dv]."""
+    return _step("gdn_recurrent_step", q, k, v, alpha, beta, state, o, stream, vec_gate=False)
+
+
+def gdn_recurrent_step_vecgate(q, k, v, alpha, beta, state, *, o=None, stream=None):
+    """gdn_recurrent_step with a per-dimension gate alpha [N,H,dk] fp32."""
+    return _step("gdn_recurrent_step_vecgate", q, k, v, alpha, beta, state, o, stream, vec_gate=True)
+
+
+def gla_recurrent_step(q, k, v, alpha, beta, state, *, o=None, stream=None):
+    """One decode step of gated linear attention (no erase term); arguments as
+    gdn_recurrent_step."""
+    return _step("gla_recurrent_step", q, k, v, alpha, beta, state, o, stream, vec_gate=False)

@@ -158,12 +158,12 @@ size_t split_ws_bytes(int64_t nseq, int G, int64_t d) {
   return G < 2 ? 0 : (size_t)(2 * nseq * (G - 1) + nseq * G) * (size_t)(d * d) * sizeof(float);
 }
 
-template <class E, int DK, int DV>
+template <class E, int DK, int DV, int GATE>
 int launch_step(const void* q, const void* k, const void* v, const float* alpha,
                 const float* beta, float* state, void* o, int64_t nheads, hipStream_t stream) {
   if (nheads > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
   constexpr int NT = DK == 128 ? 512 : 256;
-  hipLaunchKernelGGL((gdn::recurrent_step_kernel<E, DK, DV, NT>), dim3((unsigned)nheads), dim3(NT), 0,
+  hipLaunchKernelGGL((gdn::recurrent_step_kernel<E, DK, DV, NT, GATE>), dim3((unsigned)nheads), dim3(NT), 0,
                      stream, static_cast<const E*>(q), static_cast<const E*>(k),
                      static_cast<const E*>(v), alpha, beta, state, static_cast<E*>(o), nheads);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
@@ -852,9 +852,16 @@ int gdn_chunk_fwd_split_noalloc(const void* q, const void* k, const void* v, con
                         static_cast<float*>(ws), static_cast<hipStream_t>(hip_stream));
 }
 
-int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
-                       const float* beta, float* state, void* o, int64_t N, int64_t H,
-                       int64_t dk, int64_t dv, gdn_dtype dtype, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode steps share validation and dispatch; a per-dimension gate has
+// dk entries per head, a scalar gate one.
+template <int GATE>
+int step_entry(const void* q, const void* k, const void* v, const float* alpha,
+               const float* beta, float* state, void* o, int64_t N, int64_t H,
+               int64_t dk, int64_t dv, gdn_dtype dtype, void* hip_stream) {
   if (N < 0 || H < 0 || dk <= 0 || dv <= 0) return GDN_ERR_INVALID_ARG;
   if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_INVALID_ARG;
   if (too_large(N, H, 0)) return GDN_ERR_UNSUPPORTED;
@@ -865,21 +872,45 @@ int gdn_recurrent_step(const void* q, const void* k, const void* v, const float*
       misaligned(state) || misaligned(o))
     return GDN_ERR_ALIGNMENT;
   const int64_t esz = dtype == GDN_BF16 ? 2 : 4;
+  const int64_t gate_entries = GATE == gdn::STEP_VEC ? dk : 1;
   if (nheads > 0) {
     const Range ro{o, nheads * dv * esz};
-    const Range ins[] = {{q, nheads * dk * esz}, {k, nheads * dk * esz}, {v, nheads * dv * esz},
-                         {alpha, nheads * 4},    {beta, nheads * 4},     {state, nheads * dv * dk * 4}};
+    const Range ins[] = {{q, nheads * dk * esz},        {k, nheads * dk * esz}, {v, nheads * dv * esz},
+                         {alpha, nheads * gate_entries * 4}, {beta, nheads * 4},
+                         {state, nheads * dv * dk * 4}};
     for (const Range& r : ins)
       if (overlaps(ro, r)) return GDN_ERR_INVALID_ARG;
   }
   if (nheads == 0) return GDN_OK;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   if (dtype == GDN_BF16) {
-    if (dk == 128) return launch_step<bf16_t, 128, 128>(q, k, v, alpha, beta, state, o, nheads, stream);
-    return launch_step<bf16_t, 64, 64>(q, k, v, alpha, beta, state, o, nheads, stream);
+    if (dk == 128) return launch_step<bf16_t, 128, 128, GATE>(q, k, v, alpha, beta, state, o, nheads, stream);
+    return launch_step<bf16_t, 64, 64, GATE>(q, k, v, alpha, beta, state, o, nheads, stream);
   }
-  if (dk == 128) return launch_step<float, 128, 128>(q, k, v, alpha, beta, state, o, nheads, stream);
-  return launch_step<float, 64, 64>(q, k, v, alpha, beta, state, o, nheads, stream);
+  if (dk == 128) return launch_step<float, 128, 128, GATE>(q, k, v, alpha, beta, state, o, nheads, stream);
+  return launch_step<float, 64, 64, GATE>(q, k, v, alpha, beta, state, o, nheads, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
+                       const float* beta, float* state, void* o, int64_t N, int64_t H,
+                       int64_t dk, int64_t dv, gdn_dtype dtype, void* hip_stream) {
+  return step_entry<gdn::STEP_SCALAR>(q, k, v, alpha, beta, state, o, N, H, dk, dv, dtype, hip_stream);
+}
+
+int gdn_recurrent_step_vecgate(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, float* state, void* o, int64_t N, int64_t H,
+                               int64_t dk, int64_t dv, gdn_dtype dtype, void* hip_stream) {
+  return step_entry<gdn::STEP_VEC>(q, k, v, alpha, beta, state, o, N, H, dk, dv, dtype, hip_stream);
+}
+
+int gla_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
+                       const float* beta, float* state, void* o, int64_t N, int64_t H,
+                       int64_t dk, int64_t dv, gdn_dtype dtype, void* hip_stream) {
+  return step_entry<gdn::STEP_GLA>(q, k, v, alpha, beta, state, o, N, H, dk, dv, dtype, hip_stream);
 }
 
 }  // extern "C"

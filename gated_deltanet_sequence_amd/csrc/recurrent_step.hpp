@@ -15,6 +15,15 @@
 //     o_i  = alpha rq_i + (k . q) u_i
 //     S_i <- alpha S_i + u_i k^T                     (written in place)
 // Every row is independent, so the state is read once and written once.
+// Two more token updates share the kernel (template argument GATE):
+//   - a per-dimension gate alpha in R^dk ([P1] §2.2 vector gate), which decays
+//     the key columns: S <- S Diag(alpha) (I - beta k k^T) + beta v k^T.  The
+//     decay moves onto the vectors of the row dots, rk_i = S_i . (alpha o k)
+//     and rq_i = S_i . (alpha o q); then u_i = beta (v_i - rk_i),
+//     o_i = rq_i + (k . q) u_i and S_i <- alpha o S_i + u_i k^T;
+//   - gated linear attention without the erase term ([P3] §2.3):
+//     u_i = beta v_i, o_i = alpha rq_i + (k . q) u_i, S_i <- alpha S_i + u_i k^T
+//     (no rk).
 //
 // Layout of one workgroup (NT threads) = one head: LPR = dk/4 consecutive
 // lanes hold one row as float4s (a 16-byte coalesced load per lane), and
@@ -72,7 +81,9 @@ __device__ __forceinline__ int halving_row_index(int x) {
   return idx;
 }
 
-template <class T, int DK, int DV, int NT>
+enum StepGate : int { STEP_SCALAR = 0, STEP_VEC = 1, STEP_GLA = 2 };
+
+template <class T, int DK, int DV, int NT, int GATE = STEP_SCALAR>
 __global__ __launch_bounds__(NT) void recurrent_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -92,14 +103,25 @@ __global__ __launch_bounds__(NT) void recurrent_step_kernel(
   float* S = state + head * (int64_t)DV * DK;
   const T* kh = k + head * DK;
   const T* qh = q + head * DK;
-  const float a = alpha[head];
+  // scalar gate a, or this lane's four key columns of a per-dimension gate
+  float av[4];
+  if constexpr (GATE == STEP_VEC) {
+    const float4 a4 = *reinterpret_cast<const float4*>(alpha + head * DK + 4 * x);
+    av[0] = a4.x, av[1] = a4.y, av[2] = a4.z, av[3] = a4.w;
+  } else {
+    const float a = alpha[head];
+    av[0] = av[1] = av[2] = av[3] = a;
+  }
   const float b = beta[head];
 
-  float kk[4], qq[4];
+  float kk[4], qq[4], ka[4], qa[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     kk[e] = Elem<T>::to_f32(kh[4 * x + e]);
     qq[e] = Elem<T>::to_f32(qh[4 * x + e]);
+    // vectors of the row dots: the per-dimension decay folded into them
+    ka[e] = GATE == STEP_VEC ? av[e] * kk[e] : kk[e];
+    qa[e] = GATE == STEP_VEC ? av[e] * qq[e] : qq[e];
   }
 
   float4 s[R];
@@ -110,19 +132,29 @@ __global__ __launch_bounds__(NT) void recurrent_step_kernel(
   float rk[R], rq[R];
 #pragma unroll
   for (int m = 0; m < R; ++m) {
-    rk[m] = s[m].x * kk[0] + s[m].y * kk[1] + s[m].z * kk[2] + s[m].w * kk[3];
-    rq[m] = s[m].x * qq[0] + s[m].y * qq[1] + s[m].z * qq[2] + s[m].w * qq[3];
+    rk[m] = GATE == STEP_GLA ? 0.f : s[m].x * ka[0] + s[m].y * ka[1] + s[m].z * ka[2] + s[m].w * ka[3];
+    rq[m] = s[m].x * qa[0] + s[m].y * qa[1] + s[m].z * qa[2] + s[m].w * qa[3];
   }
   float kq[1] = {kk[0] * qq[0] + kk[1] * qq[1] + kk[2] * qq[2] + kk[3] * qq[3]};
-  halving_row_reduce<LPR, R>(rk, x);
+  if constexpr (GATE != STEP_GLA) halving_row_reduce<LPR, R>(rk, x);
   halving_row_reduce<LPR, R>(rq, x);
   halving_row_reduce<LPR, 1>(kq, x);
 
   // This lane now owns row grp + RG*mi of the head.
   const int mi = halving_row_index<LPR, R>(x);
   const int row = grp + RG * mi;
-  const float u = b * (Elem<T>::to_f32(v[head * DV + row]) - a * rk[0]);
-  const float out = a * rq[0] + kq[0] * u;
+  const float vr = Elem<T>::to_f32(v[head * DV + row]);
+  float u, out;
+  if constexpr (GATE == STEP_SCALAR) {
+    u = b * (vr - av[0] * rk[0]);
+    out = av[0] * rq[0] + kq[0] * u;
+  } else if constexpr (GATE == STEP_VEC) {
+    u = b * (vr - rk[0]);
+    out = rq[0] + kq[0] * u;
+  } else {
+    u = b * vr;
+    out = av[0] * rq[0] + kq[0] * u;
+  }
   // Rows are held by LPR/R lanes each; the lowest of them writes o.
   constexpr int DUP = LPR / R;
   if ((x & (DUP - 1)) == 0) o[head * DV + row] = Elem<T>::from_f32(out);
@@ -143,10 +175,10 @@ __global__ __launch_bounds__(NT) void recurrent_step_kernel(
     const int base = tid - x;  // first lane of this row group
     const float um = __shfl(u, (base + src) & 63, 64);
     float4 w = s[m];
-    w.x = a * w.x + um * kk[0];
-    w.y = a * w.y + um * kk[1];
-    w.z = a * w.z + um * kk[2];
-    w.w = a * w.w + um * kk[3];
+    w.x = av[0] * w.x + um * kk[0];
+    w.y = av[1] * w.y + um * kk[1];
+    w.z = av[2] * w.z + um * kk[2];
+    w.w = av[3] * w.w + um * kk[3];
     *reinterpret_cast<float4*>(S + (int64_t)(grp + RG * m) * DK + 4 * x) = w;
   }
 }

@@ -337,6 +337,34 @@ int gdn_recurrent_step(const void* q, const void* k, const void* v,
                        void* o, int64_t N, int64_t H, int64_t dk, int64_t dv,
                        gdn_dtype dtype, void* hip_stream);
 
+/*
+ * gdn_recurrent_step_vecgate — gdn_recurrent_step with a per-dimension gate
+ * ([P1] §2.2 vector gate): alpha is [N,H,dk] fp32, each entry in [0,1], and
+ * decays the key columns of the state,
+ *     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,
+ * the token update of gdn_chunk_fwd_vecgate (alpha is used as given; nothing
+ * clamps it).  Other arguments, layouts, dtypes and errors as for
+ * gdn_recurrent_step; `o` must not overlap any input (alpha's dk entries per
+ * head included) or the state.
+ */
+int gdn_recurrent_step_vecgate(const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta, float* state,
+                               void* o, int64_t N, int64_t H, int64_t dk, int64_t dv,
+                               gdn_dtype dtype, void* hip_stream);
+
+/*
+ * gla_recurrent_step — one decode step of gated linear attention without the
+ * delta rule ([P3] §2.3), the token update of gla_chunk_fwd:
+ *     S_t = alpha_t S_{t-1} + beta_t v_t k_t^T,      o_t = S_t q_t.
+ * Arguments, layouts, dtypes (bf16 and fp32) and errors as for
+ * gdn_recurrent_step.
+ */
+int gla_recurrent_step(const void* q, const void* k, const void* v,
+                       const float* alpha, const float* beta, float* state,
+                       void* o, int64_t N, int64_t H, int64_t dk, int64_t dv,
+                       gdn_dtype dtype, void* hip_stream);
+
 /* Static, human-readable text for a return code (never NULL). */
 const char* gdn_strerror(int code);
 

@@ -20,7 +20,7 @@ MB = 1 << 20
 def declared_functions():
     src = open(HEADER, encoding="utf-8").read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b((?:gdn|gla)_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +32,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) >= {"gdn_chunk_fwd", "gdn_recurrent_step", "gdn_strerror", "gdn_version"}
+    assert set(names) >= {"gdn_chunk_fwd", "gdn_recurrent_step", "gdn_strerror", "gdn_version",
+                          "gla_chunk_fwd", "gla_recurrent_step", "gdn_recurrent_step_vecgate"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -52,11 +53,14 @@ def fwd(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, alpha=A + 192 * MB, beta=A + 20
                              B, H, T, dk, dv, C, dtype, None)
 
 
+STEPS = ["gdn_recurrent_step", "gdn_recurrent_step_vecgate", "gla_recurrent_step"]
+
+
 def step(lib, q=A, k=A + MB, v=A + 2 * MB, alpha=A + 3 * MB, beta=A + 4 * MB,
-         state=A + 8 * MB, o=A + 64 * MB, N=1, H=1, dk=64, dv=64, dtype=1):
+         state=A + 8 * MB, o=A + 64 * MB, N=1, H=1, dk=64, dv=64, dtype=1, fn="gdn_recurrent_step"):
     P = lambda x: None if x is None else ctypes.c_void_p(x)
-    return lib.gdn_recurrent_step(P(q), P(k), P(v), P(alpha), P(beta), P(state), P(o),
-                                  N, H, dk, dv, dtype, None)
+    return getattr(lib, fn)(P(q), P(k), P(v), P(alpha), P(beta), P(state), P(o),
+                            N, H, dk, dv, dtype, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -84,19 +88,30 @@ def test_chunk_fwd_empty_is_noop(lib):
     assert fwd(lib, B=0, q=None, k=None, v=None, alpha=None, beta=None, o=None) == 0
 
 
+@pytest.mark.parametrize("fn", STEPS)
 @pytest.mark.parametrize("kw,code", [
-    (dict(q=None), 1), (dict(state=None), 1), (dict(o=None), 1), (dict(N=-1), 1),
+    (dict(q=None), 1), (dict(alpha=None), 1), (dict(beta=None), 1), (dict(state=None), 1),
+    (dict(o=None), 1), (dict(N=-1), 1), (dict(H=-1), 1),
     (dict(dtype=3), 1), (dict(dk=96, dv=96), 2), (dict(dk=64, dv=128), 2),
-    (dict(state=A + 8 * MB + 4), 3), (dict(k=A + MB + 2), 3),
+    (dict(state=A + 8 * MB + 4), 3), (dict(k=A + MB + 2), 3), (dict(alpha=A + 3 * MB + 8), 3),
     (dict(o=A + 8 * MB), 1),               # output overlaps the state
+    (dict(o=A + 2 * MB + 64), 1),          # output overlaps v
 ])
-def test_recurrent_step_rejects(lib, kw, code):
-    assert step(lib, **kw) == code
+def test_recurrent_step_rejects(lib, kw, code, fn):
+    assert step(lib, fn=fn, **kw) == code
 
 
-def test_recurrent_step_empty_is_noop(lib):
-    assert step(lib, N=0) == 0
-    assert step(lib, H=0, q=None, state=None, o=None) == 0
+def test_vecgate_step_checks_the_whole_gate_vector(lib):
+    # a per-dimension gate has dk entries per head: an output 16 bytes past the
+    # start of alpha overlaps it (a scalar gate would end there)
+    assert step(lib, fn="gdn_recurrent_step_vecgate", o=A + 3 * MB + 16) == 1
+    assert step(lib, fn="gdn_recurrent_step_vecgate", o=A + 3 * MB + 240) == 1   # last 16 of 256 bytes
+
+
+@pytest.mark.parametrize("fn", STEPS)
+def test_recurrent_step_empty_is_noop(lib, fn):
+    assert step(lib, N=0, fn=fn) == 0
+    assert step(lib, H=0, q=None, state=None, o=None, fn=fn) == 0
 
 
 def fwd_split(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, alpha=A + 192 * MB, beta=A + 200 * MB,

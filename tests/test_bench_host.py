@@ -106,6 +106,25 @@ def test_trace_summary_groups_by_kernel_and_shape_and_prices_the_main_launches(t
     assert float(frac.split("=")[1]) == pytest.approx(alg / 200000.0 / 8000.0, rel=1e-3)
 
 
+def test_trace_summary_prices_each_decode_step_variant(tmp_path, monkeypatch):
+    """The three decode steps (scalar gate, per-dimension gate, no delta rule)
+    keep rows of their own, and the per-dimension gate's extra bytes count."""
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    step = "void gdn::recurrent_step_kernel<unsigned short, 128, 128, 512, %d>(unsigned short const*, long)"
+    rows = [[(step % g, 4096, 512, 80000 + 1000 * g)] * 64 for g in (0, 1, 2)]
+    _write_trace(str(tmp_path / "tr"), [r for rs in rows for r in rs])
+    bench.summarize_trace(str(tmp_path / "tr"), "x", command="c", tail=64)
+    text = (tmp_path / "profiles" / "x.txt").read_text()
+    assert len([l for l in text.splitlines() if l.startswith("gdn::recurrent_step_kernel")]) == 3
+    fr = [float(l.split("=")[1]) for l in text.splitlines() if "fraction_of_8000_GBps" in l]
+    base = bench.alg_bytes_decode(256, 16, 128)
+    vec = base + 256 * 16 * 127 * 4
+    assert fr == pytest.approx([base / 80000.0 / 8000.0, vec / 81000.0 / 8000.0, base / 82000.0 / 8000.0],
+                               rel=1e-3)
+    assert "per-dimension gate" in text and "gated linear attention" in text
+
+
 def test_host_info_names_the_cpu():
     info = bench.host_info()
     assert info["nproc"] >= 1 and isinstance(info["cpu_model"], str)
