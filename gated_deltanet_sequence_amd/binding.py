@@ -161,8 +161,8 @@ def gdn_chunk_fwd(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 64
 def gla_chunk_fwd(q, k, v, alpha, beta, initial_state=None, chunk_size: int = 64, *,
                   o=None, final_state=None, output_final_state: bool = True, stream=None):
     """Gated linear attention without the delta rule,
-    S_t = alpha_t S_{t-1} + beta_t v_t k_t^T, o_t = S_t q_t (bf16 q/k/v).
-    Same arguments and result as gdn_chunk_fwd."""
+    S_t = alpha_t S_{t-1} + beta_t v_t k_t^T, o_t = S_t q_t.  Same arguments,
+    dtypes, chunk sizes and result as gdn_chunk_fwd."""
     B, H, T, dk, dv = _check_fwd_args(q, k, v, alpha, beta, initial_state)
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)

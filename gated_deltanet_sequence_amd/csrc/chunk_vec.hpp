@@ -153,7 +153,10 @@ struct VecRec {
 // PREP: the first pass of the two-pass evaluation (cm.mode == MAP_PREP): a
 // workgroup walks one group of consecutive chunks of a sequence in the tile,
 // with no state and no output, and writes each chunk's record to cm.ws.
-template <class T, int DK, bool VG, bool PREP = false>
+// GLA: gated linear attention without the delta rule ([P3] §2.3; scalar gate,
+// MAP_SEQ only): L = 0, so Ti = I and U = Y = diag(beta) V, with no K S^T
+// term; the gate scan, P, the output and the state update are unchanged.
+template <class T, int DK, bool VG, bool PREP = false, bool GLA = false>
 __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -174,6 +177,7 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
   static_assert(NVV <= NT && DK <= NT && C <= 64, "one thread per V vector, key column, token");
   static_assert(RB == 2, "the blocked inverse below is for two 16-token blocks");
   static_assert(IB * RB == 2 && NW == 4, "wave roles below: one Y wave, two output waves");
+  static_assert(!(GLA && (PREP || VG)), "gated linear attention: scalar gate, single pass");
   constexpr int NG = NT / DK;                    // token groups of the gate scan
   constexpr int TPG = C / NG;                    // tokens per group
 
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
         *reinterpret_cast<uint4*>(&sm.Qr[r * LDK + j0]) = zq;
       }
       if (o_on) store_vec(&sm.Qs[r * LDK + j0], qs);
-      store_vec(&sm.Kr[r * LDK + j0], kr);
+      if constexpr (!GLA) store_vec(&sm.Kr[r * LDK + j0], kr);
       store_vec(&sm.Kh[r * LDK + j0], kh);
     }
     if (ch + 1 < nchunks) load_chunk(ch + 1);
@@ -467,11 +471,13 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
       if (kind == 0 && sb == rb)
         *reinterpret_cast<float4*>(&sm.Ld[sb][r - rb * 16][s0 - sb * 16]) = make_float4(val[0], val[1], val[2], val[3]);
     };
-    if (wave < 3) gram_tile(wave);
+    // (Without the delta rule there is no L: the P tiles run here instead.)
+    if (wave < 3 && (!GLA || o_on)) gram_tile(GLA ? 3 + wave : wave);
     __syncthreads();
 
     f32x4 Oacc = zero4();
     if (wave == 0) {
+      if constexpr (!GLA) {
       // Ti = (I + L)^-1, blocked, on this wave alone: the two unit-lower 16x16
       // diagonal blocks by forward substitution in fp32 (lane = block,
       // column; each band of four L columns read as float4 rows one band
@@ -539,15 +545,18 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) sm.Ti[(16 + 4 * lg + e) * LDC + lr] = Elem<T>::from_f32(-acc[e]);
+      }
     } else if (PREP && wave == 1) {
       gram_tile(5);
     } else if (wave == 1) {
-      // Y = diag(beta) (V - K~ S^T), tiles [r][i], meanwhile.
+      // Y = diag(beta) (V - K~ S^T), tiles [r][i], meanwhile.  Without the
+      // delta rule Y = diag(beta) V is U already and goes to U^T.
 #pragma unroll
       for (int t = 0; t < RB * IB; ++t) {
         const int rb = t / IB, ib = t % IB;
-        const f32x4 acc = Mma<T>::template run<DK>(zero4(), &sm.Kr[rb * 16 * LDK], LDK,
-                                                   &sm.S[ib * 16 * LDK], LDK, lane);
+        f32x4 acc = zero4();
+        if constexpr (!GLA)
+          acc = Mma<T>::template run<DK>(zero4(), &sm.Kr[rb * 16 * LDK], LDK, &sm.S[ib * 16 * LDK], LDK, lane);
         const int i = ib * 16 + lr;
         const int r0 = rb * 16 + 4 * lg;
         float y[4];
@@ -556,9 +565,9 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
           const int r = r0 + e;
           y[e] = sm.beta[r] * (Elem<T>::to_f32(sm.V[r * DVS + i]) - acc[e]);
         }
-        store4<T>(&sm.Yt[i * LDC + r0], y[0], y[1], y[2], y[3]);
+        store4<T>(&(GLA ? sm.Ut : sm.Yt)[i * LDC + r0], y[0], y[1], y[2], y[3]);
       }
-      if (o_on) gram_tile(5);
+      if (o_on && !GLA) gram_tile(5);
     } else if (o_on) {
       // the inter-chunk part of the output, S Q~^T (tile [i][r] of this
       // output wave, kept live until the output is finished)
@@ -566,7 +575,7 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
       const int ib = t / RB, rb = t % RB;
       if constexpr (!PREP)
         Oacc = Mma<T>::template run<DK>(zero4(), &sm.S[ib * 16 * LDK], LDK, &sm.Qs[rb * 16 * LDK], LDK, lane);
-      gram_tile(3 + t);
+      if constexpr (!GLA) gram_tile(3 + t);
     }
     __syncthreads();
 
@@ -590,7 +599,7 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
     }
 
     // U = Ti Y (tiles [r][i]), stored as U^T.
-    if (wave < RB * IB) {
+    if (!GLA && wave < RB * IB) {
       const int t = wave;
       const int rb = t / IB, ib = t % IB;
       const f32x4 acc = Mma<T>::template run<C>(zero4(), &sm.Ti[rb * 16 * LDC], LDC, &sm.Yt[ib * 16 * LDC], LDC, lane);

@@ -295,7 +295,7 @@ int vec_dispatch(gdn_dtype dtype, int64_t dk, F&& f) {
   return dk == 128 ? f(bf16_t{}, D128{}) : f(bf16_t{}, D64{});
 }
 
-template <bool VG, class T, int DK>
+template <bool VG, class T, int DK, bool GLA = false>
 int launch_vec_t(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                  const float* initial_state, void* o, float* final_state, const gdn::pipe::ChainMap& cm,
                  int64_t dv, hipStream_t stream) {
@@ -303,18 +303,18 @@ int launch_vec_t(const void* q, const void* k, const void* v, const float* alpha
   const int64_t nblocks = nchain * (dv / gdn::vec::DVS);
   if (nblocks > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
   const int xcd_map = (nchain % 8) == 0;
-  hipLaunchKernelGGL((gdn::vec::chunk_vec_kernel<T, DK, VG>), dim3((unsigned)nblocks), dim3(gdn::vec::NT), 0,
+  hipLaunchKernelGGL((gdn::vec::chunk_vec_kernel<T, DK, VG, false, GLA>), dim3((unsigned)nblocks), dim3(gdn::vec::NT), 0,
                      stream, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), alpha,
                      beta, initial_state, static_cast<T*>(o), final_state, cm, (int)dv, xcd_map);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
-template <bool VG>
+template <bool VG, bool GLA = false>
 int launch_vec(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                const float* initial_state, void* o, float* final_state, const gdn::pipe::ChainMap& cm,
                int64_t dk, int64_t dv, gdn_dtype dtype, hipStream_t stream) {
   return vec_dispatch<VG>(dtype, dk, [&](auto t, auto dkc) {
-    return launch_vec_t<VG, decltype(t), decltype(dkc)::value>(q, k, v, alpha, beta, initial_state, o, final_state,
-                                                               cm, dv, stream);
+    return launch_vec_t<VG, decltype(t), decltype(dkc)::value, GLA>(q, k, v, alpha, beta, initial_state, o,
+                                                                    final_state, cm, dv, stream);
   });
 }
 
@@ -583,15 +583,22 @@ int gla_chunk_fwd(const void* q, const void* k, const void* v, const float* alph
                   const float* beta, const float* initial_state, void* o, float* final_state,
                   int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int64_t chunk_size,
                   gdn_dtype dtype, void* hip_stream) {
+  // chunk sizes and dtypes as gdn_chunk_fwd: bf16 64-token chunks on the
+  // pipelined kernel, fp32 and 32-token chunks on the 32-token kernel
+  const bool c32 = chunk_size == gdn::vec::C;
   const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
-                           chunk_size, dtype);
+                           c32 ? 64 : chunk_size, dtype);
   if (rc != GDN_OK) return rc;
-  if (dtype != GDN_BF16 || !pipe_len_ok(T, dk, dv)) return GDN_ERR_UNSUPPORTED;
+  if (dtype == GDN_BF16 && !c32 && !pipe_len_ok(T, dk, dv)) return GDN_ERR_UNSUPPORTED;
   const int64_t nchain = B * H;
   if (nchain == 0) return GDN_OK;
   if (T == 0 && !final_state) return GDN_OK;
-  return launch_chunk_pipe<true>(q, k, v, alpha, beta, initial_state, o, final_state,
-                                 seq_map(nchain, T), dk, dv, static_cast<hipStream_t>(hip_stream));
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (dtype == GDN_BF16 && !c32)
+    return launch_chunk_pipe<true>(q, k, v, alpha, beta, initial_state, o, final_state, seq_map(nchain, T),
+                                   dk, dv, stream);
+  return launch_vec<false, true>(q, k, v, alpha, beta, initial_state, o, final_state, seq_map(nchain, T), dk,
+                                 dv, dtype, stream);
 }
 
 size_t gdn_scan_fwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,

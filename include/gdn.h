@@ -108,8 +108,9 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v,
  *     S_t = alpha_t S_{t-1} + beta_t v_t k_t^T,      o_t = S_t q_t,
  *
  * with the same state orientation (S is d_v x d_k) as gdn_chunk_fwd.  Same
- * arguments, layouts, chunk size, aliasing and error codes as gdn_chunk_fwd;
- * bf16 only (GDN_ERR_UNSUPPORTED for fp32).
+ * arguments, layouts, dtypes (bf16 and fp32), chunk sizes (64, or 32 through
+ * the 32-token kernel; fp32 is evaluated 32 tokens at a time), aliasing and
+ * error codes as gdn_chunk_fwd.
  */
 int gla_chunk_fwd(const void* q, const void* k, const void* v,
                   const float* alpha, const float* beta,

@@ -79,6 +79,25 @@ def test_chunk_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
 
 
+def gla(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, alpha=A + 192 * MB, beta=A + 200 * MB,
+        s0=None, o=A + 256 * MB, sT=None, B=1, H=1, T=64, dk=64, dv=64, C=64, dtype=1):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gla_chunk_fwd(P(q), P(k), P(v), P(alpha), P(beta), P(s0), P(o), P(sT),
+                             B, H, T, dk, dv, C, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(beta=None), 1), (dict(T=-1), 1), (dict(dtype=7), 1),
+    (dict(dk=32, dv=32), 2), (dict(C=16), 2), (dict(C=48), 2), (dict(C=128), 2), (dict(C=48, dtype=0), 2),
+    (dict(q=A + 8), 3), (dict(sT=A + 400 * MB + 12, C=32), 3), (dict(dtype=0, o=A + 256 * MB + 4), 3),
+    (dict(o=A + 112, C=32), 1), (dict(sT=A + 256 * MB + 16, dtype=0), 1),
+])
+def test_gla_chunk_fwd_rejects(lib, kw, code):
+    """gla_chunk_fwd validates as gdn_chunk_fwd, for both kernels (64-token
+    bf16; fp32 and chunk_size 32)."""
+    assert gla(lib, **kw) == code
+
+
 def test_chunk_fwd_empty_is_noop(lib):
     # no sequences, or no tokens and no state to write: nothing is launched
     assert fwd(lib, B=0) == 0

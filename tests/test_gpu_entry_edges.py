@@ -1,6 +1,6 @@
 """Edge cases of the sequence-split, scan, vector-gate (scan and chunked),
-GLA, fp32 chunked, 32-token chunked and two-pass per-dimension-gate entry
-points on the GPU: zero tokens (the final state is the initial one, or zero), no
+GLA (64- and 32-token chunks, bf16 and fp32), fp32 chunked, 32-token chunked
+and two-pass per-dimension-gate entry points on the GPU: zero tokens (the final state is the initial one, or zero), no
 sequences, fewer tokens than one chunk or block, and a final state that
 aliases the initial state.  Results are compared with the fp64 oracles or
 with exact expectations."""
@@ -39,6 +39,10 @@ ENTRIES = {
     # the same bf16-rounded inputs as fp32: the fp32 chunked path
     "fp32": lambda xd: gdn_chunk_fwd(xd["q"].float(), xd["k"].float(), xd["v"].float(), xd["alpha"], xd["beta"],
                                      xd["s0"], 64),
+    # gated linear attention on the 32-token kernel: chunk_size 32, and fp32
+    "gla_c32": lambda xd: gla_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"], 32),
+    "gla_fp32": lambda xd: gla_chunk_fwd(xd["q"].float(), xd["k"].float(), xd["v"].float(), xd["alpha"],
+                                         xd["beta"], xd["s0"], 64),
 }
 
 
@@ -76,7 +80,8 @@ def test_short_sequences_match_oracle(name, T):
     assert maxrel(to_np(o), ro) <= tol and maxrel(to_np(sT), rs) <= tol
 
 
-@pytest.mark.parametrize("name", ["scan", "gla", "chunk_vecgate", "chunk_vecgate_2pass", "c32", "fp32"])
+@pytest.mark.parametrize("name", ["scan", "gla", "chunk_vecgate", "chunk_vecgate_2pass", "c32", "fp32", "gla_c32",
+                                  "gla_fp32"])
 def test_final_state_aliases_initial_state(name):
     x = inputs.make_fwd_inputs(1, 2, 700, 128, "bf16", seed=64, init_state=True)
     xd = to_dev(x)
@@ -95,6 +100,11 @@ def test_final_state_aliases_initial_state(name):
                                             final_state=s)
     elif name == "c32":
         o, s2 = gdn_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], s, 32, final_state=s)
+    elif name == "gla_c32":
+        o, s2 = gla_chunk_fwd(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], s, 32, final_state=s)
+    elif name == "gla_fp32":
+        o, s2 = gla_chunk_fwd(xd["q"].float(), xd["k"].float(), xd["v"].float(), xd["alpha"], xd["beta"], s, 64,
+                              final_state=s)
     else:
         o, s2 = gdn_chunk_fwd(xd["q"].float(), xd["k"].float(), xd["v"].float(), xd["alpha"], xd["beta"], s, 64,
                               final_state=s)
