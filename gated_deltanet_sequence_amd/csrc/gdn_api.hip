@@ -214,6 +214,21 @@ int check_fwd(const void* q, const void* k, const void* v, const float* alpha, c
     for (const Range& r : ins)
       if (overlaps(ro, r)) return GDN_ERR_INVALID_ARG;
   }
+  if (nchain > 0 && final_state) {
+    // The final state is written while other workgroups still read the
+    // inputs: it must be disjoint from them, and from the initial state
+    // unless it is that very state (each workgroup reads its part first).
+    const Range rs{final_state, nchain * dv * dk * 4};
+    const Range ins[] = {{q, nchain * T * dk * esz},
+                         {k, nchain * T * dk * esz},
+                         {v, nchain * T * dv * esz},
+                         {alpha, nchain * T * (alpha_per_dim ? dk : 1) * 4},
+                         {beta, nchain * T * 4}};
+    for (const Range& r : ins)
+      if (overlaps(rs, r)) return GDN_ERR_INVALID_ARG;
+    if (initial_state != final_state && overlaps(rs, Range{initial_state, nchain * dv * dk * 4}))
+      return GDN_ERR_INVALID_ARG;
+  }
   return GDN_OK;
 }
 }  // namespace
@@ -887,6 +902,10 @@ int step_entry(const void* q, const void* k, const void* v, const float* alpha,
                          {state, nheads * dv * dk * 4}};
     for (const Range& r : ins)
       if (overlaps(ro, r)) return GDN_ERR_INVALID_ARG;
+    // the state is rewritten in place while other heads read the token inputs
+    const Range rs{state, nheads * dv * dk * 4};
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(rs, ins[i])) return GDN_ERR_INVALID_ARG;
   }
   if (nheads == 0) return GDN_OK;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);

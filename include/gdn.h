@@ -75,8 +75,10 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *   initial_state  [B,H,dv,dk] fp32    S_0, or NULL for a zero state
  *   o              [B,H,T,dv]  dtype   OUT: o_t = S_t q_t
  *   final_state    [B,H,dv,dk] fp32    OUT: S_T, or NULL to skip it.
- *                                      May alias initial_state (each workgroup
- *                                      reads its part of S_0 before writing).
+ *                                      May be initial_state itself (each
+ *                                      workgroup reads its part of S_0 before
+ *                                      writing); otherwise it must not overlap
+ *                                      initial_state or any input.
  *   chunk_size     tokens per chunk: 64 (the pipelined bf16 kernel; the fast
  *                  path), or 32 (the 32-token kernel, bf16 or fp32).  T need
  *                  not be a multiple: the missing tokens of the last chunk act
@@ -331,7 +333,8 @@ int gdn_chunk_fwd_split_noalloc(const void* q, const void* k, const void* v,
  *   o       [N,H,dv] dtype     OUT: S_t q_t
  *   dk, dv  64 or 128, dk == dv.  N, H >= 0 (N*H == 0 is a no-op).
  *
- * `o` must not overlap any input or the state.
+ * `o` must not overlap any input or the state, and the state must not overlap
+ * q, k, v, alpha or beta (GDN_ERR_INVALID_ARG).
  */
 int gdn_recurrent_step(const void* q, const void* k, const void* v,
                        const float* alpha, const float* beta, float* state,

@@ -74,6 +74,9 @@ def step(lib, q=A, k=A + MB, v=A + 2 * MB, alpha=A + 3 * MB, beta=A + 4 * MB,
     (dict(o=A + 112), 1),                  # output overlaps q
     (dict(o=A + 192 * MB), 1),             # output overlaps alpha
     (dict(sT=A + 256 * MB + 16), 1),       # final state overlaps the output
+    (dict(sT=A + 64 * MB), 1),             # final state overlaps k
+    (dict(sT=A + 192 * MB + 16), 1),       # final state overlaps alpha
+    (dict(s0=A + 300 * MB, sT=A + 300 * MB + 16), 1),   # final state partly overlaps the initial state
 ])
 def test_chunk_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
@@ -115,6 +118,8 @@ def test_chunk_fwd_empty_is_noop(lib):
     (dict(state=A + 8 * MB + 4), 3), (dict(k=A + MB + 2), 3), (dict(alpha=A + 3 * MB + 8), 3),
     (dict(o=A + 8 * MB), 1),               # output overlaps the state
     (dict(o=A + 2 * MB + 64), 1),          # output overlaps v
+    (dict(state=A + MB), 1),               # state overlaps k
+    (dict(q=A + 8 * MB + 4096), 1),        # q inside the state
 ])
 def test_recurrent_step_rejects(lib, kw, code, fn):
     assert step(lib, fn=fn, **kw) == code
