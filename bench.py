@@ -311,8 +311,8 @@ def time_routes(torch, dev, launches=5):
                                                      gdn_chunk_fwd_vecgate_2pass_workspace,
                                                      gdn_chunk_fwd_vecgate_split,
                                                      gdn_chunk_fwd_vecgate_split_workspace,
-                                                     gdn_recurrent_step, gdn_scan_fwd, gdn_scan_fwd_vecgate,
-                                                     gdn_scan_fwd_workspace)
+                                                     gdn_recurrent_fwd, gdn_recurrent_step, gdn_scan_fwd,
+                                                     gdn_scan_fwd_vecgate, gdn_scan_fwd_workspace)
     B, H, T, d = ROUTES["B"], ROUTES["H"], ROUTES["T"], ROUTES["d"]
     x = inputs.make_fwd_inputs(B, H, T, d, "bf16", seed=ROUTES["seed"])
     xd = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
@@ -344,7 +344,9 @@ def time_routes(torch, dev, launches=5):
                                                                                   stream=stream)),
                     ("chunked_vecgate_2pass", lambda: gdn_chunk_fwd_vecgate_2pass(xd["q"], xd["k"], xd["v"], avd,
                                                                                   xd["beta"], None, workspace=ws2,
-                                                                                  stream=stream))):
+                                                                                  stream=stream)),
+                    # the token loop in one launch, the state in registers
+                    ("recurrent_fwd", lambda: gdn_recurrent_fwd(*a, stream=stream))):
         settle_clocks(torch, f)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -354,7 +356,7 @@ def time_routes(torch, dev, launches=5):
         e1.record(stream)
         torch.cuda.synchronize()
         res[name + "_ms"] = e0.elapsed_time(e1) / launches
-    # per-token route: T launches of the decode step over the B*H heads
+    # per-token route: T launches of the decode step over the B*H heads (token_loop_ms)
     n = B * H
     cols = {nm: [xd[nm][:, :, t].reshape(n, 1, -1).contiguous() for t in range(T)] for nm in ("q", "k", "v")}
     gates = {nm: [xd[nm][:, :, t].reshape(n, 1).contiguous() for t in range(T)] for nm in ("alpha", "beta")}
@@ -411,6 +413,8 @@ def time_decode(torch, dev, steps_override=None):
     avg_ms = ev[0].elapsed_time(ev[steps]) / steps
     byts = alg_bytes_decode(N, H, d)
     variants = {} if steps_override is not None else time_decode_variants(torch, dev, x, qs, ks, vs, bes, o)
+    if steps_override is None:
+        variants["few_new_tokens"] = time_few_new_tokens(torch, dev)
     return {"workload": "decode: 256 sequences x H=16, d_k=d_v=128, fp32 state [256,16,128,128] "
                         "updated in place, bf16 q/k/v, 64 consecutive steps",
             "tokens_per_s": N / (avg_ms * 1e-3), "ms_per_step": avg_ms,
@@ -421,6 +425,45 @@ def time_decode(torch, dev, steps_override=None):
             # it is missing or was taken on other kernel sources)
             "traffic": read_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES),
             **variants}
+
+
+def time_few_new_tokens(torch, dev, T=8, launches=20):
+    """Eight new tokens for each of the decode workload's 256 x 16 sequences
+    (a state ~ N(0, 0.1)): the token-by-token pass (gdn_recurrent_fwd), the
+    chunked pass and eight decode steps.  Mean times."""
+    from gated_deltanet_sequence_amd import inputs
+    from gated_deltanet_sequence_amd.binding import gdn_chunk_fwd, gdn_recurrent_fwd, gdn_recurrent_step
+    N, H, d = DECODE["N"], DECODE["H"], DECODE["d"]
+    x = inputs.make_fwd_inputs_on_device(N, H, T, d, seed=DECODE["seed"] + 200, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(DECODE["seed"] + 201)
+    s0 = 0.1 * torch.randn((N, H, d, d), generator=g, device=dev, dtype=torch.float32)
+    o = torch.empty_like(x["v"])
+    sT = torch.empty_like(s0)
+    stream = torch.cuda.current_stream()
+    a = (x["q"], x["k"], x["v"], x["alpha"], x["beta"], s0)
+    cols = [{nm: x[nm][:, :, t].contiguous() for nm in ("q", "k", "v", "alpha", "beta")} for t in range(T)]
+    state = s0.clone()
+    ob = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)
+
+    def steps():
+        for c in cols:
+            gdn_recurrent_step(c["q"], c["k"], c["v"], c["alpha"], c["beta"], state, o=ob, stream=stream)
+    res = {"workload": "%d new tokens for each of 256 sequences x H=16, d_k=d_v=128, bf16 q/k/v, fp32 state "
+                       "~ N(0, 0.1)" % T}
+    for name, f in (("recurrent_fwd", lambda: gdn_recurrent_fwd(*a, o=o, final_state=sT, stream=stream)),
+                    ("chunked", lambda: gdn_chunk_fwd(*a, 64, o=o, final_state=sT, stream=stream)),
+                    ("decode_steps", steps)):
+        settle_clocks(torch, f)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name + "_ms"] = e0.elapsed_time(e1) / launches
+    return res
 
 
 def time_decode_variants(torch, dev, x, qs, ks, vs, bes, o, launches=64):

@@ -10,7 +10,8 @@ machines without the library or a GPU.
 
 __all__ = [
     "gdn_chunk_fwd", "gdn_chunk_fwd_split", "gdn_chunk_fwd_split_workspace", "gdn_chunk_fwd_split_noalloc",
-    "gdn_scan_fwd", "gdn_scan_fwd_workspace", "gdn_scan_fwd_vecgate",
+    "gdn_scan_fwd", "gdn_scan_fwd_workspace", "gdn_scan_fwd_vecgate", "gdn_recurrent_fwd",
+    "gdn_recurrent_fwd_vecgate",
     "gdn_chunk_fwd_vecgate", "gdn_chunk_fwd_vecgate_split", "gdn_chunk_fwd_vecgate_split_workspace",
     "gdn_chunk_fwd_vecgate_2pass", "gdn_chunk_fwd_vecgate_2pass_workspace",
     "gla_chunk_fwd", "gdn_recurrent_step", "gdn_recurrent_step_vecgate", "gla_recurrent_step",

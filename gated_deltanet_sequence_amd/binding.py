@@ -56,6 +56,9 @@ def load_library(path: str | None = None):
     lib.gdn_scan_fwd.restype = i32
     lib.gdn_scan_fwd_vecgate.argtypes = lib.gdn_scan_fwd.argtypes
     lib.gdn_scan_fwd_vecgate.restype = i32
+    for fn in (lib.gdn_recurrent_fwd, lib.gdn_recurrent_fwd_vecgate):
+        fn.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i32, p]
+        fn.restype = i32
     lib.gdn_chunk_fwd_vecgate.argtypes = lib.gdn_chunk_fwd.argtypes
     lib.gdn_chunk_fwd_vecgate.restype = i32
     lib.gdn_chunk_fwd_vecgate_split.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i32,
@@ -208,6 +211,32 @@ def gdn_scan_fwd(q, k, v, alpha, beta, initial_state=None, *, o=None, final_stat
     if rc != GDN_OK:
         raise GDNError(rc, "gdn_scan_fwd_vecgate" if _vecgate else "gdn_scan_fwd")
     return o, final_state
+
+
+def gdn_recurrent_fwd(q, k, v, alpha, beta, initial_state=None, *, o=None, final_state=None,
+                      output_final_state: bool = True, stream=None, _vecgate=False):
+    """The forward pass token by token (one launch, the state in registers):
+    for many short sequences.  Same arguments and result as gdn_chunk_fwd
+    without the chunk size."""
+    B, H, T, dk, dv = _check_fwd_args(q, k, v, alpha, beta, initial_state, alpha_per_dim=_vecgate)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    name = "gdn_recurrent_fwd_vecgate" if _vecgate else "gdn_recurrent_fwd"
+    rc = getattr(load_library(), name)(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                       _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                                       _dev_ptr(initial_state, "initial_state"), _dev_ptr(o, "o"),
+                                       _dev_ptr(final_state, "final_state"), B, H, T, dk, dv,
+                                       _DTYPES[q.dtype], _stream_ptr(stream, q.device))
+    if rc != GDN_OK:
+        raise GDNError(rc, name)
+    return o, final_state
+
+
+def gdn_recurrent_fwd_vecgate(q, k, v, alpha, beta, initial_state=None, **kw):
+    """gdn_recurrent_fwd with a per-dimension gate alpha [B,H,T,dk] (fp32)."""
+    return gdn_recurrent_fwd(q, k, v, alpha, beta, initial_state, _vecgate=True, **kw)
 
 
 def gdn_scan_fwd_vecgate(q, k, v, alpha, beta, initial_state=None, **kw):

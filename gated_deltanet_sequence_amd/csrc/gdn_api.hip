@@ -630,6 +630,38 @@ size_t gdn_scan_fwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64
 }  // extern "C"
 
 namespace {
+// The token-by-token forward pass: the scan route's replay kernel with one
+// block per sequence (G = 1), starting from the initial state itself (or a
+// zero state) and writing the final state; no workspace and no other launch.
+template <class E, int D, bool VEC>
+int launch_recurrent(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                     const float* s0, void* o, float* sT, int64_t nseq, int64_t T, hipStream_t stream) {
+  using namespace gdn::scan;
+  const int64_t nb = scan_blocks(SCAN_OUT, (int)nseq, 1, D);
+  if (nb > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((scan_tokens_kernel<E, D, VEC>), dim3((unsigned)nb), dim3(THREADS), 0, stream,
+                     static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v), alpha, beta,
+                     static_cast<E*>(o), sT, (int)SCAN_OUT, (int)nseq, 1, T, T, const_cast<float*>(s0));
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+template <bool VEC>
+int recurrent_fwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                  const float* initial_state, void* o, float* final_state, int64_t B, int64_t H, int64_t T,
+                  int64_t dk, int64_t dv, gdn_dtype dtype, void* hip_stream) {
+  const int rc = check_fwd(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv,
+                           64, dtype, VEC);
+  if (rc != GDN_OK) return rc;
+  const int64_t nseq = B * H;
+  if (nseq == 0 || (T == 0 && !final_state)) return GDN_OK;
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (dtype == GDN_BF16)
+    return dk == 128 ? launch_recurrent<bf16_t, 128, VEC>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, stream)
+                     : launch_recurrent<bf16_t, 64, VEC>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, stream);
+  return dk == 128 ? launch_recurrent<float, 128, VEC>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, stream)
+                   : launch_recurrent<float, 64, VEC>(q, k, v, alpha, beta, initial_state, o, final_state, nseq, T, stream);
+}
+
 template <bool VEC>
 int scan_fwd(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
              const float* initial_state, void* o, float* final_state, int64_t B, int64_t H, int64_t T,
@@ -668,6 +700,22 @@ int scan_fwd(const void* q, const void* k, const void* v, const float* alpha, co
 }  // namespace
 
 extern "C" {
+
+int gdn_recurrent_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                      const float* beta, const float* initial_state, void* o, float* final_state,
+                      int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, gdn_dtype dtype,
+                      void* hip_stream) {
+  return recurrent_fwd<false>(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv, dtype,
+                              hip_stream);
+}
+
+int gdn_recurrent_fwd_vecgate(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, const float* initial_state, void* o, float* final_state,
+                              int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, gdn_dtype dtype,
+                              void* hip_stream) {
+  return recurrent_fwd<true>(q, k, v, alpha, beta, initial_state, o, final_state, B, H, T, dk, dv, dtype,
+                             hip_stream);
+}
 
 int gdn_scan_fwd(const void* q, const void* k, const void* v, const float* alpha,
                  const float* beta, const float* initial_state, void* o, float* final_state,

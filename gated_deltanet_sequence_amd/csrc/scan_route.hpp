@@ -16,7 +16,9 @@
 //   AGG: blocks 0 .. G-2, kind 0: B_blk (zero start, with V), kind 1: A_blk
 //        (identity start, V read as zero); written to ws slots tilde, trans.
 //   OUT: blocks 0 .. G-1 from ws slot start, output o; the last block's
-//        state is the final state.
+//        state is the final state.  With G = 1 the start slots are laid out
+//        as an initial state [nseq, D, D]: the token-by-token forward pass
+//        passes the initial state itself as ws, or NULL for a zero start.
 // Reducing a block to its map is the token loop itself on the stacked state
 // [B; A] (a rank-1 update per token, O(d^2) instead of a d^3 product).
 //
@@ -125,8 +127,8 @@ template <class E, int D, bool VEC = false>
 __global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, E* __restrict__ o,
-    float* __restrict__ final_state, int mode, int nseq, int G, int64_t T, int64_t L,
-    float* __restrict__ ws) {
+    float* final_state, int mode, int nseq, int G, int64_t T, int64_t L,
+    float* ws) {  // ws and final_state may be one array (G = 1: the start state is the initial state)
   constexpr int CPT = D / TPR;  // columns per thread
   __shared__ float ks[TILE][D], qs[TILE][D];
   __shared__ float vs[TILE][RPW], os[TILE][RPW];
@@ -163,6 +165,9 @@ __global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
   } else if (kind == 1) {
 #pragma unroll
     for (int j = 0; j < CPT; ++j) s[j] = row == c0 + j ? 1.f : 0.f;
+  } else if (!ws) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) s[j] = 0.f;
   } else {
     const float* st = ws + (2 * per + (int64_t)seq * G + g) * dd + (int64_t)row * D + c0;
 #pragma unroll

@@ -145,6 +145,31 @@ int gdn_scan_fwd(const void* q, const void* k, const void* v,
                  void* hip_stream);
 
 /*
+ * gdn_recurrent_fwd — the forward pass evaluated token by token ([P1] §1.2:
+ * each token's state follows from the previous one): one launch walks every
+ * sequence's tokens in order with the state in registers, reading the
+ * initial state once and writing the final state once.  For many short
+ * sequences (a few tokens each, e.g. several new tokens per sequence while
+ * decoding) this is much cheaper than the chunked pass, whose per-chunk work
+ * does not shrink with T; for long sequences use gdn_chunk_fwd.  Arguments,
+ * layouts, dtypes (bf16 and fp32), aliasing and errors as for gdn_chunk_fwd
+ * (no chunk size).  alpha is used as given (no clamp).
+ */
+int gdn_recurrent_fwd(const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta,
+                      const float* initial_state, void* o, float* final_state,
+                      int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                      gdn_dtype dtype, void* hip_stream);
+
+/* gdn_recurrent_fwd with the per-dimension gate of gdn_scan_fwd_vecgate
+ * (alpha [B,H,T,dk] fp32). */
+int gdn_recurrent_fwd_vecgate(const void* q, const void* k, const void* v,
+                              const float* alpha, const float* beta,
+                              const float* initial_state, void* o, float* final_state,
+                              int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                              gdn_dtype dtype, void* hip_stream);
+
+/*
  * gdn_scan_fwd_vecgate — gdn_scan_fwd with a per-dimension gate ([P1] §2.2
  * allows a vector gate): alpha is [B,H,T,dk] fp32, each entry in [0,1], and
  * decays the key columns of the state,

@@ -101,6 +101,31 @@ def test_gla_chunk_fwd_rejects(lib, kw, code):
     assert gla(lib, **kw) == code
 
 
+def rec_fwd(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, alpha=A + 192 * MB, beta=A + 200 * MB,
+            s0=None, o=A + 256 * MB, sT=None, B=1, H=1, T=64, dk=64, dv=64, dtype=1, fn="gdn_recurrent_fwd"):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return getattr(lib, fn)(P(q), P(k), P(v), P(alpha), P(beta), P(s0), P(o), P(sT),
+                            B, H, T, dk, dv, dtype, None)
+
+
+@pytest.mark.parametrize("fn", ["gdn_recurrent_fwd", "gdn_recurrent_fwd_vecgate"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(alpha=None), 1), (dict(T=-1), 1), (dict(dtype=7), 1),
+    (dict(dk=96, dv=96), 2), (dict(dk=64, dv=128), 2),
+    (dict(k=A + 64 * MB + 8), 3), (dict(sT=A + 400 * MB + 4), 3),
+    (dict(o=A + 64 * MB), 1),              # output overlaps k
+    (dict(sT=A + 128 * MB), 1),            # final state overlaps v
+    (dict(s0=A + 300 * MB, sT=A + 300 * MB + 16), 1),
+])
+def test_recurrent_fwd_rejects(lib, kw, code, fn):
+    assert rec_fwd(lib, fn=fn, **kw) == code
+
+
+def test_recurrent_fwd_vecgate_checks_the_whole_gate(lib):
+    # dk gate floats per token: an output 16 bytes into alpha's 64 * 64 floats overlaps it
+    assert rec_fwd(lib, fn="gdn_recurrent_fwd_vecgate", o=A + 192 * MB + 4096) == 1
+
+
 def test_chunk_fwd_empty_is_noop(lib):
     # no sequences, or no tokens and no state to write: nothing is launched
     assert fwd(lib, B=0) == 0
