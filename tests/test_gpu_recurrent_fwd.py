@@ -2,10 +2,10 @@
 gdn_recurrent_fwd_vecgate with a per-dimension gate) against the fp64
 oracles (oracle_fwd, oracle_fwd_vecgate), max-abs-normwise on o and the final
 state with the workloads' bars (2e-2 bf16, 1e-4 fp32): short and ragged
-lengths around the 32-token staging tile, d = 64 and 128, zero and random
-initial states, every gate law, the decode workload's shape with eight new
-tokens per sequence, a final state aliasing the initial one, and zero
-tokens."""
+lengths around the 32-token staging tile, few and many (512) sequences,
+d = 64 and 128, zero and random initial states, every gate law, the decode
+workload's shape with eight new tokens per sequence, a final state aliasing
+the initial one, and zero tokens."""
 import numpy as np
 import pytest
 import torch
@@ -30,6 +30,12 @@ CASES = [
     (1, 2, 65, 128, True, "slow", "bf16", True),
     (2, 2, 300, 64, False, "resets", "bf16", True),
     (1, 1, 500, 128, True, "default", "f32", True),
+    # many sequences (512)
+    (32, 16, 1, 128, True, "default", "bf16", False),
+    (16, 32, 17, 64, True, "slow", "f32", False),
+    (64, 8, 40, 128, False, "resets", "f32", False),
+    (32, 16, 16, 128, True, "fast", "bf16", True),
+    (8, 64, 33, 64, True, "default", "f32", True),
 ]
 
 
@@ -84,8 +90,9 @@ def test_recurrent_fwd_decode_shape_eight_tokens():
 
 
 @pytest.mark.parametrize("vec", [False, True])
-def test_recurrent_fwd_aliasing_and_edges(vec):
-    x = _inputs(2, 2, 77, 128, True, "default", "bf16", vec, seed=960)
+@pytest.mark.parametrize("heads", [4, 512])
+def test_recurrent_fwd_aliasing_and_edges(vec, heads):
+    x = _inputs(heads // 2, 2, 77, 128, True, "default", "bf16", vec, seed=960)
     xd = to_dev(x)
     ref_o, ref_s = _run(xd, vec)
     s = xd["s0"].clone()
@@ -100,9 +107,9 @@ def test_recurrent_fwd_aliasing_and_edges(vec):
     ro, rs = _oracle(xz, vec)
     assert maxrel(to_np(o), ro) <= TOL["bf16"] and maxrel(to_np(sT), rs) <= TOL["bf16"]
     # zero tokens: the final state is the initial one
-    x0 = _inputs(2, 3, 0, 64, True, "default", "bf16", vec, seed=961)
+    x0 = _inputs(heads // 2, 2, 0, 64, True, "default", "bf16", vec, seed=961)
     o, sT = _run(to_dev(x0), vec)
-    assert o.shape == (2, 3, 0, 64) and torch.equal(sT.cpu(), x0["s0"])
+    assert o.shape == (heads // 2, 2, 0, 64) and torch.equal(sT.cpu(), x0["s0"])
     # no sequences
     xn = _inputs(0, 3, 10, 64, True, "default", "bf16", vec, seed=962)
     o, sT = _run(to_dev(xn), vec)
