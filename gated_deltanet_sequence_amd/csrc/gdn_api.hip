@@ -633,15 +633,21 @@ namespace {
 // The token-by-token forward pass: the scan route's replay kernel with one
 // block per sequence (G = 1), starting from the initial state itself (or a
 // zero state) and writing the final state; no workspace and no other launch.
+constexpr int64_t SHORT_T = 64;  // up to this length, tiles of SHORT_TILE tokens
 template <class E, int D, bool VEC>
 int launch_recurrent(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                      const float* s0, void* o, float* sT, int64_t nseq, int64_t T, hipStream_t stream) {
   using namespace gdn::scan;
   const int64_t nb = scan_blocks(SCAN_OUT, (int)nseq, 1, D);
   if (nb > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((scan_tokens_kernel<E, D, VEC>), dim3((unsigned)nb), dim3(THREADS), 0, stream,
-                     static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v), alpha, beta,
-                     static_cast<E*>(o), sT, (int)SCAN_OUT, (int)nseq, 1, T, T, const_cast<float*>(s0));
+  if (T <= SHORT_T)
+    hipLaunchKernelGGL((scan_tokens_kernel<E, D, VEC, SHORT_TILE>), dim3((unsigned)nb), dim3(THREADS), 0, stream,
+                       static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v), alpha, beta,
+                       static_cast<E*>(o), sT, (int)SCAN_OUT, (int)nseq, 1, T, T, const_cast<float*>(s0));
+  else
+    hipLaunchKernelGGL((scan_tokens_kernel<E, D, VEC>), dim3((unsigned)nb), dim3(THREADS), 0, stream,
+                       static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v), alpha, beta,
+                       static_cast<E*>(o), sT, (int)SCAN_OUT, (int)nseq, 1, T, T, const_cast<float*>(s0));
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

@@ -41,7 +41,9 @@ enum { SCAN_AGG = 0, SCAN_OUT = 1 };
 constexpr int TPR = 16;              // threads per state row
 constexpr int THREADS = 256;
 constexpr int RPW = THREADS / TPR;   // rows per workgroup
-constexpr int TILE = 32;             // tokens per LDS tile
+constexpr int TILE = 32;             // tokens per LDS tile (the scan route)
+constexpr int SHORT_TILE = 8;        // tokens per tile for short sequences
+
 
 // Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
 // Each step reads lanes inside the row only, so bound_ctrl (and the old
@@ -77,26 +79,33 @@ template <> struct TileWord<bf16_t> {
   }
 };
 
+// Words of one tile's value rows (TL x RPW elements) per thread, at least
+// one: with short tiles the threads past the rows reread the tile's last
+// word and do not stage it.
+template <class E, int TL> struct VWords {
+  static constexpr int value = (TL * RPW / TileWord<E>::EPW + THREADS - 1) / THREADS;
+};
+
 // Loads one tile's inputs into registers (the tile goes to LDS after the
-// current one has been computed): keys and queries (TILE x D, word
+// current one has been computed): keys and queries (TL x D, word
 // p = tid + THREADS i holds elements EPW p ..), per-dimension gates (element
-// tid + THREADS i), this workgroup's value rows (TILE x RPW, in words like
-// the keys), scalar gates (threads below TILE).  Every load is
+// tid + THREADS i), this workgroup's value rows (TL x RPW, in words like
+// the keys), scalar gates (threads below TL).  Every load is
 // unconditional: past the n tokens of a ragged tile it reads the last token
 // again, and the tile is masked when it goes to LDS.  (A conditional load
 // ends in a register copy that waits for it, which would serialize the
 // loads.)
-template <class E, int D, bool VEC>
-__device__ __forceinline__ void fetch_tile(typename TileWord<E>::type (&kreg)[TILE * D / THREADS / TileWord<E>::EPW],
-                                           typename TileWord<E>::type (&qreg)[TILE * D / THREADS / TileWord<E>::EPW],
-                                           typename TileWord<E>::type (&vreg)[TILE * RPW / THREADS / TileWord<E>::EPW],
-                                           float (&avreg)[VEC ? TILE * D / THREADS : 1], float& areg, float& breg,
+template <class E, int D, bool VEC, int TL>
+__device__ __forceinline__ void fetch_tile(typename TileWord<E>::type (&kreg)[TL * D / THREADS / TileWord<E>::EPW],
+                                           typename TileWord<E>::type (&qreg)[TL * D / THREADS / TileWord<E>::EPW],
+                                           typename TileWord<E>::type (&vreg)[(VWords<E, TL>::value)],
+                                           float (&avreg)[VEC ? TL * D / THREADS : 1], float& areg, float& breg,
                                            const E* q, const E* k, const E* v, const float* alpha, const float* beta,
                                            int64_t base, int64_t tt, int n, int rg, int tid) {
   typedef typename TileWord<E>::type W;
   constexpr int EPW = TileWord<E>::EPW;
 #pragma unroll
-  for (int i = 0; i < TILE * D / THREADS / EPW; ++i) {
+  for (int i = 0; i < TL * D / THREADS / EPW; ++i) {
     const int e = EPW * (tid + THREADS * i), c = e % D;
     const int t = e / D < n ? e / D : n - 1;
     kreg[i] = *reinterpret_cast<const W*>(k + (base + tt + t) * D + c);
@@ -104,36 +113,41 @@ __device__ __forceinline__ void fetch_tile(typename TileWord<E>::type (&kreg)[TI
   }
   if constexpr (VEC) {
 #pragma unroll
-    for (int i = 0; i < TILE * D / THREADS; ++i) {
+    for (int i = 0; i < TL * D / THREADS; ++i) {
       const int e = tid + THREADS * i, c = e % D;
       const int t = e / D < n ? e / D : n - 1;
       avreg[i] = alpha[(base + tt + t) * D + c];
     }
   }
 #pragma unroll
-  for (int i = 0; i < TILE * RPW / THREADS / EPW; ++i) {
-    const int e = EPW * (tid + THREADS * i), r = e % RPW;
+  for (int i = 0; i < VWords<E, TL>::value; ++i) {
+    int e = EPW * (tid + THREADS * i);
+    e = e < TL * RPW ? e : TL * RPW - EPW;
+    const int r = e % RPW;
     const int t = e / RPW < n ? e / RPW : n - 1;
     vreg[i] = *reinterpret_cast<const W*>(v + (base + tt + t) * D + rg * RPW + r);
   }
-  if (tid < TILE) {
+  if (tid < TL) {
     const int t = tid < n ? tid : n - 1;
     if constexpr (!VEC) areg = alpha[base + tt + t];
     breg = beta[base + tt + t];
   }
 }
 
-template <class E, int D, bool VEC = false>
+// TL: tokens per LDS tile (TILE for the scan route, SHORT_TILE for short
+// sequences: a smaller LDS footprint, so more workgroups share a CU).
+template <class E, int D, bool VEC = false, int TL = TILE>
 __global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, E* __restrict__ o,
     float* final_state, int mode, int nseq, int G, int64_t T, int64_t L,
     float* ws) {  // ws and final_state may be one array (G = 1: the start state is the initial state)
   constexpr int CPT = D / TPR;  // columns per thread
-  __shared__ float ks[TILE][D], qs[TILE][D];
-  __shared__ float vs[TILE][RPW], os[TILE][RPW];
-  __shared__ float as_[TILE], bs_[TILE];
-  __shared__ float av[VEC ? TILE : 1][VEC ? D : 1];  // per-dimension gates
+  static_assert(TL * D % (THREADS * TileWord<E>::EPW) == 0 && TL <= THREADS, "tile words spread evenly");
+  __shared__ float ks[TL][D], qs[TL][D];
+  __shared__ float vs[TL][RPW], os[TL][RPW];
+  __shared__ float as_[TL], bs_[TL];
+  __shared__ float av[VEC ? TL : 1][VEC ? D : 1];  // per-dimension gates
 
   int64_t b = blockIdx.x;
   const int rg = (int)(b % (D / RPW));
@@ -182,15 +196,15 @@ __global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
   // registers while the current one is computed, and go to LDS after it.
   typedef typename TileWord<E>::type W;
   constexpr int EPW = TileWord<E>::EPW;
-  constexpr int NKQ = TILE * D / THREADS / EPW, NV = TILE * RPW / THREADS / EPW;
+  constexpr int NKQ = TL * D / THREADS / EPW, NV = VWords<E, TL>::value;
   W kreg[NKQ], qreg[NKQ], vreg[NV];
-  float avreg[VEC ? TILE * D / THREADS : 1];
+  float avreg[VEC ? TL * D / THREADS : 1];
   float areg = 1.f, breg = 0.f;
   if (len > 0)
-    fetch_tile<E, D, VEC>(kreg, qreg, vreg, avreg, areg, breg, q, k, v, alpha, beta, base, 0,
-                          (int)(len < TILE ? len : TILE), rg, tid);
-  for (int64_t tt = 0; tt < len; tt += TILE) {
-    const int n = (int)(len - tt < TILE ? len - tt : TILE);
+    fetch_tile<E, D, VEC, TL>(kreg, qreg, vreg, avreg, areg, breg, q, k, v, alpha, beta, base, 0,
+                              (int)(len < TL ? len : TL), rg, tid);
+  for (int64_t tt = 0; tt < len; tt += TL) {
+    const int n = (int)(len - tt < TL ? len - tt : TL);
     // stage the tile: keys, queries, this workgroup's value rows, gates
 #pragma unroll
     for (int i = 0; i < NKQ; ++i) {
@@ -204,7 +218,7 @@ __global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
     }
     if constexpr (VEC) {
 #pragma unroll
-      for (int i = 0; i < TILE * D / THREADS; ++i) {
+      for (int i = 0; i < TL * D / THREADS; ++i) {
         const int e = tid + THREADS * i, t = e / D, c = e % D;
         av[t][c] = t < n ? avreg[i] : 1.f;
       }
@@ -212,18 +226,20 @@ __global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = EPW * (tid + THREADS * i), t = e / RPW, r = e % RPW;
+      if (e < TL * RPW) {
 #pragma unroll
-      for (int h = 0; h < EPW; ++h) vs[t][r + h] = (t < n && kind != 1) ? TileWord<E>::elem(vreg[i], h) : 0.f;
+        for (int h = 0; h < EPW; ++h) vs[t][r + h] = (t < n && kind != 1) ? TileWord<E>::elem(vreg[i], h) : 0.f;
+      }
     }
-    if (tid < TILE) {
+    if (tid < TL) {
       as_[tid] = (!VEC && tid < n) ? areg : 1.f;
       bs_[tid] = tid < n ? breg : 0.f;
     }
     __syncthreads();
-    if (tt + TILE < len) {
-      const int64_t nt = tt + TILE;
-      fetch_tile<E, D, VEC>(kreg, qreg, vreg, avreg, areg, breg, q, k, v, alpha, beta, base, nt,
-                            (int)(len - nt < TILE ? len - nt : TILE), rg, tid);
+    if (tt + TL < len) {
+      const int64_t nt = tt + TL;
+      fetch_tile<E, D, VEC, TL>(kreg, qreg, vreg, avreg, areg, breg, q, k, v, alpha, beta, base, nt,
+                                (int)(len - nt < TL ? len - nt : TL), rg, tid);
     }
     for (int t = 0; t < n; ++t) {
       const float a = as_[t], bt = bs_[t];
