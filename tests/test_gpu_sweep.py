@@ -7,10 +7,12 @@ a length from 1 to 900 tokens (mostly not a multiple of any chunk), d = 64
 or 128, bf16 or fp32, with or without an initial state, and one of the gate
 laws (default, slow, fast, resets, beta2); eight more cases draw one or two
 sequences of 1,600 to 6,000 tokens, long enough for the split entry points
-to plan segments, and six more run the plain chunked pass at chunk_size 32
-(numpy.random.default_rng(2028)).  Each case names the entry point
-it runs: the plain chunked pass, the sequence split, the blocked scan, the
-chunked per-dimension gate (plain and split), and gated linear attention."""
+to plan segments, six more run the plain chunked pass at chunk_size 32
+(numpy.random.default_rng(2028)), and fifteen more the other entry points
+(numpy.random.default_rng(2029)): the two-pass per-dimension gate, the
+per-dimension-gate scan, gated linear attention at chunk_size 32 (bf16 and
+fp32), and the token-by-token pass with either gate.  Each case names the
+entry point it runs."""
 import numpy as np
 import pytest
 import torch
@@ -18,7 +20,9 @@ import torch
 import oracle
 from gated_deltanet_sequence_amd import inputs
 from gated_deltanet_sequence_amd.binding import (gdn_chunk_fwd, gdn_chunk_fwd_split, gdn_chunk_fwd_vecgate,
-                                                 gdn_chunk_fwd_vecgate_split, gdn_scan_fwd, gla_chunk_fwd)
+                                                 gdn_chunk_fwd_vecgate_2pass, gdn_chunk_fwd_vecgate_split,
+                                                 gdn_recurrent_fwd, gdn_recurrent_fwd_vecgate, gdn_scan_fwd,
+                                                 gdn_scan_fwd_vecgate, gla_chunk_fwd)
 
 from _helpers import TOL, maxrel, oracle_inputs, to_dev, to_np
 
@@ -63,7 +67,21 @@ def _draw_c32_cases(n=6):
              GATES[int(rng.integers(len(GATES)))], 5000 + i) for i in range(n)]
 
 
-CASES = _draw_cases() + _draw_long_cases() + _draw_c32_cases()
+def _draw_more_cases(n=15):
+    """The entry points added after the first draws, three cases each."""
+    rng = np.random.default_rng(2029)
+    entries = ["vecgate_2pass", "vecgate_scan", "gla32", "recurrent", "recurrent_vecgate"]
+    cases = []
+    for i in range(n):
+        entry = entries[i % len(entries)]
+        gate = GATES[int(rng.integers(4))]
+        cases.append((entry, int(rng.integers(1, 4)), int(rng.integers(1, 6)), int(rng.integers(1, 901)),
+                      int(rng.choice([64, 128])), "bf16" if rng.random() < 0.6 else "f32",
+                      bool(rng.random() < 0.5), gate, 6000 + i))
+    return cases
+
+
+CASES = _draw_cases() + _draw_long_cases() + _draw_c32_cases() + _draw_more_cases()
 
 
 def _run(entry, xd, av):
@@ -78,8 +96,15 @@ def _run(entry, xd, av):
         return gdn_scan_fwd(*a)
     if entry == "gla":
         return gla_chunk_fwd(*a, 64)
+    if entry == "gla32":
+        return gla_chunk_fwd(*a, 32)
+    if entry == "recurrent":
+        return gdn_recurrent_fwd(*a)
     va = (xd["q"], xd["k"], xd["v"], av, xd["beta"], xd["s0"])
-    return gdn_chunk_fwd_vecgate(*va) if entry == "vecgate" else gdn_chunk_fwd_vecgate_split(*va)
+    f = {"vecgate": gdn_chunk_fwd_vecgate, "vecgate_split": gdn_chunk_fwd_vecgate_split,
+         "vecgate_2pass": gdn_chunk_fwd_vecgate_2pass, "vecgate_scan": gdn_scan_fwd_vecgate,
+         "recurrent_vecgate": gdn_recurrent_fwd_vecgate}[entry]
+    return f(*va)
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "%s_B%dH%dT%dd%d_%s_%s_%s" % (
@@ -87,7 +112,7 @@ def _run(entry, xd, av):
 def test_random_shape_against_oracle(case):
     entry, B, H, T, d, dtype, init, gate, seed = case
     print("case sweep", case, flush=True)
-    vec = entry.startswith("vecgate")
+    vec = "vecgate" in entry
     x = inputs.make_fwd_inputs(B, H, T, d, dtype, seed=seed, init_state=init,
                                gate="default" if vec else gate)
     av = None
@@ -98,7 +123,7 @@ def test_random_shape_against_oracle(case):
     o, sT = _run(entry, xd, av)
     torch.cuda.synchronize()
     (q, k, v, al, b), s0 = oracle_inputs(x)
-    if entry == "gla":
+    if entry.startswith("gla"):
         ro, rs = oracle.oracle_gla_fwd(q, k, v, al, b, s0)
     elif vec:
         ro, rs = oracle.oracle_fwd_vecgate(q, k, v, al, b, s0)
