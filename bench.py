@@ -755,14 +755,14 @@ def summarize_trace(trace_dir, out_name, command, note="", tail=100):
     out += ["# " + line for line in note.splitlines() if line.strip()]
     out.append("# per kernel and launch shape: launches, mean, min and max duration, and the mean of")
     out.append("# the last %d launches of that shape (us)" % tail)
-    out.append("%-66s %6s %7s %8s %10s %10s %10s %10s" % ("kernel", "wgs", "threads", "launches",
+    out.append("%-72s %6s %7s %8s %10s %10s %10s %10s" % ("kernel", "wgs", "threads", "launches",
                                                         "mean_us", "min_us", "max_us", "tail_us"))
     derived = []
     for (k, wg, th), v in groups.items():
         t = v[-tail:]
         tmean = sum(t) / len(t)
-        out.append("%-66s %6d %7d %8d %10.2f %10.2f %10.2f %10.2f" % (
-            k[:66], wg, th, len(v), sum(v) / len(v) / 1e3, min(v) / 1e3, max(v) / 1e3, tmean / 1e3))
+        out.append("%-72s %6d %7d %8d %10.2f %10.2f %10.2f %10.2f" % (
+            k[:72], wg, th, len(v), sum(v) / len(v) / 1e3, min(v) / 1e3, max(v) / 1e3, tmean / 1e3))
         alg = None
         if "chunk_fwd_pipe_kernel<false, true>" in k and wg == 256:
             alg, what = alg_bytes_main(MAIN["B"], MAIN["H"], MAIN["T"], MAIN["d"]), "main workload"
