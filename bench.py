@@ -463,6 +463,10 @@ def time_few_new_tokens(torch, dev, T=8, launches=20):
         e1.record(stream)
         torch.cuda.synchronize()
         res[name + "_ms"] = e0.elapsed_time(e1) / launches
+    # the state read and written once, the tokens' q, k, v, alpha, beta read and o written once
+    byts = 2 * N * H * d * d * 4 + N * H * T * (3 * d * 2 + 2 * 4 + d * 2)
+    res["alg_bytes"] = byts
+    res["recurrent_fwd_hbm_frac"] = byts / (res["recurrent_fwd_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS
     return res
 
 
