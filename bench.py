@@ -149,7 +149,14 @@ def settle_clocks(torch, step, settle_ms=SETTLE_MS):
     return n
 
 
-def time_chunk(torch, xd, steps, warmup, settle_ms=SETTLE_MS):
+def time_chunk(torch, xd, steps, warmup, settle_ms=SETTLE_MS, spread=True):
+    """Settle the clocks, run `warmup` steps, then (with `spread`) `steps`
+    launches each bracketed by its own pair of HIP events, for the spread of
+    launch times, and finally the timed region: `steps` launches back to back
+    between one pair of HIP events.  Per-launch events add a few microseconds
+    of stream work between launches, so the timed region has none.  Returns
+    the timed region's wall seconds, its event time per launch (ms), the
+    per-launch event times (ms) and the outputs."""
     from gated_deltanet_sequence_amd.binding import gdn_chunk_fwd
     B, H, T, d = xd["q"].shape
     o = torch.empty_like(xd["v"])
@@ -164,18 +171,28 @@ def time_chunk(torch, xd, steps, warmup, settle_ms=SETTLE_MS):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    kms = []
+    if spread:
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for i in range(steps):
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
+    e0.record(stream)
+    for _ in range(steps):
         step()
-        ends[i].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     time_chunk.settle_launches = settle
-    return wall, kms, o, sT
+    return wall, e0.elapsed_time(e1) / steps, kms, o, sT
 
 
 LONG = dict(B=1, H=16, T=131072, d=128, seed=4, init_state=True,
@@ -379,6 +396,9 @@ def time_decode(torch, dev, steps_override=None):
     from gated_deltanet_sequence_amd import inputs
     from gated_deltanet_sequence_amd.binding import gdn_recurrent_step
     N, H, d, steps = DECODE["N"], DECODE["H"], DECODE["d"], DECODE["steps"]
+    # first, so that the timed decode steps below are the last scalar-gate
+    # steps of this shape in a kernel trace
+    few = time_few_new_tokens(torch, dev) if steps_override is None else None
     x = inputs.make_decode_inputs(N, H, d, steps, "bf16", seed=DECODE["seed"])
     if steps_override is not None:
         steps = min(steps, steps_override)
@@ -413,8 +433,8 @@ def time_decode(torch, dev, steps_override=None):
     avg_ms = ev[0].elapsed_time(ev[steps]) / steps
     byts = alg_bytes_decode(N, H, d)
     variants = {} if steps_override is not None else time_decode_variants(torch, dev, x, qs, ks, vs, bes, o)
-    if steps_override is None:
-        variants["few_new_tokens"] = time_few_new_tokens(torch, dev)
+    if few is not None:
+        variants["few_new_tokens"] = few
     return {"workload": "decode: 256 sequences x H=16, d_k=d_v=128, fp32 state [256,16,128,128] "
                         "updated in place, bf16 q/k/v, 64 consecutive steps",
             "tokens_per_s": N / (avg_ms * 1e-3), "ms_per_step": avg_ms,
@@ -854,18 +874,17 @@ def main():
         dst.copy_(src)
         del src, dst
         if args.pmc_pass == "main":
-            time_chunk(torch, xd, steps=PMC_LAUNCHES, warmup=0)
+            time_chunk(torch, xd, steps=PMC_LAUNCHES, warmup=0, spread=False)
         else:
             time_decode(torch, dev, steps_override=PMC_LAUNCHES)
         torch.cuda.synchronize()
         print("pmc pass done", flush=True)
         return
 
-    wall, kms, o, sT = time_chunk(torch, xd, args.steps, args.warmup)
+    wall, avg_k, kms, o, sT = time_chunk(torch, xd, args.steps, args.warmup)
     B, H, T, d, C = MAIN["B"], MAIN["H"], MAIN["T"], MAIN["d"], MAIN["C"]
     tokens = B * T
     ms_per_step = wall * 1e3 / args.steps
-    avg_k = sum(kms) / len(kms)
     ks = sorted(kms)
 
     def pct(q):
@@ -894,9 +913,11 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": read_traffic(),
                      "kernel": "chunk_fwd_pipe_kernel", "alg_bytes_per_launch": alg_b,
-                     "avg_launch_ms": avg_k,
+                     # event time of the timed region per launch (back to back)
+                     "avg_launch_ms": avg_k, "timed_launches": args.steps,
+                     # spread: the same number of launches, each between its own events
                      "launch_ms_median": pct(0.5), "launch_ms_p10": pct(0.1),
-                     "launch_ms_p90": pct(0.9), "timed_launches": len(kms),
+                     "launch_ms_p90": pct(0.9), "launch_ms_mean": sum(kms) / len(kms),
                      "mfma_achieved_TFLOPs": alg_f / (avg_k * 1e-3) / 1e12,
                      "mfma_frac": alg_f / (avg_k * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                      # rocprofv3 counters (profiles/activity_chunk_fwd_main.txt; None once the
