@@ -46,8 +46,11 @@
 //
 // With a scalar gate (VG = false: alpha is [.., T] and every key column
 // decays alike) the same algebra holds with G_r[j] = g_r for all j; that
-// instance is the library's path for fp32 inputs (a 64-token chunk's fp32
-// buffers would exceed the LDS at d_k = 128).
+// instance is the library's path for fp32 inputs and for 32-token chunks (a
+// 64-token chunk's fp32 buffers would exceed the LDS at d_k = 128).  The GLA
+// instance evaluates gated linear attention without the delta rule (L = 0,
+// U = diag(beta) V), and the PREP instance is the first pass of the two-pass
+// route (the chunk records, no state).
 #pragma once
 
 #include "gdn_common.hpp"
