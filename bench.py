@@ -788,7 +788,7 @@ def summarize_trace(trace_dir, out_name, command, note="", tail=100):
         out.append("%-72s %6d %7d %8d %10.2f %10.2f %10.2f %10.2f" % (
             k[:72], wg, th, len(v), sum(v) / len(v) / 1e3, min(v) / 1e3, max(v) / 1e3, tmean / 1e3))
         alg = None
-        if "chunk_fwd_pipe_kernel<false, true>" in k and wg == 256:
+        if "chunk_fwd_pipe_kernel<false, true, 4>" in k and wg == 256:
             alg, what = alg_bytes_main(MAIN["B"], MAIN["H"], MAIN["T"], MAIN["d"]), "main workload"
         elif "recurrent_step_kernel" in k and wg == DECODE["N"] * DECODE["H"]:
             # the last template argument is the gate kind: 0 scalar, 1 per

@@ -1,8 +1,8 @@
 // Pipelined chunked forward pass of the gated delta rule for bf16 inputs,
-// d_k = d_v = 128 or 64, 64-token chunks, on gfx950.  The kernel always works
-// on 128 keys; with d = 64 the keys 64..127 are zero in LDS (their loads read
-// past the buffer range, which returns zero) and in the state, so they add
-// nothing.
+// d_k = d_v = 128 or 64, 64-token chunks, on gfx950.  The LDS layout always
+// holds 128 keys; with d = 64 the keys 64..127 are zero in LDS (their loads
+// read past the buffer range, which returns zero) and in the state, and the
+// instance with KB = 2 key blocks skips the products over them.
 //
 // Sources (web pages, by title and section):
 //   [P1] "Gated DeltaNet GPU并行实现：拆解线性注意力循环的两种高效方案"
@@ -388,9 +388,10 @@ __device__ __forceinline__ void read_p(const Smem& sm, const StateAddr& A, int64
 // waves' reads queue behind the others').
 // OUT = false: no output (the first launch of the sequence split, which
 // needs only the state): no Q S^T, no P U, no stores.
-template <bool FINISH_, bool CHAIN, bool GLA, bool PRE = false, bool OUT = true>
+template <bool FINISH_, bool CHAIN, bool GLA, bool PRE = false, bool OUT = true, int KB = 4>
 __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, const StateAddr& A,
                                              StateRegs& R, int64_t c, int DV, int lane) {
+  constexpr int JB = 2 * KB;  // state tiles of 16 keys that can be nonzero
   constexpr bool FINISH = FINISH_ && OUT;
   const int lr = lane & 15, lg = lane >> 4;
   bf16x8_t pf[4][2];
@@ -402,7 +403,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   const int buf = (int)(c & 1);
   lptr kf_b[4], qf_b[4], kt_b[4];
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) {
+  for (int pp = 0; pp < KB; ++pp) {
     kf_b[pp] = lane_base(k_buf<GLA>(c), A.frag[pp]);
     qf_b[pp] = lane_base(q_buf<GLA>(c), A.frag[pp]);
     kt_b[pp] = lane_base(k_buf<GLA>(c), A.ktr[pp]);
@@ -419,7 +420,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   // operands of U are packed, and finally the state update.
   bf16x8_t Sop[4];
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) Sop[pp] = pack_op(R.S[2 * pp], R.S[2 * pp + 1]);
+  for (int pp = 0; pp < KB; ++pp) Sop[pp] = pack_op(R.S[2 * pp], R.S[2 * pp + 1]);
 
   // ---- Z = K S^T (tile per 16-token block, rows = token).  The fragments
   // of the 16-token blocks K0..K3, Q0..Q3 pass through a ring of three
@@ -431,7 +432,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     if (GLA && n < 4) return;  // without the delta rule K S^T is not needed
     if (!OUT && n >= 4) return;  // no output: Q is not needed
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp)
+    for (int pp = 0; pp < KB; ++pp)
       fr[n % 3][pp] = PRE && n < 3 ? R.Kpre[n][pp]
                                    : as_op(n < 4 ? ld3<uint4>(kf_b[pp], n * 4096) : ld3<uint4>(qf_b[pp], (n - 4) * 4096));
   };
@@ -453,10 +454,12 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     f32x4 az = zero4();
     if constexpr (!GLA) {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) az = mfma(fr[rb % 3][pp], Sop[pp], az);
+      for (int pp = 0; pp < KB; ++pp) az = mfma(fr[rb % 3][pp], Sop[pp], az);
     }
-    R.S[2 * rb] *= decay;
-    R.S[2 * rb + 1] *= decay;
+    if (2 * rb < JB) {
+      R.S[2 * rb] *= decay;
+      R.S[2 * rb + 1] *= decay;
+    }
     Z[rb] = az;
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -491,7 +494,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
     if constexpr (OUT) {
       f32x4 ao = zero4();
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) ao = mfma(Sop[pp], fr[(4 + rb) % 3][pp], ao);
+      for (int pp = 0; pp < KB; ++pp) ao = mfma(Sop[pp], fr[(4 + rb) % 3][pp], ao);
       O1[rb] = ao;
     }
     if constexpr (GLA) {
@@ -521,6 +524,7 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   read_kt(0, kt[0]);
   read_kt(1, kt[1]);
   read_kt(2, kt[2]);
+  static_assert(JB >= 4, "the K^T ring and the key pre-reads below assume at least four state tiles");
   __builtin_amdgcn_sched_barrier(0);
   // ---- U = Ti Y (Ti lower triangular: row block rb needs the 32-token blocks
   // pp <= rb/2, the upper 16x16 blocks inside them are zero) while O1 takes
@@ -578,14 +582,16 @@ __device__ __forceinline__ void state_period(const Smem& sm, const Seq& sq, cons
   lptr kn_b[4];
   if constexpr (!GLA) {
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) kn_b[pp] = lane_base(k_buf<GLA>(c + 1), A.frag[pp]);
+    for (int pp = 0; pp < KB; ++pp) kn_b[pp] = lane_base(k_buf<GLA>(c + 1), A.frag[pp]);
   }
+  // (the key pre-reads run in the last three tiles but one: JB - 4 .. JB - 2)
 #pragma unroll
-  for (int jb = 0; jb < 8; ++jb) {
-    if (jb < 5) read_kt(jb + 3, kt[(jb + 3) % 4]);
-    if (!GLA && jb >= 4 && jb <= 6) {
+  for (int jb = 0; jb < JB; ++jb) {
+    if (jb < JB - 3) read_kt(jb + 3, kt[(jb + 3) % 4]);
+    if (!GLA && jb >= JB - 4 && jb <= JB - 2) {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) R.Kpre[jb - 4][pp] = as_op(ld3<uint4>(kn_b[pp], (jb - 4) * 4096));
+      for (int pp = 0; pp < KB; ++pp)
+        R.Kpre[jb - (JB - 4)][pp] = as_op(ld3<uint4>(kn_b[pp], (jb - (JB - 4)) * 4096));
     }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc = R.S[jb];
@@ -670,13 +676,13 @@ constexpr int TILE_SB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
 // Tiles TB .. TE-1 of P of chunk c.  Tiles are software-pipelined: the
 // products of tile t + 1 are issued before the decay, mask and store of tile t.
-template <bool GLA, int TB = 0, int TE = 10>
+template <bool GLA, int TB = 0, int TE = 10, int KB = 4>
 __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const int buf = (int)(c & 1);
   lptr kf_b[4], qf_b[4];
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) {
+  for (int pp = 0; pp < KB; ++pp) {
     kf_b[pp] = lane_base(k_buf<GLA>(c), A.frag[pp]);
     qf_b[pp] = lane_base(q_buf<GLA>(c), A.frag[pp]);
   }
@@ -689,11 +695,11 @@ __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c,
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) kf[b][pp] = as_op(ld3<uint4>(kf_b[pp], b * 4096));
+    for (int pp = 0; pp < KB; ++pp) kf[b][pp] = as_op(ld3<uint4>(kf_b[pp], b * 4096));
 #pragma unroll
   for (int b = 0; b < (TB == 0 ? 2 : 4); ++b)
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) qf[b][pp] = as_op(ld3<uint4>(qf_b[pp], b * 4096));
+    for (int pp = 0; pp < KB; ++pp) qf[b][pp] = as_op(ld3<uint4>(qf_b[pp], b * 4096));
   // decay of element (s, r): 2^(g_r - g_C) 2^(g_C - g_s) when split, else
   // 2^(g_r - g_s) from the log table
   const bool split = split_decay(sm, c);
@@ -708,7 +714,7 @@ __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c,
   auto tile = [&](int t) {
     f32x4 acc = zero4();
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) acc = mfma(kf[TILE_SB[t]][pp], qf[TILE_RB[t]][pp], acc);
+    for (int pp = 0; pp < KB; ++pp) acc = mfma(kf[TILE_SB[t]][pp], qf[TILE_RB[t]][pp], acc);
     return acc;
   };
   auto run = [&](auto SPLIT) {
@@ -719,7 +725,7 @@ __device__ __forceinline__ void build_p(Smem& sm, const StateAddr& A, int64_t c,
       const int rb = TILE_RB[t], sb = TILE_SB[t];
       if (TB == 0 && sb == 0 && rb >= 1 && rb < 3) {
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) qf[rb + 1][pp] = as_op(ld3<uint4>(qf_b[pp], (rb + 1) * 4096));
+        for (int pp = 0; pp < KB; ++pp) qf[rb + 1][pp] = as_op(ld3<uint4>(qf_b[pp], (rb + 1) * 4096));
       }
       if (t + 1 < TE) acc[(t + 1) & 1] = tile(t + 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -752,10 +758,10 @@ struct FragRegs {
   uint4 kf[4][4];
 };
 
-template <bool GLA>
+template <bool GLA, int KB = 4>
 __device__ __forceinline__ void read_frags(FragRegs& R, const StateAddr& A, int64_t c) {
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) {
+  for (int pp = 0; pp < KB; ++pp) {
     const lptr b = lane_base(k_buf<GLA>(c), A.frag[pp]);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) R.kf[rb][pp] = ld3<uint4>(b, rb * 4096);
@@ -789,6 +795,7 @@ __device__ __forceinline__ void build_gates(Smem& sm, float ra, float rb, int64_
 // the order in which the inverse consumes them as MFMA A operands.  The row
 // factor beta_r multiplies the decay (split as in build_p), and the tiles are
 // software-pipelined as in build_p.
+template <int KB = 4>
 __device__ __forceinline__ void build_l(Smem& sm, const FragRegs& R, int64_t c, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const int lb = (int)(c & 1);
@@ -806,7 +813,7 @@ __device__ __forceinline__ void build_l(Smem& sm, const FragRegs& R, int64_t c, 
   auto tile = [&](int t) {
     f32x4 acc = zero4();
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) acc = mfma(as_op(R.kf[TILE_SB[t]][pp]), as_op(R.kf[TILE_RB[t]][pp]), acc);
+    for (int pp = 0; pp < KB; ++pp) acc = mfma(as_op(R.kf[TILE_SB[t]][pp]), as_op(R.kf[TILE_RB[t]][pp]), acc);
     return acc;
   };
   auto run = [&](auto SPLIT) {
@@ -1043,7 +1050,10 @@ __host__ __device__ inline int map_chains(const ChainMap& m) {
 // OUT = false (delta rule only): the first launch of the sequence split,
 // which needs the segment states and no output; the P wave, the loads of Q
 // and the output products are left out.
-template <bool GLA, bool OUT = true>
+// KB: 32-key blocks that can be nonzero, dk / 32.  With dk = 64 (KB = 2) the
+// keys 64..127 are zero in LDS and in the state, so the products over them
+// and the state tiles of those keys are skipped.
+template <bool GLA, bool OUT = true, int KB = 4>
 __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta,
@@ -1161,13 +1171,13 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     lds_barrier();
     lds_barrier();
     if (nch > 0) {
-      state_period<false, true, GLA, false, OUT>(sm, sq, A, R, 0, DV, lane);
+      state_period<false, true, GLA, false, OUT, KB>(sm, sq, A, R, 0, DV, lane);
       lds_barrier();
       for (int64_t p = 1; p < nch; ++p) {
-        state_period<true, true, GLA, !GLA, OUT>(sm, sq, A, R, p, DV, lane);
+        state_period<true, true, GLA, !GLA, OUT, KB>(sm, sq, A, R, p, DV, lane);
         lds_barrier();
       }
-      if (OUT) state_period<true, false, GLA>(sm, sq, A, R, nch, DV, lane);
+      if (OUT) state_period<true, false, GLA, false, true, KB>(sm, sq, A, R, nch, DV, lane);
     }
     lds_barrier();
     if (sT) {
@@ -1184,7 +1194,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
       // about 500 cycles into the period, behind those of the state waves,
       // whose chain is longer (without it, P is as long as the state waves).
       if constexpr (!GLA) __builtin_amdgcn_s_sleep(8);
-      if (OUT && p >= 0 && p < nch) build_p<GLA, 0, GLA ? PSPLIT : 10>(sm, A, p, lane);
+      if (OUT && p >= 0 && p < nch) build_p<GLA, 0, GLA ? PSPLIT : 10, KB>(sm, A, p, lane);
       lds_barrier();
     }
   } else if (GLA && wave == W_L) {
@@ -1209,8 +1219,8 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
       if (!GLA && p + 2 < nch) {
-        read_frags<GLA>(R, A, p + 2);
-        build_l(sm, R, p + 2, lane);
+        read_frags<GLA, KB>(R, A, p + 2);
+        build_l<KB>(sm, R, p + 2, lane);
       }
       lds_barrier();
     }
@@ -1231,7 +1241,7 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
     const StateAddr A = state_addr(lane, 0, DV);
     lds_barrier();
     for (int64_t p = -2; p <= nch; ++p) {
-      if (p >= 0 && p < nch) build_p<GLA, PSPLIT, 10>(sm, A, p, lane);
+      if (p >= 0 && p < nch) build_p<GLA, PSPLIT, 10, KB>(sm, A, p, lane);
       lds_barrier();
     }
   } else if (wave == W_INV) {

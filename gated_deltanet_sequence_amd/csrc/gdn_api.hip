@@ -57,17 +57,21 @@ int launch_chunk_pipe(const void* q, const void* k, const void* v, const float* 
   // one sequence's q, k or v must fit a 32-bit buffer range
   if (cm.T * dk * 2 > 0x7fffffff || cm.T * dv * 2 > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
   const int xcd_map = (nchain % 8) == 0;
-  // the first launch of the sequence split needs no output
-  if (!GLA && cm.mode == gdn::pipe::MAP_SPLIT_A)
-    hipLaunchKernelGGL((gdn::pipe::chunk_fwd_pipe_kernel<false, false>), dim3((unsigned)nblocks),
-                       dim3(64 * gdn::pipe::NWAVES), 0, stream, static_cast<const bf16_t*>(q),
-                       static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), alpha, beta, s0,
-                       static_cast<bf16_t*>(o), sT, cm, (int)dv, (int)dk, xcd_map);
-  else
-    hipLaunchKernelGGL(gdn::pipe::chunk_fwd_pipe_kernel<GLA>, dim3((unsigned)nblocks), dim3(64 * gdn::pipe::NWAVES),
-                       0, stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                       static_cast<const bf16_t*>(v), alpha, beta, s0, static_cast<bf16_t*>(o), sT, cm,
-                       (int)dv, (int)dk, xcd_map);
+  // the first launch of the sequence split needs no output; with dk = 64
+  // the products over the zero keys 64..127 are skipped (two key blocks)
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)nblocks), dim3(64 * gdn::pipe::NWAVES), 0, stream,
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v),
+                       alpha, beta, s0, static_cast<bf16_t*>(o), sT, cm, (int)dv, (int)dk, xcd_map);
+  };
+  const bool no_out = !GLA && cm.mode == gdn::pipe::MAP_SPLIT_A;
+  if (dk == 64) {
+    if (no_out) launch(gdn::pipe::chunk_fwd_pipe_kernel<false, false, 2>);
+    else launch(gdn::pipe::chunk_fwd_pipe_kernel<GLA, true, 2>);
+  } else {
+    if (no_out) launch(gdn::pipe::chunk_fwd_pipe_kernel<false, false, 4>);
+    else launch(gdn::pipe::chunk_fwd_pipe_kernel<GLA, true, 4>);
+  }
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

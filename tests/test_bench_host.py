@@ -85,7 +85,7 @@ def _write_trace(d, rows):
 def test_trace_summary_groups_by_kernel_and_shape_and_prices_the_main_launches(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     os.makedirs(tmp_path / "profiles")
-    chunk = "void gdn::pipe::chunk_fwd_pipe_kernel<false, true>(unsigned short const*, int)"
+    chunk = "void gdn::pipe::chunk_fwd_pipe_kernel<false, true, 4>(unsigned short const*, int)"
     rows = [(chunk, 256, 512, 300000)] * 50 + [(chunk, 256, 512, 200000)] * 100
     rows += [(chunk, 8, 512, 150000)] * 3
     rows += [("void at::native::copy_kernel(int)", 1024, 256, 5000)] * 2  # not the library's
