@@ -1131,6 +1131,20 @@ __global__ __launch_bounds__(64 * NWAVES) void chunk_fwd_pipe_kernel(
   }
   const int64_t nch = (Tlen + C - 1) / C;
 
+  if constexpr (POISON_LDS) {
+    lds_poison(sm, tid, 64 * NWAVES);
+    if constexpr (GLA) {
+      lds_poison(lds_K, tid, 64 * NWAVES);
+      lds_poison(lds_Q, tid, 64 * NWAVES);
+      lds_poison(lds_gst, tid, 64 * NWAVES);
+    } else {
+      lds_poison(lds_K4, tid, 64 * NWAVES);
+      lds_poison(lds_Q2, tid, 64 * NWAVES);
+    }
+    lds_poison(lds_V, tid, 64 * NWAVES);
+    __syncthreads();
+  }
+
   // Zero P and Ti^T: their blocks above the diagonal are never written but
   // are read as zero by 32-deep products.
   {

@@ -260,6 +260,10 @@ __global__ __launch_bounds__(NT, sizeof(T) == 2 ? 2 : 1) void chunk_vec_kernel(
   T* oc = o + tok0 * DV + slice * DVS;
   const int64_t st_off = (int64_t)slice * DVS * DK;  // this slice's rows within s0 / sT
 
+  if constexpr (POISON_LDS) {
+    lds_poison(sm, tid, NT);
+    __syncthreads();
+  }
   // The upper blocks of the triangular buffers are never written and must
   // read as zero.
   for (int e = tid; e < C * LDC; e += NT) {
@@ -745,6 +749,14 @@ __global__ __launch_bounds__(NT * SL, SL == 1 && sizeof(T) == 2 ? 2 : 1) void ve
   if (chain >= gdn::pipe::map_chains(cm)) return;
   const int slice = sg * SL + h;
   const int64_t dd = (int64_t)DK * DV;
+  if constexpr (POISON_LDS) {
+    lds_poison(recb, tid, NT * SL);
+    lds_poison(Vb, tid, NT * SL);
+    lds_poison(Ssh, tid, NT * SL);
+    lds_poison(Yt, tid, NT * SL);
+    lds_poison(Ut, tid, NT * SL);
+    __syncthreads();
+  }
 
   // this chain's sequence, chunks of the tile, start and end state, and
   // whether it reads V and writes output (cm.mode as for chunk_vec_kernel:

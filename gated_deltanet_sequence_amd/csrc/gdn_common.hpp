@@ -44,6 +44,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Debug build (GDN_POISON_LDS=1, libgdn_debug.so): every kernel first fills
+// its LDS with a NaN pattern (0x7fc0 as bf16, 0x7fc07fc0 as fp32), before
+// its own initialisation, so that a read of LDS that nothing wrote shows up
+// as NaN in the results.  The release build compiles the fills away.
+#ifndef GDN_POISON_LDS
+#define GDN_POISON_LDS 0
+#endif
+constexpr bool POISON_LDS = GDN_POISON_LDS != 0;
+template <class T>
+__device__ __forceinline__ void lds_poison(T& obj, int tid, int nthreads) {
+  if constexpr (POISON_LDS) {
+    static_assert(sizeof(T) % 4 == 0, "LDS objects are whole words");
+    uint32_t* w = reinterpret_cast<uint32_t*>(&obj);
+    for (int i = tid; i < (int)(sizeof(T) / 4); i += nthreads) w[i] = 0x7fc07fc0u;
+  }
+}
+
 template <class T> struct Elem;
 template <> struct Elem<bf16_t> {
   static __device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x); }

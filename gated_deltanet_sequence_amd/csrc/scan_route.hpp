@@ -165,6 +165,16 @@ __global__ __launch_bounds__(THREADS) void scan_tokens_kernel(
   }
   if (seq >= nseq) return;
   const int tid = threadIdx.x, rl = tid / TPR, x = tid % TPR;
+  if constexpr (POISON_LDS) {
+    lds_poison(ks, tid, THREADS);
+    lds_poison(qs, tid, THREADS);
+    lds_poison(vs, tid, THREADS);
+    lds_poison(os, tid, THREADS);
+    lds_poison(as_, tid, THREADS);
+    lds_poison(bs_, tid, THREADS);
+    lds_poison(av, tid, THREADS);
+    __syncthreads();
+  }
   const int row = rg * RPW + rl;
   const int c0 = x * CPT;
   const int64_t t0 = (int64_t)g * L;

@@ -122,6 +122,11 @@ __global__ __launch_bounds__(threads_for<D>()) void split_combine_kernel(const f
   const int r0 = (blockIdx.x % blocks_per_seq) * ROWS;
   if (seq >= nseq) return;
   const int t = threadIdx.x;
+  if constexpr (POISON_LDS) {
+    lds_poison(Ms, t, NT);
+    lds_poison(prevT, t, NT);
+    __syncthreads();
+  }
   const int lane = t % 64;
   const int ib = 4 * (lane / 16), jj = 16 * (t / 64) + lane % 16;
   const int64_t per = (int64_t)nseq * (G - 1);

@@ -38,6 +38,16 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_debug_build_exports_the_same_functions(lib):
+    """libgdn_debug.so (LDS filled with NaN before use, for the GPU check that
+    no kernel reads LDS it did not write) is a separate build of the same
+    sources with the same exports."""
+    debug = binding.load_library(_build.DEBUG_LIB)
+    for n in declared_functions():
+        assert hasattr(debug, n), n
+    assert open(_build.DEBUG_LIB, "rb").read() != open(_build.LIB, "rb").read()
+
+
 def test_strerror_and_version(lib):
     for code in range(0, 5):
         s = binding.strerror(code)
