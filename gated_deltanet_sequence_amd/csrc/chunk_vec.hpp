@@ -922,5 +922,293 @@ __global__ __launch_bounds__(NT * SL, SL == 1 && sizeof(T) == 2 ? 2 : 1) void ve
   }
 }
 
+
+// Second pass for bf16 records, pipelined: one state wave per 16-row value
+// slice (SL slices per workgroup) and one loader wave.  The loader moves each
+// chunk's record and value slices into LDS with LDS-DMA loads, two chunks
+// ahead into three buffers, and waits only for the next chunk, so a period
+// has a single barrier.  A state wave keeps its slice of S^T ([dk][dv], 16
+// columns) in MFMA accumulators and evaluates the chunk in registers, every
+// product a 16x16x32 bf16 MFMA whose 32-deep reduction index runs in the
+// order of two stacked accumulator tiles (row 4g + e of the first tile, then
+// of the second, for lane group g = lane / 16): an accumulator pair is then
+// an operand as it stands, and the LDS operand of the other side is read as
+// two 8-byte halves per lane in the same order.  Per chunk (tokens r, s;
+// slice columns i; key columns j):
+//   Z = K~ S^T            [r][i]   (the state before the chunk)
+//   O^T = S Q~^T          [i][r]
+//   Y = diag(beta) (V - Z)
+//   U = Ti Y              [r][i]
+//   O^T += U^T P^T        [i][r]   -> o, 8 bytes per lane and token
+//   S^T = diag(Ec) S^T + Kbar^T U
+// The operands are rounded to bf16 where the 32-token kernel rounds them (S,
+// Y, U), with fp32 accumulation; only the order of the sums differs.  Chains
+// and the sequence-split modes are those of vec_state_kernel, whose
+// arguments this kernel takes.
+template <int DK, int SL>
+__global__ __launch_bounds__(64 * (SL + 1), 1) void vec_state_pipe_kernel(
+    const bf16_t* __restrict__ v, const char* __restrict__ rec, const float* s0, bf16_t* __restrict__ o,
+    float* sT, int nseq, int64_t Tseq, int64_t c0, int nct, int DV, int xcd_map, gdn::pipe::ChainMap cm) {
+  using namespace gdn::pipe;
+  using R = VecRec<bf16_t, DK>;
+  using Sm = Smem<bf16_t, DK>;
+  constexpr int LDK = Sm::LDK;
+  constexpr int LDC = Sm::LDC;
+  constexpr int KB = DK / 32;        // 32-deep key blocks
+  constexpr int JB = DK / 16;        // 16-row key tiles of S^T
+  constexpr int NREC = R::BYTES / 1024;  // 1 KiB LDS-DMA loads per record
+  constexpr int NLD = NREC + SL;         // loads per chunk (record, value slices)
+  static_assert(R::BYTES % 1024 == 0 && NLD < 64, "record loads and their wait count");
+  // s_waitcnt vmcnt(NLD), other counters not waited for (vmcnt bits [3:0], [15:14])
+  constexpr int WAIT_NEXT = 0x0f70 | (NLD & 15) | ((NLD >> 4) << 14);
+  static_assert(C == 32 && DVS == 16, "two 16-token blocks, 16-column slices");
+
+  __shared__ __attribute__((aligned(1024))) char recb[3][R::BYTES];
+  __shared__ __attribute__((aligned(16))) bf16_t Vb[3][SL][C * DVS];  // [token][column] per slice
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // < SL: state wave of slice `wave`; else loader
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+
+  const int NSG = DV / (DVS * SL);
+  int chain, sg;
+  {
+    const int w = blockIdx.x;
+    if (xcd_map) {
+      const int x = w & 7, r = w >> 3;
+      sg = r % NSG;
+      chain = (r / NSG) * 8 + x;
+    } else {
+      chain = w / NSG;
+      sg = w % NSG;
+    }
+  }
+  if (chain >= map_chains(cm)) return;
+  const int64_t dd = (int64_t)DK * DV;
+  if constexpr (POISON_LDS) {
+    lds_poison(recb, tid, 64 * (SL + 1));
+    lds_poison(Vb, tid, 64 * (SL + 1));
+    __syncthreads();
+  }
+
+  // the chain: as for vec_state_kernel
+  int seq = chain, cf = 0, ncc = nct;
+  bool v_on = true, o_on = true, ident = false;
+  const float* s0c = s0 ? s0 + (int64_t)chain * dd : nullptr;
+  float* sTc = sT ? sT + (int64_t)chain * dd : nullptr;
+  if (cm.mode == MAP_SPLIT_A) {
+    const int per = nseq * (cm.G - 1);
+    const int kind = chain / per, r = chain % per;
+    seq = r / (cm.G - 1);
+    ncc = (int)(cm.L / C);
+    cf = (r % (cm.G - 1)) * ncc;
+    o_on = false;
+    v_on = kind == 0;
+    ident = kind == 1;
+    s0c = nullptr;
+    sTc = cm.ws + ((int64_t)kind * per + r) * dd;
+  } else if (cm.mode == MAP_SPLIT_C) {
+    seq = chain / cm.G;
+    const int g = chain % cm.G;
+    cf = g * (int)(cm.L / C);
+    ncc = g == cm.G - 1 ? nct - cf : (int)(cm.L / C);
+    s0c = cm.ws + (2 * (int64_t)nseq * (cm.G - 1) + (int64_t)seq * cm.G + g) * dd;
+    sTc = g == cm.G - 1 && sT ? sT + (int64_t)seq * dd : nullptr;
+  }
+  const int64_t tok0 = (int64_t)seq * Tseq + (c0 + cf) * C;  // first token of the chain in memory
+  const int64_t Tlen = Tseq - (c0 + cf) * C;                 // tokens of the sequence from there
+  const char* rc = rec + ((int64_t)seq * nct + cf) * R::BYTES;
+
+  // this workgroup's value columns; tokens past the sequence fall outside the
+  // buffer range and read as zeros, as does everything with v_on off
+  const bf16_t* vg = v + tok0 * DV + sg * SL * DVS;
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vg, v_on && Tlen > 0 ? (uint32_t)(Tlen * DV * 2) : 0u);
+  if (wave == SL) {
+    // ---------------------------------------------------------------- loader
+    // value slice s of chunk c: lane i fetches half i % 2 of token i / 2 (a
+    // token's 16 columns are 32 bytes)
+    const uint32_t voff = (uint32_t)((lane >> 1) * DV * 2 + (lane & 1) * 16);
+    auto issue = [&](int c) {
+      const int b = c % 3;
+      const __amdgpu_buffer_rsrc_t rr = make_rsrc(rc + (int64_t)c * R::BYTES, (uint32_t)R::BYTES);
+#pragma unroll
+      for (int n = 0; n < NREC; ++n)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_void*)&recb[b][n * 1024], 16, (uint32_t)(16 * lane),
+                                                 n * 1024, 0, 0);
+      const uint32_t v0 = (uint32_t)(c * C * DV * 2);
+#pragma unroll
+      for (int s = 0; s < SL; ++s)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)&Vb[b][s][0], 16, voff, (int)(v0 + s * DVS * 2), 0,
+                                                 0);
+    };
+    if (ncc > 0) issue(0);
+    if (ncc > 1) {
+      issue(1);
+      __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    }
+    lds_barrier_keep_dma();
+    for (int c = 0; c < ncc; ++c) {
+      // buffer (c + 2) % 3 held chunk c - 1, read before the last barrier
+      if (c + 2 < ncc) {
+        issue(c + 2);
+        __builtin_amdgcn_s_waitcnt(WAIT_NEXT);  // chunk c + 1 has landed
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+      }
+      lds_barrier_keep_dma();
+    }
+    return;
+  }
+
+  // ------------------------------------------------------------ state wave
+  const int slice = sg * SL + wave;
+  const int64_t st_off = (int64_t)slice * DVS * DK;  // this slice's rows within a state
+  bf16_t* oc = o + tok0 * DV + slice * DVS;
+  // Sacc[jb]: S^T tile [j = 16 jb + 4 lg + e][i = lr]
+  f32x4 Sacc[JB];
+#pragma unroll
+  for (int jb = 0; jb < JB; ++jb) {
+    const int j = jb * 16 + 4 * lg;
+    Sacc[jb] = zero4();
+    if (ident) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Sacc[jb][e] = slice * DVS + lr == j + e ? 1.f : 0.f;
+    } else if (s0c) {
+      const float4 s4 = *reinterpret_cast<const float4*>(s0c + st_off + (int64_t)lr * DK + j);
+      Sacc[jb] = f32x4{s4.x, s4.y, s4.z, s4.w};
+    }
+  }
+  lds_barrier_keep_dma();
+
+  // per-lane byte offsets of the two 8-byte halves of a fragment row
+  const int koff = 8 * lg;  // + 32 for the second half
+  for (int c = 0; c < ncc; ++c) {
+    const char* rb_ = recb[c % 3];
+    const lptr Qb = lane_base(rb_ + R::QS, lr * LDK * 2 + koff);
+    const lptr Kb = lane_base(rb_ + R::KR, lr * LDK * 2 + koff);
+    const lptr Bt = lane_base(rb_ + R::KBT, lr * LDC * 2 + koff);
+    const lptr Tb = lane_base(rb_ + R::TI, lr * LDC * 2 + koff);
+    const lptr Pb = lane_base(rb_ + R::PM, lr * LDC * 2 + koff);
+    const char* Ec = rb_ + R::EC;
+    const char* be = rb_ + R::BETA;
+    const bf16_t* Vh = Vb[c % 3][wave];
+
+    // Four phases separated by scheduling fences, so that each phase's LDS
+    // reads are in flight while the previous phase's products run (left to
+    // itself the compiler issues every read just before its use, and the
+    // period then waits for dozens of LDS round trips in a row).
+    // 1: the operands of Z and the decay; S as an operand
+    uint2 kr[2][KB][2];
+    float4 ec[JB];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int pp = 0; pp < KB; ++pp) {
+        const int off = rb * 16 * LDK * 2 + pp * 64;
+        kr[rb][pp][0] = ld3<uint2>(Kb, off);
+        kr[rb][pp][1] = ld3<uint2>(Kb, off + 32);
+      }
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) ec[jb] = lds_at<float4>(Ec, (jb * 16 + 4 * lg) * 4);
+    bf16x8_t Sop[KB];
+#pragma unroll
+    for (int pp = 0; pp < KB; ++pp) Sop[pp] = pack_op(Sacc[2 * pp], Sacc[2 * pp + 1]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2: Z = K~ S^T; the decay diag(Ec) S^T; reads for the output and Y
+    uint2 qs[2][KB][2];
+    float4 b4[2];
+    float vv[2][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int pp = 0; pp < KB; ++pp) {
+        const int off = rb * 16 * LDK * 2 + pp * 64;
+        qs[rb][pp][0] = ld3<uint2>(Qb, off);
+        qs[rb][pp][1] = ld3<uint2>(Qb, off + 32);
+      }
+      const int r0 = rb * 16 + 4 * lg;
+      b4[rb] = lds_at<float4>(be, r0 * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[rb][e] = bf16_to_f32(Vh[(r0 + e) * DVS + lr]);
+    }
+    f32x4 Z[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      Z[rb] = zero4();
+#pragma unroll
+      for (int pp = 0; pp < KB; ++pp) Z[rb] = mfma(as_op(kr[rb][pp][0], kr[rb][pp][1]), Sop[pp], Z[rb]);
+    }
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      Sacc[jb][0] *= ec[jb].x;
+      Sacc[jb][1] *= ec[jb].y;
+      Sacc[jb][2] *= ec[jb].z;
+      Sacc[jb][3] *= ec[jb].w;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3: O^T = S Q~^T; Y = diag(beta) (V - Z), rows r = 16 rb + 4 lg + e;
+    // reads for U, the output and the state update
+    uint2 ti[2][2], pm[2][2], kt[JB][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int off = rb * 16 * LDC * 2;
+      ti[rb][0] = ld3<uint2>(Tb, off);
+      ti[rb][1] = ld3<uint2>(Tb, off + 32);
+      pm[rb][0] = ld3<uint2>(Pb, off);
+      pm[rb][1] = ld3<uint2>(Pb, off + 32);
+    }
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      const int off = jb * 16 * LDC * 2;
+      kt[jb][0] = ld3<uint2>(Bt, off);
+      kt[jb][1] = ld3<uint2>(Bt, off + 32);
+    }
+    f32x4 O[2], Y[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      O[rb] = zero4();
+#pragma unroll
+      for (int pp = 0; pp < KB; ++pp) O[rb] = mfma(Sop[pp], as_op(qs[rb][pp][0], qs[rb][pp][1]), O[rb]);
+      const float bb[4] = {b4[rb].x, b4[rb].y, b4[rb].z, b4[rb].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Y[rb][e] = bb[e] * (vv[rb][e] - Z[rb][e]);
+    }
+    const bf16x8_t Yop = pack_op(Y[0], Y[1]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 4: U = Ti Y; O^T += U^T P^T and o (token 16 rb + lr, columns 4 lg ..
+    // 4 lg + 3); S^T += Kbar^T U
+    f32x4 U[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) U[rb] = mfma(as_op(ti[rb][0], ti[rb][1]), Yop, zero4());
+    const bf16x8_t Uop = pack_op(U[0], U[1]);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) O[rb] = mfma(Uop, as_op(pm[rb][0], pm[rb][1]), O[rb]);
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) Sacc[jb] = mfma(as_op(kt[jb][0], kt[jb][1]), Uop, Sacc[jb]);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int64_t tk = (int64_t)c * C + rb * 16 + lr;
+      if (o_on && tk < Tlen) store4<bf16_t>(oc + tk * DV + 4 * lg, O[rb][0], O[rb][1], O[rb][2], O[rb][3]);
+    }
+    lds_barrier_keep_dma();
+  }
+
+  if (sTc) {
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      const int j = jb * 16 + 4 * lg;
+      *reinterpret_cast<float4*>(sTc + st_off + (int64_t)lr * DK + j) =
+          make_float4(Sacc[jb][0], Sacc[jb][1], Sacc[jb][2], Sacc[jb][3]);
+    }
+  }
+}
+
 }  // namespace vec
 }  // namespace gdn

@@ -453,16 +453,70 @@ int vec2p_prep(const void* q, const void* k, const void* v, const float* alpha, 
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
-// The second pass over the chains of cm (cm.nseq = the sequences) with sl
-// value slices per workgroup.
+// Resident workgroups per CU of a kernel at `threads` threads (0 when the
+// runtime cannot tell).
+int occupancy(const void* kern, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    n = 0;
+  }
+  return n;
+}
+// The pipelined second pass for bf16 records with SL value slices per
+// workgroup (SL state waves and a loader wave).
+template <int DK, int SL>
+const void* vec_pipe_kernel() {
+  return reinterpret_cast<const void*>(&gdn::vec::vec_state_pipe_kernel<DK, SL>);
+}
+template <int DK, int SL>
+int vec_pipe_occupancy() {
+  static const int n = occupancy(vec_pipe_kernel<DK, SL>(), 64 * (SL + 1));
+  return n;
+}
+// Value slices per workgroup of the pipelined second pass over nchain chains
+// of ns slices: the fewest (1, 2 or 4) with which every workgroup is resident
+// at once; else 4, which shares each record among the most slices.
+template <int DK>
+int vec_pipe_slices(int64_t nchain, int64_t ns) {
+  const int ncu = device_cus();
+  if (ncu > 0) {
+    if (nchain * ns <= (int64_t)vec_pipe_occupancy<DK, 1>() * ncu) return 1;
+    if (ns % 2 == 0 && nchain * (ns / 2) <= (int64_t)vec_pipe_occupancy<DK, 2>() * ncu) return 2;
+  }
+  return ns % 4 == 0 ? 4 : ns % 2 == 0 ? 2 : 1;
+}
+
+// The second pass over the chains of cm (cm.nseq = the sequences): bf16
+// records go to the pipelined kernel (its slices per workgroup chosen here),
+// fp32 records to vec_state_kernel with sl value slices per workgroup.
 template <class T, int DK>
 int vec2p_state(int sl, const void* v, const char* rec, const float* in, void* o, float* out, int64_t nseq,
                 int64_t Tseq, int64_t c0, int64_t n, int64_t dv, const gdn::pipe::ChainMap& cm,
                 hipStream_t stream) {
   const int64_t nchain = gdn::pipe::map_chains(cm);
+  const int xcd_map = (nchain % 8) == 0;
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    const int64_t ns = dv / gdn::vec::DVS;
+    const int spw = vec_pipe_slices<DK>(nchain, ns);
+    const int64_t nblocks = nchain * (ns / spw);
+    if (nblocks > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
+    auto launch = [&](auto slc) {
+      constexpr int S = decltype(slc)::value;
+      hipLaunchKernelGGL((gdn::vec::vec_state_pipe_kernel<DK, S>), dim3((unsigned)nblocks), dim3(64 * (S + 1)), 0,
+                         stream, static_cast<const bf16_t*>(v), rec, in, static_cast<bf16_t*>(o), out, (int)nseq,
+                         Tseq, c0, (int)n, (int)dv, xcd_map, cm);
+    };
+    if (spw == 4)
+      launch(std::integral_constant<int, 4>{});
+    else if (spw == 2)
+      launch(std::integral_constant<int, 2>{});
+    else
+      launch(std::integral_constant<int, 1>{});
+    return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+  }
   const int64_t nblocks = nchain * (dv / (gdn::vec::DVS * sl));
   if (nblocks > 0x7fffffff) return GDN_ERR_UNSUPPORTED;
-  const int xcd_map = (nchain % 8) == 0;
   if (sl == 2)
     hipLaunchKernelGGL((gdn::vec::vec_state_kernel<T, DK, 2>), dim3((unsigned)nblocks), dim3(gdn::vec::NT * 2), 0,
                        stream, static_cast<const T*>(v), rec, in, static_cast<T*>(o), out, (int)nseq, Tseq, c0,
@@ -488,14 +542,9 @@ void vec2p_split_plan(int64_t nseq, int64_t T, int64_t dk, int64_t dv, gdn_dtype
   const int ncu = device_cus();
   if (ncu <= 0) return;
   const int per_cu = vec_dispatch<true>(dtype, dk, [&](auto t, auto dkc) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(&gdn::vec::vec_state_kernel<decltype(t), decltype(dkc)::value, 1>),
-            gdn::vec::NT, 0) != hipSuccess) {
-      (void)hipGetLastError();
-      n = 0;
-    }
-    return n;
+    constexpr int DK = decltype(dkc)::value;
+    if constexpr (std::is_same<decltype(t), bf16_t>::value) return vec_pipe_occupancy<DK, 1>();
+    return occupancy(reinterpret_cast<const void*>(&gdn::vec::vec_state_kernel<decltype(t), DK, 1>), gdn::vec::NT);
   });
   if (per_cu <= 0) return;
   const int64_t ns = dv / gdn::vec::DVS;

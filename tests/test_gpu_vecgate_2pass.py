@@ -1,11 +1,13 @@
 """GPU parity of the two-pass chunked route with a per-dimension gate
 (gdn_chunk_fwd_vecgate_2pass) against the fp64 oracle (oracle_fwd_vecgate),
 with the workloads' bars (2e-2 bf16, 1e-4 fp32, max-abs-normwise on o and
-the final state).  Without a sequence split the two passes compute the same
-products in the same order as the single-pass route, so they also match it
-bit for bit, and the tile length (set by the workspace size) does not change
-the result.  With few sequences the route splits them into segments (when
-the workspace holds the split), which changes the rounding only."""
+the final state).  fp32 records are walked by the 32-token kernel's own
+products in the same order as the single-pass route, so fp32 results match it
+bit for bit; bf16 records are walked by the pipelined second pass, whose
+MFMA sums run in another order, so bf16 results match it within the bar.  The
+tile length (set by the workspace size) does not change the result.  With few
+sequences the route splits them into segments (when the workspace holds the
+split), which changes the rounding only."""
 import numpy as np
 import pytest
 import torch
@@ -94,7 +96,10 @@ def test_2pass_against_oracle_and_single_pass(case):
         assert np.all(np.isfinite(to_np(o))) and np.all(np.isfinite(to_np(sT)))
         assert eo <= TOL[dtype] and es <= TOL[dtype]
         if not (split and ws is None):
-            assert torch.equal(o, o1) and torch.equal(sT, s1)
+            if dtype == "f32":
+                assert torch.equal(o, o1) and torch.equal(sT, s1)
+            else:
+                assert maxrel(to_np(o), to_np(o1)) <= TOL[dtype] and maxrel(to_np(sT), to_np(s1)) <= TOL[dtype]
 
 
 def test_2pass_tile_length_does_not_change_the_result():
@@ -118,8 +123,9 @@ def test_2pass_tile_length_does_not_change_the_result():
 
 def test_2pass_main_shape_matches_single_pass():
     """The main workload's shape (B=4, H=16, T=8192, d=128, bf16, per-dimension
-    default gate): bit for bit the single-pass route, which is checked against
-    the oracle on every output by the single-pass suite."""
+    default gate): the single-pass route, which is checked against the oracle
+    on every output by the single-pass suite, within the bf16 bar (the
+    pipelined second pass sums in another order)."""
     B, H, T, d = 4, 16, 8192, 128
     print("case vecgate 2pass main shape", flush=True)
     x = inputs.make_fwd_inputs(B, H, T, d, "bf16", seed=3)
@@ -128,7 +134,13 @@ def test_2pass_main_shape_matches_single_pass():
     o, sT = _run2(xd)
     o1, s1 = gdn_chunk_fwd_vecgate(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], xd["s0"])
     torch.cuda.synchronize()
-    assert torch.equal(o, o1) and torch.equal(sT, s1)
+    # max-abs-normwise, on the GPU (2^28 outputs)
+    def rel(a, b):
+        return float((a.float() - b.float()).abs().max() / b.float().abs().max())
+
+    eo, es = rel(o, o1), rel(sT, s1)
+    print("  two-pass vs single-pass: o %.3e  S_T %.3e" % (eo, es), flush=True)
+    assert bool(torch.isfinite(o).all()) and eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
 def test_2pass_aliasing_and_errors():
