@@ -36,6 +36,11 @@ CASES = [
     # of the second pass
     (8, 8, 100, 128, True, "default", "bf16"),
     (8, 16, 70, 64, True, "resets", "bf16"),
+    # more slices than the device holds at two per workgroup: four value
+    # slices per workgroup of the bf16 second pass (128 sequences at d = 128,
+    # 512 at d = 64 on a 256-CU device)
+    (8, 16, 100, 128, True, "slow", "bf16"),
+    (16, 32, 40, 64, False, "fast", "bf16"),
     (8, 8, 40, 128, True, "default", "f32"),
     (1, 1, 50, 64, True, "default", "f32"),
     (2, 1, 2100, 128, False, "default", "f32"),
