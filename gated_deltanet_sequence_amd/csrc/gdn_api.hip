@@ -543,7 +543,9 @@ void vec2p_split_plan(int64_t nseq, int64_t T, int64_t dk, int64_t dv, gdn_dtype
   if (ncu <= 0) return;
   const int per_cu = vec_dispatch<true>(dtype, dk, [&](auto t, auto dkc) {
     constexpr int DK = decltype(dkc)::value;
-    if constexpr (std::is_same<decltype(t), bf16_t>::value) return vec_pipe_occupancy<DK, 1>();
+    // bf16: chains x slices resident at four slices per workgroup (the
+    // second pass's slice count adapts to its launch)
+    if constexpr (std::is_same<decltype(t), bf16_t>::value) return 4 * vec_pipe_occupancy<DK, 4>();
     return occupancy(reinterpret_cast<const void*>(&gdn::vec::vec_state_kernel<decltype(t), DK, 1>), gdn::vec::NT);
   });
   if (per_cu <= 0) return;
