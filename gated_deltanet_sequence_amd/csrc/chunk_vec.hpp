@@ -50,7 +50,10 @@
 // 64-token chunk's fp32 buffers would exceed the LDS at d_k = 128).  The GLA
 // instance evaluates gated linear attention without the delta rule (L = 0,
 // U = diag(beta) V), and the PREP instance is the first pass of the two-pass
-// route (the chunk records, no state).
+// route (the chunk records, no state).  The second pass of that route walks
+// the records: vec_state_kernel (four waves per slice, three barriers per
+// chunk; fp32 records) and vec_state_pipe_kernel (one wave per slice and a
+// loader wave, one barrier per chunk; bf16 records).
 #pragma once
 
 #include "gdn_common.hpp"
