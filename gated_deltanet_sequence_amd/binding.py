@@ -281,8 +281,9 @@ def gdn_chunk_fwd_vecgate_2pass(q, k, v, alpha, beta, initial_state=None, chunk_
                                 workspace=None, stream=None):
     """gdn_chunk_fwd_vecgate in two passes (the state-independent chunk work
     once per chunk, into workspace records; then the state products per value
-    slice).  Same arguments and result; the workspace (a uint8 GPU tensor) is
-    allocated here when not given."""
+    slice).  Same arguments and result (for bf16 up to the order of the
+    products' fp32 sums); the workspace (a uint8 GPU tensor) is allocated here
+    when not given."""
     B, H, T, dk, dv = _check_fwd_args(q, k, v, alpha, beta, initial_state, alpha_per_dim=True)
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)

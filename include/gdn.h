@@ -235,9 +235,10 @@ size_t gdn_chunk_fwd_vecgate_split_workspace(int64_t B, int64_t H, int64_t T, in
                                              int64_t dv, int64_t chunk_size, gdn_dtype dtype);
 
 /*
- * gdn_chunk_fwd_vecgate_2pass — the same result as gdn_chunk_fwd_vecgate
- * ([P1] §2.2 per-dimension gate, §3.2 chunked evaluation), in two passes
- * over tiles of at most 256 chunks (8192 tokens) per sequence:
+ * gdn_chunk_fwd_vecgate_2pass — the result of gdn_chunk_fwd_vecgate
+ * ([P1] §2.2 per-dimension gate, §3.2 chunked evaluation; bit for bit for
+ * fp32, up to the order of the bf16 products' fp32 sums for bf16), in two
+ * passes over tiles of at most 256 chunks (8192 tokens) per sequence:
  *   1. per chunk, once: the gate prefix, the scaled operand copies of q and
  *      k, L, (I+L)^-1 and P, written to a record in the workspace;
  *   2. per 16-row value slice: the state-dependent products of every chunk
